@@ -1,0 +1,161 @@
+"""CPU oracle for the HiSparse hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, the package's ``smoke()`` check and the benchmark's
+``cpu_baseline`` leg may import this package.  The device library never loads
+it, and it shares no code with the device library.
+
+``hs_oracle.c`` is the plain C oracle (literal LRU resolve with qsort, fp64
+attention); :mod:`oracle.naive` is a second, pure-Python restatement used to pin
+it.  This module is the ctypes loader plus a small stateful wrapper,
+:class:`OracleCache`, that holds one state per (request, layer) exactly as the
+method defines it: page table, slot owner map, recency stamps, step counter and
+(optionally) the bytes of the device slots.
+
+Pinned by tests/test_oracle_pins.py (closed forms, brute force over
+presentation orders, a textbook LRU for k = 1, torch fp64 attention, the
+torch E4M3FN decode table, and the exactness property of the paper abstract).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from functools import lru_cache
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "liboracle.so")
+_SRC = os.path.join(_HERE, "hs_oracle.c")
+
+OK, BAD_TOKEN, DUPLICATE, NO_ROOM, NOMEM = 0, -1, -2, -3, -4
+ENTRY_BYTES = {0: 1152, 1: 656}
+
+
+class OracleError(ValueError):
+    pass
+
+
+def build(force: bool = True) -> str:
+    if force or not os.path.exists(_SO):
+        tmp = _SO + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+@lru_cache(maxsize=1)
+def lib():
+    if not os.path.exists(_SO):
+        build(force=False)
+    L = ctypes.CDLL(_SO)
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    L.orc_resolve.restype = ctypes.c_int
+    L.orc_resolve.argtypes = [i64, i64, i64, p, p, p, i64, p, p, p, p, p, i64]
+    L.orc_resolve_batch.restype = ctypes.c_int
+    L.orc_resolve_batch.argtypes = [i64, i64, i64, i64, p, p, p, p, p, p, p, p, p, i64, ctypes.c_int]
+    L.orc_e4m3_decode.restype = ctypes.c_double
+    L.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+    L.orc_attend.restype = ctypes.c_int
+    L.orc_attend.argtypes = [i64, ctypes.c_int, i64, p, p, p, i64, ctypes.c_double, p, p]
+    L.orc_attend_batch.restype = ctypes.c_int
+    L.orc_attend_batch.argtypes = [i64, i64, ctypes.c_int, i64, p, p, p, i64, i64, ctypes.c_double, p, p,
+                                   ctypes.c_int]
+    return L
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def e4m3_decode(code: int) -> float:
+    return lib().orc_e4m3_decode(code)
+
+
+def default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+class OracleCache:
+    """Per-(request, layer) cache states, resolved and attended by the C oracle.
+
+    host: optional [n][L][cap][E] uint8 array holding each request's full KV
+    history; when given, the oracle also keeps the device-slot bytes
+    ``dev[n][L][B][E]`` and fills them on every miss.
+    """
+
+    def __init__(self, n: int, L: int, B: int, cap: int, layout: int = 0, host: np.ndarray | None = None,
+                 threads: int | None = None):
+        if B <= 0 or cap <= 0 or n <= 0 or L <= 0:
+            raise OracleError("bad shape")
+        self.n, self.L, self.B, self.cap, self.layout = n, L, B, cap, layout
+        self.E = ENTRY_BYTES[layout]
+        self.PT = np.full((n, L, cap), -1, dtype=np.int32)
+        self.RM = np.full((n, L, B), -1, dtype=np.int32)
+        self.ST = np.full((n, L, B), -1, dtype=np.int64)
+        self.t = np.zeros((n, L), dtype=np.int64)
+        self.host = host
+        if host is not None:
+            assert host.shape == (n, L, cap, self.E) and host.dtype == np.uint8 and host.flags.c_contiguous
+            self.dev = np.zeros((n, L, B, self.E), dtype=np.uint8)
+        else:
+            self.dev = None
+        self.threads = threads or default_threads()
+
+    def resolve(self, layer: int, S: np.ndarray, requests: int | None = None):
+        """Resolve S[n_req][k] for layer ``layer``; returns (slots[n_req][k] int32, miss[n_req] int64)."""
+        S = np.ascontiguousarray(S, dtype=np.int32)
+        nr = S.shape[0] if requests is None else requests
+        k = S.shape[1]
+        slots = np.empty((nr, k), dtype=np.int32)
+        miss = np.empty(nr, dtype=np.int64)
+        PT = np.ascontiguousarray(self.PT[:nr, layer])
+        RM = np.ascontiguousarray(self.RM[:nr, layer])
+        ST = np.ascontiguousarray(self.ST[:nr, layer])
+        t = np.ascontiguousarray(self.t[:nr, layer])
+        dev = host = None
+        if self.dev is not None:
+            dev = np.ascontiguousarray(self.dev[:nr, layer])
+            host = np.ascontiguousarray(self.host[:nr, layer])
+        rc = lib().orc_resolve_batch(nr, self.B, self.cap, k, _ptr(PT), _ptr(RM), _ptr(ST), _ptr(t), _ptr(S),
+                                     _ptr(slots), _ptr(miss), _ptr(dev), _ptr(host), self.E, self.threads)
+        if rc != OK:
+            raise OracleError(f"invalid selection (code {rc})")
+        self.PT[:nr, layer] = PT
+        self.RM[:nr, layer] = RM
+        self.ST[:nr, layer] = ST
+        if dev is not None:
+            self.dev[:nr, layer] = dev
+        self.t[:nr, layer] += 1
+        return slots, miss
+
+    def attend(self, layer: int, q: np.ndarray, slots: np.ndarray, scale: float):
+        """q[n_req][H][576] bf16 bits (uint16) -> (out[n_req][H][512] f64, lse[n_req][H] f64)."""
+        if self.dev is None:
+            raise OracleError("attention needs the slot bytes (construct with host=...)")
+        q = np.ascontiguousarray(q, dtype=np.uint16)
+        slots = np.ascontiguousarray(slots, dtype=np.int32)
+        nr, H = q.shape[0], q.shape[1]
+        dev = np.ascontiguousarray(self.dev[:nr, layer])
+        return attend_rows(q, slots, dev, self.layout, scale, self.threads)
+
+
+def attend_rows(q: np.ndarray, idx: np.ndarray, rows: np.ndarray, layout: int, scale: float,
+                threads: int | None = None):
+    """Attention of q[n][H][576] over rows[n][R][E] picked by idx[n][k] (-1 skipped), fp64."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.uint8)
+    n, H = q.shape[0], q.shape[1]
+    k = idx.shape[1]
+    E = rows.shape[-1]
+    if idx.size and int(idx.max()) >= rows.shape[1]:
+        raise OracleError("row index out of range")
+    out = np.empty((n, H, 512), dtype=np.float64)
+    lse = np.empty((n, H), dtype=np.float64)
+    rc = lib().orc_attend_batch(n, k, layout, H, _ptr(q), _ptr(idx), _ptr(rows), rows.shape[1] * E, E, scale,
+                                _ptr(out), _ptr(lse), threads or default_threads())
+    if rc != OK:
+        raise OracleError(f"attention failed (code {rc})")
+    return out, lse

@@ -1,0 +1,67 @@
+"""Second, pure-Python statement of the resolver -- TEST INFRASTRUCTURE ONLY.
+
+Written independently of ``hs_oracle.c`` to pin it: instead of sorting the
+candidate slots once, every missing token (taken in ascending token order)
+scans all slots and takes the least recently used one, (stamp, slot index)
+smallest, among those that hold no hit and were not already taken in this
+step; then every selected token's slot is stamped with the step.  This is the
+HiSparse replacement step ("HiSparse" note, section 2: a miss is swapped in
+from host memory and the eviction candidate is chosen by LRU; paper abstract:
+hit detection, LRU replacement, host-to-device fetch), with the tie rules
+stated in ``hs_oracle.c``.
+
+Small inputs only (O(misses x B) per step in Python).
+"""
+from __future__ import annotations
+
+
+class NaiveState:
+    def __init__(self, B: int, cap: int):
+        self.B, self.cap = B, cap
+        self.pt = {}                  # token -> slot (absent = not resident)
+        self.owner = [None] * B       # slot -> token
+        self.stamp = [-1] * B
+        self.t = 0
+        self.rows = [None] * B        # what each slot holds (a token's row, by value)
+
+    def resolve(self, S, host_row=None):
+        valid = [s for s in S if s != -1]
+        if any(not (0 <= s < self.cap) for s in valid):
+            raise ValueError("token out of range")
+        if len(set(valid)) != len(valid):
+            raise ValueError("duplicate token")
+        hit_slots = {self.pt[s] for s in valid if s in self.pt}
+        misses = sorted(s for s in valid if s not in self.pt)
+        taken = set()
+        for s in misses:
+            best = None
+            for j in range(self.B):
+                if j in hit_slots or j in taken:
+                    continue
+                key = (self.stamp[j], j)
+                if best is None or key < best[0]:
+                    best = (key, j)
+            if best is None:
+                raise ValueError("no free slot")
+            j = best[1]
+            taken.add(j)
+            old = self.owner[j]
+            if old is not None:
+                del self.pt[old]
+            self.pt[s] = j
+            self.owner[j] = s
+            if host_row is not None:
+                self.rows[j] = host_row(s)
+        for s in valid:
+            self.stamp[self.pt[s]] = self.t
+        self.t += 1
+        slots = [(-1 if s == -1 else self.pt[s]) for s in S]
+        return slots, len(misses)
+
+    def arrays(self):
+        """(PT[cap], RM[B], ST[B]) as plain lists with -1 for absent."""
+        PT = [-1] * self.cap
+        for s, j in self.pt.items():
+            PT[s] = j
+        RM = [(-1 if o is None else o) for o in self.owner]
+        return PT, RM, list(self.stamp)
