@@ -1,0 +1,240 @@
+"""MI355X-native HiSparse hot path: Python binding of libhs.so (include/hs.h).
+
+Argument marshalling only.  Every step of the path -- hit detection, LRU
+replacement, page-table update, host-to-device fetch, sparse MLA attention --
+runs in the library's HIP kernels.  PyTorch supplies device memory (the
+library's device block is a torch allocation) and streams.  There is no CPU
+fallback: if libhs.so is missing the import fails.
+
+    hs = HiSparse(top_k=2048, device_buffer_size=4096, host_to_device_ratio=8,
+                  max_requests=64, num_layers=1, layout=LAYOUT_BF16)
+    hs.host_kv(layer, request)[:] = rows           # pinned host history
+    slots, miss = hs.resolve(layer, sel)           # sel: int32 cuda [n_req][top_k]
+    out, lse = hs.attend(layer, q, slots, scale)   # q: bf16 cuda [n_req][H][576]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhs.so")
+
+LAYOUT_BF16 = 0      # HS_KV_BF16_576
+LAYOUT_FP8 = 1       # HS_KV_FP8_MLA_656
+ENTRY_BYTES = {LAYOUT_BF16: 1152, LAYOUT_FP8: 656}
+FLAG_NO_IO = 0x1
+DEVERR_TOKEN_RANGE = 0x1
+DEVERR_DUPLICATE = 0x2
+
+HS_OK, HS_ERR_INVALID_ARG, HS_ERR_OUT_OF_MEMORY, HS_ERR_UNSUPPORTED, HS_ERR_HIP, HS_ERR_DEVICE = range(6)
+
+SYMBOLS = ("hs_create", "hs_resolve", "hs_attend", "hs_destroy", "hs_device_bytes", "hs_host_bytes", "hs_host_kv",
+           "hs_device_state", "hs_reset_requests", "hs_get_device_error", "hs_status_string",
+           "hs_last_error_message")
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("top_k", ctypes.c_int32), ("device_buffer_size", ctypes.c_int32),
+                ("host_to_device_ratio", ctypes.c_int32), ("max_requests", ctypes.c_int32),
+                ("num_layers", ctypes.c_int32), ("layout", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("flags", ctypes.c_uint32), ("device_mem", ctypes.c_void_p), ("device_mem_bytes", ctypes.c_size_t)]
+
+
+class StateView(ctypes.Structure):
+    _fields_ = [("page_table", ctypes.c_void_p), ("slot_owner", ctypes.c_void_p), ("slot_stamp", ctypes.c_void_p),
+                ("lru_order", ctypes.c_void_p), ("step", ctypes.c_void_p), ("kv_buffer", ctypes.c_void_p),
+                ("capacity", ctypes.c_int64), ("slot_stride", ctypes.c_int64), ("entry_bytes", ctypes.c_int64)]
+
+
+class HSError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+_lib_cache = None
+
+
+def lib():
+    """The loaded libhs.so; raises if it has not been built (no fallback)."""
+    global _lib_cache
+    if _lib_cache is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m hierarchical_kv_cache_hs_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i32 = ctypes.c_void_p, ctypes.c_int32
+        L.hs_device_bytes.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_size_t)]
+        L.hs_host_bytes.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_size_t)]
+        L.hs_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(p)]
+        L.hs_resolve.argtypes = [p, i32, i32, p, p, p, p]
+        L.hs_attend.argtypes = [p, i32, i32, p, p, ctypes.c_float, p, p, p]
+        L.hs_destroy.argtypes = [p]
+        L.hs_host_kv.argtypes = [p, i32, i32, ctypes.POINTER(p), ctypes.POINTER(ctypes.c_int64),
+                                 ctypes.POINTER(ctypes.c_int64)]
+        L.hs_device_state.argtypes = [p, i32, ctypes.POINTER(StateView)]
+        L.hs_reset_requests.argtypes = [p, i32, i32, p]
+        L.hs_get_device_error.argtypes = [p, ctypes.POINTER(ctypes.c_int32)]
+        L.hs_status_string.argtypes = [ctypes.c_int]
+        L.hs_status_string.restype = ctypes.c_char_p
+        L.hs_last_error_message.argtypes = []
+        L.hs_last_error_message.restype = ctypes.c_char_p
+        for name in ("hs_device_bytes", "hs_host_bytes", "hs_create", "hs_resolve", "hs_attend", "hs_destroy",
+                     "hs_host_kv", "hs_device_state", "hs_reset_requests", "hs_get_device_error"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib_cache = L
+    return _lib_cache
+
+
+def _check(status: int):
+    if status != HS_OK:
+        raise HSError(status, lib().hs_last_error_message().decode())
+
+
+def make_config(top_k, device_buffer_size, host_to_device_ratio, max_requests, num_layers=1, layout=LAYOUT_BF16,
+                num_heads=0, flags=0) -> Config:
+    return Config(top_k, device_buffer_size, host_to_device_ratio, max_requests, num_layers, layout, num_heads,
+                  flags, None, 0)
+
+
+def device_bytes(cfg: Config) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().hs_device_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def host_bytes(cfg: Config) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().hs_host_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def _stream_ptr(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+class HiSparse:
+    """One handle: per-(request, layer) page tables, LRU state, device slots and pinned host history."""
+
+    def __init__(self, top_k: int, device_buffer_size: int, host_to_device_ratio: int, max_requests: int,
+                 num_layers: int = 1, layout: int = LAYOUT_BF16, num_heads: int = 0, flags: int = 0,
+                 device: str | torch.device = "cuda"):
+        self.cfg = make_config(top_k, device_buffer_size, host_to_device_ratio, max_requests, num_layers, layout,
+                               num_heads, flags)
+        nbytes = device_bytes(self.cfg)
+        self.device = torch.device(device)
+        # torch owns the device block; the library lays its tables out inside it
+        self.block = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+        torch.cuda.synchronize(self.device)  # the fill must land before the library initialises its tables
+        self.cfg.device_mem = self.block.data_ptr()
+        self.cfg.device_mem_bytes = nbytes
+        h = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            _check(lib().hs_create(ctypes.byref(self.cfg), ctypes.byref(h)))
+        self._h = h
+        self.top_k, self.B, self.n, self.L = top_k, device_buffer_size, max_requests, num_layers
+        self.layout, self.heads = layout, num_heads
+        self.entry_bytes = ENTRY_BYTES[layout]
+        self.capacity = host_to_device_ratio * device_buffer_size
+
+    # -- lifetime ------------------------------------------------------------------------------
+    def close(self):
+        if self._h is not None and self._h.value:
+            _check(lib().hs_destroy(self._h))
+        self._h = None
+        self.block = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    @property
+    def handle(self) -> int:
+        return self._h.value
+
+    # -- host pool -----------------------------------------------------------------------------
+    def host_kv(self, layer: int, request: int) -> np.ndarray:
+        """[capacity][entry_bytes] uint8 view of the pinned host rows of (layer, request)."""
+        ptr = ctypes.c_void_p()
+        cap = ctypes.c_int64()
+        stride = ctypes.c_int64()
+        _check(lib().hs_host_kv(self._h, layer, request, ctypes.byref(ptr), ctypes.byref(cap), ctypes.byref(stride)))
+        buf = (ctypes.c_uint8 * (cap.value * stride.value)).from_address(ptr.value)
+        return np.frombuffer(buf, dtype=np.uint8).reshape(cap.value, stride.value)[:, : self.entry_bytes]
+
+    def host_kv_ptr(self, layer: int, request: int) -> tuple[int, int, int]:
+        ptr = ctypes.c_void_p()
+        cap = ctypes.c_int64()
+        stride = ctypes.c_int64()
+        _check(lib().hs_host_kv(self._h, layer, request, ctypes.byref(ptr), ctypes.byref(cap), ctypes.byref(stride)))
+        return ptr.value, cap.value, stride.value
+
+    # -- hot path ------------------------------------------------------------------------------
+    def resolve(self, layer: int, sel: torch.Tensor, slots: torch.Tensor | None = None,
+                miss: torch.Tensor | None = None, stream=None):
+        n_req = sel.shape[0]
+        assert sel.dtype == torch.int32 and sel.is_contiguous() and sel.shape[1] == self.top_k
+        if slots is None:
+            slots = torch.empty_like(sel)
+        if miss is None:
+            miss = torch.empty(n_req, dtype=torch.int32, device=sel.device)
+        assert slots.shape == sel.shape and slots.dtype == torch.int32 and slots.is_contiguous()
+        _check(lib().hs_resolve(self._h, layer, n_req, sel.data_ptr(), slots.data_ptr(), miss.data_ptr(),
+                                _stream_ptr(stream)))
+        return slots, miss
+
+    def attend(self, layer: int, q: torch.Tensor, slots: torch.Tensor, scale: float,
+               out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream=None):
+        n_req = q.shape[0]
+        assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.shape[2] == 576
+        assert slots.dtype == torch.int32 and slots.is_contiguous() and slots.shape == (n_req, self.top_k)
+        if out is None:
+            out = torch.empty(n_req, q.shape[1], 512, dtype=torch.bfloat16, device=q.device)
+        if lse is None:
+            lse = torch.empty(n_req, q.shape[1], dtype=torch.float32, device=q.device)
+        _check(lib().hs_attend(self._h, layer, n_req, q.data_ptr(), slots.data_ptr(), float(scale), out.data_ptr(),
+                               lse.data_ptr(), _stream_ptr(stream)))
+        return out, lse
+
+    # -- state -----------------------------------------------------------------------------------
+    def state(self, layer: int) -> dict:
+        """Torch views (no copies) of one layer's device tables and slot buffer."""
+        v = StateView()
+        _check(lib().hs_device_state(self._h, layer, ctypes.byref(v)))
+        base = self.block.data_ptr()
+
+        def view(ptr, count, dtype, shape):
+            off = ptr - base
+            esz = torch.empty(0, dtype=dtype).element_size()
+            return self.block[off: off + count * esz].view(dtype).view(*shape)
+
+        n, B, cap = self.n, self.B, v.capacity
+        return {
+            "page_table": view(v.page_table, n * cap, torch.int32, (n, cap)),
+            "slot_owner": view(v.slot_owner, n * B, torch.int32, (n, B)),
+            "slot_stamp": view(v.slot_stamp, n * B, torch.int32, (n, B)),
+            "lru_order": view(v.lru_order, n * B, torch.int32, (n, B)),
+            "step": view(v.step, n, torch.int32, (n,)),
+            "kv_buffer": view(v.kv_buffer, n * B * v.slot_stride, torch.uint8, (n, B, v.slot_stride)),
+            "entry_bytes": v.entry_bytes,
+        }
+
+    def reset_requests(self, first: int, count: int, stream=None):
+        _check(lib().hs_reset_requests(self._h, first, count, _stream_ptr(stream)))
+
+    def device_error(self) -> int:
+        bits = ctypes.c_int32(0)
+        _check(lib().hs_get_device_error(self._h, ctypes.byref(bits)))
+        return bits.value

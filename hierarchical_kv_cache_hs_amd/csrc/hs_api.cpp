@@ -1,0 +1,345 @@
+// Host side of the C ABI in include/hs.h: configuration checks, the pinned host pool,
+// the device block (tables + slot buffer + attention partials) and kernel launches.
+//
+// Device block layout (each part 256-byte aligned), per layer l and request r:
+//   err                        int32 error word
+//   pt    [L][n][cap]          token -> slot
+//   rm    [L][n][B]            slot -> token
+//   st    [L][n][B]            slot stamp
+//   ord   [L][n][B]            slots in (stamp, slot) order
+//   step  [L][n]               resolves done
+//   cnt   [L][n]               attention split arrival counters
+//   part  [L][n][...]          attention split partials (if num_heads > 0)
+//   buf   [L][n][B][stride]    KV rows of the slots (stride = entry bytes rounded up to 128)
+// Host pool (pinned, mapped): [L][n][cap][entry bytes].
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "hs_internal.h"
+
+struct hs_handle {
+  hs::Geometry g;
+  int device = 0;
+  uint8_t* dev_block = nullptr;
+  bool own_dev = false;
+  size_t dev_bytes = 0;
+  uint8_t* host_pool = nullptr;      // host address
+  uint8_t* host_pool_dev = nullptr;  // device address of the same memory
+  size_t host_bytes = 0;
+  int32_t* err = nullptr;
+  int32_t* pt = nullptr;
+  int32_t* rm = nullptr;
+  int32_t* st = nullptr;
+  int32_t* ord = nullptr;
+  int32_t* step = nullptr;
+  uint32_t* cnt = nullptr;
+  float* part = nullptr;
+  uint8_t* buf = nullptr;
+  size_t part_floats = 0;  // per request
+};
+
+namespace {
+
+thread_local std::string g_msg;
+
+hs_status fail(hs_status s, const std::string& msg) {
+  g_msg = msg;
+  return s;
+}
+
+hs_status fail_hip(hipError_t e, const char* what) {
+  g_msg = std::string(what) + ": " + hipGetErrorString(e);
+  return HS_ERR_HIP;
+}
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+// a*b with overflow detection
+bool mul_ok(size_t a, size_t b, size_t* out) {
+  if (a != 0 && b > SIZE_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+bool add_ok(size_t a, size_t b, size_t* out) {
+  if (b > SIZE_MAX - a) return false;
+  *out = a + b;
+  return true;
+}
+
+struct Layout {
+  size_t err, pt, rm, st, ord, step, cnt, part, buf, total;
+  size_t host_total;
+  size_t part_floats;
+};
+
+// Validates cfg and computes the geometry and both memory layouts, touching no HIP API.
+hs_status plan(const hs_config* cfg, hs::Geometry* g, Layout* lay) {
+  if (!cfg) return fail(HS_ERR_INVALID_ARG, "config is NULL");
+  if (cfg->top_k < 1) return fail(HS_ERR_INVALID_ARG, "top_k must be >= 1");
+  if (cfg->device_buffer_size < cfg->top_k)
+    return fail(HS_ERR_INVALID_ARG, "device_buffer_size must be >= top_k (every selected token must fit)");
+  if (cfg->host_to_device_ratio < 1) return fail(HS_ERR_INVALID_ARG, "host_to_device_ratio must be >= 1");
+  if (cfg->max_requests < 1) return fail(HS_ERR_INVALID_ARG, "max_requests must be >= 1");
+  if (cfg->num_layers < 1) return fail(HS_ERR_INVALID_ARG, "num_layers must be >= 1");
+  if (cfg->layout != HS_KV_BF16_576 && cfg->layout != HS_KV_FP8_MLA_656)
+    return fail(HS_ERR_INVALID_ARG, "unknown KV layout");
+  if (cfg->num_heads < 0 || cfg->num_heads > 16) return fail(HS_ERR_INVALID_ARG, "num_heads must lie in [0, 16]");
+  if (cfg->flags & ~HS_FLAG_NO_IO) return fail(HS_ERR_INVALID_ARG, "unknown flag bits");
+  if (cfg->top_k > hs::kMaxTopK) return fail(HS_ERR_UNSUPPORTED, "top_k above 8192");
+  if (cfg->device_buffer_size > hs::kMaxBuffer) return fail(HS_ERR_UNSUPPORTED, "device_buffer_size above 16384");
+  const int64_t cap = (int64_t)cfg->host_to_device_ratio * (int64_t)cfg->device_buffer_size;
+  if (cap > INT32_MAX) return fail(HS_ERR_INVALID_ARG, "capacity (ratio * B) exceeds 2^31-1 tokens");
+  if (hs::resolve_lds_bytes(cap, cfg->top_k, cfg->device_buffer_size) > hs::kLdsLimit)
+    return fail(HS_ERR_UNSUPPORTED, "capacity too large for the resolver's on-chip token bitmap");
+
+  g->k = cfg->top_k;
+  g->B = cfg->device_buffer_size;
+  g->n = cfg->max_requests;
+  g->L = cfg->num_layers;
+  g->layout = cfg->layout;
+  g->heads = cfg->num_heads;
+  g->cap = cap;
+  g->entry_bytes = cfg->layout == HS_KV_BF16_576 ? 1152 : 656;
+  g->host_stride = g->entry_bytes;
+  g->slot_stride = (g->entry_bytes + 127) / 128 * 128;
+  g->flags = cfg->flags;
+
+  const size_t LN = (size_t)g->L * (size_t)g->n;
+  size_t off = 0, sz = 0, t = 0;
+  auto take = [&](size_t bytes, size_t* where) -> bool {
+    *where = off;
+    return add_ok(off, align_up(bytes), &off);
+  };
+  bool ok = true;
+  ok = ok && take(sizeof(int32_t), &lay->err);
+  ok = ok && mul_ok(LN, (size_t)cap, &t) && mul_ok(t, 4, &sz) && take(sz, &lay->pt);
+  ok = ok && mul_ok(LN, (size_t)g->B, &t) && mul_ok(t, 4, &sz) && take(sz, &lay->rm);
+  ok = ok && take(sz, &lay->st) && take(sz, &lay->ord);
+  ok = ok && take(LN * 4, &lay->step) && take(LN * 4, &lay->cnt);
+  lay->part_floats = g->heads > 0 ? hs::attend_partial_floats(*g) : 0;
+  ok = ok && mul_ok(LN, lay->part_floats, &t) && mul_ok(t, 4, &sz) && take(sz, &lay->part);
+  ok = ok && mul_ok(LN, (size_t)g->B, &t) && mul_ok(t, (size_t)g->slot_stride, &sz) && take(sz, &lay->buf);
+  lay->total = off;
+  ok = ok && mul_ok(LN, (size_t)cap, &t) && mul_ok(t, (size_t)g->host_stride, &lay->host_total);
+  if (!ok) return fail(HS_ERR_INVALID_ARG, "configuration sizes overflow");
+  return HS_OK;
+}
+
+hs::LayerTables layer_tables(const hs_handle* h, int32_t layer) {
+  const hs::Geometry& g = h->g;
+  const size_t base = (size_t)layer * (size_t)g.n;
+  hs::LayerTables t;
+  t.pt = h->pt + base * (size_t)g.cap;
+  t.rm = h->rm + base * (size_t)g.B;
+  t.st = h->st + base * (size_t)g.B;
+  t.ord = h->ord + base * (size_t)g.B;
+  t.step = h->step + base;
+  t.cnt = h->cnt + base;
+  t.part = h->part ? h->part + base * h->part_floats : nullptr;
+  t.buf = h->buf + base * (size_t)g.B * (size_t)g.slot_stride;
+  return t;
+}
+
+void release(hs_handle* h) {
+  if (!h) return;
+  if (h->host_pool) (void)hipHostFree(h->host_pool);
+  if (h->own_dev && h->dev_block) (void)hipFree(h->dev_block);
+  delete h;
+}
+
+}  // namespace
+
+extern "C" {
+
+hs_status hs_device_bytes(const hs_config* cfg, size_t* bytes) {
+  hs::Geometry g;
+  Layout lay;
+  if (!bytes) return fail(HS_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = 0;
+  hs_status s = plan(cfg, &g, &lay);
+  if (s != HS_OK) return s;
+  *bytes = lay.total;
+  return HS_OK;
+}
+
+hs_status hs_host_bytes(const hs_config* cfg, size_t* bytes) {
+  hs::Geometry g;
+  Layout lay;
+  if (!bytes) return fail(HS_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = 0;
+  hs_status s = plan(cfg, &g, &lay);
+  if (s != HS_OK) return s;
+  *bytes = lay.host_total;
+  return HS_OK;
+}
+
+hs_status hs_create(const hs_config* cfg, hs_handle** out) {
+  if (!out) return fail(HS_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  hs::Geometry g;
+  Layout lay;
+  hs_status s = plan(cfg, &g, &lay);
+  if (s != HS_OK) return s;
+  if (cfg->device_mem) {
+    if (cfg->device_mem_bytes < lay.total) return fail(HS_ERR_INVALID_ARG, "device_mem smaller than hs_device_bytes()");
+    if (((uintptr_t)cfg->device_mem) % kAlign) return fail(HS_ERR_INVALID_ARG, "device_mem must be 256-byte aligned");
+  }
+
+  hs_handle* h = new hs_handle();
+  h->g = g;
+  h->part_floats = lay.part_floats;
+  hipError_t e = hipGetDevice(&h->device);
+  if (e != hipSuccess) { release(h); return fail_hip(e, "hipGetDevice"); }
+  if (cfg->device_mem) {
+    h->dev_block = (uint8_t*)cfg->device_mem;
+  } else {
+    e = hipMalloc((void**)&h->dev_block, lay.total);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      release(h);
+      return fail(HS_ERR_OUT_OF_MEMORY, "device allocation failed");
+    }
+    h->own_dev = true;
+  }
+  h->dev_bytes = lay.total;
+
+  const char* inject = getenv("HS_FAULT_INJECT");
+  if (inject && strcmp(inject, "host_alloc") == 0) {
+    release(h);
+    return fail(HS_ERR_OUT_OF_MEMORY, "pinned host allocation failed (injected)");
+  }
+  e = hipHostMalloc((void**)&h->host_pool, lay.host_total, hipHostMallocMapped | hipHostMallocPortable);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    h->host_pool = nullptr;
+    release(h);
+    return fail(HS_ERR_OUT_OF_MEMORY, "pinned host allocation failed");
+  }
+  h->host_bytes = lay.host_total;
+  e = hipHostGetDevicePointer((void**)&h->host_pool_dev, h->host_pool, 0);
+  if (e != hipSuccess) { release(h); return fail_hip(e, "hipHostGetDevicePointer"); }
+
+  uint8_t* b = h->dev_block;
+  h->err = (int32_t*)(b + lay.err);
+  h->pt = (int32_t*)(b + lay.pt);
+  h->rm = (int32_t*)(b + lay.rm);
+  h->st = (int32_t*)(b + lay.st);
+  h->ord = (int32_t*)(b + lay.ord);
+  h->step = (int32_t*)(b + lay.step);
+  h->cnt = (uint32_t*)(b + lay.cnt);
+  h->part = lay.part_floats ? (float*)(b + lay.part) : nullptr;
+  h->buf = b + lay.buf;
+
+  hs::prepare_resolve();
+  e = hipMemset(h->err, 0, sizeof(int32_t));
+  if (e != hipSuccess) { release(h); return fail_hip(e, "hipMemset"); }
+  e = hs::launch_reset(g, h->pt, h->rm, h->st, h->ord, h->step, h->cnt, 0, g.n, nullptr);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) { release(h); return fail_hip(e, "initialising tables"); }
+  *out = h;
+  return HS_OK;
+}
+
+hs_status hs_resolve(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* d_sel, int32_t* d_slots,
+                     int32_t* d_miss, void* stream) {
+  if (!h) return fail(HS_ERR_INVALID_ARG, "handle is NULL");
+  if (layer < 0 || layer >= h->g.L) return fail(HS_ERR_INVALID_ARG, "layer out of range");
+  if (n_req < 0 || n_req > h->g.n) return fail(HS_ERR_INVALID_ARG, "n_req out of range");
+  if (n_req == 0) return HS_OK;
+  if (!d_sel || !d_slots) return fail(HS_ERR_INVALID_ARG, "selection or slot pointer is NULL");
+  hs::LayerTables t = layer_tables(h, layer);
+  const uint8_t* host_layer = h->host_pool_dev + (size_t)layer * h->g.n * (size_t)h->g.cap * h->g.host_stride;
+  hipError_t e = hs::launch_resolve(h->g, t, host_layer, n_req, d_sel, d_slots, d_miss, h->err, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "resolve launch");
+  return HS_OK;
+}
+
+hs_status hs_attend(hs_handle* h, int32_t layer, int32_t n_req, const void* d_q, const int32_t* d_slots, float scale,
+                    void* d_out, float* d_lse, void* stream) {
+  if (!h) return fail(HS_ERR_INVALID_ARG, "handle is NULL");
+  if (h->g.heads == 0) return fail(HS_ERR_UNSUPPORTED, "handle created with num_heads = 0");
+  if (layer < 0 || layer >= h->g.L) return fail(HS_ERR_INVALID_ARG, "layer out of range");
+  if (n_req < 0 || n_req > h->g.n) return fail(HS_ERR_INVALID_ARG, "n_req out of range");
+  if (n_req == 0) return HS_OK;
+  if (!d_q || !d_slots || !d_out) return fail(HS_ERR_INVALID_ARG, "query, slot or output pointer is NULL");
+  hs::LayerTables t = layer_tables(h, layer);
+  hipError_t e = hs::launch_attend(h->g, t, n_req, d_q, d_slots, scale, d_out, d_lse, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "attend launch");
+  return HS_OK;
+}
+
+hs_status hs_destroy(hs_handle* h) {
+  if (!h) return HS_OK;
+  hipError_t e = hipDeviceSynchronize();
+  release(h);
+  if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
+  return HS_OK;
+}
+
+hs_status hs_host_kv(hs_handle* h, int32_t layer, int32_t request, void** ptr, int64_t* capacity, int64_t* row_stride) {
+  if (!h || !ptr) return fail(HS_ERR_INVALID_ARG, "handle or ptr is NULL");
+  if (layer < 0 || layer >= h->g.L || request < 0 || request >= h->g.n)
+    return fail(HS_ERR_INVALID_ARG, "layer or request out of range");
+  const size_t rows = ((size_t)layer * h->g.n + (size_t)request) * (size_t)h->g.cap;
+  *ptr = h->host_pool + rows * (size_t)h->g.host_stride;
+  if (capacity) *capacity = h->g.cap;
+  if (row_stride) *row_stride = h->g.host_stride;
+  return HS_OK;
+}
+
+hs_status hs_device_state(hs_handle* h, int32_t layer, hs_state_view* v) {
+  if (!h || !v) return fail(HS_ERR_INVALID_ARG, "handle or view is NULL");
+  if (layer < 0 || layer >= h->g.L) return fail(HS_ERR_INVALID_ARG, "layer out of range");
+  hs::LayerTables t = layer_tables(h, layer);
+  v->page_table = t.pt;
+  v->slot_owner = t.rm;
+  v->slot_stamp = t.st;
+  v->lru_order = t.ord;
+  v->step = t.step;
+  v->kv_buffer = t.buf;
+  v->capacity = h->g.cap;
+  v->slot_stride = h->g.slot_stride;
+  v->entry_bytes = h->g.entry_bytes;
+  return HS_OK;
+}
+
+hs_status hs_reset_requests(hs_handle* h, int32_t first, int32_t count, void* stream) {
+  if (!h) return fail(HS_ERR_INVALID_ARG, "handle is NULL");
+  if (first < 0 || count < 0 || (int64_t)first + count > h->g.n) return fail(HS_ERR_INVALID_ARG, "request range");
+  if (count == 0) return HS_OK;
+  hipError_t e = hs::launch_reset(h->g, h->pt, h->rm, h->st, h->ord, h->step, h->cnt, first, count, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "reset launch");
+  return HS_OK;
+}
+
+hs_status hs_get_device_error(hs_handle* h, int32_t* bits) {
+  if (!h || !bits) return fail(HS_ERR_INVALID_ARG, "handle or bits is NULL");
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(bits, h->err, sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemset(h->err, 0, sizeof(int32_t));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return fail_hip(e, "reading the device error word");
+  return HS_OK;
+}
+
+const char* hs_status_string(hs_status s) {
+  switch (s) {
+    case HS_OK: return "ok";
+    case HS_ERR_INVALID_ARG: return "invalid argument";
+    case HS_ERR_OUT_OF_MEMORY: return "out of memory";
+    case HS_ERR_UNSUPPORTED: return "unsupported";
+    case HS_ERR_HIP: return "HIP runtime error";
+    case HS_ERR_DEVICE: return "device reported invalid input";
+  }
+  return "unknown status";
+}
+
+const char* hs_last_error_message(void) { return g_msg.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Internal declarations shared by the host API (hs_api.cpp) and the kernels (*.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "hs.h"
+
+namespace hs {
+
+// Threads of one resolver workgroup (one workgroup per request).
+constexpr int kResolveThreads = 512;
+// Upper bounds the resolver's register tiling supports.
+constexpr int kMaxTopK = 16 * kResolveThreads;          // 8192
+constexpr int kMaxBuffer = 32 * kResolveThreads;        // 16384 slots (hit bitmap: one word per thread)
+constexpr size_t kLdsLimit = 160 * 1024;                // gfx950 LDS per workgroup
+
+// Device tables of one layer for requests 0..max_requests-1.
+struct LayerTables {
+  int32_t* pt;     // [n][cap]
+  int32_t* rm;     // [n][B]
+  int32_t* st;     // [n][B]
+  int32_t* ord;    // [n][B]
+  int32_t* step;   // [n]
+  uint8_t* buf;    // [n][B][slot_stride]
+  float* part;     // attention split partials (see attend.hip)
+  uint32_t* cnt;   // attention split arrival counters [n]
+};
+
+struct Geometry {
+  int32_t k, B, n, L, layout, heads;
+  int64_t cap;
+  int64_t entry_bytes;
+  int64_t host_stride;
+  int64_t slot_stride;
+  uint32_t flags;
+};
+
+// Once per process, before the first launch (outside any graph capture).
+void prepare_resolve();
+
+// Dynamic LDS bytes the resolver needs for this geometry.
+size_t resolve_lds_bytes(int64_t cap, int32_t k, int32_t B);
+
+hipError_t launch_resolve(const Geometry& g, const LayerTables& t, const uint8_t* host_layer, int32_t n_req,
+                          const int32_t* sel, int32_t* slots, int32_t* miss, int32_t* err, hipStream_t s);
+
+hipError_t launch_reset(const Geometry& g, int32_t* pt, int32_t* rm, int32_t* st, int32_t* ord, int32_t* step,
+                        uint32_t* cnt, int32_t first, int32_t count, hipStream_t s);
+
+// Attention: split factor and partial-buffer floats per request.
+int attend_splits(const Geometry& g);
+size_t attend_partial_floats(const Geometry& g);
+
+hipError_t launch_attend(const Geometry& g, const LayerTables& t, int32_t n_req, const void* q, const int32_t* slots,
+                         float scale, void* out, float* lse, hipStream_t s);
+
+}  // namespace hs

@@ -1,0 +1,377 @@
+// Resolver: per-layer resolution of a top-k selection against the fixed device buffer.
+//
+// What is computed (HiSparse paper abstract: hit detection, LRU replacement and
+// host-to-device fetches of each layer's selections; "HiSparse" note, section 3:
+// find the top-k misses, choose LRU eviction candidates, update the page table,
+// pull the rows from host memory), with the replacement rule stated in hs.h.
+//
+// Design for gfx950.  One 512-thread workgroup (8 wave64s) per request; a request's
+// tables are private, so workgroups never communicate.
+//   P0  clear two LDS bitmaps (hit slots [B bits], missing tokens [capacity bits]) and
+//       load this thread's contiguous chunk of the LRU order into registers;
+//   P1  gather the page-table entry of every selected token (coalesced selection read,
+//       random 4-byte table reads); hits set their slot bit, misses their token bit
+//       (LDS atomics; a bit already set flags a repeated token);
+//   P2  one packed block scan gives (a) for each word of the token bitmap the number of
+//       misses below it, so a miss's ascending-token rank is prefix[word] +
+//       popcount(lower bits of the word), and (b) each non-hit slot's rank in LRU order;
+//   P3  the first m non-hit slots in LRU order are the victims; the remaining non-hit
+//       slots keep their order and move to position rank - m of the new order;
+//   P4  hit and victim slots, all stamped with this step, form the back of the new
+//       order in ascending slot index (a scan over the slot bitmap); the i-th miss takes
+//       victim i: evict its owner from the page table, install the token, stamp, and
+//       write the output slot;
+//   P5  the workgroup copies the missing rows from pinned host memory (zero-copy 16-byte
+//       loads over PCIe, row-major over the miss list so a wave reads ~1 KiB runs) into
+//       the victim slots.
+// The new order equals the slots sorted by (stamp, slot): untouched slots keep their
+// relative order, and every touched slot now has the largest stamp, so among them the
+// slot index decides.  No sort is needed and a step costs O(k + B + capacity/32).
+
+#include "hs_internal.h"
+
+namespace hs {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int NT = kResolveThreads;
+constexpr int NW = NT / 64;
+constexpr int32_t kPad = -2;  // entry to skip: padding, out-of-range or repeated token
+
+struct ResolveArgs {
+  const int32_t* sel;
+  int32_t* slots;
+  int32_t* miss;
+  int32_t* pt;
+  int32_t* rm;
+  int32_t* st;
+  int32_t* ord;
+  int32_t* step;
+  const uint8_t* host;
+  uint8_t* buf;
+  int32_t* err;
+  int64_t cap;
+  int64_t host_stride;
+  int64_t slot_stride;
+  int32_t k;
+  int32_t B;
+  int32_t chunks;  // 16-byte chunks per row
+  int32_t no_io;
+};
+
+// Exclusive block-wide prefix sum of v; *total gets the block sum.  Every thread must call.
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wid] = x;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    uint32_t s = wsum[w];
+    before += (w < wid) ? s : 0u;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + x - v;
+}
+
+// KPT: selection entries per thread (KPT * NT >= k); OPT: LRU-order entries per thread (OPT * NT >= B).
+template <int KPT, int OPT>
+__global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
+  extern __shared__ uint32_t lds[];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int B = a.B;
+  const int k = a.k;
+  const int64_t cap = a.cap;
+  const int W = (int)((cap + 31) >> 5);
+  const int HB = (B + 31) >> 5;
+  uint32_t* hitmap = lds;                       // [HB]  hit slots, then hit + victim slots
+  uint32_t* missmap = hitmap + HB;              // [W]   missing tokens
+  uint32_t* victims = missmap + W;              // [k]   victim slot of the i-th miss
+  uint32_t* misstok = victims + k;              // [k]   token of the i-th miss (-1: none)
+  uint32_t* wsum = misstok + k;                 // [NW]  scan scratch
+  uint16_t* prefix = (uint16_t*)(wsum + NW);    // [W]   misses below each bitmap word
+
+  int32_t* pt = a.pt + (int64_t)r * cap;
+  int32_t* rm = a.rm + (int64_t)r * B;
+  int32_t* st = a.st + (int64_t)r * B;
+  int32_t* ord = a.ord + (int64_t)r * B;
+  const int32_t* sel = a.sel + (int64_t)r * k;
+  int32_t* slots = a.slots + (int64_t)r * k;
+  const int32_t t = a.step[r];
+
+  // ---- P0
+  for (int w = tid; w < HB; w += NT) hitmap[w] = 0u;
+  for (int w = tid; w < W; w += NT) missmap[w] = 0u;
+  int32_t ordv[OPT];
+  const int o0 = tid * OPT;
+#pragma unroll
+  for (int x = 0; x < OPT; ++x) ordv[x] = (o0 + x < B) ? ord[o0 + x] : -1;
+  int32_t selv[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int i = tid + j * NT;
+    selv[j] = (i < k) ? sel[i] : -1;
+  }
+  __syncthreads();
+
+  // ---- P1
+  uint32_t err = 0;
+  int32_t ptv[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int32_t s = selv[j];
+    int32_t p = kPad;
+    if (s != -1) {
+      if (s < 0 || (int64_t)s >= cap) err |= HS_DEVERR_TOKEN_RANGE;
+      else p = pt[s];
+    }
+    ptv[j] = p;
+  }
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int32_t p = ptv[j];
+    if (p >= 0) {
+      if (p >= B) {
+        ptv[j] = kPad;
+      } else {
+        const uint32_t bit = 1u << (p & 31);
+        if (atomicOr(&hitmap[p >> 5], bit) & bit) { err |= HS_DEVERR_DUPLICATE; ptv[j] = kPad; }
+      }
+    } else if (p == -1) {
+      const int32_t s = selv[j];
+      const uint32_t bit = 1u << (s & 31);
+      if (atomicOr(&missmap[s >> 5], bit) & bit) { err |= HS_DEVERR_DUPLICATE; ptv[j] = kPad; }
+    } else {
+      ptv[j] = kPad;
+    }
+  }
+  if (err) atomicOr(a.err, (int32_t)err);
+  __syncthreads();
+
+  // ---- P2
+  const int WPT = (W + NT - 1) / NT;
+  const int w0 = tid * WPT;
+  const int w1 = min(W, w0 + WPT);
+  uint32_t mcnt = 0;
+  for (int w = w0; w < w1; ++w) mcnt += __popc(missmap[w]);
+  uint32_t nhcnt = 0, nhmask = 0;
+#pragma unroll
+  for (int x = 0; x < OPT; ++x) {
+    const int32_t j = ordv[x];
+    if (j >= 0 && j < B && !((hitmap[j >> 5] >> (j & 31)) & 1u)) {
+      ++nhcnt;
+      nhmask |= 1u << x;
+    }
+  }
+  uint32_t tot;
+  const uint32_t pre = block_scan((mcnt << 16) | nhcnt, wsum, &tot);
+  const int m = (int)(tot >> 16);
+  const int nonhit = (int)(tot & 0xFFFFu);
+  {
+    uint32_t run = pre >> 16;
+    for (int w = w0; w < w1; ++w) {
+      prefix[w] = (uint16_t)run;
+      run += __popc(missmap[w]);
+    }
+  }
+
+  // ---- P3
+  {
+    int rank = (int)(pre & 0xFFFFu);
+#pragma unroll
+    for (int x = 0; x < OPT; ++x) {
+      if (nhmask & (1u << x)) {
+        const int32_t j = ordv[x];
+        if (rank < m) {
+          victims[rank] = (uint32_t)j;
+          atomicOr(&hitmap[j >> 5], 1u << (j & 31));
+        } else {
+          ord[rank - m] = j;
+        }
+        ++rank;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- P4
+  {
+    uint32_t word = (tid < HB) ? hitmap[tid] : 0u;
+    uint32_t touched;
+    int pos = (nonhit - m) + (int)block_scan((uint32_t)__popc(word), wsum, &touched);
+    while (word) {
+      const int b = __ffs(word) - 1;
+      word &= word - 1u;
+      ord[pos++] = tid * 32 + b;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int i = tid + j * NT;
+    if (i < k) {
+      const int32_t p = ptv[j];
+      int32_t out = -1;
+      if (p >= 0) {
+        st[p] = t;
+        out = p;
+      } else if (p == -1) {
+        const int32_t s = selv[j];
+        const int w = s >> 5;
+        const int q = (int)prefix[w] + __popc(missmap[w] & ((1u << (s & 31)) - 1u));
+        const int32_t v = (q < m && q < nonhit) ? (int32_t)victims[q] : -1;
+        int32_t tok = -1;
+        if (v >= 0 && v < B) {
+          const int32_t old = rm[v];
+          if (old >= 0 && (int64_t)old < cap) pt[old] = -1;
+          pt[s] = v;
+          rm[v] = s;
+          st[v] = t;
+          out = v;
+          tok = s;
+        }
+        if (q < k) misstok[q] = (uint32_t)tok;
+      }
+      slots[i] = out;
+    }
+  }
+  if (tid == 0) {
+    a.step[r] = t + 1;
+    if (a.miss) a.miss[r] = m;
+  }
+  __syncthreads();
+
+  // ---- P5
+  if (a.no_io || m == 0) return;
+  const int C = a.chunks;
+  const int total = m * C;
+  const uint8_t* host = a.host + (int64_t)r * cap * a.host_stride;
+  uint8_t* buf = a.buf + (int64_t)r * B * a.slot_stride;
+  constexpr int U = 4;
+  for (int base = tid; base < total; base += NT * U) {
+    v4i v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = base + u * NT;
+      if (idx < total) {
+        const int q = idx / C;
+        const int c = idx - q * C;
+        const int32_t s = (int32_t)misstok[q];
+        if (s >= 0) v[u] = __builtin_nontemporal_load((const v4i*)(host + (int64_t)s * a.host_stride) + c);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = base + u * NT;
+      if (idx < total) {
+        const int q = idx / C;
+        const int c = idx - q * C;
+        if ((int32_t)misstok[q] >= 0) ((v4i*)(buf + (int64_t)victims[q] * a.slot_stride))[c] = v[u];
+      }
+    }
+  }
+}
+
+__global__ void reset_kernel(int32_t* pt, int32_t* rm, int32_t* st, int32_t* ord, int32_t* step, uint32_t* cnt,
+                             int32_t L, int32_t n, int32_t first, int32_t count, int64_t cap, int32_t B) {
+  const int64_t pairs = (int64_t)L * count;
+  for (int64_t lr = blockIdx.y; lr < pairs; lr += gridDim.y) {
+    const int32_t l = (int32_t)(lr / count);
+    const int32_t r = first + (int32_t)(lr % count);
+    const int64_t id = (int64_t)l * n + r;
+    int32_t* p = pt + id * cap;
+    for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < cap; x += (int64_t)gridDim.x * blockDim.x)
+      p[x] = -1;
+    for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < B; x += (int64_t)gridDim.x * blockDim.x) {
+      rm[id * B + x] = -1;
+      st[id * B + x] = -1;
+      ord[id * B + x] = (int32_t)x;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      step[id] = 0;
+      if (cnt) cnt[id] = 0u;
+    }
+  }
+}
+
+template <int KPT, int OPT>
+void allow_large_lds() {
+  // Lets a workgroup take up to the whole 160 KiB of LDS; errors are left to the launch.
+  (void)hipFuncSetAttribute((const void*)resolve_kernel<KPT, OPT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kLdsLimit);
+  (void)hipGetLastError();
+}
+
+template <int KPT, int OPT>
+hipError_t launch_one(const ResolveArgs& a, int n_req, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL((resolve_kernel<KPT, OPT>), dim3(n_req), dim3(NT), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+void prepare_resolve() {
+  allow_large_lds<4, 8>();
+  allow_large_lds<4, 32>();
+  allow_large_lds<16, 8>();
+  allow_large_lds<16, 32>();
+}
+
+size_t resolve_lds_bytes(int64_t cap, int32_t k, int32_t B) {
+  const size_t W = (size_t)((cap + 31) >> 5);
+  const size_t HB = (size_t)((B + 31) >> 5);
+  size_t words = HB + W + 2 * (size_t)k + NW;
+  size_t bytes = words * 4 + W * 2;
+  return (bytes + 15) & ~(size_t)15;
+}
+
+hipError_t launch_resolve(const Geometry& g, const LayerTables& t, const uint8_t* host_layer, int32_t n_req,
+                          const int32_t* sel, int32_t* slots, int32_t* miss, int32_t* err, hipStream_t s) {
+  ResolveArgs a;
+  a.sel = sel;
+  a.slots = slots;
+  a.miss = miss;
+  a.pt = t.pt;
+  a.rm = t.rm;
+  a.st = t.st;
+  a.ord = t.ord;
+  a.step = t.step;
+  a.host = host_layer;
+  a.buf = t.buf;
+  a.err = err;
+  a.cap = g.cap;
+  a.host_stride = g.host_stride;
+  a.slot_stride = g.slot_stride;
+  a.k = g.k;
+  a.B = g.B;
+  a.chunks = (int32_t)(g.entry_bytes / 16);
+  a.no_io = (g.flags & HS_FLAG_NO_IO) ? 1 : 0;
+  const size_t lds = resolve_lds_bytes(g.cap, g.k, g.B);
+  const int kpt = (g.k + NT - 1) / NT;
+  const int opt = (g.B + NT - 1) / NT;
+  if (kpt <= 4) {
+    return opt <= 8 ? launch_one<4, 8>(a, n_req, lds, s) : launch_one<4, 32>(a, n_req, lds, s);
+  }
+  return opt <= 8 ? launch_one<16, 8>(a, n_req, lds, s) : launch_one<16, 32>(a, n_req, lds, s);
+}
+
+hipError_t launch_reset(const Geometry& g, int32_t* pt, int32_t* rm, int32_t* st, int32_t* ord, int32_t* step,
+                        uint32_t* cnt, int32_t first, int32_t count, hipStream_t s) {
+  const int64_t pairs = (int64_t)g.L * count;
+  const unsigned gy = (unsigned)(pairs < 65535 ? pairs : 65535);
+  hipLaunchKernelGGL(reset_kernel, dim3(16, gy), dim3(256), 0, s, pt, rm, st, ord, step, cnt, g.L, g.n, first, count,
+                     g.cap, g.B);
+  return hipGetLastError();
+}
+
+}  // namespace hs

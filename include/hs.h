@@ -1,0 +1,178 @@
+/*
+ * hs.h -- C ABI of the MI355X (gfx950) HiSparse hot-path library (libhs.so).
+ *
+ * What the library does (HiSparse paper abstract, arXiv 2608.07009; "HiSparse"
+ * note, sections 2 and 3): every request keeps its full KV history in pinned
+ * host memory and only a fixed number B of device slots per layer in HBM.  At
+ * each decode step and layer, the top-k token selection of a sparse-attention
+ * indexer is resolved against that buffer -- hit detection through a
+ * token->slot page table, LRU replacement among the slots not selected in the
+ * step, page-table and recency update, host-to-device fetch of the missing
+ * rows -- and a sparse MLA decode attention then reads only the resolved slots.
+ * The exact replacement rule (the pages say "LRU"): a slot's recency stamp is
+ * the step at which it was last selected (a fill counts as a selection); the
+ * candidates for a step are the slots holding no token selected in that step,
+ * least recent first, ties to the lower slot index; missing tokens are served
+ * in ascending token order, the i-th missing token taking the i-th candidate.
+ *
+ * Conventions for every function:
+ *   - device pointers ("d_" prefix) are HIP device addresses; host pointers are
+ *     ordinary process addresses;
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream);
+ *   - argument errors are detected on the host and returned before any device
+ *     work is queued; nothing is written in that case;
+ *   - hs_resolve and hs_attend only enqueue kernels: they never allocate, copy
+ *     synchronously or synchronise, so they may be captured in a hipGraph;
+ *   - a handle is not thread-safe; calls on one handle must be serialised by
+ *     the caller.
+ */
+#ifndef HS_H
+#define HS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hs_status {
+  HS_OK = 0,
+  HS_ERR_INVALID_ARG = 1,   /* bad configuration or call argument (message: hs_last_error_message) */
+  HS_ERR_OUT_OF_MEMORY = 2, /* a host or device allocation failed */
+  HS_ERR_UNSUPPORTED = 3,   /* valid request the library does not implement (e.g. no attention heads) */
+  HS_ERR_HIP = 4,           /* a HIP runtime call failed (message has the HIP error string) */
+  HS_ERR_DEVICE = 5         /* the device flagged invalid input (see hs_get_device_error) */
+} hs_status;
+
+/* KV entry layouts (bytes per token).  Rows are stored as given, byte for byte. */
+typedef enum hs_kv_layout {
+  HS_KV_BF16_576 = 0,   /* 576 bf16: 512 latent + 64 rope                                  = 1152 B */
+  HS_KV_FP8_MLA_656 = 1 /* 512 E4M3FN latent codes, 4 fp32 scales (one per 128 latent
+                           values), 64 bf16 rope                                            =  656 B */
+} hs_kv_layout;
+
+/* Handle flags (hs_config.flags). */
+#define HS_FLAG_NO_IO 0x1u /* resolve updates every table but moves no row: measures the
+                              resolution cost alone (the paper's no-IO oracle) */
+
+/* Device error bits, accumulated (OR) until read by hs_get_device_error. */
+#define HS_DEVERR_TOKEN_RANGE 0x1 /* a selected token outside [0, capacity) and not -1 */
+#define HS_DEVERR_DUPLICATE 0x2   /* a token selected twice in one row */
+
+/*
+ * Configuration.  top_k, device_buffer_size and host_to_device_ratio are the
+ * three tuning parameters the note names (section 3); the host capacity per
+ * (request, layer) is host_to_device_ratio * device_buffer_size tokens.
+ */
+typedef struct hs_config {
+  int32_t top_k;                /* k: selections per request and step, >= 1                  */
+  int32_t device_buffer_size;   /* B: device slots per (request, layer), B >= top_k           */
+  int32_t host_to_device_ratio; /* >= 1; capacity = ratio * B tokens of history              */
+  int32_t max_requests;         /* request slots 0..max_requests-1                           */
+  int32_t num_layers;           /* layers, each with its own buffer and tables               */
+  int32_t layout;               /* hs_kv_layout                                              */
+  int32_t num_heads;            /* query heads for hs_attend (0: resolve only), <= 16        */
+  uint32_t flags;               /* HS_FLAG_*                                                 */
+  void* device_mem;             /* optional caller-owned device block of hs_device_bytes()
+                                   bytes, 256-byte aligned; NULL: the library allocates     */
+  size_t device_mem_bytes;      /* size of device_mem                                        */
+} hs_config;
+
+typedef struct hs_handle hs_handle;
+
+/* Device-side state of one layer; all pointers are device addresses owned by the handle. */
+typedef struct hs_state_view {
+  int32_t* page_table;   /* [max_requests][capacity] token -> slot, -1 = not resident  */
+  int32_t* slot_owner;   /* [max_requests][B] slot -> token, -1 = empty               */
+  int32_t* slot_stamp;   /* [max_requests][B] step of last selection, -1 = never       */
+  int32_t* lru_order;    /* [max_requests][B] slots sorted by (stamp, slot) ascending  */
+  int32_t* step;         /* [max_requests] resolves done so far (the next stamp)        */
+  uint8_t* kv_buffer;    /* [max_requests][B][slot_stride] KV rows of the slots         */
+  int64_t capacity;      /* host tokens per (request, layer)                            */
+  int64_t slot_stride;   /* bytes between slots in kv_buffer (>= entry_bytes)           */
+  int64_t entry_bytes;   /* bytes of one KV entry                                       */
+} hs_state_view;
+
+/* Bytes the device block must have for this configuration (0 and an error if invalid). */
+hs_status hs_device_bytes(const hs_config* cfg, size_t* bytes);
+
+/* Bytes of the pinned host pool for this configuration. */
+hs_status hs_host_bytes(const hs_config* cfg, size_t* bytes);
+
+/*
+ * Create a handle: validates cfg (B >= top_k, ratio >= 1, known layout, sizes
+ * without overflow, tables within the resolver's on-chip limits) before any HIP
+ * call, then allocates the pinned host pool (hipHostMalloc, mapped) and the
+ * device state, and sets every request to the empty state (no token resident,
+ * all stamps -1, step 0).  On error *out is NULL.
+ */
+hs_status hs_create(const hs_config* cfg, hs_handle** out);
+
+/*
+ * Resolve one layer's selections for requests 0..n_req-1 (paper abstract:
+ * hit detection, LRU replacement and host-to-device fetch for each layer's
+ * selections; note, section 3: identify the misses, pick LRU victims, update
+ * the page table, pull the rows from host memory).
+ *   d_sel   [n_req][top_k] int32 token positions, -1 = padding
+ *   d_slots [n_req][top_k] int32 out: slot now holding d_sel[r][i], -1 for padding or
+ *           rejected entries
+ *   d_miss  [n_req] int32 out: number of rows fetched for the request, or NULL
+ * Ends with every selected token resident and its row in kv_buffer (unless
+ * HS_FLAG_NO_IO).  Entries outside [0, capacity) or repeated in a row are
+ * skipped (slot -1) and set the device error word; the library never reads or
+ * writes outside its tables.  Ordering: resolve(l, t) must complete before
+ * attend(l, t) and attend(l, t) before resolve(l, t+1) on the caller's streams;
+ * different layers may run concurrently.
+ */
+hs_status hs_resolve(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* d_sel, int32_t* d_slots,
+                     int32_t* d_miss, void* stream);
+
+/*
+ * Sparse MLA decode attention over the resolved slots (paper abstract: each
+ * step reads only the selected KV entries; only placement changes, so the
+ * result equals attention over the selected tokens of the full history).
+ *   d_q     [n_req][num_heads][576] bf16 queries (512 latent + 64 rope)
+ *   d_slots [n_req][top_k] int32 slots from hs_resolve (-1 entries skipped)
+ *   scale   softmax scale applied to q.K
+ *   d_out   [n_req][num_heads][512] bf16: sum_j softmax_j(scale q.K_j) V_j,
+ *           with K_j all 576 decoded values of slot j and V_j its first 512
+ *   d_lse   [n_req][num_heads] fp32 log-sum-exp of the scaled scores, or NULL
+ * A row with no valid slot gives out = 0 and lse = -inf.  HS_ERR_UNSUPPORTED
+ * when the handle was created with num_heads = 0.
+ */
+hs_status hs_attend(hs_handle* h, int32_t layer, int32_t n_req, const void* d_q, const int32_t* d_slots,
+                    float scale, void* d_out, float* d_lse, void* stream);
+
+/* Synchronise the device and free everything the handle owns.  NULL is accepted. */
+hs_status hs_destroy(hs_handle* h);
+
+/*
+ * Host rows of (layer, request): *ptr = first of `*capacity` rows, `*row_stride`
+ * bytes apart, in pinned memory owned by the handle (valid until hs_destroy).
+ * The caller writes a token's row before any selection names it (prefill
+ * offload / decode append); the library only reads this memory.
+ */
+hs_status hs_host_kv(hs_handle* h, int32_t layer, int32_t request, void** ptr, int64_t* capacity,
+                     int64_t* row_stride);
+
+/* Device pointers of one layer's tables and slot buffer. */
+hs_status hs_device_state(hs_handle* h, int32_t layer, hs_state_view* view);
+
+/* Return requests first..first+count-1 of every layer to the empty state (enqueued on stream). */
+hs_status hs_reset_requests(hs_handle* h, int32_t first, int32_t count, void* stream);
+
+/* Synchronise the device, return the accumulated HS_DEVERR_* bits in *bits and clear them. */
+hs_status hs_get_device_error(hs_handle* h, int32_t* bits);
+
+/* Static description of a status code. */
+const char* hs_status_string(hs_status s);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* hs_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HS_H */

@@ -1,0 +1,85 @@
+"""The C ABI library: it loads, exports every function include/hs.h declares, and rejects
+bad configurations on the host before any HIP call (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hierarchical_kv_cache_hs_amd as hsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "hs.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hs_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("hs_create", "hs_resolve", "hs_attend", "hs_destroy"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = hsa.lib()
+    for n in _declared():
+        assert hasattr(L, n), n
+    assert set(_declared()) == set(hsa.SYMBOLS)
+
+
+def _cfg(**kw):
+    base = dict(top_k=64, device_buffer_size=128, host_to_device_ratio=32, max_requests=2, num_layers=1,
+                layout=hsa.LAYOUT_BF16, num_heads=16, flags=0)
+    base.update(kw)
+    return hsa.make_config(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(top_k=0), hsa.HS_ERR_INVALID_ARG),
+    (dict(device_buffer_size=63), hsa.HS_ERR_INVALID_ARG),
+    (dict(host_to_device_ratio=0), hsa.HS_ERR_INVALID_ARG),
+    (dict(max_requests=0), hsa.HS_ERR_INVALID_ARG),
+    (dict(num_layers=0), hsa.HS_ERR_INVALID_ARG),
+    (dict(layout=7), hsa.HS_ERR_INVALID_ARG),
+    (dict(num_heads=17), hsa.HS_ERR_INVALID_ARG),
+    (dict(num_heads=-1), hsa.HS_ERR_INVALID_ARG),
+    (dict(flags=0x80), hsa.HS_ERR_INVALID_ARG),
+    (dict(top_k=8193, device_buffer_size=9000), hsa.HS_ERR_UNSUPPORTED),
+    (dict(device_buffer_size=16385), hsa.HS_ERR_UNSUPPORTED),
+    (dict(device_buffer_size=4096, host_to_device_ratio=600000), hsa.HS_ERR_INVALID_ARG),
+    (dict(device_buffer_size=4096, host_to_device_ratio=300), hsa.HS_ERR_UNSUPPORTED),
+])
+def test_create_rejects_bad_config_before_hip(kw, status):
+    cfg = _cfg(**kw)
+    h = ctypes.c_void_p(123)
+    assert hsa.lib().hs_create(ctypes.byref(cfg), ctypes.byref(h)) == status
+    assert h.value is None
+    assert hsa.lib().hs_last_error_message().decode() != ""
+    n = ctypes.c_size_t(7)
+    assert hsa.lib().hs_device_bytes(ctypes.byref(cfg), ctypes.byref(n)) == status
+    assert n.value == 0
+
+
+def test_sizes_for_the_batch64_workload():
+    cfg = _cfg(top_k=2048, device_buffer_size=4096, host_to_device_ratio=8, max_requests=64, num_heads=0)
+    dev = hsa.device_bytes(cfg)
+    host = hsa.host_bytes(cfg)
+    assert host == 64 * 32768 * 1152
+    slots = 64 * 4096 * 1152
+    tables = 64 * 32768 * 4 + 3 * 64 * 4096 * 4
+    assert slots + tables <= dev <= slots + tables + 16 * 4096
+
+
+def test_null_arguments():
+    L = hsa.lib()
+    assert L.hs_destroy(None) == hsa.HS_OK
+    assert L.hs_resolve(None, 0, 1, None, None, None, None) == hsa.HS_ERR_INVALID_ARG
+    assert L.hs_attend(None, 0, 1, None, None, ctypes.c_float(1.0), None, None, None) == hsa.HS_ERR_INVALID_ARG
+    assert L.hs_create(None, None) == hsa.HS_ERR_INVALID_ARG
+    bits = ctypes.c_int32()
+    assert L.hs_get_device_error(None, ctypes.byref(bits)) == hsa.HS_ERR_INVALID_ARG
+    for s in range(6):
+        assert L.hs_status_string(s)

@@ -1,0 +1,232 @@
+"""Resolver parity on the GPU: bit-exact page table, slot owners, stamps, step counters,
+output slots, miss counts and slot bytes against the CPU oracle, on the seeded workloads
+and on edge cases (padding, ragged sizes, B = k, k = 1, invalid input, no-IO mode,
+reset, graph capture)."""
+import numpy as np
+import pytest
+import torch
+
+import hierarchical_kv_cache_hs_amd as hsa
+from synth import configs as C
+from synth import kv as skv
+
+from gpu_harness import Pair, say, trace_for, fill_host_pool
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")]
+
+
+def _run(w, steps=None, requests=None, check_every=1, oracle_rows=True, sample_rows=None):
+    x = trace_for(w, steps=steps, requests=requests)
+    n = x.shape[1]
+    p = Pair(n, 1, w.k, w.B, w.ratio, w.layout, w.seed, oracle_rows=oracle_rows)
+    misses = []
+    try:
+        for t in range(x.shape[0]):
+            check = (t % check_every == 0) or t == x.shape[0] - 1
+            _, m = p.step(0, x[t], check_state=False)
+            if check:
+                p.check_state(0, n, sample_rows=sample_rows)
+            misses.append(m)
+    finally:
+        p.close()
+    return np.stack(misses)
+
+
+def test_tiny_all_steps():
+    say("tiny: 1 request, k 64, B 128, 32 steps")
+    m = _run(C.TINY)
+    assert m[0, 0] == 64 and m[1:].max() <= 64
+
+
+def test_batch64_full():
+    say("batch64: 64 requests, k 2048, B 4096, cap 32768, 200 steps")
+    m = _run(C.BATCH64, check_every=20)
+    assert (m[0] == 2048).all()
+
+
+@pytest.mark.parametrize("B", C.SWEEP_BUFFERS)
+def test_sweep_buffers_full_size(B):
+    w = C.sweep_point(B)
+    say(f"sweep: 32 requests, ctx 131072, k 2048, B {B}, cap {w.cap}")
+    m = _run(w, steps=40, check_every=13, oracle_rows=False, sample_rows=256)
+    assert (m[0] == 2048).all()
+
+
+@pytest.mark.parametrize("churn", C.FP8_256_CHURNS)
+def test_fp8_256_resolve_full_size(churn):
+    w = C.churn_point(churn)
+    say(f"fp8_256 resolve: 256 requests, fp8 656 B, churn {churn}, 25 steps")
+    _run(w, steps=25, check_every=8, oracle_rows=False, sample_rows=128)
+
+
+@pytest.mark.parametrize("k,B,ratio,n", [(700, 1000, 3, 3), (1, 7, 5, 2), (33, 33, 4, 5), (512, 512, 2, 1),
+                                          (513, 777, 9, 4), (2048, 2048, 3, 2), (4096, 6000, 2, 2)])
+def test_ragged_shapes_random_traces(k, B, ratio, n):
+    say(f"ragged: k {k}, B {B}, ratio {ratio}, n {n}")
+    cap = B * ratio
+    rng = np.random.default_rng(k * 7 + B)
+    p = Pair(n, 1, k, B, ratio, hsa.LAYOUT_BF16, seed=77)
+    try:
+        pop = rng.permutation(cap)
+        w = 1.0 / np.arange(1, cap + 1) ** 0.9
+        w /= w.sum()
+        for t in range(12):
+            S = np.stack([rng.choice(pop, k, replace=False, p=w) for _ in range(n)]).astype(np.int32)
+            S[rng.random(S.shape) < 0.05] = -1
+            if t == 5:
+                S[0] = -1          # a row of padding only
+            p.step(0, S, check_state=True)
+    finally:
+        p.close()
+
+
+def test_fewer_requests_than_slots_and_layers_independent():
+    say("n_req < max_requests, two layers")
+    p = Pair(6, 2, 64, 128, 4, hsa.LAYOUT_FP8, seed=5)
+    rng = np.random.default_rng(0)
+    try:
+        for t in range(10):
+            nr = 1 + t % 6
+            for layer in (0, 1):
+                S = np.stack([rng.choice(512, 64, replace=False) for _ in range(nr)]).astype(np.int32)
+                p.step(layer, S, check_state=False)
+                p.check_state(layer, 6)
+    finally:
+        p.close()
+
+
+def test_invalid_entries_flagged_and_skipped():
+    say("invalid tokens: out of range and duplicates")
+    hs = hsa.HiSparse(top_k=8, device_buffer_size=16, host_to_device_ratio=4, max_requests=2)
+    try:
+        fill_host_pool(hs, 3)
+        assert hs.device_error() == 0
+        sel = torch.tensor([[1, 2, 64, -5, 3, -1, 4, 5], [1, 2, 3, 4, 5, 6, 7, 8]], dtype=torch.int32).cuda()
+        slots, miss = hs.resolve(0, sel)
+        s = slots.cpu().numpy()
+        assert hs.device_error() == hsa.DEVERR_TOKEN_RANGE
+        assert s[0, 2] == -1 and s[0, 3] == -1 and s[0, 5] == -1
+        assert miss.cpu().numpy().tolist() == [5, 8]
+        sel = torch.tensor([[9, 9, 1, 2, 3, 4, 5, 6], [1, 1, 1, 1, 1, 1, 1, 1]], dtype=torch.int32).cuda()
+        slots, miss = hs.resolve(0, sel)
+        s = slots.cpu().numpy()
+        assert hs.device_error() == hsa.DEVERR_DUPLICATE
+        assert sorted([s[0, 0], s[0, 1]])[0] == -1 and max(s[0, 0], s[0, 1]) >= 0
+        assert (s[1] >= 0).sum() == 1
+        st = hs.state(0)
+        pt = st["page_table"].cpu().numpy()
+        rm = st["slot_owner"].cpu().numpy()
+        for r in range(2):
+            res = np.nonzero(pt[r] >= 0)[0]
+            assert all(rm[r, pt[r, x]] == x for x in res)
+        assert hs.device_error() == 0
+    finally:
+        hs.close()
+
+
+def test_no_io_mode_same_tables_no_rows():
+    say("no-IO mode")
+    w = C.TINY.with_(n=3)
+    x = trace_for(w)
+    a = hsa.HiSparse(64, 128, 32, 3)
+    b = hsa.HiSparse(64, 128, 32, 3, flags=hsa.FLAG_NO_IO)
+    try:
+        fill_host_pool(a, w.seed)
+        fill_host_pool(b, w.seed)
+        b.state(0)["kv_buffer"].zero_()
+        for t in range(x.shape[0]):
+            sel = torch.from_numpy(x[t]).cuda()
+            sa, ma = a.resolve(0, sel)
+            sb, mb = b.resolve(0, sel)
+            assert torch.equal(sa, sb) and torch.equal(ma, mb)
+        A, Bs = a.state(0), b.state(0)
+        for key in ("page_table", "slot_owner", "slot_stamp", "lru_order", "step"):
+            assert torch.equal(A[key], Bs[key]), key
+        assert not bool(Bs["kv_buffer"].any())
+    finally:
+        a.close()
+        b.close()
+
+
+def test_reset_requests_restores_empty_state():
+    say("reset_requests")
+    p = Pair(4, 2, 64, 128, 8, hsa.LAYOUT_BF16, seed=9)
+    rng = np.random.default_rng(1)
+    try:
+        for t in range(5):
+            for layer in (0, 1):
+                S = np.stack([rng.choice(1024, 64, replace=False) for _ in range(4)]).astype(np.int32)
+                p.step(layer, S, check_state=False)
+        p.hs.reset_requests(1, 2)
+        torch.cuda.synchronize()
+        for layer in (0, 1):
+            st = p.hs.state(layer)
+            assert (st["page_table"][1:3] == -1).all() and (st["slot_owner"][1:3] == -1).all()
+            assert (st["slot_stamp"][1:3] == -1).all() and (st["step"][1:3] == 0).all()
+            assert torch.equal(st["lru_order"][1:3].cpu(), torch.arange(128, dtype=torch.int32).repeat(2, 1))
+            assert (st["step"][0] == 5) and (st["step"][3] == 5)
+    finally:
+        p.close()
+
+
+def test_deterministic_repeat():
+    say("determinism: two handles, same trace")
+    w = C.BATCH64.with_(n=8, steps=20)
+    x = trace_for(w)
+    outs = []
+    for _ in range(2):
+        hs = hsa.HiSparse(2048, 4096, 8, 8)
+        fill_host_pool(hs, w.seed)
+        res = []
+        for t in range(x.shape[0]):
+            s, m = hs.resolve(0, torch.from_numpy(x[t]).cuda())
+            res.append((s.cpu(), m.cpu()))
+        st = hs.state(0)
+        res.append(tuple(st[k].cpu() for k in ("page_table", "slot_owner", "slot_stamp", "lru_order")))
+        res.append(st["kv_buffer"].cpu())
+        outs.append(res)
+        hs.close()
+    for a, b in zip(*outs):
+        if isinstance(a, tuple):
+            assert all(torch.equal(u, v) for u, v in zip(a, b))
+        else:
+            assert torch.equal(a, b)
+
+
+def test_graph_capture_replays_match_eager():
+    say("hipGraph capture of resolve, replayed over a trace")
+    w = C.BATCH64.with_(n=4, steps=12)
+    x = trace_for(w)
+    eager = hsa.HiSparse(2048, 4096, 8, 4)
+    graphed = hsa.HiSparse(2048, 4096, 8, 4)
+    try:
+        for h in (eager, graphed):
+            fill_host_pool(h, w.seed)
+        sel = torch.from_numpy(x[0]).cuda()
+        slots = torch.empty_like(sel)
+        miss = torch.empty(4, dtype=torch.int32, device="cuda")
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                graphed.resolve(0, sel, slots, miss, stream=s)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        # capture did not run the kernel: tables are still empty
+        assert int(graphed.state(0)["step"].sum()) == 0
+        for t in range(x.shape[0]):
+            sel.copy_(torch.from_numpy(x[t]))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            es, em = eager.resolve(0, torch.from_numpy(x[t]).cuda())
+            torch.cuda.synchronize()
+            assert torch.equal(es, slots) and torch.equal(em, miss), f"replay {t}"
+        A, Bs = eager.state(0), graphed.state(0)
+        for key in ("page_table", "slot_owner", "slot_stamp", "lru_order", "step", "kv_buffer"):
+            assert torch.equal(A[key], Bs[key]), key
+    finally:
+        eager.close()
+        graphed.close()
