@@ -1,0 +1,401 @@
+#!/usr/bin/env python3
+"""Benchmark of the HiSparse hot path on one MI355X.
+
+Default workload: 64 requests, 1 layer, context 32768, bf16 576-value entries (1152 B),
+top_k 2048, device buffer 4096 slots, host_to_device_ratio 8, resolve only; the selection
+trace is the seeded 200-step recency-window + Zipf(1.05) history with 10 % churn.  A step is
+one resolve of every request's selection (hit detection, LRU replacement, table update and
+the host-to-device fetch of the missing rows), replayed from a captured hipGraph; the first
+--warmup steps run untimed, then exactly --steps steps are timed.
+
+Metric: resolved top-k selections/s (whole job), with the miss-fetch rate against the
+host-link peak measured in the same run.  The JSON line also carries:
+  roofline     the resolver kernel against the host link (its bound): the timed graph holds
+               only resolver launches, so HIP events around it on the launch stream give
+               the kernel's average launch duration;
+  resolve_only the same steps on a handle that moves no rows (resolution cost alone);
+  cpu_baseline the CPU oracle on a bounded sample of the same trace, on this host's cores.
+
+--workload fp8_256 measures resolve + sparse MLA attention (256 requests, fp8 656-byte
+entries) instead and reports attention throughput against the HBM roofline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PCIE_GEN5_X16_GBPS = 64.0      # published host link peak per direction (MI355X, PCIe 5.0 x16)
+HBM_PEAK_GBPS = 8000.0         # published MI355X HBM3E peak
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+KERNEL_SRC = os.path.join(ROOT, "hierarchical_kv_cache_hs_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def _sha256(path):
+    import hashlib
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def recorded_traffic(key, source):
+    """HBM bytes per launch from the committed counter runs, or None if the kernel changed since."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))[key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256") != _sha256(os.path.join(KERNEL_SRC, source)):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def summarize_profile(args):
+    """Markdown summary of rocprofv3 output for one kernel (stats, timed dispatches, counters)."""
+    import csv
+    kern = args.kernel
+
+    def rows(path):
+        return list(csv.DictReader(open(path)))
+
+    lines = []
+    st = [r for r in rows(os.path.join(args.trace_dir, "run_kernel_stats.csv")) if kern in r["Name"]]
+    for r in st:
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    tr = sorted((r for r in rows(os.path.join(args.trace_dir, "run_kernel_trace.csv")) if kern in r["Kernel_Name"]),
+                key=lambda r: int(r["Dispatch_Id"]))
+    last = tr[-args.last:] if args.last else tr
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in last]
+    print("| kernel | calls | avg us | min us | max us |\n|---|---|---|---|---|")
+    print("\n".join(lines))
+    print(f"\nLast {len(last)} dispatches of the kernel (the timed steps): average {np.mean(dur):.2f} us, "
+          f"median {np.median(dur):.2f} us.")
+    out = {"avg_us_timed": float(np.mean(dur))}
+    if args.pmc_dir and args.copy_dir:
+        scale = {}
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            cr = sorted(rows(os.path.join(f"{args.copy_dir}_{c}", "run_counter_collection.csv")),
+                        key=lambda r: int(r["Dispatch_Id"]))[-5:]
+            kib = np.median([float(r["Counter_Value"]) for r in cr])
+            scale[c] = (256 * 1024) / kib
+            kr = sorted((r for r in rows(os.path.join(f"{args.pmc_dir}_{c}", "run_counter_collection.csv"))
+                         if kern in r["Kernel_Name"]), key=lambda r: int(r["Dispatch_Id"]))
+            kr = kr[-args.pmc_last:] if args.pmc_last else kr
+            v = float(np.mean([float(r["Counter_Value"]) for r in kr]))
+            out[c] = v
+            print(f"\n{c}: {v:.1f} KiB per dispatch over the last {len(kr)} dispatches; a plain copy of 256 MiB "
+                  f"reads as {kib:.1f} KiB, so scale x{scale[c]:.3f} -> {v * scale[c] * 1024 / 1e6:.2f} MB per launch")
+        out["bytes_per_launch"] = (out["FETCH_SIZE"] * scale["FETCH_SIZE"] + out["WRITE_SIZE"] * scale["WRITE_SIZE"]) * 1024
+        out["fetch_scale"], out["write_scale"] = scale["FETCH_SIZE"], scale["WRITE_SIZE"]
+        print(f"\nHBM + host-link traffic per launch (scaled FETCH + WRITE): {out['bytes_per_launch'] / 1e6:.2f} MB")
+    if args.record:
+        try:
+            rec = json.load(open(TRAFFIC_FILE))
+        except (OSError, ValueError):
+            rec = {}
+        out["kernel"] = kern
+        out["source_sha256"] = _sha256(os.path.join(KERNEL_SRC, args.source))
+        rec[args.record] = out
+        json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1, sort_keys=True)
+
+
+def measure_h2d_peak(torch, nbytes=1 << 30, reps=5):
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src, non_blocking=True)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return nbytes / ms / 1e6
+
+
+def cpu_baseline_resolve(w, trace, warm, budget_s=15.0):
+    """The oracle, as it stands, on the timed steps of the same trace.
+
+    The trace is replayed from an empty cache as many times as fit in about budget_s
+    seconds; only steps warm.. of each pass are timed, as on the GPU."""
+    import oracle
+    from synth import kv as skv
+    n, E = w.n, w.entry_bytes
+    host = np.empty((n, 1, w.cap, E), dtype=np.uint8)
+    for r in range(n):
+        skv.fill_rows(w.seed, r, 0, 0, w.cap, w.layout, host[r, 0].ctypes.data, E)
+    threads = oracle.default_threads()
+    done, el, passes = 0, 0.0, 0
+    while passes == 0 or el < budget_s:
+        oc = oracle.OracleCache(n, 1, w.B, w.cap, layout=w.layout, host=host, threads=threads)
+        for t in range(warm):
+            oc.resolve(0, trace[t])
+        t0 = time.perf_counter()
+        for t in range(warm, trace.shape[0]):
+            oc.resolve(0, trace[t])
+        el += time.perf_counter() - t0
+        done += trace.shape[0] - warm
+        passes += 1
+    return {"value": n * done / el, "unit": "selections/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle resolve (LRU tables + row copies) of all {n} requests on steps {warm}.."
+                      f"{trace.shape[0] - 1} of the same trace, {passes} passes from an empty cache "
+                      f"({done} steps timed, {el:.1f} s)"}
+
+
+def bench_resolve(args, torch, hsa, w):
+    from synth import kv as skv
+    from synth import trace as tr
+
+    T = args.warmup + args.steps
+    spec = w.trace_spec()
+    if T > spec.steps:
+        spec = w.with_(steps=T).trace_spec()
+    t0 = time.perf_counter()
+    trace = tr.generate(spec, steps=T)
+    log(f"trace {trace.shape} in {time.perf_counter() - t0:.1f}s")
+    d_trace = torch.from_numpy(trace).cuda()
+
+    handles = {}
+    for name, flags in (("io", 0), ("noio", hsa.FLAG_NO_IO)):
+        hs = hsa.HiSparse(w.k, w.B, w.ratio, w.n, 1, w.layout, 0, flags)
+        if flags == 0:
+            t0 = time.perf_counter()
+            for r in range(w.n):
+                ptr, cap, stride = hs.host_kv_ptr(0, r)
+                skv.fill_rows(w.seed, r, 0, 0, cap, w.layout, ptr, stride)
+            log(f"host pool {hsa.host_bytes(hs.cfg) / 2**30:.2f} GiB filled in {time.perf_counter() - t0:.1f}s")
+        handles[name] = hs
+
+    slots = torch.empty(w.n, w.k, dtype=torch.int32, device="cuda")
+    miss = torch.zeros(T, w.n, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    results = {}
+    for name, hs in handles.items():
+        with torch.cuda.stream(stream):
+            for t in range(args.warmup):
+                hs.resolve(0, d_trace[t], slots, miss[t], stream=stream)
+        stream.synchronize()
+        # capture the timed steps; the graph holds only resolver launches, so the region
+        # time over the launch count is the kernel's average launch duration
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(args.steps):
+                    t = args.warmup + i
+                    hs.resolve(0, d_trace[t], slots, miss[t], stream=stream)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):      # replay() launches on the current stream
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        region_ms = a.elapsed_time(b)
+        m = miss[args.warmup:].cpu().numpy().astype(np.int64)
+        results[name] = {"region_ms": region_ms, "kernel_ms": region_ms / args.steps, "miss": m}
+        log(f"{name}: {region_ms:.3f} ms for {args.steps} steps; {region_ms / args.steps * 1e3:.1f} us per launch")
+        del g
+
+    io, noio = results["io"], results["noio"]
+    assert (io["miss"] == noio["miss"]).all()
+    K = args.steps
+    total_miss = int(io["miss"].sum())
+    fetch_bytes = total_miss * w.entry_bytes
+    sel_per_s = w.n * K / (io["region_ms"] / 1e3)
+    avg_kernel_s = io["kernel_ms"] / 1e3
+    avg_kernel_noio_s = noio["kernel_ms"] / 1e3
+    bytes_per_launch = fetch_bytes / K
+    achieved = bytes_per_launch / avg_kernel_s / 1e9
+    fetch_only_s = max(avg_kernel_s - avg_kernel_noio_s, 1e-12)
+    h2d = measure_h2d_peak(torch)
+    log(f"H2D memcpy peak {h2d:.1f} GB/s")
+    traffic = recorded_traffic("resolve_batch64", "resolve.hip")
+    out = {
+        "metric": "resolved top-k selections/s + miss-fetch GB/s vs host-link peak, 1 MI355X",
+        "value": sel_per_s,
+        "unit": "selections/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": io["region_ms"] / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i32",
+        "data": "synthetic",
+        "config": {"workload": w.description, "global_batch": w.n, "seq_len": w.ctx, "top_k": w.k,
+                   "device_buffer_size": w.B, "host_to_device_ratio": w.ratio, "entry_bytes": w.entry_bytes,
+                   "steps_timed": f"{args.warmup}..{args.warmup + K - 1}", "graph": True},
+        "selected_tokens_per_s": sel_per_s * w.k,
+        "misses_per_selection": total_miss / (w.n * K),
+        "miss_fetch_GBps": fetch_bytes / (io["region_ms"] / 1e3) / 1e9,
+        "miss_fetch_GBps_fetch_only": bytes_per_launch / fetch_only_s / 1e9,
+        "h2d_peak_GBps_measured": h2d,
+        "miss_fetch_frac_of_measured_peak": (fetch_bytes / (io["region_ms"] / 1e3) / 1e9) / h2d,
+        "resolve_only": {"us_per_step": avg_kernel_noio_s * 1e6,
+                         "selections_per_s": w.n / avg_kernel_noio_s,
+                         "share_of_io_step": avg_kernel_noio_s / avg_kernel_s},
+        "roofline": {"bound": "host_link", "achieved": achieved, "peak": PCIE_GEN5_X16_GBPS, "unit": "GB/s",
+                     "frac": achieved / PCIE_GEN5_X16_GBPS, "traffic": traffic,
+                     "kernel": "resolve_kernel", "avg_kernel_us": avg_kernel_s * 1e6,
+                     "algorithmic_bytes_per_launch": bytes_per_launch,
+                     "frac_of_measured_peak": achieved / h2d},
+    }
+    for hs in handles.values():
+        hs.close()
+    return out, trace
+
+
+def bench_attend(args, torch, hsa, w):
+    """Resolve + attention on the fp8 256-request workload (attention against HBM)."""
+    from synth import kv as skv
+    from synth import trace as tr
+
+    T = args.warmup + args.steps
+    spec = w.with_(steps=max(T, w.steps)).trace_spec()
+    trace = tr.generate(spec, steps=T)
+    d_trace = torch.from_numpy(trace).cuda()
+    hs = hsa.HiSparse(w.k, w.B, w.ratio, w.n, 1, w.layout, 16, 0)
+    for r in range(w.n):
+        ptr, cap, stride = hs.host_kv_ptr(0, r)
+        skv.fill_rows(w.seed, r, 0, 0, cap, w.layout, ptr, stride)
+    qs = torch.from_numpy(np.stack([skv.queries(w.seed, t % 8, w.n, 0, 16) for t in range(8)]).view(np.int16)) \
+        .cuda().view(torch.bfloat16)
+    slots = torch.empty(T, w.n, w.k, dtype=torch.int32, device="cuda")
+    miss = torch.zeros(T, w.n, dtype=torch.int32, device="cuda")
+    out = torch.empty(w.n, 16, 512, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(w.n, 16, dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(576)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for t in range(args.warmup):
+            hs.resolve(0, d_trace[t], slots[t], miss[t], stream=stream)
+            hs.attend(0, qs[t % 8], slots[t], scale, out, lse, stream=stream)
+    stream.synchronize()
+
+    def timed(g):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):      # replay() launches on the current stream
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(args.steps):
+                t = args.warmup + i
+                hs.resolve(0, d_trace[t], slots[t], miss[t], stream=stream)
+                hs.attend(0, qs[t % 8], slots[t], scale, out, lse, stream=stream)
+    region_ms = timed(g)
+    # attention alone (it reads but does not change the cache): the same launches, no resolve
+    ga = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(ga, stream=stream):
+            for i in range(args.steps):
+                t = args.warmup + i
+                hs.attend(0, qs[t % 8], slots[t], scale, out, lse, stream=stream)
+    att_region_ms = timed(ga)
+    att_ms = [att_region_ms / args.steps]
+    res_ms = [(region_ms - att_region_ms) / args.steps]
+    K = args.steps
+    att_s = float(np.mean(att_ms)) / 1e3
+    valid = (slots[args.warmup:] >= 0).sum().item() / K
+    att_bytes = w.n * (4 * w.k) + valid * w.entry_bytes + w.n * 16 * (576 * 2 + 512 * 2 + 4)
+    achieved = att_bytes / att_s / 1e9
+    m = miss[args.warmup:].cpu().numpy().astype(np.int64)
+    out_line = {
+        "metric": "attention tokens/s over resolved slots, 1 MI355X",
+        "value": w.n * w.k / att_s,
+        "unit": "attended tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": region_ms / K,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.description + f" (churn {w.churn})", "global_batch": w.n, "seq_len": w.ctx,
+                   "top_k": w.k, "heads": 16, "graph": True},
+        "resolve_us_per_step": float(np.mean(res_ms)) * 1e3,
+        "misses_per_selection": float(m.mean()),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "attend_kernel",
+                     "avg_kernel_us": att_s * 1e6, "algorithmic_bytes_per_launch": att_bytes},
+    }
+    hs.close()
+    return out_line
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=190)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="batch64", choices=["batch64", "fp8_256"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--summarize-profile", action="store_true",
+                    help="print a markdown summary of rocprofv3 csv output (--trace-dir, --kernel, ...)")
+    ap.add_argument("--trace-dir")
+    ap.add_argument("--kernel")
+    ap.add_argument("--last", type=int, default=0)
+    ap.add_argument("--pmc-dir", help="prefix of the counter runs' directories (<prefix>_FETCH_SIZE, ...)")
+    ap.add_argument("--copy-dir", help="prefix of the copy-calibration counter runs' directories")
+    ap.add_argument("--pmc-last", type=int, default=0)
+    ap.add_argument("--record", help="store the traffic under this key in profiles/traffic.json")
+    ap.add_argument("--source", default="resolve.hip", help="kernel source file the record is keyed to")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 256 MiB (x5), to scale hardware byte counters")
+    args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(args)
+        return
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        sys.exit("--steps must be >= 1 and --warmup >= 0")
+
+    import torch
+    import hierarchical_kv_cache_hs_amd as hsa
+    from synth import configs as C
+
+    if not torch.cuda.is_available():
+        sys.exit("no GPU visible")
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": src.numel() * 4, "bytes_written": dst.numel() * 4}))
+        return
+    if args.workload == "batch64":
+        line, trace = bench_resolve(args, torch, hsa, C.BATCH64)
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline_resolve(C.BATCH64, trace, args.warmup, args.cpu_budget)
+            log(f"cpu baseline {line['cpu_baseline']['value']:.1f} selections/s")
+        else:
+            line["cpu_baseline"] = None
+    else:
+        line = bench_attend(args, torch, hsa, C.FP8_256)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -57,7 +57,6 @@ struct ResolveArgs {
   int32_t k;
   int32_t B;
   int32_t chunks;  // 16-byte chunks per row
-  int32_t no_io;
 };
 
 // Exclusive block-wide prefix sum of v; *total gets the block sum.  Every thread must call.
@@ -84,8 +83,9 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint3
   return before + x - v;
 }
 
-// KPT: selection entries per thread (KPT * NT >= k); OPT: LRU-order entries per thread (OPT * NT >= B).
-template <int KPT, int OPT>
+// KPT: selection entries per thread (KPT * NT >= k); OPT: LRU-order entries per thread (OPT * NT >= B);
+// FETCH: copy the missing rows (false: tables only, the no-IO measurement mode).
+template <int KPT, int OPT, bool FETCH>
 __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
   extern __shared__ uint32_t lds[];
   const int r = blockIdx.x;
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
   __syncthreads();
 
   // ---- P5
-  if (a.no_io || m == 0) return;
+  if (!FETCH || m == 0) return;
   const int C = a.chunks;
   const int total = m * C;
   const uint8_t* host = a.host + (int64_t)r * cap * a.host_stride;
@@ -307,14 +307,19 @@ __global__ void reset_kernel(int32_t* pt, int32_t* rm, int32_t* st, int32_t* ord
 template <int KPT, int OPT>
 void allow_large_lds() {
   // Lets a workgroup take up to the whole 160 KiB of LDS; errors are left to the launch.
-  (void)hipFuncSetAttribute((const void*)resolve_kernel<KPT, OPT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+  (void)hipFuncSetAttribute((const void*)resolve_kernel<KPT, OPT, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kLdsLimit);
+  (void)hipFuncSetAttribute((const void*)resolve_kernel<KPT, OPT, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)kLdsLimit);
   (void)hipGetLastError();
 }
 
 template <int KPT, int OPT>
-hipError_t launch_one(const ResolveArgs& a, int n_req, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((resolve_kernel<KPT, OPT>), dim3(n_req), dim3(NT), lds, s, a);
+hipError_t launch_one(const ResolveArgs& a, bool fetch, int n_req, size_t lds, hipStream_t s) {
+  if (fetch)
+    hipLaunchKernelGGL((resolve_kernel<KPT, OPT, true>), dim3(n_req), dim3(NT), lds, s, a);
+  else
+    hipLaunchKernelGGL((resolve_kernel<KPT, OPT, false>), dim3(n_req), dim3(NT), lds, s, a);
   return hipGetLastError();
 }
 
@@ -355,14 +360,14 @@ hipError_t launch_resolve(const Geometry& g, const LayerTables& t, const uint8_t
   a.k = g.k;
   a.B = g.B;
   a.chunks = (int32_t)(g.entry_bytes / 16);
-  a.no_io = (g.flags & HS_FLAG_NO_IO) ? 1 : 0;
+  const bool fetch = !(g.flags & HS_FLAG_NO_IO);
   const size_t lds = resolve_lds_bytes(g.cap, g.k, g.B);
   const int kpt = (g.k + NT - 1) / NT;
   const int opt = (g.B + NT - 1) / NT;
   if (kpt <= 4) {
-    return opt <= 8 ? launch_one<4, 8>(a, n_req, lds, s) : launch_one<4, 32>(a, n_req, lds, s);
+    return opt <= 8 ? launch_one<4, 8>(a, fetch, n_req, lds, s) : launch_one<4, 32>(a, fetch, n_req, lds, s);
   }
-  return opt <= 8 ? launch_one<16, 8>(a, n_req, lds, s) : launch_one<16, 32>(a, n_req, lds, s);
+  return opt <= 8 ? launch_one<16, 8>(a, fetch, n_req, lds, s) : launch_one<16, 32>(a, fetch, n_req, lds, s);
 }
 
 hipError_t launch_reset(const Geometry& g, int32_t* pt, int32_t* rm, int32_t* st, int32_t* ord, int32_t* step,
