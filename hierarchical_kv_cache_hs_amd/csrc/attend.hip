@@ -8,23 +8,30 @@
 // of the slot's entry (512 latent + 64 rope) and V_j its first 512 values (MLA form).
 // FP8 entries decode as e4m3 code * fp32 block scale (one scale per 128 latent values).
 //
-// Design for gfx950 (HBM-bound: ~1.3 MB of rows per request at k = 2048 against 71 MFLOP):
-//  * grid (splits, requests); a workgroup of 4 wave64s takes a contiguous chunk of the
-//    selection; each wave walks 16-token subtiles of it with its own online softmax and
-//    its own 16 x 512 fp32 output accumulator;
-//  * scores are computed transposed, S^T = K Q^T, on v_mfma_f32_16x16x32_bf16: a lane loads
-//    16-byte pieces of one token's row straight into the A operand (no LDS for K); Q sits in
-//    LDS and is read as the B operand.  The reduction index of the MFMA is mapped onto the
-//    576 values so that each lane's pieces of a 128-value block are contiguous in memory;
-//  * in S^T's accumulator layout a lane holds one head and four consecutive tokens, which is
-//    exactly the A-operand layout of v_mfma_f32_16x16x16bf16_1k, so P needs no shuffle;
-//  * V must arrive with four consecutive tokens per lane and a fixed column, the transpose of
-//    how rows are read.  One MFMA against a 0/1 selector matrix (exact: one product per
-//    output) turns the K registers into that layout, so V is never re-read or staged;
-//  * FP8 scales: per 128-value block, partial scores are scaled per token before they are
-//    summed; for P V the token's block scale is folded into P;
-//  * the four waves merge through LDS; with splits > 1 every workgroup writes an
-//    unnormalised partial (max, sum, 16 x 512 values) and the last one to arrive (atomic
+// Design for gfx950.  The kernel is bound by HBM (about 1.3 MB of rows per request at
+// k = 2048 against 71 MFLOP), so the design is about keeping rows in flight:
+//  * grid (splits, requests); a workgroup of 8 wave64s walks its chunk of the selection in
+//    64-token tiles.  Rows of a tile are gathered global -> LDS with 16-byte LDS-DMA loads
+//    (global_load_lds_dwordx4), up to NBUF - 1 tiles ahead of the one being computed, so
+//    the bytes in flight do not occupy registers; one barrier per tile both publishes the
+//    tile and frees the buffer the next DMA refills;
+//  * a tile's 64 tokens form four 16-token groups; each group is taken by a pair of waves
+//    that split the 576 values: wave half 0 owns latent values 0..255 and rope 0..31, half 1
+//    latent 256..511 and rope 32..63.  A wave converts only its half, computes its partial
+//    scores, and the pair exchanges the partials through LDS; both then hold the full scores
+//    and the same softmax state, and each accumulates P V for its own 256 output columns;
+//  * scores are computed transposed, S^T = K Q^T, on v_mfma_f32_16x16x32_bf16 with the
+//    K values as the A operand (a lane holds 8 consecutive values of one token).  In S^T's
+//    accumulator layout a lane holds one head and four consecutive tokens -- exactly the
+//    A-operand layout of v_mfma_f32_16x16x16bf16_1k -- so P needs no data movement;
+//  * V must reach the P V MFMA as four consecutive tokens of one column per lane, the
+//    transpose of how rows are held.  One MFMA of the K operand against a 0/1 selector
+//    (exact: one product per output) produces that layout;
+//  * FP8 codes decode with v_cvt_scalef32_pk_bf16_fp8 (exact); block scales are applied per
+//    token to the partial scores of each 128-value block and folded into P for the P V
+//    product of that block;
+//  * four token groups merge through LDS at the end; with splits > 1 each workgroup writes
+//    an unnormalised partial (max, sum, 16 x 512 values) and the last one to arrive (atomic
 //    counter, reset by that workgroup) combines them in split order, so results do not
 //    depend on arrival order.
 
@@ -41,12 +48,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int WAVES = 4;
+constexpr int WAVES = 8;
 constexpr int NT = WAVES * 64;
-constexpr int HMAX = 16;        // heads per workgroup (one MFMA tile)
-constexpr int DQK = 576;        // q.K length
-constexpr int DV = 512;         // value length
-constexpr int QS = DQK + 8;     // padded LDS row of Q (bf16 elements)
+constexpr int GROUPS = 4;                   // 16-token groups per tile
+constexpr int HMAX = 16;                    // heads per workgroup (one MFMA tile)
+constexpr int DQK = 576;                    // q.K length
+constexpr int DV = 512;                     // value length
+constexpr int KB_HALF = 9;                  // reduction blocks of 32 values per half
 constexpr int PART = 2 * HMAX + HMAX * DV;  // floats of one split partial
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -72,58 +80,113 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return u >> 16;
 }
 
-__device__ __forceinline__ s16x4 pack4(float a, float b, float c, float d) {
-  s16x4 v;
-  v[0] = (short)bf16_rne(a);
-  v[1] = (short)bf16_rne(b);
-  v[2] = (short)bf16_rne(c);
-  v[3] = (short)bf16_rne(d);
-  return v;
-}
-
-// Two E4M3FN codes (low 16 bits) -> two bf16 (exact).  The 7 magnitude bits shifted to
-// bit 20 form an fp32 whose exponent field is the code's exponent: scaling by 2^120
-// re-biases normals (bias 7 -> 127) and turns subnormal codes, which land in fp32's
-// subnormal range, into m * 2^-9.  The result has at most 4 significant bits, so its
-// top 16 bits are the bf16 value.
-__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t two) {
-  const uint32_t c0 = two & 0xFFu, c1 = (two >> 8) & 0xFFu;
-  const float f0 = __uint_as_float((c0 & 0x7Fu) << 20) * 0x1p120f;
-  const float f1 = __uint_as_float((c1 & 0x7Fu) << 20) * 0x1p120f;
-  const uint32_t b0 = (__float_as_uint(f0) >> 16) | ((c0 & 0x80u) << 8);
-  const uint32_t b1 = (__float_as_uint(f1) >> 16) | ((c1 & 0x80u) << 8);
-  return b0 | (b1 << 16);
-}
-
+// Eight E4M3FN codes -> eight bf16, exact (E4M3 values, subnormals included, are bf16
+// values): v_cvt_scalef32_pk_bf16_fp8 with scale 1 converts two codes per instruction.
 __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   u32x4 v;
-  v[0] = e4m3x2_to_bf16x2(lo);
-  v[1] = e4m3x2_to_bf16x2(lo >> 16);
-  v[2] = e4m3x2_to_bf16x2(hi);
-  v[3] = e4m3x2_to_bf16x2(hi >> 16);
+  v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+  v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+  v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+  v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
   return v;
 }
 
-// Element offset in a 576-value row of reduction block kb for lane group g:
-// latent blocks kb = 4b + i cover d = 128b + 32g + 8i + [0, 8); rope kb = 16 + i covers
-// d = 512 + 16g + 8i + [0, 8).
+// Four fp32 that are bf16 values already (the transposed V) -> packed bf16, by truncation.
+__device__ __forceinline__ s16x4 pack4_exact(const f32x4 x) {
+  u32x2 v;
+  v[0] = __builtin_amdgcn_perm(__float_as_uint(x[1]), __float_as_uint(x[0]), 0x07060302u);
+  v[1] = __builtin_amdgcn_perm(__float_as_uint(x[3]), __float_as_uint(x[2]), 0x07060302u);
+  return __builtin_bit_cast(s16x4, v);
+}
+
+// Four fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ s16x4 pack4_rne(float a, float b, float c, float d) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  v[2] = (__bf16)c;
+  v[3] = (__bf16)d;
+  return __builtin_bit_cast(s16x4, v);
+}
+
+// Value offset (within the 576) of reduction block kb (0..17) for lane group g: latent
+// blocks kb = 4b + i hold d = 128b + 32g + 8i + [0, 8); rope blocks kb = 16 + i hold
+// d = 512 + 16g + 8i + [0, 8).  Half hf owns latent kb 8hf..8hf+7 and rope kb 16 + hf.
 __device__ __forceinline__ int kb_offset(int kb, int g) {
   return kb < 16 ? 128 * (kb >> 2) + 32 * g + 8 * (kb & 3) : 512 + 16 * g + 8 * (kb - 16);
 }
 
-// Output column held by accumulator tile tau = 2 kb + sigma, column n of the tile.
+// Output column of accumulator tile tau (= 2 kb + sigma over latent kb) at tile column n.
 __device__ __forceinline__ int out_col(int tau, int n) {
   const int kb = tau >> 1, sigma = tau & 1;
   const int kappa = 16 * sigma + n;
   return 128 * (kb >> 2) + 32 * (kappa >> 3) + 8 * (kb & 3) + (kappa & 7);
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// A workgroup barrier without the fence __syncthreads() implies: that fence would wait for
+// every LDS-DMA load in flight, which is exactly what the ring must not do.  LDS writes made
+// before it must be waited for explicitly (lgkmcnt) by the caller.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ void lds_done_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <int LAYOUT>
-__global__ __launch_bounds__(NT) void attend_kernel(AttendArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[HMAX * QS];
-  __shared__ float wm[WAVES][HMAX];
-  __shared__ float wl[WAVES][HMAX];
-  __shared__ float o_acc[HMAX * DV];
+struct TileGeo {
+  static constexpr int E = LAYOUT == 0 ? 1152 : 656;      // bytes per row
+  static constexpr int C = E / 16;                        // 16-byte chunks per row
+  static constexpr int NBUF = LAYOUT == 0 ? 2 : 3;        // ring depth
+  static constexpr int T = 16 * GROUPS;                   // tokens per tile
+  static constexpr int TILE = T * E;                      // bytes per tile
+  static constexpr int CHUNKS = T * C;
+  static constexpr int L0 = (CHUNKS + NT - 1) / NT;       // DMA instructions per tile, wave 0
+  static constexpr int MAXCHUNK = LAYOUT == 0 ? 1024 : 2048;  // tokens per workgroup
+  static_assert(CHUNKS % 64 == 0, "tile chunks must fill whole waves");
+};
+
+// DMA instructions wave w issues per tile: j with j * NT + 64 w < CHUNKS (wave-uniform).
+template <int LAYOUT>
+__device__ __forceinline__ int dma_per_tile(int w) {
+  return (TileGeo<LAYOUT>::CHUNKS - 64 * w + NT - 1) / NT;
+}
+
+// Wait until at most `pending` (0 .. NBUF - 2) later tiles of this wave's DMA are outstanding.
+template <int LAYOUT>
+__device__ __forceinline__ void wait_tiles(int pending, int per) {
+  if (LAYOUT == 0) {
+    static_assert(TileGeo<0>::NBUF == 2, "wait table");
+    wait_vmcnt<0>();
+  } else {
+    static_assert(TileGeo<1>::NBUF == 3 && TileGeo<1>::L0 == 6, "wait table");
+    if (pending == 0) wait_vmcnt<0>();
+    else if (per == 6) wait_vmcnt<6>();
+    else wait_vmcnt<5>();
+  }
+}
+
+template <int LAYOUT>
+constexpr size_t ring_bytes() { return (size_t)TileGeo<LAYOUT>::NBUF * TileGeo<LAYOUT>::TILE; }
+
+template <int LAYOUT>
+constexpr size_t attend_lds_bytes() {
+  return ring_bytes<LAYOUT>() + TileGeo<LAYOUT>::MAXCHUNK * sizeof(int32_t) + WAVES * 64 * sizeof(f32x4);
+}
+
+template <int LAYOUT>
+__global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
+  using G = TileGeo<LAYOUT>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* ring = smem;                                              // [NBUF][TILE]
+  int32_t* slot_lds = (int32_t*)(smem + ring_bytes<LAYOUT>());       // [MAXCHUNK]
+  f32x4* xch = (f32x4*)(smem + ring_bytes<LAYOUT>() + G::MAXCHUNK * sizeof(int32_t));  // [WAVES][64]
+  float* o_acc = (float*)smem;                                       // after the loop: [16][512]
+  __shared__ float wm[GROUPS][HMAX];
+  __shared__ float wl[GROUPS][HMAX];
   __shared__ int last_flag;
 
   const int s = blockIdx.x;
@@ -131,21 +194,57 @@ __global__ __launch_bounds__(NT) void attend_kernel(AttendArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const int tg = w & 3;          // token group within a tile
+  const int hf = w >> 2;         // value half
   const int g = lane >> 4;
   const int c16 = lane & 15;
   const int heads = a.heads;
 
-  // ---- Q to LDS (rows >= heads are zero)
-  for (int c = tid; c < HMAX * (DQK / 8); c += NT) {
-    const int h = c / (DQK / 8), part = c - h * (DQK / 8);
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (h < heads) v = load16(a.q + ((int64_t)r * heads + h) * DQK + part * 8);
-    *(u32x4*)(q_lds + h * QS + part * 8) = v;
+  const int tok0 = s * a.chunk;
+  const int tok1 = min(a.k, tok0 + a.chunk);
+  const int ntok = tok1 > tok0 ? tok1 - tok0 : 0;
+  const int ntiles = (ntok + G::T - 1) / G::T;
+  const uint8_t* rbase = a.buf + (int64_t)r * a.B * a.stride;
+
+  // ---- this workgroup's slot list (invalid or missing -> -1) and this wave's Q operands
+  {
+    const int32_t* sl = a.slots + (int64_t)r * a.k + tok0;
+    for (int i = tid; i < ntiles * G::T; i += NT) {
+      const int32_t v = (i < ntok) ? sl[i] : -1;
+      slot_lds[i] = (v >= 0 && v < a.B) ? v : -1;
+    }
+  }
+  u32x4 qreg[KB_HALF];
+#pragma unroll
+  for (int i = 0; i < KB_HALF; ++i) {
+    const int kb = (i < 8) ? 8 * hf + i : 16 + hf;
+    qreg[i] = (c16 < heads) ? load16(a.q + ((int64_t)r * heads + c16) * DQK + kb_offset(kb, g))
+                            : (u32x4){0u, 0u, 0u, 0u};
   }
   __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0);
 
-  // selector B operands: lane (g, n=c16) holds reduction rows 8g..8g+7 of column n;
-  // sigma = 0 picks reduction row n, sigma = 1 picks row 16 + n.
+  const int per = dma_per_tile<LAYOUT>(w);
+  auto issue = [&](int t) {
+    uint8_t* dst = ring + (t % G::NBUF) * G::TILE;
+#pragma unroll
+    for (int j = 0; j < G::L0; ++j) {
+      const int base = j * NT + 64 * w;
+      if (base < G::CHUNKS) {
+        const int c = base + lane;
+        const int row = c / G::C;
+        const int col = c - row * G::C;
+        int32_t sl = slot_lds[t * G::T + row];
+        sl = sl < 0 ? 0 : sl;  // padding reads an in-bounds row; its operands are zeroed below
+        const uint8_t* src = rbase + (int64_t)sl * a.stride + col * 16;
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                         (void __attribute__((address_space(3)))*)(dst + base * 16), 16, 0, 0);
+      }
+    }
+  };
+
+  // selector B operands of the V transposition: lane (g, n = c16) holds reduction rows
+  // 8g..8g+7 of column n; sigma = 0 selects row n, sigma = 1 row 16 + n.
   bf16x8 sel0, sel1;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -154,93 +253,103 @@ __global__ __launch_bounds__(NT) void attend_kernel(AttendArgs a) {
     sel1[e] = (kappa == 16 + c16) ? (__bf16)1.0f : (__bf16)0.0f;
   }
 
-  f32x4 O[32];
+  f32x4 O[16];
 #pragma unroll
-  for (int t = 0; t < 32; ++t) O[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < 16; ++t) O[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int tok0 = s * a.chunk;
-  const int tok1 = min(a.k, tok0 + a.chunk);
-  const int nsub = tok1 > tok0 ? (tok1 - tok0 + 15) / 16 : 0;
-  const int32_t* slots = a.slots + (int64_t)r * a.k;
-  const uint8_t* rbase = a.buf + (int64_t)r * a.B * a.stride;
+  for (int t = 0; t < G::NBUF - 1 && t < ntiles; ++t) issue(t);
 
-  for (int sub = w; sub < nsub; sub += WAVES) {
-    const int t = tok0 + sub * 16 + c16;
-    const int32_t slot = (t < tok1) ? slots[t] : -1;
-    const bool valid = slot >= 0 && slot < a.B;
-    const uint8_t* row = rbase + (int64_t)(valid ? slot : 0) * a.stride;
+  for (int t = 0; t < ntiles; ++t) {
+    // Tiles t .. t + NBUF - 2 are in flight.  Once every wave is past this barrier, all
+    // are done with tile t - 1, whose buffer then takes tile t + NBUF - 1.
+    wait_tiles<LAYOUT>(min(G::NBUF - 2, ntiles - 1 - t), per);
+    barrier_only();
+    if (t + G::NBUF - 1 < ntiles) issue(t + G::NBUF - 1);
 
-    u32x4 kreg[18];
-    float sc[4] = {1.f, 1.f, 1.f, 1.f};
+    const uint8_t* tile = ring + (t % G::NBUF) * G::TILE;
+    const int trow = 16 * tg + c16;                       // this lane's token (A-operand row)
+    const bool valid = slot_lds[t * G::T + trow] >= 0;
+    const u32x4 vq = *(const u32x4*)(slot_lds + t * G::T + 16 * tg + 4 * g);  // tokens 4g..4g+3
+    const uint8_t* row = tile + trow * G::E;
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+
+    // ---- this half's K operands
+    u32x4 kreg[KB_HALF];
+    float sc[4][2];   // scales of tokens 4g + j, blocks 2hf and 2hf + 1
     if (LAYOUT == 0) {
 #pragma unroll
-      for (int kb = 0; kb < 18; ++kb)
-        kreg[kb] = valid ? load16(row + 2 * kb_offset(kb, g)) : (u32x4){0u, 0u, 0u, 0u};
+      for (int i = 0; i < KB_HALF; ++i) {
+        const int kb = (i < 8) ? 8 * hf + i : 16 + hf;
+        const u32x4 v = *(const u32x4*)(row + 2 * kb_offset(kb, g));
+        kreg[i] = valid ? v : z4;
+      }
     } else {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        u32x4 lo = valid ? load16(row + 128 * b + 32 * g) : (u32x4){0u, 0u, 0u, 0u};
-        u32x4 hi = valid ? load16(row + 128 * b + 32 * g + 16) : (u32x4){0u, 0u, 0u, 0u};
-        kreg[4 * b + 0] = e4m3x8_to_bf16x8(lo[0], lo[1]);
-        kreg[4 * b + 1] = e4m3x8_to_bf16x8(lo[2], lo[3]);
-        kreg[4 * b + 2] = e4m3x8_to_bf16x8(hi[0], hi[1]);
-        kreg[4 * b + 3] = e4m3x8_to_bf16x8(hi[2], hi[3]);
+      for (int bb = 0; bb < 2; ++bb) {
+        const int b = 2 * hf + bb;
+        u32x4 lo = *(const u32x4*)(row + 128 * b + 32 * g);
+        u32x4 hi = *(const u32x4*)(row + 128 * b + 32 * g + 16);
+        lo = valid ? lo : z4;
+        hi = valid ? hi : z4;
+        kreg[4 * bb + 0] = e4m3x8_to_bf16x8(lo[0], lo[1]);
+        kreg[4 * bb + 1] = e4m3x8_to_bf16x8(lo[2], lo[3]);
+        kreg[4 * bb + 2] = e4m3x8_to_bf16x8(hi[0], hi[1]);
+        kreg[4 * bb + 3] = e4m3x8_to_bf16x8(hi[2], hi[3]);
       }
-      kreg[16] = valid ? load16(row + 528 + 32 * g) : (u32x4){0u, 0u, 0u, 0u};
-      kreg[17] = valid ? load16(row + 528 + 32 * g + 16) : (u32x4){0u, 0u, 0u, 0u};
-      if (valid) {
-        const u32x4 sv = load16(row + 512);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) sc[b] = __uint_as_float(sv[b]);
-      }
-    }
-
-    // ---- S^T[tok][h] = K Q^T
-    float sv4[4];
-    const uint16_t* qrow = q_lds + c16 * QS;
-    if (LAYOUT == 0) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < 18; ++kb) {
-        const bf16x8 qb = *(const bf16x8*)(qrow + kb_offset(kb, g));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[kb]), qb, acc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sv4[j] = acc[j];
-    } else {
-      f32x4 accb[4], accr = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        accb[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kb = 4 * b + i;
-          const bf16x8 qb = *(const bf16x8*)(qrow + kb_offset(kb, g));
-          accb[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[kb]), qb, accb[b], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int kb = 16; kb < 18; ++kb) {
-        const bf16x8 qb = *(const bf16x8*)(qrow + kb_offset(kb, g));
-        accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[kb]), qb, accr, 0, 0, 0);
-      }
+      const u32x4 rv = *(const u32x4*)(row + 528 + 32 * g + 16 * hf);
+      kreg[8] = valid ? rv : z4;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float v = accr[j];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) v += __shfl(sc[b], 4 * g + j) * accb[b][j];
-        sv4[j] = v;
+        const u32x2 sv = *(const u32x2*)(tile + (16 * tg + 4 * g + j) * G::E + 512 + 8 * hf);
+        sc[j][0] = __uint_as_float(sv[0]);
+        sc[j][1] = __uint_as_float(sv[1]);
       }
     }
 
-    // ---- online softmax for head c16 over tokens 4g + j of this subtile
+    // ---- partial S^T[tok][h] over this half
+    f32x4 part;
+    if (LAYOUT == 0) {
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < KB_HALF; i += 2)
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[i]),
+                                                       __builtin_bit_cast(bf16x8, qreg[i]), acc0, 0, 0, 0);
+#pragma unroll
+      for (int i = 1; i < KB_HALF; i += 2)
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[i]),
+                                                       __builtin_bit_cast(bf16x8, qreg[i]), acc1, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) part[j] = acc0[j] + acc1[j];
+    } else {
+      f32x4 accb[2], accr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        accb[bb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          accb[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[4 * bb + i]),
+                                                             __builtin_bit_cast(bf16x8, qreg[4 * bb + i]),
+                                                             accb[bb], 0, 0, 0);
+      }
+      accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[8]),
+                                                     __builtin_bit_cast(bf16x8, qreg[8]), accr, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) part[j] = accr[j] + sc[j][0] * accb[0][j] + sc[j][1] * accb[1][j];
+    }
+
+    // ---- pair exchange: both halves end with the full scores
+    xch[w * 64 + lane] = part;
+    lds_done_barrier();
+    const f32x4 other = xch[(w ^ 4) * 64 + lane];
     float s2[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int vj = __shfl((int)valid, 4 * g + j);
-      s2[j] = vj ? sv4[j] * a.scale_log2 : -INFINITY;
+      const float sj = part[j] + other[j];
+      s2[j] = (vq[j] != 0xFFFFFFFFu) ? sj * a.scale_log2 : -INFINITY;
     }
+
+    // ---- online softmax for head c16 over tokens 4g + j of this group
     float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -257,45 +366,45 @@ __global__ __launch_bounds__(NT) void attend_kernel(AttendArgs a) {
     l_run = l_run * alpha + rs;
     m_run = m_new;
 
-    // rescale the accumulator rows (heads 4g + j)
-    float aj[4];
+    // rescale the accumulator rows (heads 4g + j) only when some head's maximum moved
+    if (__any(alpha != 1.f)) {
+      float aj[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) aj[j] = __shfl(alpha, 4 * g + j);
+      for (int j = 0; j < 4; ++j) aj[j] = __shfl(alpha, 4 * g + j);
 #pragma unroll
-    for (int tau = 0; tau < 32; ++tau)
+      for (int tau = 0; tau < 16; ++tau)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) O[tau][j] *= aj[j];
+        for (int j = 0; j < 4; ++j) O[tau][j] *= aj[j];
+    }
 
-    // ---- O += P V
-    s16x4 pa[4];
+    // ---- O += P V over this half's 256 columns
+    s16x4 pa[2];
     if (LAYOUT == 0) {
-      pa[0] = pack4(p[0], p[1], p[2], p[3]);
+      pa[0] = pack4_rne(p[0], p[1], p[2], p[3]);
+      pa[1] = pa[0];
     } else {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        float t4[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) t4[j] = p[j] * __shfl(sc[b], 4 * g + j);
-        pa[b] = pack4(t4[0], t4[1], t4[2], t4[3]);
-      }
+      for (int bb = 0; bb < 2; ++bb)
+        pa[bb] = pack4_rne(p[0] * sc[0][bb], p[1] * sc[1][bb], p[2] * sc[2][bb], p[3] * sc[3][bb]);
     }
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < 16; ++kb) {
-      const bf16x8 kv = __builtin_bit_cast(bf16x8, kreg[kb]);
-      const s16x4 P = (LAYOUT == 0) ? pa[0] : pa[kb >> 2];
+    for (int i = 0; i < 8; ++i) {
+      const bf16x8 kv = __builtin_bit_cast(bf16x8, kreg[i]);
+      const s16x4 P = pa[i >> 2];
       const f32x4 t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, sel0, zero, 0, 0, 0);
       const f32x4 t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, sel1, zero, 0, 0, 0);
-      O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(P, pack4(t0[0], t0[1], t0[2], t0[3]), O[2 * kb], 0, 0, 0);
-      O[2 * kb + 1] =
-          __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(P, pack4(t1[0], t1[1], t1[2], t1[3]), O[2 * kb + 1], 0, 0, 0);
+      O[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(P, pack4_exact(t0), O[2 * i], 0, 0, 0);
+      O[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(P, pack4_exact(t1), O[2 * i + 1], 0, 0, 0);
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
-  // ---- merge the four waves (fixed order)
-  if (g == 0) {
-    wm[w][c16] = m_run;
-    wl[w][c16] = l_run;
+  // ---- merge the four token groups (fixed order); o_acc reuses the ring
+  if (hf == 0 && g == 0) {
+    wm[tg][c16] = m_run;
+    wl[tg][c16] = l_run;
   }
   __syncthreads();
   float f[4];
@@ -304,18 +413,18 @@ __global__ __launch_bounds__(NT) void attend_kernel(AttendArgs a) {
     const int h = 4 * g + j;
     float M = wm[0][h];
 #pragma unroll
-    for (int v = 1; v < WAVES; ++v) M = fmaxf(M, wm[v][h]);
-    f[j] = (M == -INFINITY) ? 0.f : exp2f(wm[w][h] - M);
+    for (int v = 1; v < GROUPS; ++v) M = fmaxf(M, wm[v][h]);
+    f[j] = (M == -INFINITY) ? 0.f : exp2f(wm[tg][h] - M);
   }
-  for (int v = 0; v < WAVES; ++v) {
-    if (w == v) {
+  for (int v = 0; v < GROUPS; ++v) {
+    if (tg == v) {
 #pragma unroll
-      for (int tau = 0; tau < 32; ++tau) {
-        const int col = out_col(tau, c16);
+      for (int i = 0; i < 16; ++i) {
+        const int col = out_col(16 * hf + i, c16);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int idx = (4 * g + j) * DV + col;
-          const float val = O[tau][j] * f[j];
+          const float val = O[i][j] * f[j];
           o_acc[idx] = (v == 0) ? val : o_acc[idx] + val;
         }
       }
@@ -323,19 +432,15 @@ __global__ __launch_bounds__(NT) void attend_kernel(AttendArgs a) {
     __syncthreads();
   }
 
-  // per-head max and sum of the workgroup
-  float Mh[1], Lh[1];
-  (void)Mh;
-  (void)Lh;
   const int splits = a.splits;
   if (splits == 1) {
     for (int idx = tid; idx < heads * DV; idx += NT) {
       const int h = idx / DV;
       float M = wm[0][h];
-      for (int v = 1; v < WAVES; ++v) M = fmaxf(M, wm[v][h]);
+      for (int v = 1; v < GROUPS; ++v) M = fmaxf(M, wm[v][h]);
       float L = 0.f;
       if (M != -INFINITY)
-        for (int v = 0; v < WAVES; ++v) L += exp2f(wm[v][h] - M) * wl[v][h];
+        for (int v = 0; v < GROUPS; ++v) L += exp2f(wm[v][h] - M) * wl[v][h];
       const float val = L > 0.f ? o_acc[idx] / L : 0.f;
       a.out[(int64_t)r * heads * DV + idx] = (uint16_t)bf16_rne(val);
       if ((idx % DV) == 0 && a.lse) a.lse[(int64_t)r * heads + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
@@ -347,10 +452,10 @@ __global__ __launch_bounds__(NT) void attend_kernel(AttendArgs a) {
   if (tid < HMAX) {
     const int h = tid;
     float M = wm[0][h];
-    for (int v = 1; v < WAVES; ++v) M = fmaxf(M, wm[v][h]);
+    for (int v = 1; v < GROUPS; ++v) M = fmaxf(M, wm[v][h]);
     float L = 0.f;
     if (M != -INFINITY)
-      for (int v = 0; v < WAVES; ++v) L += exp2f(wm[v][h] - M) * wl[v][h];
+      for (int v = 0; v < GROUPS; ++v) L += exp2f(wm[v][h] - M) * wl[v][h];
     mypart[h] = M;
     mypart[HMAX + h] = L;
   }
@@ -381,20 +486,35 @@ __global__ __launch_bounds__(NT) void attend_kernel(AttendArgs a) {
   if (tid == 0) a.cnt[r] = 0u;
 }
 
+int max_chunk(const Geometry& g) {
+  return g.layout == HS_KV_BF16_576 ? TileGeo<0>::MAXCHUNK : TileGeo<1>::MAXCHUNK;
+}
+
 }  // namespace
 
 int attend_splits(const Geometry& g) {
-  // enough workgroups for two per compute unit at full batch, at least 64 tokens each
-  const int by_batch = (2 * 256 + g.n - 1) / g.n;
+  // one workgroup per compute unit at full batch (a workgroup's ring fills most of a CU's
+  // LDS), at most MAXCHUNK tokens per workgroup, and at least one 64-token tile each
+  int s = (256 + g.n - 1) / g.n;
   const int by_len = (g.k + 63) / 64;
-  int s = by_batch < by_len ? by_batch : by_len;
+  const int need = (g.k + max_chunk(g) - 1) / max_chunk(g);
+  if (s > by_len) s = by_len;
   if (s > 16) s = 16;
+  if (s < need) s = need;
   return s < 1 ? 1 : s;
 }
 
 size_t attend_partial_floats(const Geometry& g) {
   const int s = attend_splits(g);
   return s > 1 ? (size_t)s * PART : 0;
+}
+
+void prepare_attend() {
+  (void)hipFuncSetAttribute((const void*)attend_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)attend_lds_bytes<0>());
+  (void)hipFuncSetAttribute((const void*)attend_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)attend_lds_bytes<1>());
+  (void)hipGetLastError();
 }
 
 hipError_t launch_attend(const Geometry& g, const LayerTables& t, int32_t n_req, const void* q, const int32_t* slots,
@@ -416,11 +536,12 @@ hipError_t launch_attend(const Geometry& g, const LayerTables& t, int32_t n_req,
   a.chunk = (per + 15) / 16 * 16;
   a.scale_log2 = scale * kLog2e;
   if (a.splits > 1 && !a.part) return hipErrorInvalidValue;
+  if (a.chunk > max_chunk(g)) return hipErrorInvalidValue;
   dim3 grid(a.splits, n_req);
   if (g.layout == HS_KV_BF16_576)
-    hipLaunchKernelGGL(attend_kernel<0>, grid, dim3(NT), 0, st, a);
+    hipLaunchKernelGGL(attend_kernel<0>, grid, dim3(NT), attend_lds_bytes<0>(), st, a);
   else
-    hipLaunchKernelGGL(attend_kernel<1>, grid, dim3(NT), 0, st, a);
+    hipLaunchKernelGGL(attend_kernel<1>, grid, dim3(NT), attend_lds_bytes<1>(), st, a);
   return hipGetLastError();
 }
 

@@ -237,6 +237,7 @@ hs_status hs_create(const hs_config* cfg, hs_handle** out) {
   h->buf = b + lay.buf;
 
   hs::prepare_resolve();
+  hs::prepare_attend();
   e = hipMemset(h->err, 0, sizeof(int32_t));
   if (e != hipSuccess) { release(h); return fail_hip(e, "hipMemset"); }
   e = hs::launch_reset(g, h->pt, h->rm, h->st, h->ord, h->step, h->cnt, 0, g.n, nullptr);

@@ -49,6 +49,9 @@ hipError_t launch_resolve(const Geometry& g, const LayerTables& t, const uint8_t
 hipError_t launch_reset(const Geometry& g, int32_t* pt, int32_t* rm, int32_t* st, int32_t* ord, int32_t* step,
                         uint32_t* cnt, int32_t first, int32_t count, hipStream_t s);
 
+// Once per process, before the first attention launch.
+void prepare_attend();
+
 // Attention: split factor and partial-buffer floats per request.
 int attend_splits(const Geometry& g);
 size_t attend_partial_floats(const Geometry& g);
