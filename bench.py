@@ -322,6 +322,7 @@ def bench_attend(args, torch, hsa, w):
     att_bytes = w.n * (4 * w.k) + valid * w.entry_bytes + w.n * 16 * (576 * 2 + 512 * 2 + 4)
     achieved = att_bytes / att_s / 1e9
     m = miss[args.warmup:].cpu().numpy().astype(np.int64)
+    traffic = recorded_traffic("attend_fp8_256", "attend.hip")
     out_line = {
         "metric": "attention tokens/s over resolved slots, 1 MI355X",
         "value": w.n * w.k / att_s,
@@ -333,7 +334,7 @@ def bench_attend(args, torch, hsa, w):
         "resolve_us_per_step": float(np.mean(res_ms)) * 1e3,
         "misses_per_selection": float(m.mean()),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "attend_kernel",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic, "kernel": "attend_kernel",
                      "avg_kernel_us": att_s * 1e6, "algorithmic_bytes_per_launch": att_bytes},
     }
     hs.close()
