@@ -18,6 +18,8 @@ host-link peak measured in the same run.  The JSON line also carries:
 
 --workload fp8_256 measures resolve + sparse MLA attention (256 requests, fp8 656-byte
 entries) instead and reports attention throughput against the HBM roofline.
+--workload prefetch times whole decode steps over 8 layers sharing one selection (128
+requests, fp8), in serial order and with layer-wise prefetch.
 """
 from __future__ import annotations
 
@@ -306,16 +308,24 @@ def bench_attend(args, torch, hsa, w):
                 hs.resolve(0, d_trace[t], slots[t], miss[t], stream=stream)
                 hs.attend(0, qs[t % 8], slots[t], scale, out, lse, stream=stream)
     region_ms = timed(g)
-    # attention alone (it reads but does not change the cache): the same launches, no resolve
-    ga = torch.cuda.CUDAGraph()
+    # attention alone, cold: before every launch a 1 GiB read evicts the rows from the L2 and
+    # the 256 MB last-level cache (a read leaves clean lines, so the timed launch pays no
+    # write-back), as in a real step where other layers' rows intervene; HIP events on the
+    # launch stream bracket each attention launch
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    att_ms = []
     with torch.cuda.stream(stream):
-        with torch.cuda.graph(ga, stream=stream):
-            for i in range(args.steps):
-                t = args.warmup + i
-                hs.attend(0, qs[t % 8], slots[t], scale, out, lse, stream=stream)
-    att_region_ms = timed(ga)
-    att_ms = [att_region_ms / args.steps]
-    res_ms = [(region_ms - att_region_ms) / args.steps]
+        for i in range(args.steps):
+            t = args.warmup + i
+            flush.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            hs.attend(0, qs[t % 8], slots[t], scale, out, lse, stream=stream)
+            b.record(stream)
+            b.synchronize()
+            att_ms.append(a.elapsed_time(b))
+    del flush
+    res_ms = [region_ms / args.steps - float(np.mean(att_ms))]
     K = args.steps
     att_s = float(np.mean(att_ms)) / 1e3
     valid = (slots[args.warmup:] >= 0).sum().item() / K
@@ -341,12 +351,95 @@ def bench_attend(args, torch, hsa, w):
     return out_line
 
 
+def bench_prefetch(args, torch, hsa, w):
+    """Decode steps over 8 layers sharing a selection: serial order vs layer-wise prefetch."""
+    from hierarchical_kv_cache_hs_amd.decode_step import DecodeSteps
+    from synth import kv as skv
+    from synth import trace as tr
+
+    K = min(args.steps, w.steps - args.warmup)
+    T = args.warmup + K
+    trace = tr.generate(w.trace_spec(), steps=T)
+    d_trace = torch.from_numpy(trace).cuda()
+    hs = hsa.HiSparse(w.k, w.B, w.ratio, w.n, w.layers, w.layout, 16, 0)
+    t0 = time.perf_counter()
+    for l in range(w.layers):
+        for r in range(w.n):
+            ptr, cap, stride = hs.host_kv_ptr(l, r)
+            skv.fill_rows(w.seed, r, l, 0, cap, w.layout, ptr, stride)
+    log(f"host pool {hsa.host_bytes(hs.cfg) / 2**30:.1f} GiB filled in {time.perf_counter() - t0:.1f}s")
+    qs = [torch.from_numpy(np.stack([skv.queries(w.seed, t, w.n, l, 16) for l in range(w.layers)]).view(np.int16))
+          .cuda().view(torch.bfloat16) for t in range(4)]
+    scale = 1.0 / math.sqrt(576)
+    sels = [d_trace[t] for t in range(T)]
+    qsteps = [qs[t % 4] for t in range(T)]
+
+    def timed(prefetch, attend):
+        hs.reset_requests(0, w.n)
+        DecodeSteps(hs, sels[:args.warmup], qsteps[:args.warmup], scale, prefetch=False, attend=attend).replay()
+        steps = DecodeSteps(hs, sels[args.warmup:], qsteps[args.warmup:], scale, prefetch=prefetch, attend=attend)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(steps.stream):
+            a.record(steps.stream)
+            steps.graph.replay()
+            b.record(steps.stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / K, steps
+
+    t_ser, s_ser = timed(False, True)
+    t_pre, s_pre = timed(True, True)
+    t_res, _ = timed(False, False)
+    same = torch.equal(s_ser.out, s_pre.out) and torch.equal(s_ser.miss, s_pre.miss)
+    t_att = t_ser - t_res
+    # attention alone over the 8 layers (each launch reads another layer's rows), K times
+    ga = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(ga, stream=st):
+            for i in range(K):
+                for l in range(w.layers):
+                    hs.attend(l, qsteps[i][l], s_ser.slots[l], scale, s_ser.out[l], s_ser.lse[l], stream=st)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(st):
+        a.record(st)
+        ga.replay()
+        b.record(st)
+    torch.cuda.synchronize()
+    t_att_only = a.elapsed_time(b) / K
+    valid = float((s_ser.slots >= 0).sum().item()) / w.layers
+    att_bytes = valid * w.entry_bytes + w.n * (4 * w.k + 16 * (576 * 2 + 512 * 2 + 4))
+    misses = float(s_ser.miss.double().mean())
+    out = {
+        "metric": "decode steps/s, 8 layers sharing a selection, layer-wise prefetch, 1 MI355X",
+        "value": 1e3 / t_pre, "unit": "steps/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": t_pre, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.description, "global_batch": w.n, "layers": w.layers, "seq_len": w.ctx,
+                   "top_k": w.k, "graph": True},
+        "serial_ms_per_step": t_ser, "prefetch_ms_per_step": t_pre, "resolve_only_ms_per_step": t_res,
+        "attention_ms_per_step": t_att,
+        "attention_alone_ms_per_step": t_att_only,
+        "attention_alone_GBps": att_bytes * w.layers / (t_att_only / 1e3) / 1e9,
+        "overlap_saved_ms_per_step": t_ser - t_pre,
+        "attention_hidden_fraction": (t_ser - t_pre) / t_att if t_att > 0 else None,
+        "misses_per_selection": misses,
+        "miss_GB_per_step": misses * w.n * w.layers * w.entry_bytes / 1e9,
+        "prefetch_equals_serial": bool(same),
+        "selections_per_s": w.n * w.layers / (t_pre / 1e3),
+    }
+    hs.close()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=190)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="batch64", choices=["batch64", "fp8_256"])
+    ap.add_argument("--workload", default="batch64", choices=["batch64", "fp8_256", "prefetch"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--summarize-profile", action="store_true",
@@ -393,6 +486,8 @@ def main():
             log(f"cpu baseline {line['cpu_baseline']['value']:.1f} selections/s")
         else:
             line["cpu_baseline"] = None
+    elif args.workload == "prefetch":
+        line = bench_prefetch(args, torch, hsa, C.PREFETCH)
     else:
         line = bench_attend(args, torch, hsa, C.FP8_256)
     print(json.dumps(line), flush=True)

@@ -31,9 +31,9 @@
 //    token to the partial scores of each 128-value block and folded into P for the P V
 //    product of that block;
 //  * four token groups merge through LDS at the end; with splits > 1 each workgroup writes
-//    an unnormalised partial (max, sum, 16 x 512 values) and the last one to arrive (atomic
-//    counter, reset by that workgroup) combines them in split order, so results do not
-//    depend on arrival order.
+//    an unnormalised partial (max, sum, 16 x 512 values) and a second kernel combines them in
+//    split order.  (A last-arriving-workgroup combine needs a device-scope fence in every
+//    workgroup; on this chip each such fence writes back an XCD's L2, and they serialize.)
 
 #include <math.h>
 
@@ -66,7 +66,6 @@ struct AttendArgs {
   uint16_t* out;          // [n_req][heads][512] bf16
   float* lse;             // [n_req][heads] or null
   float* part;            // [n][splits][PART]
-  uint32_t* cnt;          // [n]
   int64_t stride;
   int32_t k, B, heads, chunk, splits;
   float scale_log2;       // softmax scale * log2(e)
@@ -122,6 +121,25 @@ __device__ __forceinline__ int out_col(int tau, int n) {
   const int kb = tau >> 1, sigma = tau & 1;
   const int kappa = 16 * sigma + n;
   return 128 * (kb >> 2) + 32 * (kappa >> 3) + 8 * (kb & 3) + (kappa & 7);
+}
+
+// Reductions across the four 16-lane rows of a wave with gfx950's row-swap moves (plain VALU,
+// no LDS round trip).  v_permlane16_swap(x, x) leaves every lane holding its own value and
+// that of the lane 16 away (rows 0<->1, 2<->3); v_permlane32_swap(x, x) likewise for the lane
+// 32 away.  Both operands combine in the same order in both lanes, so every lane of the wave
+// ends with the bitwise same result.
+__device__ __forceinline__ float rows_max(float v) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
+__device__ __forceinline__ float rows_sum(float v) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 template <int N>
@@ -187,7 +205,6 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
   float* o_acc = (float*)smem;                                       // after the loop: [16][512]
   __shared__ float wm[GROUPS][HMAX];
   __shared__ float wl[GROUPS][HMAX];
-  __shared__ int last_flag;
 
   const int s = blockIdx.x;
   const int r = blockIdx.y;
@@ -350,9 +367,7 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
     }
 
     // ---- online softmax for head c16 over tokens 4g + j of this group
-    float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mx = rows_max(fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3])));
     const float m_new = fmaxf(m_run, mx);
     float alpha = 1.f, p[4] = {0.f, 0.f, 0.f, 0.f};
     if (m_new != -INFINITY) {
@@ -360,9 +375,7 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) p[j] = exp2f(s2[j] - m_new);
     }
-    float rs = (p[0] + p[1]) + (p[2] + p[3]);
-    rs += __shfl_xor(rs, 16);
-    rs += __shfl_xor(rs, 32);
+    const float rs = rows_sum((p[0] + p[1]) + (p[2] + p[3]));
     l_run = l_run * alpha + rs;
     m_run = m_new;
 
@@ -448,6 +461,9 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
     return;
   }
 
+  // splits > 1: an unnormalised partial (per-head max and sum, 16 x 512 values); the combine
+  // kernel that follows on the stream merges the splits (the kernel boundary makes these
+  // stores visible, so no device-scope fence is needed here)
   float* mypart = a.part + ((int64_t)r * splits + s) * PART;
   if (tid < HMAX) {
     const int h = tid;
@@ -460,30 +476,40 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
     mypart[HMAX + h] = L;
   }
   for (int idx = tid; idx < HMAX * DV; idx += NT) mypart[2 * HMAX + idx] = o_acc[idx];
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) last_flag = (atomicAdd(&a.cnt[r], 1u) == (uint32_t)(splits - 1)) ? 1 : 0;
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
+}
 
-  const float* prow = a.part + (int64_t)r * splits * PART;
-  for (int idx = tid; idx < heads * DV; idx += NT) {
-    const int h = idx / DV;
-    float M = -INFINITY;
-    for (int v = 0; v < splits; ++v) M = fmaxf(M, prow[v * PART + h]);
-    float L = 0.f, acc = 0.f;
-    if (M != -INFINITY) {
-      for (int v = 0; v < splits; ++v) {
-        const float fv = exp2f(prow[v * PART + h] - M);
-        L += fv * prow[v * PART + HMAX + h];
-        acc += fv * prow[v * PART + 2 * HMAX + idx];
-      }
+// Merges the splits of every request in split order: with M the largest split maximum,
+// out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s  and  lse = (M + log2 L) ln 2.
+// Grid (HMAX * DV / 4 / 256, requests): each thread owns four consecutive outputs of one head
+// and issues its splits' loads independently.
+constexpr int COMBINE_THREADS = 256;
+constexpr int COMBINE_BLOCKS = HMAX * DV / 4 / COMBINE_THREADS;
+
+__global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(const float* __restrict__ part, int splits, int heads,
+                                                                  uint16_t* __restrict__ out, float* __restrict__ lse) {
+  const int r = blockIdx.y;
+  const int i4 = blockIdx.x * COMBINE_THREADS + threadIdx.x;   // float4 index within 16 x 512
+  const int h = (4 * i4) / DV;
+  if (h >= heads) return;
+  const float* prow = part + (int64_t)r * splits * PART;
+  float M = -INFINITY;
+  for (int v = 0; v < splits; ++v) M = fmaxf(M, prow[v * PART + h]);
+  float L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (M != -INFINITY) {
+    for (int v = 0; v < splits; ++v) {
+      const float fv = exp2f(prow[v * PART + h] - M);
+      const f32x4 o = *(const f32x4*)(prow + v * PART + 2 * HMAX + 4 * i4);
+      L += fv * prow[v * PART + HMAX + h];
+      acc += fv * o;
     }
-    a.out[(int64_t)r * heads * DV + idx] = (uint16_t)bf16_rne(L > 0.f ? acc / L : 0.f);
-    if ((idx % DV) == 0 && a.lse) a.lse[(int64_t)r * heads + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
   }
-  if (tid == 0) a.cnt[r] = 0u;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint2 packed;
+  packed.x = bf16_rne(acc[0] * inv) | (bf16_rne(acc[1] * inv) << 16);
+  packed.y = bf16_rne(acc[2] * inv) | (bf16_rne(acc[3] * inv) << 16);
+  *(uint2*)(out + ((int64_t)r * heads + h) * DV + (4 * i4) % DV) = packed;
+  if ((4 * i4) % DV == 0 && lse) lse[(int64_t)r * heads + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 int max_chunk(const Geometry& g) {
@@ -526,7 +552,6 @@ hipError_t launch_attend(const Geometry& g, const LayerTables& t, int32_t n_req,
   a.out = (uint16_t*)out;
   a.lse = lse;
   a.part = t.part;
-  a.cnt = t.cnt;
   a.stride = g.slot_stride;
   a.k = g.k;
   a.B = g.B;
@@ -542,6 +567,10 @@ hipError_t launch_attend(const Geometry& g, const LayerTables& t, int32_t n_req,
     hipLaunchKernelGGL(attend_kernel<0>, grid, dim3(NT), attend_lds_bytes<0>(), st, a);
   else
     hipLaunchKernelGGL(attend_kernel<1>, grid, dim3(NT), attend_lds_bytes<1>(), st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  hipLaunchKernelGGL(combine_kernel, dim3(COMBINE_BLOCKS, n_req), dim3(COMBINE_THREADS), 0, st, t.part, a.splits, g.heads,
+                     (uint16_t*)out, lse);
   return hipGetLastError();
 }
 

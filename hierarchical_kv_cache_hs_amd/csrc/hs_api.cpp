@@ -10,7 +10,7 @@
 //   step  [L][n]               resolves done
 //   cnt   [L][n]               attention split arrival counters
 //   part  [L][n][...]          attention split partials (if num_heads > 0)
-//   buf   [L][n][B][stride]    KV rows of the slots (stride = entry bytes rounded up to 128)
+//   buf   [L][n][B][E]         KV rows of the slots, packed
 // Host pool (pinned, mapped): [L][n][cap][entry bytes].
 
 #include <cstdio>
@@ -107,7 +107,7 @@ hs_status plan(const hs_config* cfg, hs::Geometry* g, Layout* lay) {
   g->cap = cap;
   g->entry_bytes = cfg->layout == HS_KV_BF16_576 ? 1152 : 656;
   g->host_stride = g->entry_bytes;
-  g->slot_stride = (g->entry_bytes + 127) / 128 * 128;
+  g->slot_stride = g->entry_bytes;  // packed: scattered 656-byte rows gather faster packed than padded to 768
   g->flags = cfg->flags;
 
   const size_t LN = (size_t)g->L * (size_t)g->n;

@@ -1,0 +1,81 @@
+"""A whole decode step over every layer, captured in one hipGraph.
+
+For each layer l the step resolves the layer's selection (hit detection, LRU
+replacement, table update, host-to-device fetch) and then runs sparse attention
+over the resolved slots.  With ``prefetch=True`` the layers' resolves run back to
+back on a second stream and each attention waits only for its own layer's
+resolve, so resolving (and fetching) layer l + 1 overlaps attention of layer l.
+This is valid when the layers share one selection known at the start of the step
+(HiSparse paper abstract: exact layer-wise prefetching for models that share
+selections across layers); the results are the same as the serial order because
+layers own disjoint tables, slots and scratch.
+
+Everything inside the graph is a libhs kernel launch; torch provides the streams,
+events and buffers.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import HiSparse
+
+
+class DecodeSteps:
+    """Captures ``len(sels)`` consecutive decode steps of ``hs`` into one graph.
+
+    sels:  list of int32 [n][top_k] device tensors, one shared selection per step
+    qs:    list of bf16 [L][n][H][576] device tensors, the queries of each step
+    Outputs of the last replayed step are left in ``slots``, ``out`` and ``lse``;
+    ``miss[i][l][r]`` records every step's miss counts.
+    """
+
+    def __init__(self, hs: HiSparse, sels, qs, scale: float, prefetch: bool, attend: bool = True):
+        assert len(sels) == len(qs) and len(sels) > 0
+        self.hs, self.prefetch, self.attend = hs, prefetch, attend
+        n = sels[0].shape[0]
+        L, k = hs.L, hs.top_k
+        dev = sels[0].device
+        H = qs[0].shape[2]
+        self.slots = torch.empty(L, n, k, dtype=torch.int32, device=dev)
+        self.miss = torch.zeros(len(sels), L, n, dtype=torch.int32, device=dev)
+        self.out = torch.empty(L, n, H, 512, dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty(L, n, H, dtype=torch.float32, device=dev)
+        self.stream = torch.cuda.Stream(device=dev)
+        self.side = torch.cuda.Stream(device=dev)
+        self.graph = torch.cuda.CUDAGraph()
+        self.stream.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(self.stream):
+            with torch.cuda.graph(self.graph, stream=self.stream):
+                for i, (sel, q) in enumerate(zip(sels, qs)):
+                    self._one_step(i, sel, q, scale)
+        torch.cuda.current_stream(dev).wait_stream(self.stream)
+
+    def _one_step(self, i, sel, q, scale):
+        hs, main = self.hs, self.stream
+        if not self.prefetch:
+            for l in range(hs.L):
+                hs.resolve(l, sel, self.slots[l], self.miss[i, l], stream=main)
+                if self.attend:
+                    hs.attend(l, q[l], self.slots[l], scale, self.out[l], self.lse[l], stream=main)
+            return
+        side = self.side
+        side.wait_stream(main)                       # fork
+        done = []
+        for l in range(hs.L):
+            hs.resolve(l, sel, self.slots[l], self.miss[i, l], stream=side)
+            e = torch.cuda.Event()
+            e.record(side)
+            done.append(e)
+        for l in range(hs.L):
+            main.wait_event(done[l])
+            if self.attend:
+                hs.attend(l, q[l], self.slots[l], scale, self.out[l], self.lse[l], stream=main)
+        main.wait_stream(side)                       # join
+
+    def replay(self):
+        """Runs the captured steps on this object's stream (ordered after the caller's stream)."""
+        dev = self.slots.device
+        self.stream.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(self.stream):
+            self.graph.replay()
+        torch.cuda.current_stream(dev).wait_stream(self.stream)

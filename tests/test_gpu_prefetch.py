@@ -1,0 +1,88 @@
+"""Layer-wise prefetch: eight layers sharing one selection per step, resolves of all
+layers on a second stream overlapping the attention of earlier layers, captured in one
+hipGraph.  Outputs, miss counts and every table must equal the serial order bitwise,
+and both must match the oracle (tables for all layers; attention on sampled requests)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import hierarchical_kv_cache_hs_amd as hsa
+from hierarchical_kv_cache_hs_amd.decode_step import DecodeSteps
+import oracle
+from synth import configs as C
+from synth import kv as skv
+
+from gpu_harness import fill_host_pool, say, trace_for
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")]
+
+SCALE = 1.0 / math.sqrt(576)
+
+
+def _queries(w, t, L):
+    q = np.stack([skv.queries(w.seed, t, w.n, l, 16) for l in range(L)])
+    return torch.from_numpy(q.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _run(hs, w, x, qs, prefetch):
+    rec = []
+    for t in range(x.shape[0]):
+        sel = torch.from_numpy(x[t]).cuda()
+        steps = DecodeSteps(hs, [sel], [qs[t]], SCALE, prefetch=prefetch)
+        steps.replay()
+        torch.cuda.synchronize()
+        rec.append((steps.slots.clone(), steps.miss[0].clone(), steps.out.clone(), steps.lse.clone()))
+    st = [hs.state(l) for l in range(hs.L)]
+    tables = [tuple(s[key].clone() for key in ("page_table", "slot_owner", "slot_stamp", "lru_order", "step"))
+              for s in st]
+    return rec, tables
+
+
+@pytest.mark.parametrize("full", [False, True])
+def test_prefetch_equals_serial_and_oracle(full):
+    w = C.PREFETCH if full else C.PREFETCH.with_(n=6, ctx=8192, ratio=2)
+    T = 5 if full else 8
+    say(f"prefetch: {w.n} requests, {w.layers} layers, cap {w.cap}, fp8, {T} steps")
+    x = trace_for(w, steps=T)
+    hs = hsa.HiSparse(w.k, w.B, w.ratio, w.n, w.layers, w.layout, num_heads=16)
+    try:
+        fill_host_pool(hs, w.seed)
+        qs = [_queries(w, t, w.layers) for t in range(T)]
+        ser, ser_tables = _run(hs, w, x, qs, prefetch=False)
+        hs.reset_requests(0, w.n)
+        torch.cuda.synchronize()
+        pre, pre_tables = _run(hs, w, x, qs, prefetch=True)
+        for t, (a, b) in enumerate(zip(ser, pre)):
+            for u, v, name in zip(a, b, ("slots", "miss", "out", "lse")):
+                assert torch.equal(u, v), f"step {t}: {name} differs between serial and prefetch"
+        for l in range(w.layers):
+            for u, v in zip(ser_tables[l], pre_tables[l]):
+                assert torch.equal(u, v), f"layer {l}: tables differ"
+
+        # oracle: every layer saw the same selections, so every layer's tables equal one oracle state
+        orc = oracle.OracleCache(w.n, 1, w.B, w.cap, layout=w.layout)
+        for t in range(T):
+            s_o, m_o = orc.resolve(0, x[t])
+            for l in range(w.layers):
+                assert (ser[t][0][l].cpu().numpy() == s_o).all(), f"step {t} layer {l}: slots vs oracle"
+                assert (ser[t][1][l].cpu().numpy() == m_o).all(), f"step {t} layer {l}: misses vs oracle"
+        for l in range(w.layers):
+            pt, rm, stamp = (u.cpu().numpy() for u in ser_tables[l][:3])
+            assert (pt == orc.PT[:, 0]).all() and (rm == orc.RM[:, 0]).all()
+            assert (stamp.astype(np.int64) == orc.ST[:, 0]).all()
+        # attention of the last step on sampled requests, against rows gathered from the history
+        qb = np.stack([skv.queries(w.seed, T - 1, w.n, l, 16) for l in range(w.layers)])
+        for l in range(w.layers):
+            for r in sorted({0, w.n // 2, w.n - 1}):
+                rows = skv.rows_at(w.seed, r, l, x[T - 1, r], w.layout)[None]
+                o_o, l_o = oracle.attend_rows(qb[l, r][None], np.arange(w.k, dtype=np.int32)[None], rows,
+                                              w.layout, SCALE)
+                og = ser[T - 1][2][l, r].float().cpu().numpy()
+                err = np.abs(og - o_o[0]).max()
+                assert err <= 2e-2, f"layer {l} request {r}: attention error {err}"
+                assert np.abs(ser[T - 1][3][l, r].cpu().numpy() - l_o[0]).max() <= 1e-3
+    finally:
+        hs.close()
