@@ -11,8 +11,8 @@ the host-to-device fetch of the missing rows), replayed from a captured hipGraph
 Metric: resolved top-k selections/s (whole job), with the miss-fetch rate against the
 host-link peak measured in the same run.  The JSON line also carries:
   roofline     the resolver kernel against the host link (its bound): the timed graph holds
-               only resolver launches, so HIP events around it on the launch stream give
-               the kernel's average launch duration;
+               only resolver launches, so HIP events around it on the launch stream give the
+               kernel's average launch duration;
   resolve_only the same steps on a handle that moves no rows (resolution cost alone);
   cpu_baseline the CPU oracle on a bounded sample of the same trace, on this host's cores.
 
@@ -173,9 +173,9 @@ def bench_resolve(args, torch, hsa, w):
     d_trace = torch.from_numpy(trace).cuda()
 
     handles = {}
-    for name, flags in (("io", 0), ("noio", hsa.FLAG_NO_IO)):
+    for name, flags in (("io", 0), ("noio", hsa.FLAG_NO_IO), ("split", 0)):
         hs = hsa.HiSparse(w.k, w.B, w.ratio, w.n, 1, w.layout, 0, flags)
-        if flags == 0:
+        if not flags & hsa.FLAG_NO_IO:
             t0 = time.perf_counter()
             for r in range(w.n):
                 ptr, cap, stride = hs.host_kv_ptr(0, r)
@@ -199,7 +199,7 @@ def bench_resolve(args, torch, hsa, w):
             with torch.cuda.graph(g, stream=stream):
                 for i in range(args.steps):
                     t = args.warmup + i
-                    hs.resolve(0, d_trace[t], slots, miss[t], stream=stream)
+                    hs.resolve(0, d_trace[t], slots, miss[t], stream=stream, split=(name == "split"))
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):      # replay() launches on the current stream
@@ -213,8 +213,8 @@ def bench_resolve(args, torch, hsa, w):
         log(f"{name}: {region_ms:.3f} ms for {args.steps} steps; {region_ms / args.steps * 1e3:.1f} us per launch")
         del g
 
-    io, noio = results["io"], results["noio"]
-    assert (io["miss"] == noio["miss"]).all()
+    io, noio, split = results["io"], results["noio"], results["split"]
+    assert (io["miss"] == noio["miss"]).all() and (io["miss"] == split["miss"]).all()
     K = args.steps
     total_miss = int(io["miss"].sum())
     fetch_bytes = total_miss * w.entry_bytes
@@ -249,6 +249,7 @@ def bench_resolve(args, torch, hsa, w):
         "miss_fetch_GBps_fetch_only": bytes_per_launch / fetch_only_s / 1e9,
         "h2d_peak_GBps_measured": h2d,
         "miss_fetch_frac_of_measured_peak": (fetch_bytes / (io["region_ms"] / 1e3) / 1e9) / h2d,
+        "split_tables_and_fetch_us_per_step": split["kernel_ms"] * 1e3,
         "resolve_only": {"us_per_step": avg_kernel_noio_s * 1e6,
                          "selections_per_s": w.n / avg_kernel_noio_s,
                          "share_of_io_step": avg_kernel_noio_s / avg_kernel_s},

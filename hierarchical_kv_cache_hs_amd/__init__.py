@@ -32,7 +32,8 @@ DEVERR_DUPLICATE = 0x2
 
 HS_OK, HS_ERR_INVALID_ARG, HS_ERR_OUT_OF_MEMORY, HS_ERR_UNSUPPORTED, HS_ERR_HIP, HS_ERR_DEVICE = range(6)
 
-SYMBOLS = ("hs_create", "hs_resolve", "hs_attend", "hs_destroy", "hs_device_bytes", "hs_host_bytes", "hs_host_kv",
+SYMBOLS = ("hs_create", "hs_resolve", "hs_resolve_tables", "hs_fetch_misses", "hs_attend", "hs_destroy",
+           "hs_device_bytes", "hs_host_bytes", "hs_host_kv",
            "hs_device_state", "hs_reset_requests", "hs_get_device_error", "hs_status_string",
            "hs_last_error_message")
 
@@ -71,6 +72,8 @@ def lib():
         L.hs_host_bytes.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_size_t)]
         L.hs_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(p)]
         L.hs_resolve.argtypes = [p, i32, i32, p, p, p, p]
+        L.hs_resolve_tables.argtypes = [p, i32, i32, p, p, p, p]
+        L.hs_fetch_misses.argtypes = [p, i32, i32, p]
         L.hs_attend.argtypes = [p, i32, i32, p, p, ctypes.c_float, p, p, p]
         L.hs_destroy.argtypes = [p]
         L.hs_host_kv.argtypes = [p, i32, i32, ctypes.POINTER(p), ctypes.POINTER(ctypes.c_int64),
@@ -82,7 +85,8 @@ def lib():
         L.hs_status_string.restype = ctypes.c_char_p
         L.hs_last_error_message.argtypes = []
         L.hs_last_error_message.restype = ctypes.c_char_p
-        for name in ("hs_device_bytes", "hs_host_bytes", "hs_create", "hs_resolve", "hs_attend", "hs_destroy",
+        for name in ("hs_device_bytes", "hs_host_bytes", "hs_create", "hs_resolve", "hs_resolve_tables",
+                     "hs_fetch_misses", "hs_attend", "hs_destroy",
                      "hs_host_kv", "hs_device_state", "hs_reset_requests", "hs_get_device_error"):
             getattr(L, name).restype = ctypes.c_int
         _lib_cache = L
@@ -183,7 +187,8 @@ class HiSparse:
 
     # -- hot path ------------------------------------------------------------------------------
     def resolve(self, layer: int, sel: torch.Tensor, slots: torch.Tensor | None = None,
-                miss: torch.Tensor | None = None, stream=None):
+                miss: torch.Tensor | None = None, stream=None, split: bool = False):
+        """hs_resolve; with split=True, hs_resolve_tables followed by hs_fetch_misses on the same stream."""
         n_req = sel.shape[0]
         assert sel.dtype == torch.int32 and sel.is_contiguous() and sel.shape[1] == self.top_k
         if slots is None:
@@ -191,9 +196,22 @@ class HiSparse:
         if miss is None:
             miss = torch.empty(n_req, dtype=torch.int32, device=sel.device)
         assert slots.shape == sel.shape and slots.dtype == torch.int32 and slots.is_contiguous()
-        _check(lib().hs_resolve(self._h, layer, n_req, sel.data_ptr(), slots.data_ptr(), miss.data_ptr(),
-                                _stream_ptr(stream)))
+        if split:
+            self.resolve_tables(layer, sel, slots, miss, stream)
+            self.fetch_misses(layer, n_req, stream)
+        else:
+            _check(lib().hs_resolve(self._h, layer, n_req, sel.data_ptr(), slots.data_ptr(), miss.data_ptr(),
+                                    _stream_ptr(stream)))
         return slots, miss
+
+    def resolve_tables(self, layer: int, sel: torch.Tensor, slots: torch.Tensor, miss: torch.Tensor, stream=None):
+        assert sel.dtype == torch.int32 and sel.is_contiguous() and sel.shape[1] == self.top_k
+        assert slots.shape == sel.shape and slots.dtype == torch.int32 and slots.is_contiguous()
+        _check(lib().hs_resolve_tables(self._h, layer, sel.shape[0], sel.data_ptr(), slots.data_ptr(),
+                                       miss.data_ptr(), _stream_ptr(stream)))
+
+    def fetch_misses(self, layer: int, n_req: int, stream=None):
+        _check(lib().hs_fetch_misses(self._h, layer, n_req, _stream_ptr(stream)))
 
     def attend(self, layer: int, q: torch.Tensor, slots: torch.Tensor, scale: float,
                out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream=None):

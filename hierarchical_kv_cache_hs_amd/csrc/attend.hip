@@ -56,6 +56,7 @@ constexpr int DQK = 576;                    // q.K length
 constexpr int DV = 512;                     // value length
 constexpr int KB_HALF = 9;                  // reduction blocks of 32 values per half
 constexpr int PART = 2 * HMAX + HMAX * DV;  // floats of one split partial
+constexpr int OACC_LD = DV + 4;             // merge-buffer row: 4 floats of padding spread the head rows over LDS banks
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -190,6 +191,8 @@ __device__ __forceinline__ void wait_tiles(int pending, int per) {
 template <int LAYOUT>
 constexpr size_t ring_bytes() { return (size_t)TileGeo<LAYOUT>::NBUF * TileGeo<LAYOUT>::TILE; }
 
+static_assert(HMAX * OACC_LD * sizeof(float) <= 2 * 64 * 656, "merge buffer must fit in the ring");
+
 template <int LAYOUT>
 constexpr size_t attend_lds_bytes() {
   return ring_bytes<LAYOUT>() + TileGeo<LAYOUT>::MAXCHUNK * sizeof(int32_t) + WAVES * 64 * sizeof(f32x4);
@@ -202,7 +205,7 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
   uint8_t* ring = smem;                                              // [NBUF][TILE]
   int32_t* slot_lds = (int32_t*)(smem + ring_bytes<LAYOUT>());       // [MAXCHUNK]
   f32x4* xch = (f32x4*)(smem + ring_bytes<LAYOUT>() + G::MAXCHUNK * sizeof(int32_t));  // [WAVES][64]
-  float* o_acc = (float*)smem;                                       // after the loop: [16][512]
+  float* o_acc = (float*)smem;                                       // after the loop: [16][OACC_LD]
   __shared__ float wm[GROUPS][HMAX];
   __shared__ float wl[GROUPS][HMAX];
 
@@ -298,30 +301,34 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
 #pragma unroll
       for (int i = 0; i < KB_HALF; ++i) {
         const int kb = (i < 8) ? 8 * hf + i : 16 + hf;
-        const u32x4 v = *(const u32x4*)(row + 2 * kb_offset(kb, g));
-        kreg[i] = valid ? v : z4;
+        kreg[i] = *(const u32x4*)(row + 2 * kb_offset(kb, g));
       }
     } else {
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb) {
         const int b = 2 * hf + bb;
-        u32x4 lo = *(const u32x4*)(row + 128 * b + 32 * g);
-        u32x4 hi = *(const u32x4*)(row + 128 * b + 32 * g + 16);
-        lo = valid ? lo : z4;
-        hi = valid ? hi : z4;
+        const u32x4 lo = *(const u32x4*)(row + 128 * b + 32 * g);
+        const u32x4 hi = *(const u32x4*)(row + 128 * b + 32 * g + 16);
         kreg[4 * bb + 0] = e4m3x8_to_bf16x8(lo[0], lo[1]);
         kreg[4 * bb + 1] = e4m3x8_to_bf16x8(lo[2], lo[3]);
         kreg[4 * bb + 2] = e4m3x8_to_bf16x8(hi[0], hi[1]);
         kreg[4 * bb + 3] = e4m3x8_to_bf16x8(hi[2], hi[3]);
       }
-      const u32x4 rv = *(const u32x4*)(row + 528 + 32 * g + 16 * hf);
-      kreg[8] = valid ? rv : z4;
+      kreg[8] = *(const u32x4*)(row + 528 + 32 * g + 16 * hf);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const u32x2 sv = *(const u32x2*)(tile + (16 * tg + 4 * g + j) * G::E + 512 + 8 * hf);
         sc[j][0] = __uint_as_float(sv[0]);
         sc[j][1] = __uint_as_float(sv[1]);
       }
+    }
+
+    // A padded or missing token reads some in-bounds row; its operands are zeroed so that
+    // no stray value (NaN in particular) reaches the P V product.  Skipped when all 16 of the
+    // wave's tokens are real, as in every full tile.
+    if (!__all(valid)) {
+#pragma unroll
+      for (int i = 0; i < KB_HALF; ++i) kreg[i] = valid ? kreg[i] : z4;
     }
 
     // ---- partial S^T[tok][h] over this half
@@ -368,7 +375,10 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
 
     // ---- online softmax for head c16 over tokens 4g + j of this group
     const float mx = rows_max(fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3])));
-    const float m_new = fmaxf(m_run, mx);
+    // The reference maximum moves only when a score exceeds it by more than 2^8 (lazy
+    // rescaling): P = 2^(s - m) then stays below 256, well inside fp32 and bf16 range, and the
+    // accumulator rescale below runs only on the rare tiles that move some head's reference.
+    const float m_new = (mx > m_run + 8.f) ? mx : m_run;
     float alpha = 1.f, p[4] = {0.f, 0.f, 0.f, 0.f};
     if (m_new != -INFINITY) {
       alpha = exp2f(m_run - m_new);
@@ -436,7 +446,7 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
         const int col = out_col(16 * hf + i, c16);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int idx = (4 * g + j) * DV + col;
+          const int idx = (4 * g + j) * OACC_LD + col;
           const float val = O[i][j] * f[j];
           o_acc[idx] = (v == 0) ? val : o_acc[idx] + val;
         }
@@ -454,7 +464,7 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
       float L = 0.f;
       if (M != -INFINITY)
         for (int v = 0; v < GROUPS; ++v) L += exp2f(wm[v][h] - M) * wl[v][h];
-      const float val = L > 0.f ? o_acc[idx] / L : 0.f;
+      const float val = L > 0.f ? o_acc[h * OACC_LD + idx % DV] / L : 0.f;
       a.out[(int64_t)r * heads * DV + idx] = (uint16_t)bf16_rne(val);
       if ((idx % DV) == 0 && a.lse) a.lse[(int64_t)r * heads + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
     }
@@ -475,7 +485,7 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
     mypart[h] = M;
     mypart[HMAX + h] = L;
   }
-  for (int idx = tid; idx < HMAX * DV; idx += NT) mypart[2 * HMAX + idx] = o_acc[idx];
+  for (int idx = tid; idx < HMAX * DV; idx += NT) mypart[2 * HMAX + idx] = o_acc[(idx / DV) * OACC_LD + idx % DV];
 }
 
 // Merges the splits of every request in split order: with M the largest split maximum,

@@ -10,6 +10,7 @@
 //   step  [L][n]               resolves done
 //   cnt   [L][n]               attention split arrival counters
 //   part  [L][n][...]          attention split partials (if num_heads > 0)
+//   ml_*  [L][n][k], [L][n]    per-request miss lists (token, slot) and counts for the fetch kernel
 //   buf   [L][n][B][E]         KV rows of the slots, packed
 // Host pool (pinned, mapped): [L][n][cap][entry bytes].
 
@@ -37,6 +38,9 @@ struct hs_handle {
   int32_t* step = nullptr;
   uint32_t* cnt = nullptr;
   float* part = nullptr;
+  int32_t* ml_tok = nullptr;
+  int32_t* ml_slot = nullptr;
+  int32_t* ml_cnt = nullptr;
   uint8_t* buf = nullptr;
   size_t part_floats = 0;  // per request
 };
@@ -73,7 +77,7 @@ bool add_ok(size_t a, size_t b, size_t* out) {
 }
 
 struct Layout {
-  size_t err, pt, rm, st, ord, step, cnt, part, buf, total;
+  size_t err, pt, rm, st, ord, step, cnt, part, ml_tok, ml_slot, ml_cnt, buf, total;
   size_t host_total;
   size_t part_floats;
 };
@@ -124,6 +128,8 @@ hs_status plan(const hs_config* cfg, hs::Geometry* g, Layout* lay) {
   ok = ok && take(LN * 4, &lay->step) && take(LN * 4, &lay->cnt);
   lay->part_floats = g->heads > 0 ? hs::attend_partial_floats(*g) : 0;
   ok = ok && mul_ok(LN, lay->part_floats, &t) && mul_ok(t, 4, &sz) && take(sz, &lay->part);
+  ok = ok && mul_ok(LN, (size_t)g->k, &t) && mul_ok(t, 4, &sz) && take(sz, &lay->ml_tok) && take(sz, &lay->ml_slot);
+  ok = ok && take(LN * 4, &lay->ml_cnt);
   ok = ok && mul_ok(LN, (size_t)g->B, &t) && mul_ok(t, (size_t)g->slot_stride, &sz) && take(sz, &lay->buf);
   lay->total = off;
   ok = ok && mul_ok(LN, (size_t)cap, &t) && mul_ok(t, (size_t)g->host_stride, &lay->host_total);
@@ -142,6 +148,9 @@ hs::LayerTables layer_tables(const hs_handle* h, int32_t layer) {
   t.step = h->step + base;
   t.cnt = h->cnt + base;
   t.part = h->part ? h->part + base * h->part_floats : nullptr;
+  t.ml_tok = h->ml_tok + base * (size_t)g.k;
+  t.ml_slot = h->ml_slot + base * (size_t)g.k;
+  t.ml_cnt = h->ml_cnt + base;
   t.buf = h->buf + base * (size_t)g.B * (size_t)g.slot_stride;
   return t;
 }
@@ -234,6 +243,9 @@ hs_status hs_create(const hs_config* cfg, hs_handle** out) {
   h->step = (int32_t*)(b + lay.step);
   h->cnt = (uint32_t*)(b + lay.cnt);
   h->part = lay.part_floats ? (float*)(b + lay.part) : nullptr;
+  h->ml_tok = (int32_t*)(b + lay.ml_tok);
+  h->ml_slot = (int32_t*)(b + lay.ml_slot);
+  h->ml_cnt = (int32_t*)(b + lay.ml_cnt);
   h->buf = b + lay.buf;
 
   hs::prepare_resolve();
@@ -247,8 +259,10 @@ hs_status hs_create(const hs_config* cfg, hs_handle** out) {
   return HS_OK;
 }
 
-hs_status hs_resolve(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* d_sel, int32_t* d_slots,
-                     int32_t* d_miss, void* stream) {
+namespace {
+
+hs_status resolve_impl(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* d_sel, int32_t* d_slots,
+                       int32_t* d_miss, bool list_only, void* stream) {
   if (!h) return fail(HS_ERR_INVALID_ARG, "handle is NULL");
   if (layer < 0 || layer >= h->g.L) return fail(HS_ERR_INVALID_ARG, "layer out of range");
   if (n_req < 0 || n_req > h->g.n) return fail(HS_ERR_INVALID_ARG, "n_req out of range");
@@ -256,8 +270,33 @@ hs_status hs_resolve(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* 
   if (!d_sel || !d_slots) return fail(HS_ERR_INVALID_ARG, "selection or slot pointer is NULL");
   hs::LayerTables t = layer_tables(h, layer);
   const uint8_t* host_layer = h->host_pool_dev + (size_t)layer * h->g.n * (size_t)h->g.cap * h->g.host_stride;
-  hipError_t e = hs::launch_resolve(h->g, t, host_layer, n_req, d_sel, d_slots, d_miss, h->err, (hipStream_t)stream);
+  hipError_t e = hs::launch_resolve(h->g, t, host_layer, n_req, d_sel, d_slots, d_miss, h->err, list_only,
+                                    (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "resolve launch");
+  return HS_OK;
+}
+
+}  // namespace
+
+hs_status hs_resolve(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* d_sel, int32_t* d_slots,
+                     int32_t* d_miss, void* stream) {
+  return resolve_impl(h, layer, n_req, d_sel, d_slots, d_miss, false, stream);
+}
+
+hs_status hs_resolve_tables(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* d_sel, int32_t* d_slots,
+                            int32_t* d_miss, void* stream) {
+  return resolve_impl(h, layer, n_req, d_sel, d_slots, d_miss, true, stream);
+}
+
+hs_status hs_fetch_misses(hs_handle* h, int32_t layer, int32_t n_req, void* stream) {
+  if (!h) return fail(HS_ERR_INVALID_ARG, "handle is NULL");
+  if (layer < 0 || layer >= h->g.L) return fail(HS_ERR_INVALID_ARG, "layer out of range");
+  if (n_req < 0 || n_req > h->g.n) return fail(HS_ERR_INVALID_ARG, "n_req out of range");
+  if (n_req == 0) return HS_OK;
+  hs::LayerTables t = layer_tables(h, layer);
+  const uint8_t* host_layer = h->host_pool_dev + (size_t)layer * h->g.n * (size_t)h->g.cap * h->g.host_stride;
+  hipError_t e = hs::launch_fetch(h->g, t, host_layer, n_req, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "fetch launch");
   return HS_OK;
 }
 

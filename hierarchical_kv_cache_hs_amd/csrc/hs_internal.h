@@ -25,7 +25,10 @@ struct LayerTables {
   int32_t* step;   // [n]
   uint8_t* buf;    // [n][B][slot_stride]
   float* part;     // attention split partials (see attend.hip)
-  uint32_t* cnt;   // attention split arrival counters [n]
+  uint32_t* cnt;   // reserved per-request counters [n]
+  int32_t* ml_tok;   // miss lists [n][k]
+  int32_t* ml_slot;  // [n][k]
+  int32_t* ml_cnt;   // [n]
 };
 
 struct Geometry {
@@ -43,8 +46,13 @@ void prepare_resolve();
 // Dynamic LDS bytes the resolver needs for this geometry.
 size_t resolve_lds_bytes(int64_t cap, int32_t k, int32_t B);
 
+// list_only: write the miss lists instead of copying the rows (launch_fetch copies them).
 hipError_t launch_resolve(const Geometry& g, const LayerTables& t, const uint8_t* host_layer, int32_t n_req,
-                          const int32_t* sel, int32_t* slots, int32_t* miss, int32_t* err, hipStream_t s);
+                          const int32_t* sel, int32_t* slots, int32_t* miss, int32_t* err, bool list_only,
+                          hipStream_t s);
+
+hipError_t launch_fetch(const Geometry& g, const LayerTables& t, const uint8_t* host_layer, int32_t n_req,
+                        hipStream_t s);
 
 hipError_t launch_reset(const Geometry& g, int32_t* pt, int32_t* rm, int32_t* st, int32_t* ord, int32_t* step,
                         uint32_t* cnt, int32_t first, int32_t count, hipStream_t s);

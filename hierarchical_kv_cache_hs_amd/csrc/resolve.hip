@@ -21,9 +21,13 @@
 //       order in ascending slot index (a scan over the slot bitmap); the i-th miss takes
 //       victim i: evict its owner from the page table, install the token, stamp, and
 //       write the output slot;
-//   P5  the workgroup copies the missing rows from pinned host memory (zero-copy 16-byte
-//       loads over PCIe, row-major over the miss list so a wave reads ~1 KiB runs) into
-//       the victim slots.
+//   P5  the missing rows are copied from pinned host memory (zero-copy 16-byte loads over
+//       PCIe, row-major over the miss list so a wave reads ~1 KiB runs) into the victim
+//       slots.  hs_resolve does this inside the resolving workgroup (each request's copy
+//       starts as soon as its own tables are done).  hs_resolve_tables + hs_fetch_misses
+//       instead write the miss list and copy with a second, LDS-free kernel of ~512 small
+//       workgroups: that kernel can share compute units with a running attention kernel,
+//       which a resolving workgroup holding its LDS for the whole PCIe-bound copy cannot.
 // The new order equals the slots sorted by (stamp, slot): untouched slots keep their
 // relative order, and every touched slot now has the largest stamp, so among them the
 // slot index decides.  No sort is needed and a step costs O(k + B + capacity/32).
@@ -51,6 +55,9 @@ struct ResolveArgs {
   const uint8_t* host;
   uint8_t* buf;
   int32_t* err;
+  int32_t* ml_tok;   // [n][k] missing tokens, ascending (mode LIST)
+  int32_t* ml_slot;  // [n][k] their slots
+  int32_t* ml_cnt;   // [n]
   int64_t cap;
   int64_t host_stride;
   int64_t slot_stride;
@@ -83,9 +90,15 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint3
   return before + x - v;
 }
 
-// KPT: selection entries per thread (KPT * NT >= k); OPT: LRU-order entries per thread (OPT * NT >= B);
-// FETCH: copy the missing rows (false: tables only, the no-IO measurement mode).
-template <int KPT, int OPT, bool FETCH>
+// What the resolving workgroup does with the missing rows.
+enum Mode : int {
+  TABLES = 0,  // tables only (the no-IO measurement mode)
+  FUSED = 1,   // the workgroup copies its rows itself
+  LIST = 2,    // the workgroup writes its miss list; fetch_kernel copies the rows
+};
+
+// KPT: selection entries per thread (KPT * NT >= k); OPT: LRU-order entries per thread (OPT * NT >= B).
+template <int KPT, int OPT, int MODE>
 __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
   extern __shared__ uint32_t lds[];
   const int r = blockIdx.x;
@@ -241,6 +254,10 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
           tok = s;
         }
         if (q < k) misstok[q] = (uint32_t)tok;
+        if (MODE == LIST && q < k) {
+          a.ml_tok[(int64_t)r * k + q] = tok;
+          a.ml_slot[(int64_t)r * k + q] = v;
+        }
       }
       slots[i] = out;
     }
@@ -248,11 +265,13 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
   if (tid == 0) {
     a.step[r] = t + 1;
     if (a.miss) a.miss[r] = m;
+    if (MODE == LIST) a.ml_cnt[r] = m;
   }
+  if (MODE != FUSED) return;
   __syncthreads();
 
   // ---- P5
-  if (!FETCH || m == 0) return;
+  if (m == 0) return;
   const int C = a.chunks;
   const int total = m * C;
   const uint8_t* host = a.host + (int64_t)r * cap * a.host_stride;
@@ -277,6 +296,51 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
         const int q = idx / C;
         const int c = idx - q * C;
         if ((int32_t)misstok[q] >= 0) ((v4i*)(buf + (int64_t)victims[q] * a.slot_stride))[c] = v[u];
+      }
+    }
+  }
+}
+
+// Copies the rows of the miss lists written by resolve_kernel<..., LIST>: grid (per-request
+// blocks, requests), 16-byte zero-copy loads from pinned host memory, four in flight per
+// thread.  No LDS and few registers, so its workgroups fit beside a running attention kernel.
+constexpr int FT = 256;
+
+__global__ __launch_bounds__(FT) void fetch_kernel(const int32_t* __restrict__ ml_tok, const int32_t* __restrict__ ml_slot,
+                                                   const int32_t* __restrict__ ml_cnt, const uint8_t* __restrict__ host,
+                                                   uint8_t* __restrict__ buf, int64_t cap, int64_t host_stride,
+                                                   int64_t slot_stride, int32_t k, int32_t B, int32_t chunks) {
+  const int r = blockIdx.y;
+  const int m = min(ml_cnt[r], k);
+  const int total = m * chunks;
+  const int32_t* tok = ml_tok + (int64_t)r * k;
+  const int32_t* slot = ml_slot + (int64_t)r * k;
+  const uint8_t* hrow = host + (int64_t)r * cap * host_stride;
+  uint8_t* drow = buf + (int64_t)r * B * slot_stride;
+  constexpr int U = 4;
+  const int step = gridDim.x * FT;
+  for (int base = blockIdx.x * FT + threadIdx.x; base < total; base += step * U) {
+    v4i v[U];
+    int32_t dst[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = base + u * step;
+      dst[u] = -1;
+      if (idx < total) {
+        const int q = idx / chunks;
+        const int c = idx - q * chunks;
+        const int32_t s = tok[q], j = slot[q];
+        if (s >= 0 && (int64_t)s < cap && j >= 0 && j < B) {
+          v[u] = __builtin_nontemporal_load((const v4i*)(hrow + (int64_t)s * host_stride) + c);
+          dst[u] = j * chunks + c;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (dst[u] >= 0) {
+        const int j = dst[u] / chunks, c = dst[u] - j * chunks;
+        ((v4i*)(drow + (int64_t)j * slot_stride))[c] = v[u];
       }
     }
   }
@@ -307,19 +371,23 @@ __global__ void reset_kernel(int32_t* pt, int32_t* rm, int32_t* st, int32_t* ord
 template <int KPT, int OPT>
 void allow_large_lds() {
   // Lets a workgroup take up to the whole 160 KiB of LDS; errors are left to the launch.
-  (void)hipFuncSetAttribute((const void*)resolve_kernel<KPT, OPT, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)kLdsLimit);
-  (void)hipFuncSetAttribute((const void*)resolve_kernel<KPT, OPT, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)kLdsLimit);
+  (void)hipFuncSetAttribute((const void*)resolve_kernel<KPT, OPT, TABLES>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
+  (void)hipFuncSetAttribute((const void*)resolve_kernel<KPT, OPT, FUSED>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
+  (void)hipFuncSetAttribute((const void*)resolve_kernel<KPT, OPT, LIST>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
   (void)hipGetLastError();
 }
 
 template <int KPT, int OPT>
-hipError_t launch_one(const ResolveArgs& a, bool fetch, int n_req, size_t lds, hipStream_t s) {
-  if (fetch)
-    hipLaunchKernelGGL((resolve_kernel<KPT, OPT, true>), dim3(n_req), dim3(NT), lds, s, a);
+hipError_t launch_one(const ResolveArgs& a, int mode, int n_req, size_t lds, hipStream_t s) {
+  if (mode == FUSED)
+    hipLaunchKernelGGL((resolve_kernel<KPT, OPT, FUSED>), dim3(n_req), dim3(NT), lds, s, a);
+  else if (mode == LIST)
+    hipLaunchKernelGGL((resolve_kernel<KPT, OPT, LIST>), dim3(n_req), dim3(NT), lds, s, a);
   else
-    hipLaunchKernelGGL((resolve_kernel<KPT, OPT, false>), dim3(n_req), dim3(NT), lds, s, a);
+    hipLaunchKernelGGL((resolve_kernel<KPT, OPT, TABLES>), dim3(n_req), dim3(NT), lds, s, a);
   return hipGetLastError();
 }
 
@@ -341,7 +409,8 @@ size_t resolve_lds_bytes(int64_t cap, int32_t k, int32_t B) {
 }
 
 hipError_t launch_resolve(const Geometry& g, const LayerTables& t, const uint8_t* host_layer, int32_t n_req,
-                          const int32_t* sel, int32_t* slots, int32_t* miss, int32_t* err, hipStream_t s) {
+                          const int32_t* sel, int32_t* slots, int32_t* miss, int32_t* err, bool list_only,
+                          hipStream_t s) {
   ResolveArgs a;
   a.sel = sel;
   a.slots = slots;
@@ -360,14 +429,29 @@ hipError_t launch_resolve(const Geometry& g, const LayerTables& t, const uint8_t
   a.k = g.k;
   a.B = g.B;
   a.chunks = (int32_t)(g.entry_bytes / 16);
-  const bool fetch = !(g.flags & HS_FLAG_NO_IO);
+  a.ml_tok = t.ml_tok;
+  a.ml_slot = t.ml_slot;
+  a.ml_cnt = t.ml_cnt;
+  const int mode = (g.flags & HS_FLAG_NO_IO) ? TABLES : list_only ? LIST : FUSED;
   const size_t lds = resolve_lds_bytes(g.cap, g.k, g.B);
   const int kpt = (g.k + NT - 1) / NT;
   const int opt = (g.B + NT - 1) / NT;
-  if (kpt <= 4) {
-    return opt <= 8 ? launch_one<4, 8>(a, fetch, n_req, lds, s) : launch_one<4, 32>(a, fetch, n_req, lds, s);
-  }
-  return opt <= 8 ? launch_one<16, 8>(a, fetch, n_req, lds, s) : launch_one<16, 32>(a, fetch, n_req, lds, s);
+  hipError_t e;
+  if (kpt <= 4)
+    e = opt <= 8 ? launch_one<4, 8>(a, mode, n_req, lds, s) : launch_one<4, 32>(a, mode, n_req, lds, s);
+  else
+    e = opt <= 8 ? launch_one<16, 8>(a, mode, n_req, lds, s) : launch_one<16, 32>(a, mode, n_req, lds, s);
+  return e;
+}
+
+hipError_t launch_fetch(const Geometry& g, const LayerTables& t, const uint8_t* host_layer, int32_t n_req,
+                        hipStream_t s) {
+  if (g.flags & HS_FLAG_NO_IO) return hipSuccess;
+  // enough fetch workgroups for ~512 in total, whatever the batch
+  const int per_req = (512 + n_req - 1) / n_req < 16 ? (512 + n_req - 1) / n_req : 16;
+  hipLaunchKernelGGL(fetch_kernel, dim3(per_req, n_req), dim3(FT), 0, s, t.ml_tok, t.ml_slot, t.ml_cnt, host_layer,
+                     t.buf, g.cap, g.host_stride, g.slot_stride, g.k, g.B, (int32_t)(g.entry_bytes / 16));
+  return hipGetLastError();
 }
 
 hipError_t launch_reset(const Geometry& g, int32_t* pt, int32_t* rm, int32_t* st, int32_t* ord, int32_t* step,

@@ -62,7 +62,9 @@ class DecodeSteps:
         side.wait_stream(main)                       # fork
         done = []
         for l in range(hs.L):
-            hs.resolve(l, sel, self.slots[l], self.miss[i, l], stream=side)
+            # tables first, then the row copy by the LDS-free kernel, which can run beside the
+            # attention of an earlier layer on the main stream
+            hs.resolve(l, sel, self.slots[l], self.miss[i, l], stream=side, split=True)
             e = torch.cuda.Event()
             e.record(side)
             done.append(e)

@@ -129,6 +129,20 @@ hs_status hs_resolve(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* 
                      int32_t* d_miss, void* stream);
 
 /*
+ * hs_resolve in two halves, for schedulers that overlap the host-to-device copy with other
+ * work (layer-wise prefetch runs the copies of later layers beside the attention of earlier
+ * ones).  hs_resolve_tables does everything hs_resolve does except moving rows, and records
+ * each request's miss list (token, slot) in the handle; hs_fetch_misses then copies those
+ * rows with a kernel that uses no LDS and few registers, so it can share compute units with
+ * a running attention kernel.  The pair must run in this order on the caller's streams,
+ * with no other resolve of the same layer in between; together they equal hs_resolve.
+ * With HS_FLAG_NO_IO, hs_fetch_misses enqueues nothing.
+ */
+hs_status hs_resolve_tables(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* d_sel, int32_t* d_slots,
+                            int32_t* d_miss, void* stream);
+hs_status hs_fetch_misses(hs_handle* h, int32_t layer, int32_t n_req, void* stream);
+
+/*
  * Sparse MLA decode attention over the resolved slots (paper abstract: each
  * step reads only the selected KV entries; only placement changes, so the
  * result equals attention over the selected tokens of the full history).

@@ -49,7 +49,9 @@ def lru_order_ok(stamp: np.ndarray, order: np.ndarray) -> bool:
 class Pair:
     """A device handle and the oracle, fed the same trace."""
 
-    def __init__(self, n, L, k, B, ratio, layout, seed, heads=0, flags=0, oracle_rows=True, requests=None):
+    def __init__(self, n, L, k, B, ratio, layout, seed, heads=0, flags=0, oracle_rows=True, requests=None,
+                 split=False):
+        self.split = split
         self.hs = hsa.HiSparse(top_k=k, device_buffer_size=B, host_to_device_ratio=ratio, max_requests=n,
                                num_layers=L, layout=layout, num_heads=heads, flags=flags)
         self.seed, self.n, self.L, self.k, self.B, self.layout = seed, n, L, k, B, layout
@@ -61,7 +63,7 @@ class Pair:
 
     def step(self, layer: int, S: np.ndarray, check_state: bool):
         sel = torch.from_numpy(np.ascontiguousarray(S, dtype=np.int32)).cuda()
-        slots_d, miss_d = self.hs.resolve(layer, sel)
+        slots_d, miss_d = self.hs.resolve(layer, sel, split=self.split)
         slots_o, miss_o = self.orc.resolve(layer, S)
         torch.cuda.synchronize()
         slots_g = slots_d.cpu().numpy()

@@ -69,8 +69,8 @@ def test_sizes_for_the_batch64_workload():
     host = hsa.host_bytes(cfg)
     assert host == 64 * 32768 * 1152
     slots = 64 * 4096 * 1152
-    tables = 64 * 32768 * 4 + 3 * 64 * 4096 * 4
-    assert slots + tables <= dev <= slots + tables + 16 * 4096
+    tables = 64 * 32768 * 4 + 3 * 64 * 4096 * 4 + 2 * 64 * 2048 * 4  # page table, owners/stamps/order, miss lists
+    assert slots + tables <= dev <= slots + tables + 64 * 1024
 
 
 def test_null_arguments():

@@ -16,10 +16,10 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")]
 
 
-def _run(w, steps=None, requests=None, check_every=1, oracle_rows=True, sample_rows=None):
+def _run(w, steps=None, requests=None, check_every=1, oracle_rows=True, sample_rows=None, split=False):
     x = trace_for(w, steps=steps, requests=requests)
     n = x.shape[1]
-    p = Pair(n, 1, w.k, w.B, w.ratio, w.layout, w.seed, oracle_rows=oracle_rows)
+    p = Pair(n, 1, w.k, w.B, w.ratio, w.layout, w.seed, oracle_rows=oracle_rows, split=split)
     misses = []
     try:
         for t in range(x.shape[0]):
@@ -33,15 +33,17 @@ def _run(w, steps=None, requests=None, check_every=1, oracle_rows=True, sample_r
     return np.stack(misses)
 
 
-def test_tiny_all_steps():
-    say("tiny: 1 request, k 64, B 128, 32 steps")
-    m = _run(C.TINY)
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_tiny_all_steps(mode):
+    say(f"tiny: 1 request, k 64, B 128, 32 steps, {mode}")
+    m = _run(C.TINY, split=(mode == "split"))
     assert m[0, 0] == 64 and m[1:].max() <= 64
 
 
-def test_batch64_full():
-    say("batch64: 64 requests, k 2048, B 4096, cap 32768, 200 steps")
-    m = _run(C.BATCH64, check_every=20)
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_batch64_full(mode):
+    say(f"batch64: 64 requests, k 2048, B 4096, cap 32768, 200 steps, {mode}")
+    m = _run(C.BATCH64, check_every=20, split=(mode == "split"))
     assert (m[0] == 2048).all()
 
 
@@ -60,13 +62,15 @@ def test_fp8_256_resolve_full_size(churn):
     _run(w, steps=25, check_every=8, oracle_rows=False, sample_rows=128)
 
 
-@pytest.mark.parametrize("k,B,ratio,n", [(700, 1000, 3, 3), (1, 7, 5, 2), (33, 33, 4, 5), (512, 512, 2, 1),
-                                          (513, 777, 9, 4), (2048, 2048, 3, 2), (4096, 6000, 2, 2)])
-def test_ragged_shapes_random_traces(k, B, ratio, n):
-    say(f"ragged: k {k}, B {B}, ratio {ratio}, n {n}")
+@pytest.mark.parametrize("k,B,ratio,n,split", [(700, 1000, 3, 3, False), (1, 7, 5, 2, False), (33, 33, 4, 5, False),
+                                                (512, 512, 2, 1, False), (513, 777, 9, 4, False),
+                                                (2048, 2048, 3, 2, False), (4096, 6000, 2, 2, False),
+                                                (700, 1000, 3, 3, True), (1, 7, 5, 2, True), (4096, 6000, 2, 2, True)])
+def test_ragged_shapes_random_traces(k, B, ratio, n, split):
+    say(f"ragged: k {k}, B {B}, ratio {ratio}, n {n}, split {split}")
     cap = B * ratio
     rng = np.random.default_rng(k * 7 + B)
-    p = Pair(n, 1, k, B, ratio, hsa.LAYOUT_BF16, seed=77)
+    p = Pair(n, 1, k, B, ratio, hsa.LAYOUT_BF16, seed=77, split=split)
     try:
         pop = rng.permutation(cap)
         w = 1.0 / np.arange(1, cap + 1) ** 0.9
