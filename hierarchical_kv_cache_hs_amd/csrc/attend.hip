@@ -99,14 +99,13 @@ __device__ __forceinline__ s16x4 pack4_exact(const f32x4 x) {
   return __builtin_bit_cast(s16x4, v);
 }
 
-// Four fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+// Four fp32 -> packed bf16, round to nearest even (two v_cvt_pk_bf16_f32).
 __device__ __forceinline__ s16x4 pack4_rne(float a, float b, float c, float d) {
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  bf16x4 v;
-  v[0] = (__bf16)a;
-  v[1] = (__bf16)b;
-  v[2] = (__bf16)c;
-  v[3] = (__bf16)d;
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  u32x2 v;
+  v[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+  v[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){c, d}, bf16x2));
   return __builtin_bit_cast(s16x4, v);
 }
 
@@ -165,6 +164,10 @@ struct TileGeo {
   static constexpr int CHUNKS = T * C;
   static constexpr int L0 = (CHUNKS + NT - 1) / NT;       // DMA instructions per tile, wave 0
   static constexpr int MAXCHUNK = LAYOUT == 0 ? 1024 : 2048;  // tokens per workgroup
+  // Score exchange slots.  With two, one barrier per tile suffices (a slot is rewritten only
+  // two tiles later, after a barrier its reader has passed); the bf16 ring leaves room for one
+  // only, and a second barrier per tile guards its reuse.
+  static constexpr int XCH = LAYOUT == 0 ? 1 : 2;
   static_assert(CHUNKS % 64 == 0, "tile chunks must fill whole waves");
 };
 
@@ -174,17 +177,19 @@ __device__ __forceinline__ int dma_per_tile(int w) {
   return (TileGeo<LAYOUT>::CHUNKS - 64 * w + NT - 1) / NT;
 }
 
-// Wait until at most `pending` (0 .. NBUF - 2) later tiles of this wave's DMA are outstanding.
+// Wait until at most `pending` (0 .. NBUF - 1) later tiles of this wave's DMA are outstanding;
+// `per` is the wave's DMA instruction count per tile (the counter counts instructions).
 template <int LAYOUT>
 __device__ __forceinline__ void wait_tiles(int pending, int per) {
   if (LAYOUT == 0) {
-    static_assert(TileGeo<0>::NBUF == 2, "wait table");
-    wait_vmcnt<0>();
+    static_assert(TileGeo<0>::NBUF == 2 && TileGeo<0>::CHUNKS % NT == 0, "wait table");
+    if (pending == 0) wait_vmcnt<0>();
+    else wait_vmcnt<TileGeo<0>::L0>();
   } else {
     static_assert(TileGeo<1>::NBUF == 3 && TileGeo<1>::L0 == 6, "wait table");
     if (pending == 0) wait_vmcnt<0>();
-    else if (per == 6) wait_vmcnt<6>();
-    else wait_vmcnt<5>();
+    else if (pending == 1) { if (per == 6) wait_vmcnt<6>(); else wait_vmcnt<5>(); }
+    else { if (per == 6) wait_vmcnt<12>(); else wait_vmcnt<10>(); }
   }
 }
 
@@ -195,8 +200,12 @@ static_assert(HMAX * OACC_LD * sizeof(float) <= 2 * 64 * 656, "merge buffer must
 
 template <int LAYOUT>
 constexpr size_t attend_lds_bytes() {
-  return ring_bytes<LAYOUT>() + TileGeo<LAYOUT>::MAXCHUNK * sizeof(int32_t) + WAVES * 64 * sizeof(f32x4);
+  return ring_bytes<LAYOUT>() + TileGeo<LAYOUT>::MAXCHUNK * sizeof(int32_t) +
+         TileGeo<LAYOUT>::XCH * WAVES * 64 * sizeof(f32x4);
 }
+
+static_assert(attend_lds_bytes<0>() + 2 * GROUPS * HMAX * sizeof(float) <= kLdsLimit, "bf16 LDS budget");
+static_assert(attend_lds_bytes<1>() + 2 * GROUPS * HMAX * sizeof(float) <= kLdsLimit, "fp8 LDS budget");
 
 template <int LAYOUT>
 __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
@@ -244,20 +253,32 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
   __syncthreads();
   __builtin_amdgcn_s_waitcnt(0);
 
-  const int per = dma_per_tile<LAYOUT>(w);
-  auto issue = [&](int t) {
-    uint8_t* dst = ring + (t % G::NBUF) * G::TILE;
+  const int wu = __builtin_amdgcn_readfirstlane(w) & (WAVES - 1);  // the wave index, scalar and known < WAVES
+  const int per = dma_per_tile<LAYOUT>(wu);
+  // The row and 16-byte column of each of this lane's DMA chunks are the same in every tile.
+  int drow[G::L0], dcol[G::L0];
+#pragma unroll
+  for (int j = 0; j < G::L0; ++j) {
+    const int c = j * NT + 64 * wu + lane;
+    drow[j] = c / G::C;
+    dcol[j] = 16 * (c - drow[j] * G::C);
+  }
+  const uint32_t stride32 = (uint32_t)a.stride;  // a request's rows span less than 4 GiB
+  auto issue = [&](int u) {
+    uint8_t* dst = ring + (u % G::NBUF) * G::TILE;
+    const int32_t* su = slot_lds + u * G::T;
+    // All slots first, then the loads: the compiler keeps an LDS read that follows an
+    // LDS-DMA load behind it, so interleaving them costs one LDS round trip per load.
+    int32_t sl[G::L0];
+#pragma unroll
+    for (int j = 0; j < G::L0; ++j) sl[j] = (j * NT + 64 * wu < G::CHUNKS) ? su[drow[j]] : 0;
 #pragma unroll
     for (int j = 0; j < G::L0; ++j) {
-      const int base = j * NT + 64 * w;
+      const int base = j * NT + 64 * wu;
       if (base < G::CHUNKS) {
-        const int c = base + lane;
-        const int row = c / G::C;
-        const int col = c - row * G::C;
-        int32_t sl = slot_lds[t * G::T + row];
-        sl = sl < 0 ? 0 : sl;  // padding reads an in-bounds row; its operands are zeroed below
-        const uint8_t* src = rbase + (int64_t)sl * a.stride + col * 16;
-        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+        // padding reads an in-bounds row (slot 0); its operands are zeroed before use
+        const uint32_t off = (uint32_t)max(sl[j], 0) * stride32 + (uint32_t)dcol[j];
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(rbase + off),
                                          (void __attribute__((address_space(3)))*)(dst + base * 16), 16, 0, 0);
       }
     }
@@ -278,15 +299,16 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
   for (int t = 0; t < 16; ++t) O[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int t = 0; t < G::NBUF - 1 && t < ntiles; ++t) issue(t);
+  // A tile's buffer is refilled as soon as every wave holds the tile's K values in
+  // registers, so all NBUF buffers start in flight.
+  for (int u = 0; u < G::NBUF && u < ntiles; ++u) issue(u);
+  if (ntiles > 0) {
+    wait_tiles<LAYOUT>(min(G::NBUF - 1, ntiles - 1), per);  // this wave's share of tile 0
+    barrier_only();
+  }
 
   for (int t = 0; t < ntiles; ++t) {
-    // Tiles t .. t + NBUF - 2 are in flight.  Once every wave is past this barrier, all
-    // are done with tile t - 1, whose buffer then takes tile t + NBUF - 1.
-    wait_tiles<LAYOUT>(min(G::NBUF - 2, ntiles - 1 - t), per);
-    barrier_only();
-    if (t + G::NBUF - 1 < ntiles) issue(t + G::NBUF - 1);
-
+    // tile t is in LDS; tiles t + 1 .. t + NBUF - 1 are in flight
     const uint8_t* tile = ring + (t % G::NBUF) * G::TILE;
     const int trow = 16 * tg + c16;                       // this lane's token (A-operand row)
     const bool valid = slot_lds[t * G::T + trow] >= 0;
@@ -362,10 +384,16 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
       for (int j = 0; j < 4; ++j) part[j] = accr[j] + sc[j][0] * accb[0][j] + sc[j][1] * accb[1][j];
     }
 
-    // ---- pair exchange: both halves end with the full scores
-    xch[w * 64 + lane] = part;
+    // ---- pair exchange: both halves end with the full scores.  One barrier publishes the
+    // partial scores and this wave's share of tile t + 1, and frees tile t's buffer (its K
+    // values are in registers), which then takes tile t + NBUF.
+    f32x4* xs = xch + (t % G::XCH) * (WAVES * 64);
+    if (G::XCH == 1) lds_done_barrier();  // the partner has read the previous tile's scores
+    xs[w * 64 + lane] = part;
+    wait_tiles<LAYOUT>(max(0, min(G::NBUF - 2, ntiles - 2 - t)), per);
     lds_done_barrier();
-    const f32x4 other = xch[(w ^ 4) * 64 + lane];
+    if (t + G::NBUF < ntiles) issue(t + G::NBUF);
+    const f32x4 other = xs[(w ^ 4) * 64 + lane];
     float s2[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -381,9 +409,9 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
     const float m_new = (mx > m_run + 8.f) ? mx : m_run;
     float alpha = 1.f, p[4] = {0.f, 0.f, 0.f, 0.f};
     if (m_new != -INFINITY) {
-      alpha = exp2f(m_run - m_new);
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) p[j] = exp2f(s2[j] - m_new);
+      for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(s2[j] - m_new);
     }
     const float rs = rows_sum((p[0] + p[1]) + (p[2] + p[3]));
     l_run = l_run * alpha + rs;
