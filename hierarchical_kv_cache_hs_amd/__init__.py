@@ -48,7 +48,8 @@ class Config(ctypes.Structure):
 class StateView(ctypes.Structure):
     _fields_ = [("page_table", ctypes.c_void_p), ("slot_owner", ctypes.c_void_p), ("slot_stamp", ctypes.c_void_p),
                 ("lru_order", ctypes.c_void_p), ("step", ctypes.c_void_p), ("kv_buffer", ctypes.c_void_p),
-                ("capacity", ctypes.c_int64), ("slot_stride", ctypes.c_int64), ("entry_bytes", ctypes.c_int64)]
+                ("capacity", ctypes.c_int64), ("slot_stride", ctypes.c_int64), ("entry_bytes", ctypes.c_int64),
+                ("request_stride", ctypes.c_int64)]
 
 
 class HSError(RuntimeError):
@@ -239,13 +240,17 @@ class HiSparse:
             return self.block[off: off + count * esz].view(dtype).view(*shape)
 
         n, B, cap = self.n, self.B, v.capacity
+        assert v.request_stride == (B + 1) * v.slot_stride
+        rows = view(v.kv_buffer, n * v.request_stride, torch.uint8, (n, B + 1, v.slot_stride))
         return {
             "page_table": view(v.page_table, n * cap, torch.int32, (n, cap)),
             "slot_owner": view(v.slot_owner, n * B, torch.int32, (n, B)),
             "slot_stamp": view(v.slot_stamp, n * B, torch.int32, (n, B)),
             "lru_order": view(v.lru_order, n * B, torch.int32, (n, B)),
             "step": view(v.step, n, torch.int32, (n,)),
-            "kv_buffer": view(v.kv_buffer, n * B * v.slot_stride, torch.uint8, (n, B, v.slot_stride)),
+            # per request: B slot rows, then a row of zeros that padded attention entries read
+            "kv_buffer": rows[:, :B],
+            "zero_row": rows[:, B],
             "entry_bytes": v.entry_bytes,
         }
 

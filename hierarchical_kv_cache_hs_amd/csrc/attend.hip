@@ -56,7 +56,6 @@ constexpr int DQK = 576;                    // q.K length
 constexpr int DV = 512;                     // value length
 constexpr int KB_HALF = 9;                  // reduction blocks of 32 values per half
 constexpr int PART = 2 * HMAX + HMAX * DV;  // floats of one split partial
-constexpr int OACC_LD = DV + 4;             // merge-buffer row: 4 floats of padding spread the head rows over LDS banks
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -67,7 +66,8 @@ struct AttendArgs {
   uint16_t* out;          // [n_req][heads][512] bf16
   float* lse;             // [n_req][heads] or null
   float* part;            // [n][splits][PART]
-  int64_t stride;
+  int64_t stride;         // bytes between slot rows
+  int64_t rstride;        // bytes between requests: B slot rows, then a row of zeros
   int32_t k, B, heads, chunk, splits;
   float scale_log2;       // softmax scale * log2(e)
 };
@@ -196,7 +196,6 @@ __device__ __forceinline__ void wait_tiles(int pending, int per) {
 template <int LAYOUT>
 constexpr size_t ring_bytes() { return (size_t)TileGeo<LAYOUT>::NBUF * TileGeo<LAYOUT>::TILE; }
 
-static_assert(HMAX * OACC_LD * sizeof(float) <= 2 * 64 * 656, "merge buffer must fit in the ring");
 
 template <int LAYOUT>
 constexpr size_t attend_lds_bytes() {
@@ -204,8 +203,11 @@ constexpr size_t attend_lds_bytes() {
          TileGeo<LAYOUT>::XCH * WAVES * 64 * sizeof(f32x4);
 }
 
-static_assert(attend_lds_bytes<0>() + 2 * GROUPS * HMAX * sizeof(float) <= kLdsLimit, "bf16 LDS budget");
-static_assert(attend_lds_bytes<1>() + 2 * GROUPS * HMAX * sizeof(float) <= kLdsLimit, "fp8 LDS budget");
+constexpr size_t kStaticLds = (3 * GROUPS + 1) * HMAX * sizeof(float);  // wm, wl, fac, inv_l
+constexpr size_t kParkBytes = (size_t)GROUPS * 2 * 16 * 64 * sizeof(f32x4);   // parked accumulators
+static_assert(attend_lds_bytes<0>() + kStaticLds <= kLdsLimit, "bf16 LDS budget");
+static_assert(attend_lds_bytes<1>() + kStaticLds <= kLdsLimit, "fp8 LDS budget");
+static_assert(kParkBytes <= attend_lds_bytes<0>() && kParkBytes <= attend_lds_bytes<1>(), "parking fits");
 
 template <int LAYOUT>
 __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
@@ -214,9 +216,11 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
   uint8_t* ring = smem;                                              // [NBUF][TILE]
   int32_t* slot_lds = (int32_t*)(smem + ring_bytes<LAYOUT>());       // [MAXCHUNK]
   f32x4* xch = (f32x4*)(smem + ring_bytes<LAYOUT>() + G::MAXCHUNK * sizeof(int32_t));  // [WAVES][64]
-  float* o_acc = (float*)smem;                                       // after the loop: [16][OACC_LD]
+  f32x4* o_park = (f32x4*)smem;  // after the loop: [GROUPS][2][16][64] accumulators
   __shared__ float wm[GROUPS][HMAX];
   __shared__ float wl[GROUPS][HMAX];
+  __shared__ float fac[GROUPS][HMAX];
+  __shared__ float inv_l[HMAX];
 
   const int s = blockIdx.x;
   const int r = blockIdx.y;
@@ -233,7 +237,7 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
   const int tok1 = min(a.k, tok0 + a.chunk);
   const int ntok = tok1 > tok0 ? tok1 - tok0 : 0;
   const int ntiles = (ntok + G::T - 1) / G::T;
-  const uint8_t* rbase = a.buf + (int64_t)r * a.B * a.stride;
+  const uint8_t* rbase = a.buf + (int64_t)r * a.rstride;
 
   // ---- this workgroup's slot list (invalid or missing -> -1) and this wave's Q operands
   {
@@ -264,6 +268,7 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
     dcol[j] = 16 * (c - drow[j] * G::C);
   }
   const uint32_t stride32 = (uint32_t)a.stride;  // a request's rows span less than 4 GiB
+  const int32_t zero_slot = a.B;                 // the zero row after the request's slots
   auto issue = [&](int u) {
     uint8_t* dst = ring + (u % G::NBUF) * G::TILE;
     const int32_t* su = slot_lds + u * G::T;
@@ -276,8 +281,8 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
     for (int j = 0; j < G::L0; ++j) {
       const int base = j * NT + 64 * wu;
       if (base < G::CHUNKS) {
-        // padding reads an in-bounds row (slot 0); its operands are zeroed before use
-        const uint32_t off = (uint32_t)max(sl[j], 0) * stride32 + (uint32_t)dcol[j];
+        // padding reads the zero row, so its operands are finite and contribute nothing
+        const uint32_t off = (uint32_t)(sl[j] < 0 ? zero_slot : sl[j]) * stride32 + (uint32_t)dcol[j];
         __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(rbase + off),
                                          (void __attribute__((address_space(3)))*)(dst + base * 16), 16, 0, 0);
       }
@@ -299,31 +304,18 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
   for (int t = 0; t < 16; ++t) O[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // A tile's buffer is refilled as soon as every wave holds the tile's K values in
-  // registers, so all NBUF buffers start in flight.
-  for (int u = 0; u < G::NBUF && u < ntiles; ++u) issue(u);
-  if (ntiles > 0) {
-    wait_tiles<LAYOUT>(min(G::NBUF - 1, ntiles - 1), per);  // this wave's share of tile 0
-    barrier_only();
-  }
-
-  for (int t = 0; t < ntiles; ++t) {
-    // tile t is in LDS; tiles t + 1 .. t + NBUF - 1 are in flight
+  // This wave's K operands (its half of the 576 values of tokens 16 tg .. 16 tg + 15 of
+  // tile t, converted to bf16), block scales of tokens 4g + j, and the slots of tokens
+  // 4g .. 4g + 3 (-1 = padding).
+  auto load_tile = [&](int t, u32x4 (&kr)[KB_HALF], float (&scl)[4][2], u32x4& vqr) {
     const uint8_t* tile = ring + (t % G::NBUF) * G::TILE;
-    const int trow = 16 * tg + c16;                       // this lane's token (A-operand row)
-    const bool valid = slot_lds[t * G::T + trow] >= 0;
-    const u32x4 vq = *(const u32x4*)(slot_lds + t * G::T + 16 * tg + 4 * g);  // tokens 4g..4g+3
-    const uint8_t* row = tile + trow * G::E;
-    const u32x4 z4 = {0u, 0u, 0u, 0u};
-
-    // ---- this half's K operands
-    u32x4 kreg[KB_HALF];
-    float sc[4][2];   // scales of tokens 4g + j, blocks 2hf and 2hf + 1
+    const uint8_t* row = tile + (16 * tg + c16) * G::E;  // this lane's token (A-operand row)
+    vqr = *(const u32x4*)(slot_lds + t * G::T + 16 * tg + 4 * g);
     if (LAYOUT == 0) {
 #pragma unroll
       for (int i = 0; i < KB_HALF; ++i) {
         const int kb = (i < 8) ? 8 * hf + i : 16 + hf;
-        kreg[i] = *(const u32x4*)(row + 2 * kb_offset(kb, g));
+        kr[i] = *(const u32x4*)(row + 2 * kb_offset(kb, g));
       }
     } else {
 #pragma unroll
@@ -331,39 +323,33 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
         const int b = 2 * hf + bb;
         const u32x4 lo = *(const u32x4*)(row + 128 * b + 32 * g);
         const u32x4 hi = *(const u32x4*)(row + 128 * b + 32 * g + 16);
-        kreg[4 * bb + 0] = e4m3x8_to_bf16x8(lo[0], lo[1]);
-        kreg[4 * bb + 1] = e4m3x8_to_bf16x8(lo[2], lo[3]);
-        kreg[4 * bb + 2] = e4m3x8_to_bf16x8(hi[0], hi[1]);
-        kreg[4 * bb + 3] = e4m3x8_to_bf16x8(hi[2], hi[3]);
+        kr[4 * bb + 0] = e4m3x8_to_bf16x8(lo[0], lo[1]);
+        kr[4 * bb + 1] = e4m3x8_to_bf16x8(lo[2], lo[3]);
+        kr[4 * bb + 2] = e4m3x8_to_bf16x8(hi[0], hi[1]);
+        kr[4 * bb + 3] = e4m3x8_to_bf16x8(hi[2], hi[3]);
       }
-      kreg[8] = *(const u32x4*)(row + 528 + 32 * g + 16 * hf);
+      kr[8] = *(const u32x4*)(row + 528 + 32 * g + 16 * hf);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const u32x2 sv = *(const u32x2*)(tile + (16 * tg + 4 * g + j) * G::E + 512 + 8 * hf);
-        sc[j][0] = __uint_as_float(sv[0]);
-        sc[j][1] = __uint_as_float(sv[1]);
+        scl[j][0] = __uint_as_float(sv[0]);
+        scl[j][1] = __uint_as_float(sv[1]);
       }
     }
+  };
 
-    // A padded or missing token reads some in-bounds row; its operands are zeroed so that
-    // no stray value (NaN in particular) reaches the P V product.  Skipped when all 16 of the
-    // wave's tokens are real, as in every full tile.
-    if (!__all(valid)) {
-#pragma unroll
-      for (int i = 0; i < KB_HALF; ++i) kreg[i] = valid ? kreg[i] : z4;
-    }
-
-    // ---- partial S^T[tok][h] over this half
+  // Partial S^T[tok][h] over this wave's half of the values.
+  auto qk = [&](const u32x4 (&kr)[KB_HALF], const float (&scl)[4][2]) -> f32x4 {
     f32x4 part;
     if (LAYOUT == 0) {
       f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < KB_HALF; i += 2)
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[i]),
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[i]),
                                                        __builtin_bit_cast(bf16x8, qreg[i]), acc0, 0, 0, 0);
 #pragma unroll
       for (int i = 1; i < KB_HALF; i += 2)
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[i]),
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[i]),
                                                        __builtin_bit_cast(bf16x8, qreg[i]), acc1, 0, 0, 0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) part[j] = acc0[j] + acc1[j];
@@ -374,31 +360,55 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
         accb[bb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          accb[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[4 * bb + i]),
+          accb[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[4 * bb + i]),
                                                              __builtin_bit_cast(bf16x8, qreg[4 * bb + i]),
                                                              accb[bb], 0, 0, 0);
       }
-      accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[8]),
+      accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[8]),
                                                      __builtin_bit_cast(bf16x8, qreg[8]), accr, 0, 0, 0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) part[j] = accr[j] + sc[j][0] * accb[0][j] + sc[j][1] * accb[1][j];
+      for (int j = 0; j < 4; ++j) part[j] = accr[j] + scl[j][0] * accb[0][j] + scl[j][1] * accb[1][j];
     }
+    return part;
+  };
 
-    // ---- pair exchange: both halves end with the full scores.  One barrier publishes the
-    // partial scores and this wave's share of tile t + 1, and frees tile t's buffer (its K
-    // values are in registers), which then takes tile t + NBUF.
+  // Pair exchange of tile t's partial scores.  One barrier publishes them together with this
+  // wave's share of tile t + 1, and frees tile t's buffer (every wave holds its K values in
+  // registers by then), which takes tile t + NBUF.
+  auto publish = [&](int t, const f32x4& part) {
     f32x4* xs = xch + (t % G::XCH) * (WAVES * 64);
     if (G::XCH == 1) lds_done_barrier();  // the partner has read the previous tile's scores
     xs[w * 64 + lane] = part;
     wait_tiles<LAYOUT>(max(0, min(G::NBUF - 2, ntiles - 2 - t)), per);
     lds_done_barrier();
     if (t + G::NBUF < ntiles) issue(t + G::NBUF);
-    const f32x4 other = xs[(w ^ 4) * 64 + lane];
+  };
+
+  // A tile's buffer is refilled as soon as every wave holds the tile's K values in
+  // registers, so all NBUF buffers start in flight.
+  for (int u = 0; u < G::NBUF && u < ntiles; ++u) issue(u);
+
+  u32x4 kcur[KB_HALF];
+  float sccur[4][2];
+  u32x4 vqcur;
+  f32x4 partcur;
+  if (ntiles > 0) {
+    wait_tiles<LAYOUT>(min(G::NBUF - 1, ntiles - 1), per);  // this wave's share of tile 0
+    barrier_only();
+    load_tile(0, kcur, sccur, vqcur);
+    partcur = qk(kcur, sccur);
+    publish(0, partcur);
+  }
+
+  // Software pipelined: while the P V products of tile t run on the matrix cores, the
+  // operands of tile t + 1 are read, converted and multiplied by Q in the same block.
+  for (int t = 0; t < ntiles; ++t) {
+    const f32x4 other = xch[(t % G::XCH) * (WAVES * 64) + (w ^ 4) * 64 + lane];
     float s2[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float sj = part[j] + other[j];
-      s2[j] = (vq[j] != 0xFFFFFFFFu) ? sj * a.scale_log2 : -INFINITY;
+      const float sj = partcur[j] + other[j];
+      s2[j] = (vqcur[j] != 0xFFFFFFFFu) ? sj * a.scale_log2 : -INFINITY;
     }
 
     // ---- online softmax for head c16 over tokens 4g + j of this group
@@ -428,7 +438,6 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
         for (int j = 0; j < 4; ++j) O[tau][j] *= aj[j];
     }
 
-    // ---- O += P V over this half's 256 columns
     s16x4 pa[2];
     if (LAYOUT == 0) {
       pa[0] = pack4_rne(p[0], p[1], p[2], p[3]);
@@ -436,84 +445,103 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
     } else {
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb)
-        pa[bb] = pack4_rne(p[0] * sc[0][bb], p[1] * sc[1][bb], p[2] * sc[2][bb], p[3] * sc[3][bb]);
+        pa[bb] = pack4_rne(p[0] * sccur[0][bb], p[1] * sccur[1][bb], p[2] * sccur[2][bb], p[3] * sccur[3][bb]);
     }
+
+    // ---- tile t + 1's operands (its bytes landed before the last barrier); the last
+    // iteration re-reads tile t, which keeps this block free of branches
+    u32x4 knext[KB_HALF];
+    float scnext[4][2];
+    u32x4 vqnext;
+    load_tile(min(t + 1, ntiles - 1), knext, scnext, vqnext);
+
+    // ---- O += P V over this half's 256 columns
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const bf16x8 kv = __builtin_bit_cast(bf16x8, kreg[i]);
+      const bf16x8 kv = __builtin_bit_cast(bf16x8, kcur[i]);
       const s16x4 P = pa[i >> 2];
       const f32x4 t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, sel0, zero, 0, 0, 0);
       const f32x4 t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, sel1, zero, 0, 0, 0);
       O[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(P, pack4_exact(t0), O[2 * i], 0, 0, 0);
       O[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(P, pack4_exact(t1), O[2 * i + 1], 0, 0, 0);
     }
+
+    const f32x4 partnext = qk(knext, scnext);
+#pragma unroll
+    for (int i = 0; i < KB_HALF; ++i) kcur[i] = knext[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sccur[j][0] = scnext[j][0];
+      sccur[j][1] = scnext[j][1];
+    }
+    vqcur = vqnext;
+    partcur = partnext;
+    if (t + 1 < ntiles) publish(t + 1, partcur);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // ---- merge the four token groups (fixed order); o_acc reuses the ring
+  // ---- merge the four token groups (fixed order).  Each wave parks its accumulators in
+  // the now idle ring, in their register layout (lane-contiguous 16-byte rows, no bank
+  // conflicts); 16 threads work out each head's merge factors once; then every thread
+  // combines float4s of 4 heads x 1 column.
   if (hf == 0 && g == 0) {
     wm[tg][c16] = m_run;
     wl[tg][c16] = l_run;
   }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) o_park[((tg * 2 + hf) * 16 + i) * 64 + lane] = O[i];
   __syncthreads();
-  float f[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int h = 4 * g + j;
-    float M = wm[0][h];
-#pragma unroll
-    for (int v = 1; v < GROUPS; ++v) M = fmaxf(M, wm[v][h]);
-    f[j] = (M == -INFINITY) ? 0.f : exp2f(wm[tg][h] - M);
-  }
-  for (int v = 0; v < GROUPS; ++v) {
-    if (tg == v) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int col = out_col(16 * hf + i, c16);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int idx = (4 * g + j) * OACC_LD + col;
-          const float val = O[i][j] * f[j];
-          o_acc[idx] = (v == 0) ? val : o_acc[idx] + val;
-        }
-      }
-    }
-    __syncthreads();
-  }
-
   const int splits = a.splits;
-  if (splits == 1) {
-    for (int idx = tid; idx < heads * DV; idx += NT) {
-      const int h = idx / DV;
-      float M = wm[0][h];
-      for (int v = 1; v < GROUPS; ++v) M = fmaxf(M, wm[v][h]);
-      float L = 0.f;
-      if (M != -INFINITY)
-        for (int v = 0; v < GROUPS; ++v) L += exp2f(wm[v][h] - M) * wl[v][h];
-      const float val = L > 0.f ? o_acc[h * OACC_LD + idx % DV] / L : 0.f;
-      a.out[(int64_t)r * heads * DV + idx] = (uint16_t)bf16_rne(val);
-      if ((idx % DV) == 0 && a.lse) a.lse[(int64_t)r * heads + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
-    }
-    return;
-  }
-
-  // splits > 1: an unnormalised partial (per-head max and sum, 16 x 512 values); the combine
-  // kernel that follows on the stream merges the splits (the kernel boundary makes these
-  // stores visible, so no device-scope fence is needed here)
-  float* mypart = a.part + ((int64_t)r * splits + s) * PART;
+  float* mypart = a.part + ((int64_t)r * splits + s) * PART;  // used when splits > 1
   if (tid < HMAX) {
     const int h = tid;
     float M = wm[0][h];
+#pragma unroll
     for (int v = 1; v < GROUPS; ++v) M = fmaxf(M, wm[v][h]);
     float L = 0.f;
-    if (M != -INFINITY)
-      for (int v = 0; v < GROUPS; ++v) L += exp2f(wm[v][h] - M) * wl[v][h];
-    mypart[h] = M;
-    mypart[HMAX + h] = L;
+#pragma unroll
+    for (int v = 0; v < GROUPS; ++v) {
+      const float f = (M == -INFINITY) ? 0.f : exp2f(wm[v][h] - M);
+      fac[v][h] = f;
+      L += f * wl[v][h];
+    }
+    if (splits == 1) {
+      inv_l[h] = L > 0.f ? 1.f / L : 0.f;
+      if (a.lse && h < heads) a.lse[(int64_t)r * heads + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    } else {
+      inv_l[h] = 1.f;
+      mypart[h] = M;
+      mypart[HMAX + h] = L;
+    }
   }
-  for (int idx = tid; idx < HMAX * DV; idx += NT) mypart[2 * HMAX + idx] = o_acc[(idx / DV) * OACC_LD + idx % DV];
+  __syncthreads();
+  // slot e = (value half, accumulator tile, lane): heads 4 (lane / 16) + j, one column
+  for (int e = tid; e < 2 * 16 * 64; e += NT) {
+    const int he = e >> 10, tau = (e >> 6) & 15, ln = e & 63;
+    const int h0 = 4 * (ln >> 4);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < GROUPS; ++v) {
+      const f32x4 o = o_park[((v * 2 + he) * 16 + tau) * 64 + ln];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += fac[v][h0 + j] * o[j];
+    }
+    const int col = out_col(16 * he + tau, ln & 15);
+    if (splits == 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (h0 + j < heads)
+          a.out[((int64_t)r * heads + h0 + j) * DV + col] = (uint16_t)bf16_rne(acc[j] * inv_l[h0 + j]);
+    } else {
+      // an unnormalised partial (per-head max and sum, 16 x 512 values); the combine kernel
+      // that follows on the stream merges the splits (the kernel boundary makes these stores
+      // visible, so no device-scope fence is needed)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mypart[2 * HMAX + (h0 + j) * DV + col] = acc[j];
+    }
+  }
 }
 
 // Merges the splits of every request in split order: with M the largest split maximum,
@@ -591,6 +619,7 @@ hipError_t launch_attend(const Geometry& g, const LayerTables& t, int32_t n_req,
   a.lse = lse;
   a.part = t.part;
   a.stride = g.slot_stride;
+  a.rstride = g.req_stride;
   a.k = g.k;
   a.B = g.B;
   a.heads = g.heads;

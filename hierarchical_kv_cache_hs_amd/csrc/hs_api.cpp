@@ -11,7 +11,8 @@
 //   cnt   [L][n]               attention split arrival counters
 //   part  [L][n][...]          attention split partials (if num_heads > 0)
 //   ml_*  [L][n][k], [L][n]    per-request miss lists (token, slot) and counts for the fetch kernel
-//   buf   [L][n][B][E]         KV rows of the slots, packed
+//   buf   [L][n][B + 1][E]     KV rows of the slots, packed; row B stays zero (attention reads it
+//                              for padded selection entries)
 // Host pool (pinned, mapped): [L][n][cap][entry bytes].
 
 #include <cstdio>
@@ -112,6 +113,7 @@ hs_status plan(const hs_config* cfg, hs::Geometry* g, Layout* lay) {
   g->entry_bytes = cfg->layout == HS_KV_BF16_576 ? 1152 : 656;
   g->host_stride = g->entry_bytes;
   g->slot_stride = g->entry_bytes;  // packed: scattered 656-byte rows gather faster packed than padded to 768
+  g->req_stride = ((int64_t)g->B + 1) * g->slot_stride;
   g->flags = cfg->flags;
 
   const size_t LN = (size_t)g->L * (size_t)g->n;
@@ -130,7 +132,7 @@ hs_status plan(const hs_config* cfg, hs::Geometry* g, Layout* lay) {
   ok = ok && mul_ok(LN, lay->part_floats, &t) && mul_ok(t, 4, &sz) && take(sz, &lay->part);
   ok = ok && mul_ok(LN, (size_t)g->k, &t) && mul_ok(t, 4, &sz) && take(sz, &lay->ml_tok) && take(sz, &lay->ml_slot);
   ok = ok && take(LN * 4, &lay->ml_cnt);
-  ok = ok && mul_ok(LN, (size_t)g->B, &t) && mul_ok(t, (size_t)g->slot_stride, &sz) && take(sz, &lay->buf);
+  ok = ok && mul_ok(LN, (size_t)g->req_stride, &sz) && take(sz, &lay->buf);
   lay->total = off;
   ok = ok && mul_ok(LN, (size_t)cap, &t) && mul_ok(t, (size_t)g->host_stride, &lay->host_total);
   if (!ok) return fail(HS_ERR_INVALID_ARG, "configuration sizes overflow");
@@ -151,7 +153,7 @@ hs::LayerTables layer_tables(const hs_handle* h, int32_t layer) {
   t.ml_tok = h->ml_tok + base * (size_t)g.k;
   t.ml_slot = h->ml_slot + base * (size_t)g.k;
   t.ml_cnt = h->ml_cnt + base;
-  t.buf = h->buf + base * (size_t)g.B * (size_t)g.slot_stride;
+  t.buf = h->buf + base * (size_t)g.req_stride;
   return t;
 }
 
@@ -251,6 +253,9 @@ hs_status hs_create(const hs_config* cfg, hs_handle** out) {
   hs::prepare_resolve();
   hs::prepare_attend();
   e = hipMemset(h->err, 0, sizeof(int32_t));
+  if (e == hipSuccess)  // the zero row after each request's slots
+    e = hipMemset2D(h->buf + (size_t)g.B * (size_t)g.slot_stride, (size_t)g.req_stride, 0, (size_t)g.slot_stride,
+                    (size_t)g.L * (size_t)g.n);
   if (e != hipSuccess) { release(h); return fail_hip(e, "hipMemset"); }
   e = hs::launch_reset(g, h->pt, h->rm, h->st, h->ord, h->step, h->cnt, 0, g.n, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -346,6 +351,7 @@ hs_status hs_device_state(hs_handle* h, int32_t layer, hs_state_view* v) {
   v->capacity = h->g.cap;
   v->slot_stride = h->g.slot_stride;
   v->entry_bytes = h->g.entry_bytes;
+  v->request_stride = h->g.req_stride;
   return HS_OK;
 }
 

@@ -23,7 +23,7 @@ struct LayerTables {
   int32_t* st;     // [n][B]
   int32_t* ord;    // [n][B]
   int32_t* step;   // [n]
-  uint8_t* buf;    // [n][B][slot_stride]
+  uint8_t* buf;    // [n][req_stride]: B rows of slot_stride bytes, then a zero row (attention padding)
   float* part;     // attention split partials (see attend.hip)
   uint32_t* cnt;   // reserved per-request counters [n]
   int32_t* ml_tok;   // miss lists [n][k]
@@ -37,6 +37,7 @@ struct Geometry {
   int64_t entry_bytes;
   int64_t host_stride;
   int64_t slot_stride;
+  int64_t req_stride;   // bytes per request in the slot buffer: B slot rows, then one row of zeros
   uint32_t flags;
 };
 

@@ -61,6 +61,7 @@ struct ResolveArgs {
   int64_t cap;
   int64_t host_stride;
   int64_t slot_stride;
+  int64_t req_stride;  // bytes per request in buf
   int32_t k;
   int32_t B;
   int32_t chunks;  // 16-byte chunks per row
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
   const int C = a.chunks;
   const int total = m * C;
   const uint8_t* host = a.host + (int64_t)r * cap * a.host_stride;
-  uint8_t* buf = a.buf + (int64_t)r * B * a.slot_stride;
+  uint8_t* buf = a.buf + (int64_t)r * a.req_stride;
   constexpr int U = 4;
   for (int base = tid; base < total; base += NT * U) {
     v4i v[U];
@@ -309,14 +310,15 @@ constexpr int FT = 256;
 __global__ __launch_bounds__(FT) void fetch_kernel(const int32_t* __restrict__ ml_tok, const int32_t* __restrict__ ml_slot,
                                                    const int32_t* __restrict__ ml_cnt, const uint8_t* __restrict__ host,
                                                    uint8_t* __restrict__ buf, int64_t cap, int64_t host_stride,
-                                                   int64_t slot_stride, int32_t k, int32_t B, int32_t chunks) {
+                                                   int64_t slot_stride, int64_t req_stride, int32_t k, int32_t B,
+                                                   int32_t chunks) {
   const int r = blockIdx.y;
   const int m = min(ml_cnt[r], k);
   const int total = m * chunks;
   const int32_t* tok = ml_tok + (int64_t)r * k;
   const int32_t* slot = ml_slot + (int64_t)r * k;
   const uint8_t* hrow = host + (int64_t)r * cap * host_stride;
-  uint8_t* drow = buf + (int64_t)r * B * slot_stride;
+  uint8_t* drow = buf + (int64_t)r * req_stride;
   constexpr int U = 4;
   const int step = gridDim.x * FT;
   for (int base = blockIdx.x * FT + threadIdx.x; base < total; base += step * U) {
@@ -426,6 +428,7 @@ hipError_t launch_resolve(const Geometry& g, const LayerTables& t, const uint8_t
   a.cap = g.cap;
   a.host_stride = g.host_stride;
   a.slot_stride = g.slot_stride;
+  a.req_stride = g.req_stride;
   a.k = g.k;
   a.B = g.B;
   a.chunks = (int32_t)(g.entry_bytes / 16);
@@ -450,7 +453,7 @@ hipError_t launch_fetch(const Geometry& g, const LayerTables& t, const uint8_t* 
   // enough fetch workgroups for ~512 in total, whatever the batch
   const int per_req = (512 + n_req - 1) / n_req < 16 ? (512 + n_req - 1) / n_req : 16;
   hipLaunchKernelGGL(fetch_kernel, dim3(per_req, n_req), dim3(FT), 0, s, t.ml_tok, t.ml_slot, t.ml_cnt, host_layer,
-                     t.buf, g.cap, g.host_stride, g.slot_stride, g.k, g.B, (int32_t)(g.entry_bytes / 16));
+                     t.buf, g.cap, g.host_stride, g.slot_stride, g.req_stride, g.k, g.B, (int32_t)(g.entry_bytes / 16));
   return hipGetLastError();
 }
 

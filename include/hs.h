@@ -88,10 +88,13 @@ typedef struct hs_state_view {
   int32_t* slot_stamp;   /* [max_requests][B] step of last selection, -1 = never       */
   int32_t* lru_order;    /* [max_requests][B] slots sorted by (stamp, slot) ascending  */
   int32_t* step;         /* [max_requests] resolves done so far (the next stamp)        */
-  uint8_t* kv_buffer;    /* [max_requests][B][slot_stride] KV rows of the slots         */
+  uint8_t* kv_buffer;    /* per request (request_stride bytes apart): B slot rows of    */
+                         /* slot_stride bytes, then one row of zeros the attention     */
+                         /* kernel reads for padded selection entries (never written)  */
   int64_t capacity;      /* host tokens per (request, layer)                            */
   int64_t slot_stride;   /* bytes between slots in kv_buffer (>= entry_bytes)           */
   int64_t entry_bytes;   /* bytes of one KV entry                                       */
+  int64_t request_stride; /* bytes between requests in kv_buffer ((B + 1) * slot_stride) */
 } hs_state_view;
 
 /* Bytes the device block must have for this configuration (0 and an error if invalid). */

@@ -68,7 +68,7 @@ def test_sizes_for_the_batch64_workload():
     dev = hsa.device_bytes(cfg)
     host = hsa.host_bytes(cfg)
     assert host == 64 * 32768 * 1152
-    slots = 64 * 4096 * 1152
+    slots = 64 * (4096 + 1) * 1152  # each request's slot rows and its zero row
     tables = 64 * 32768 * 4 + 3 * 64 * 4096 * 4 + 2 * 64 * 2048 * 4  # page table, owners/stamps/order, miss lists
     assert slots + tables <= dev <= slots + tables + 64 * 1024
 

@@ -114,6 +114,47 @@ def test_ragged_shapes_and_padding(layout, heads, k, B, n):
         p.close()
 
 
+@pytest.mark.parametrize("layout,k,n", [(hsa.LAYOUT_FP8, 200, 3), (hsa.LAYOUT_BF16, 70, 2)])
+def test_padding_ignores_nan_rows(layout, k, n):
+    """Padded (-1) and out-of-range slot entries contribute nothing even when every slot that
+    is not selected -- slot 0 included -- holds NaN bytes; the zero row after each request's
+    slots is what padded entries read, and resolves never write it."""
+    B = 256
+    say(f"attend padding over NaN rows: layout {layout}, k {k}, B {B}, n {n}")
+    rng = np.random.default_rng(7)
+    hs = hsa.HiSparse(k, B, 2, n, 1, layout, num_heads=16)
+    try:
+        E = skv.ENTRY_BYTES[layout]
+        rows = np.full((n, B, E), 0xFF, dtype=np.uint8)           # NaN in fp8 and bf16 alike
+        slots = np.stack([rng.choice(np.arange(1, B), k, replace=False) for _ in range(n)]).astype(np.int32)
+        for r in range(n):
+            good = skv.rows_at(5, r, 0, np.arange(k), layout)
+            rows[r, slots[r]] = good
+        pad = rng.random(slots.shape) < 0.3
+        slots[pad] = -1
+        slots[0, :3] = [B, B + 7, -5]                             # out of range: treated as padding
+        st = hs.state(0)
+        st["kv_buffer"].copy_(torch.from_numpy(rows).cuda())
+        assert not bool(st["zero_row"].any())
+        qb = skv.queries(5, 0, n, 0, 16)
+        q = torch.from_numpy(qb.view(np.int16)).cuda().view(torch.bfloat16)
+        out, lse = hs.attend(0, q, torch.from_numpy(slots).cuda(), SCALE)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+        idx = np.where((slots >= 0) & (slots < B), slots, -1)
+        out_o, lse_o = oracle.attend_rows(qb, idx, rows, layout, SCALE)
+        _compare(out, lse, out_o, lse_o, "padding over NaN rows")
+        # resolves (row copies included) leave the zero rows untouched
+        sel = torch.from_numpy(np.stack([rng.choice(4 * B // 2, k, replace=False) for _ in range(n)])
+                               .astype(np.int32)).cuda()
+        hs.resolve(0, sel)
+        hs.resolve(0, sel, split=True)
+        torch.cuda.synchronize()
+        assert not bool(hs.state(0)["zero_row"].any())
+    finally:
+        hs.close()
+
+
 def _decode_torch(rows: np.ndarray) -> np.ndarray:
     t = torch.from_numpy(np.ascontiguousarray(rows))
     lat = t[:, :512].contiguous().view(torch.float8_e4m3fn).to(torch.float64)
