@@ -79,11 +79,14 @@ def summarize_profile(args):
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     tr = sorted((r for r in rows(os.path.join(args.trace_dir, "run_kernel_trace.csv")) if kern in r["Kernel_Name"]),
                 key=lambda r: int(r["Dispatch_Id"]))
+    if args.skip:
+        tr = tr[args.skip:args.skip + args.last] if args.last else tr[args.skip:]
     last = tr[-args.last:] if args.last else tr
     dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in last]
     print("| kernel | calls | avg us | min us | max us |\n|---|---|---|---|---|")
     print("\n".join(lines))
-    print(f"\nLast {len(last)} dispatches of the kernel (the timed steps): average {np.mean(dur):.2f} us, "
+    what = f"dispatches {args.skip}..{args.skip + len(last) - 1}" if args.skip else f"last {len(last)} dispatches"
+    print(f"\nTimed steps ({what} of the kernel): average {np.mean(dur):.2f} us, "
           f"median {np.median(dur):.2f} us.")
     out = {"avg_us_timed": float(np.mean(dur))}
     if args.pmc_dir and args.copy_dir:
@@ -95,10 +98,12 @@ def summarize_profile(args):
             scale[c] = (256 * 1024) / kib
             kr = sorted((r for r in rows(os.path.join(f"{args.pmc_dir}_{c}", "run_counter_collection.csv"))
                          if kern in r["Kernel_Name"]), key=lambda r: int(r["Dispatch_Id"]))
+            if args.pmc_skip:
+                kr = kr[args.pmc_skip:args.pmc_skip + args.pmc_last] if args.pmc_last else kr[args.pmc_skip:]
             kr = kr[-args.pmc_last:] if args.pmc_last else kr
             v = float(np.mean([float(r["Counter_Value"]) for r in kr]))
             out[c] = v
-            print(f"\n{c}: {v:.1f} KiB per dispatch over the last {len(kr)} dispatches; a plain copy of 256 MiB "
+            print(f"\n{c}: {v:.1f} KiB per dispatch over {len(kr)} timed dispatches; a plain copy of 256 MiB "
                   f"reads as {kib:.1f} KiB, so scale x{scale[c]:.3f} -> {v * scale[c] * 1024 / 1e6:.2f} MB per launch")
         out["bytes_per_launch"] = (out["FETCH_SIZE"] * scale["FETCH_SIZE"] + out["WRITE_SIZE"] * scale["WRITE_SIZE"]) * 1024
         out["fetch_scale"], out["write_scale"] = scale["FETCH_SIZE"], scale["WRITE_SIZE"]
@@ -157,6 +162,33 @@ def cpu_baseline_resolve(w, trace, warm, budget_s=15.0):
             "sample": f"oracle resolve (LRU tables + row copies) of all {n} requests on steps {warm}.."
                       f"{trace.shape[0] - 1} of the same trace, {passes} passes from an empty cache "
                       f"({done} steps timed, {el:.1f} s)"}
+
+
+def cpu_baseline_attend(w, step, budget_s=15.0):
+    """The oracle's fp64 attention, as it stands, over the selection of one timed step.
+
+    Requests are attended in batches of 16 until about budget_s seconds of oracle time
+    have passed; the rows are generated outside the timed calls."""
+    import oracle
+    from synth import kv as skv
+    from synth import trace as tr
+    trace = tr.generate(w.trace_spec(), steps=step + 1)
+    threads = oracle.default_threads()
+    q = skv.queries(w.seed, step, w.n, 0, 16)
+    done, el, r0 = 0, 0.0, 0
+    while done == 0 or el < budget_s:
+        rs = [(r0 + i) % w.n for i in range(16)]
+        r0 += 16
+        sel = trace[step, rs]
+        rows = np.stack([skv.rows_at(w.seed, r, 0, sel[i], w.layout) for i, r in enumerate(rs)])
+        idx = np.tile(np.arange(w.k, dtype=np.int32), (len(rs), 1))
+        t0 = time.perf_counter()
+        oracle.attend_rows(q[rs], idx, rows, w.layout, 1.0 / math.sqrt(576), threads=threads)
+        el += time.perf_counter() - t0
+        done += len(rs)
+    return {"value": done * w.k / el, "unit": "attended tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle fp64 attention of {done} request selections (k {w.k}, 16 heads) of step {step}, "
+                      f"in batches of 16 ({el:.1f} s)"}
 
 
 def bench_resolve(args, torch, hsa, w):
@@ -326,6 +358,23 @@ def bench_attend(args, torch, hsa, w):
             b.synchronize()
             att_ms.append(a.elapsed_time(b))
     del flush
+    # resolution alone: a handle that moves no rows, the same selections, one graph of K launches
+    hs_noio = hsa.HiSparse(w.k, w.B, w.ratio, w.n, 1, w.layout, 0, hsa.FLAG_NO_IO)
+    slots_n = torch.empty(w.n, w.k, dtype=torch.int32, device="cuda")
+    miss_n = torch.zeros(T, w.n, dtype=torch.int32, device="cuda")
+    with torch.cuda.stream(stream):
+        for t in range(args.warmup):
+            hs_noio.resolve(0, d_trace[t], slots_n, miss_n[t], stream=stream)
+    stream.synchronize()
+    gn = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(gn, stream=stream):
+            for i in range(args.steps):
+                hs_noio.resolve(0, d_trace[args.warmup + i], slots_n, miss_n[args.warmup + i], stream=stream)
+    noio_us = timed(gn) / args.steps * 1e3
+    assert torch.equal(miss_n[args.warmup:], miss[args.warmup:])
+    del gn
+    hs_noio.close()
     res_ms = [region_ms / args.steps - float(np.mean(att_ms))]
     K = args.steps
     att_s = float(np.mean(att_ms)) / 1e3
@@ -343,7 +392,15 @@ def bench_attend(args, torch, hsa, w):
         "config": {"workload": w.description + f" (churn {w.churn})", "global_batch": w.n, "seq_len": w.ctx,
                    "top_k": w.k, "heads": 16, "graph": True},
         "resolve_us_per_step": float(np.mean(res_ms)) * 1e3,
+        "resolve_noio_us_per_step": noio_us,
         "misses_per_selection": float(m.mean()),
+        # resolution (table work, no row copies) + attention against HBM, over the sum of their
+        # times: per selection 16k + 4B + 16m bytes of tables plus the attention bytes
+        "hbm_resolve_plus_attend": {
+            "bytes": w.n * (16 * w.k + 4 * w.B + 16 * float(m.mean())) + att_bytes,
+            "us": noio_us + att_s * 1e6,
+            "frac": (w.n * (16 * w.k + 4 * w.B + 16 * float(m.mean())) + att_bytes)
+                    / ((noio_us * 1e-6 + att_s) * HBM_PEAK_GBPS * 1e9)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic, "kernel": "attend_kernel",
                      "avg_kernel_us": att_s * 1e6, "algorithmic_bytes_per_launch": att_bytes},
@@ -451,6 +508,8 @@ def main():
     ap.add_argument("--pmc-dir", help="prefix of the counter runs' directories (<prefix>_FETCH_SIZE, ...)")
     ap.add_argument("--copy-dir", help="prefix of the copy-calibration counter runs' directories")
     ap.add_argument("--pmc-last", type=int, default=0)
+    ap.add_argument("--skip", type=int, default=0, help="with --last: take --last dispatches after the first --skip")
+    ap.add_argument("--pmc-skip", type=int, default=0, help="the same for the counter runs")
     ap.add_argument("--record", help="store the traffic under this key in profiles/traffic.json")
     ap.add_argument("--source", default="resolve.hip", help="kernel source file the record is keyed to")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -491,6 +550,8 @@ def main():
         line = bench_prefetch(args, torch, hsa, C.PREFETCH)
     else:
         line = bench_attend(args, torch, hsa, C.FP8_256)
+        line["cpu_baseline"] = None if args.no_cpu_baseline else \
+            cpu_baseline_attend(C.FP8_256, args.warmup, args.cpu_budget)
     print(json.dumps(line), flush=True)
 
 
