@@ -55,6 +55,8 @@ def lib():
     L.orc_resolve.argtypes = [i64, i64, i64, p, p, p, i64, p, p, p, p, p, i64]
     L.orc_resolve_batch.restype = ctypes.c_int
     L.orc_resolve_batch.argtypes = [i64, i64, i64, i64, p, p, p, p, p, p, p, p, p, i64, ctypes.c_int]
+    L.orc_append.restype = ctypes.c_int
+    L.orc_append.argtypes = [i64, i64, p, p, p, i64, ctypes.c_int32, p, p, p, i64, p]
     L.orc_e4m3_decode.restype = ctypes.c_double
     L.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
     L.orc_attend.restype = ctypes.c_int
@@ -129,6 +131,37 @@ class OracleCache:
             self.dev[:nr, layer] = dev
         self.t[:nr, layer] += 1
         return slots, miss
+
+    def append(self, layer: int, pos: np.ndarray, rows: np.ndarray) -> np.ndarray:
+        """Write-through append of one new token per request: pos[n_req] (-1 = none), rows[n_req][E].
+
+        Each row goes to the host history (``host``, when kept) and the token becomes
+        resident (``orc_append``); returns the slot of each appended token (-1 for none).
+        The step counters do not move: the stamp given is the next resolve's step."""
+        pos = np.ascontiguousarray(pos, dtype=np.int32)
+        rows = np.ascontiguousarray(rows, dtype=np.uint8)
+        assert rows.shape == (pos.shape[0], self.E)
+        out = np.full(pos.shape[0], -1, dtype=np.int32)
+        for r in range(pos.shape[0]):
+            if pos[r] == -1:
+                continue
+            PT = np.ascontiguousarray(self.PT[r, layer])
+            RM = np.ascontiguousarray(self.RM[r, layer])
+            ST = np.ascontiguousarray(self.ST[r, layer])
+            dev = None if self.dev is None else np.ascontiguousarray(self.dev[r, layer])
+            host = None if self.host is None else np.ascontiguousarray(self.host[r, layer])
+            slot = ctypes.c_int32(-1)
+            rc = lib().orc_append(self.B, self.cap, _ptr(PT), _ptr(RM), _ptr(ST), int(self.t[r, layer]), int(pos[r]),
+                                  _ptr(rows[r]), _ptr(dev), _ptr(host), self.E, ctypes.byref(slot))
+            if rc != OK:
+                raise OracleError(f"invalid append (code {rc})")
+            self.PT[r, layer], self.RM[r, layer], self.ST[r, layer] = PT, RM, ST
+            if dev is not None:
+                self.dev[r, layer] = dev
+            if host is not None:
+                self.host[r, layer] = host
+            out[r] = slot.value
+        return out
 
     def attend(self, layer: int, q: np.ndarray, slots: np.ndarray, scale: float):
         """q[n_req][H][576] bf16 bits (uint16) -> (out[n_req][H][512] f64, lse[n_req][H] f64)."""

@@ -169,6 +169,39 @@ int orc_resolve_batch(int64_t n, int64_t B, int64_t cap, int64_t k, int32_t* PT,
   return ORC_OK;
 }
 
+/* ------------------------------------------------------------------- append */
+
+/*
+ * Write-through append of one newly generated token p (the note's introduction:
+ * inactive KV is actively offloaded to host memory; paper abstract: each request's
+ * full history lives in host memory).  Its row R (E bytes) is written to HOST[p]
+ * and the token is made resident before the next resolve:
+ *   - a resident token keeps its slot;
+ *   - otherwise it takes the first slot in (stamp, slot) order over all slots --
+ *     empty slots first -- evicting that slot's token from the page table;
+ * the slot's stamp becomes t, the step number the next resolve will use, and
+ * with DEV non-NULL the slot's bytes become R.  *slot_out gets the slot.
+ * Returns ORC_OK, or ORC_BAD_TOKEN (state untouched) when p is not in [0, cap).
+ */
+int orc_append(int64_t B, int64_t cap, int32_t* PT, int32_t* RM, int64_t* ST, int64_t t, int32_t p,
+               const uint8_t* R, uint8_t* DEV, uint8_t* HOST, int64_t E, int32_t* slot_out) {
+  if (p < 0 || p >= cap) return ORC_BAD_TOKEN;
+  int32_t j = PT[p];
+  if (j < 0) {
+    j = 0;
+    for (int64_t i = 1; i < B; ++i)
+      if (ST[i] < ST[j]) j = (int32_t)i;   /* strict: the lowest slot wins ties */
+    if (RM[j] >= 0) PT[RM[j]] = -1;
+    PT[p] = j;
+    RM[j] = p;
+  }
+  ST[j] = t;
+  if (DEV) memcpy(DEV + (size_t)j * (size_t)E, R, (size_t)E);
+  if (HOST) memcpy(HOST + (size_t)p * (size_t)E, R, (size_t)E);
+  *slot_out = j;
+  return ORC_OK;
+}
+
 /* ---------------------------------------------------------------- attention */
 
 /* OCP FP8 E4M3FN: bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN. */

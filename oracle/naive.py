@@ -58,6 +58,27 @@ class NaiveState:
         slots = [(-1 if s == -1 else self.pt[s]) for s in S]
         return slots, len(misses)
 
+    def append(self, s, row=None):
+        """Write-through append of a new token s (the note's introduction: KV is offloaded to
+        host memory actively): it becomes resident before the next step -- in its own slot if
+        it already has one, else in the slot used longest ago over all slots, (stamp, slot)
+        smallest -- and that slot is stamped with the next step's number."""
+        if not (0 <= s < self.cap):
+            raise ValueError("token out of range")
+        if s in self.pt:
+            j = self.pt[s]
+        else:
+            j = min(range(self.B), key=lambda i: (self.stamp[i], i))
+            old = self.owner[j]
+            if old is not None:
+                del self.pt[old]
+            self.pt[s] = j
+            self.owner[j] = s
+        self.stamp[j] = self.t
+        if row is not None:
+            self.rows[j] = row
+        return j
+
     def arrays(self):
         """(PT[cap], RM[B], ST[B]) as plain lists with -1 for absent."""
         PT = [-1] * self.cap
