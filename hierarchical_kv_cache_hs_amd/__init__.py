@@ -33,6 +33,7 @@ DEVERR_DUPLICATE = 0x2
 HS_OK, HS_ERR_INVALID_ARG, HS_ERR_OUT_OF_MEMORY, HS_ERR_UNSUPPORTED, HS_ERR_HIP, HS_ERR_DEVICE = range(6)
 
 SYMBOLS = ("hs_create", "hs_resolve", "hs_resolve_tables", "hs_fetch_misses", "hs_attend", "hs_destroy",
+           "hs_append", "hs_offload",
            "hs_device_bytes", "hs_host_bytes", "hs_host_kv",
            "hs_device_state", "hs_reset_requests", "hs_get_device_error", "hs_status_string",
            "hs_last_error_message")
@@ -75,6 +76,8 @@ def lib():
         L.hs_resolve.argtypes = [p, i32, i32, p, p, p, p]
         L.hs_resolve_tables.argtypes = [p, i32, i32, p, p, p, p]
         L.hs_fetch_misses.argtypes = [p, i32, i32, p]
+        L.hs_append.argtypes = [p, i32, i32, p, p, ctypes.c_int64, p, p]
+        L.hs_offload.argtypes = [p, i32, i32, ctypes.c_int64, ctypes.c_int64, p, ctypes.c_int64, p]
         L.hs_attend.argtypes = [p, i32, i32, p, p, ctypes.c_float, p, p, p]
         L.hs_destroy.argtypes = [p]
         L.hs_host_kv.argtypes = [p, i32, i32, ctypes.POINTER(p), ctypes.POINTER(ctypes.c_int64),
@@ -213,6 +216,24 @@ class HiSparse:
 
     def fetch_misses(self, layer: int, n_req: int, stream=None):
         _check(lib().hs_fetch_misses(self._h, layer, n_req, _stream_ptr(stream)))
+
+    def append(self, layer: int, pos: torch.Tensor, rows: torch.Tensor, slot_out: torch.Tensor | None = None,
+               stream=None):
+        """hs_append: pos int32 [n_req] (-1 = none), rows uint8 [n_req][>= entry bytes] on the device."""
+        n_req = pos.shape[0]
+        assert pos.dtype == torch.int32 and pos.is_contiguous()
+        assert rows.dtype == torch.uint8 and rows.dim() == 2 and rows.shape[0] == n_req and rows.stride(1) == 1
+        if slot_out is None:
+            slot_out = torch.empty(n_req, dtype=torch.int32, device=pos.device)
+        _check(lib().hs_append(self._h, layer, n_req, pos.data_ptr(), rows.data_ptr(), rows.stride(0),
+                               slot_out.data_ptr(), _stream_ptr(stream)))
+        return slot_out
+
+    def offload(self, layer: int, request: int, first: int, rows: torch.Tensor, stream=None):
+        """hs_offload: rows uint8 [count][>= entry bytes] on the device -> history positions first.."""
+        assert rows.dtype == torch.uint8 and rows.dim() == 2 and rows.stride(1) == 1
+        _check(lib().hs_offload(self._h, layer, request, first, rows.shape[0], rows.data_ptr(), rows.stride(0),
+                                _stream_ptr(stream)))
 
     def attend(self, layer: int, q: torch.Tensor, slots: torch.Tensor, scale: float,
                out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream=None):

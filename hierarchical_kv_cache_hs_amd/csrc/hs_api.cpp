@@ -8,7 +8,7 @@
 //   st    [L][n][B]            slot stamp
 //   ord   [L][n][B]            slots in (stamp, slot) order
 //   step  [L][n]               resolves done
-//   cnt   [L][n]               attention split arrival counters
+//   fresh [L][n][B/32]         slots appended since the last resolve (stamped with its step)
 //   part  [L][n][...]          attention split partials (if num_heads > 0)
 //   ml_*  [L][n][k], [L][n]    per-request miss lists (token, slot) and counts for the fetch kernel
 //   buf   [L][n][B + 1][E]     KV rows of the slots, packed; row B stays zero (attention reads it
@@ -37,7 +37,7 @@ struct hs_handle {
   int32_t* st = nullptr;
   int32_t* ord = nullptr;
   int32_t* step = nullptr;
-  uint32_t* cnt = nullptr;
+  uint32_t* fresh = nullptr;
   float* part = nullptr;
   int32_t* ml_tok = nullptr;
   int32_t* ml_slot = nullptr;
@@ -78,7 +78,7 @@ bool add_ok(size_t a, size_t b, size_t* out) {
 }
 
 struct Layout {
-  size_t err, pt, rm, st, ord, step, cnt, part, ml_tok, ml_slot, ml_cnt, buf, total;
+  size_t err, pt, rm, st, ord, step, fresh, part, ml_tok, ml_slot, ml_cnt, buf, total;
   size_t host_total;
   size_t part_floats;
 };
@@ -127,7 +127,8 @@ hs_status plan(const hs_config* cfg, hs::Geometry* g, Layout* lay) {
   ok = ok && mul_ok(LN, (size_t)cap, &t) && mul_ok(t, 4, &sz) && take(sz, &lay->pt);
   ok = ok && mul_ok(LN, (size_t)g->B, &t) && mul_ok(t, 4, &sz) && take(sz, &lay->rm);
   ok = ok && take(sz, &lay->st) && take(sz, &lay->ord);
-  ok = ok && take(LN * 4, &lay->step) && take(LN * 4, &lay->cnt);
+  ok = ok && take(LN * 4, &lay->step);
+  ok = ok && mul_ok(LN, (size_t)((g->B + 31) / 32) * 4, &sz) && take(sz, &lay->fresh);
   lay->part_floats = g->heads > 0 ? hs::attend_partial_floats(*g) : 0;
   ok = ok && mul_ok(LN, lay->part_floats, &t) && mul_ok(t, 4, &sz) && take(sz, &lay->part);
   ok = ok && mul_ok(LN, (size_t)g->k, &t) && mul_ok(t, 4, &sz) && take(sz, &lay->ml_tok) && take(sz, &lay->ml_slot);
@@ -148,7 +149,7 @@ hs::LayerTables layer_tables(const hs_handle* h, int32_t layer) {
   t.st = h->st + base * (size_t)g.B;
   t.ord = h->ord + base * (size_t)g.B;
   t.step = h->step + base;
-  t.cnt = h->cnt + base;
+  t.fresh = h->fresh + base * (size_t)((g.B + 31) / 32);
   t.part = h->part ? h->part + base * h->part_floats : nullptr;
   t.ml_tok = h->ml_tok + base * (size_t)g.k;
   t.ml_slot = h->ml_slot + base * (size_t)g.k;
@@ -243,7 +244,7 @@ hs_status hs_create(const hs_config* cfg, hs_handle** out) {
   h->st = (int32_t*)(b + lay.st);
   h->ord = (int32_t*)(b + lay.ord);
   h->step = (int32_t*)(b + lay.step);
-  h->cnt = (uint32_t*)(b + lay.cnt);
+  h->fresh = (uint32_t*)(b + lay.fresh);
   h->part = lay.part_floats ? (float*)(b + lay.part) : nullptr;
   h->ml_tok = (int32_t*)(b + lay.ml_tok);
   h->ml_slot = (int32_t*)(b + lay.ml_slot);
@@ -252,12 +253,13 @@ hs_status hs_create(const hs_config* cfg, hs_handle** out) {
 
   hs::prepare_resolve();
   hs::prepare_attend();
+  hs::prepare_append();
   e = hipMemset(h->err, 0, sizeof(int32_t));
   if (e == hipSuccess)  // the zero row after each request's slots
     e = hipMemset2D(h->buf + (size_t)g.B * (size_t)g.slot_stride, (size_t)g.req_stride, 0, (size_t)g.slot_stride,
                     (size_t)g.L * (size_t)g.n);
   if (e != hipSuccess) { release(h); return fail_hip(e, "hipMemset"); }
-  e = hs::launch_reset(g, h->pt, h->rm, h->st, h->ord, h->step, h->cnt, 0, g.n, nullptr);
+  e = hs::launch_reset(g, h->pt, h->rm, h->st, h->ord, h->step, h->fresh, 0, g.n, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) { release(h); return fail_hip(e, "initialising tables"); }
   *out = h;
@@ -355,11 +357,46 @@ hs_status hs_device_state(hs_handle* h, int32_t layer, hs_state_view* v) {
   return HS_OK;
 }
 
+hs_status hs_append(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* d_pos, const void* d_rows,
+                    int64_t row_stride, int32_t* d_slot_out, void* stream) {
+  if (!h) return fail(HS_ERR_INVALID_ARG, "handle is NULL");
+  if (layer < 0 || layer >= h->g.L) return fail(HS_ERR_INVALID_ARG, "layer out of range");
+  if (n_req < 0 || n_req > h->g.n) return fail(HS_ERR_INVALID_ARG, "n_req out of range");
+  if (n_req == 0) return HS_OK;
+  if (!d_pos || !d_rows) return fail(HS_ERR_INVALID_ARG, "position or row pointer is NULL");
+  if (row_stride < h->g.entry_bytes || row_stride % 16 || ((uintptr_t)d_rows) % 16)
+    return fail(HS_ERR_INVALID_ARG, "rows must be 16-byte aligned, row_stride >= entry bytes and a multiple of 16");
+  hs::LayerTables t = layer_tables(h, layer);
+  uint8_t* host_layer = h->host_pool_dev + (size_t)layer * h->g.n * (size_t)h->g.cap * h->g.host_stride;
+  hipError_t e = hs::launch_append(h->g, t, host_layer, n_req, d_pos, d_rows, row_stride, d_slot_out, h->err,
+                                   (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "append launch");
+  return HS_OK;
+}
+
+hs_status hs_offload(hs_handle* h, int32_t layer, int32_t request, int64_t first, int64_t count,
+                     const void* d_rows, int64_t row_stride, void* stream) {
+  if (!h) return fail(HS_ERR_INVALID_ARG, "handle is NULL");
+  if (layer < 0 || layer >= h->g.L) return fail(HS_ERR_INVALID_ARG, "layer out of range");
+  if (request < 0 || request >= h->g.n) return fail(HS_ERR_INVALID_ARG, "request out of range");
+  if (first < 0 || count < 0 || first > h->g.cap - count) return fail(HS_ERR_INVALID_ARG, "positions out of range");
+  if (count == 0) return HS_OK;
+  if (!d_rows) return fail(HS_ERR_INVALID_ARG, "row pointer is NULL");
+  if (row_stride < h->g.entry_bytes) return fail(HS_ERR_INVALID_ARG, "row_stride below the entry size");
+  const size_t E = (size_t)h->g.entry_bytes;
+  uint8_t* dst = h->host_pool + (((size_t)layer * h->g.n + (size_t)request) * (size_t)h->g.cap + (size_t)first) * E;
+  hipError_t e = hipMemcpy2DAsync(dst, E, d_rows, (size_t)row_stride, E, (size_t)count, hipMemcpyDeviceToHost,
+                                  (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "offload copy");
+  return HS_OK;
+}
+
 hs_status hs_reset_requests(hs_handle* h, int32_t first, int32_t count, void* stream) {
   if (!h) return fail(HS_ERR_INVALID_ARG, "handle is NULL");
   if (first < 0 || count < 0 || (int64_t)first + count > h->g.n) return fail(HS_ERR_INVALID_ARG, "request range");
   if (count == 0) return HS_OK;
-  hipError_t e = hs::launch_reset(h->g, h->pt, h->rm, h->st, h->ord, h->step, h->cnt, first, count, (hipStream_t)stream);
+  hipError_t e =
+      hs::launch_reset(h->g, h->pt, h->rm, h->st, h->ord, h->step, h->fresh, first, count, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "reset launch");
   return HS_OK;
 }

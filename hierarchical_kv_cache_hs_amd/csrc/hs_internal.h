@@ -25,7 +25,7 @@ struct LayerTables {
   int32_t* step;   // [n]
   uint8_t* buf;    // [n][req_stride]: B rows of slot_stride bytes, then a zero row (attention padding)
   float* part;     // attention split partials (see attend.hip)
-  uint32_t* cnt;   // reserved per-request counters [n]
+  uint32_t* fresh; // [n][B/32] bits of slots appended since the last resolve (their stamp is its step)
   int32_t* ml_tok;   // miss lists [n][k]
   int32_t* ml_slot;  // [n][k]
   int32_t* ml_cnt;   // [n]
@@ -56,7 +56,16 @@ hipError_t launch_fetch(const Geometry& g, const LayerTables& t, const uint8_t* 
                         hipStream_t s);
 
 hipError_t launch_reset(const Geometry& g, int32_t* pt, int32_t* rm, int32_t* st, int32_t* ord, int32_t* step,
-                        uint32_t* cnt, int32_t first, int32_t count, hipStream_t s);
+                        uint32_t* fresh, int32_t first, int32_t count, hipStream_t s);
+
+// Once per process, before the first append launch.
+void prepare_append();
+
+// Write-through append: for each request with pos[r] >= 0, the row at rows + r * row_stride
+// becomes resident and is written to the host history (host_layer: device-mapped address).
+hipError_t launch_append(const Geometry& g, const LayerTables& t, uint8_t* host_layer, int32_t n_req,
+                         const int32_t* pos, const void* rows, int64_t row_stride, int32_t* slot_out, int32_t* err,
+                         hipStream_t s);
 
 // Once per process, before the first attention launch.
 void prepare_attend();

@@ -18,7 +18,8 @@
 //   P3  the first m non-hit slots in LRU order are the victims; the remaining non-hit
 //       slots keep their order and move to position rank - m of the new order;
 //   P4  hit and victim slots, all stamped with this step, form the back of the new
-//       order in ascending slot index (a scan over the slot bitmap); the i-th miss takes
+//       order in ascending slot index (a scan over the slot bitmap), together with any slot
+//       appended since the last resolve (hs_append stamps it with this step); the i-th miss takes
 //       victim i: evict its owner from the page table, install the token, stamp, and
 //       write the output slot;
 //   P5  the missing rows are copied from pinned host memory (zero-copy 16-byte loads over
@@ -52,6 +53,7 @@ struct ResolveArgs {
   int32_t* st;
   int32_t* ord;
   int32_t* step;
+  uint32_t* fresh;  // [n][HB] slots appended since the last resolve
   const uint8_t* host;
   uint8_t* buf;
   int32_t* err;
@@ -114,7 +116,8 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
   uint32_t* victims = missmap + W;              // [k]   victim slot of the i-th miss
   uint32_t* misstok = victims + k;              // [k]   token of the i-th miss (-1: none)
   uint32_t* wsum = misstok + k;                 // [NW]  scan scratch
-  uint16_t* prefix = (uint16_t*)(wsum + NW);    // [W]   misses below each bitmap word
+  uint32_t* freshmap = wsum + NW;               // [HB]  slots appended since the last resolve
+  uint16_t* prefix = (uint16_t*)(freshmap + HB);  // [W] misses below each bitmap word
 
   int32_t* pt = a.pt + (int64_t)r * cap;
   int32_t* rm = a.rm + (int64_t)r * B;
@@ -125,7 +128,13 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
   const int32_t t = a.step[r];
 
   // ---- P0
-  for (int w = tid; w < HB; w += NT) hitmap[w] = 0u;
+  uint32_t* fresh = a.fresh + (int64_t)r * HB;
+  for (int w = tid; w < HB; w += NT) {
+    hitmap[w] = 0u;
+    const uint32_t f = fresh[w];
+    freshmap[w] = f;
+    if (f) fresh[w] = 0u;  // consumed by this resolve
+  }
   for (int w = tid; w < W; w += NT) missmap[w] = 0u;
   int32_t ordv[OPT];
   const int o0 = tid * OPT;
@@ -210,6 +219,11 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
         if (rank < m) {
           victims[rank] = (uint32_t)j;
           atomicOr(&hitmap[j >> 5], 1u << (j & 31));
+        } else if ((freshmap[j >> 5] >> (j & 31)) & 1u) {
+          // appended since the last resolve: its stamp is already this step's, so it joins
+          // the back of the order with the hit and victim slots (appended slots come last in
+          // LRU order, so the slots before them keep their positions rank - m)
+          atomicOr(&hitmap[j >> 5], 1u << (j & 31));
         } else {
           ord[rank - m] = j;
         }
@@ -223,7 +237,8 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
   {
     uint32_t word = (tid < HB) ? hitmap[tid] : 0u;
     uint32_t touched;
-    int pos = (nonhit - m) + (int)block_scan((uint32_t)__popc(word), wsum, &touched);
+    const uint32_t below = block_scan((uint32_t)__popc(word), wsum, &touched);
+    int pos = B - (int)touched + (int)below;
     while (word) {
       const int b = __ffs(word) - 1;
       word &= word - 1u;
@@ -348,7 +363,7 @@ __global__ __launch_bounds__(FT) void fetch_kernel(const int32_t* __restrict__ m
   }
 }
 
-__global__ void reset_kernel(int32_t* pt, int32_t* rm, int32_t* st, int32_t* ord, int32_t* step, uint32_t* cnt,
+__global__ void reset_kernel(int32_t* pt, int32_t* rm, int32_t* st, int32_t* ord, int32_t* step, uint32_t* fresh,
                              int32_t L, int32_t n, int32_t first, int32_t count, int64_t cap, int32_t B) {
   const int64_t pairs = (int64_t)L * count;
   for (int64_t lr = blockIdx.y; lr < pairs; lr += gridDim.y) {
@@ -363,10 +378,9 @@ __global__ void reset_kernel(int32_t* pt, int32_t* rm, int32_t* st, int32_t* ord
       st[id * B + x] = -1;
       ord[id * B + x] = (int32_t)x;
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-      step[id] = 0;
-      if (cnt) cnt[id] = 0u;
-    }
+    const int HB = (B + 31) >> 5;
+    for (int x = blockIdx.x * blockDim.x + threadIdx.x; x < HB; x += gridDim.x * blockDim.x) fresh[id * HB + x] = 0u;
+    if (blockIdx.x == 0 && threadIdx.x == 0) step[id] = 0;
   }
 }
 
@@ -405,7 +419,7 @@ void prepare_resolve() {
 size_t resolve_lds_bytes(int64_t cap, int32_t k, int32_t B) {
   const size_t W = (size_t)((cap + 31) >> 5);
   const size_t HB = (size_t)((B + 31) >> 5);
-  size_t words = HB + W + 2 * (size_t)k + NW;
+  size_t words = 2 * HB + W + 2 * (size_t)k + NW;
   size_t bytes = words * 4 + W * 2;
   return (bytes + 15) & ~(size_t)15;
 }
@@ -422,6 +436,7 @@ hipError_t launch_resolve(const Geometry& g, const LayerTables& t, const uint8_t
   a.st = t.st;
   a.ord = t.ord;
   a.step = t.step;
+  a.fresh = t.fresh;
   a.host = host_layer;
   a.buf = t.buf;
   a.err = err;
@@ -458,10 +473,10 @@ hipError_t launch_fetch(const Geometry& g, const LayerTables& t, const uint8_t* 
 }
 
 hipError_t launch_reset(const Geometry& g, int32_t* pt, int32_t* rm, int32_t* st, int32_t* ord, int32_t* step,
-                        uint32_t* cnt, int32_t first, int32_t count, hipStream_t s) {
+                        uint32_t* fresh, int32_t first, int32_t count, hipStream_t s) {
   const int64_t pairs = (int64_t)g.L * count;
   const unsigned gy = (unsigned)(pairs < 65535 ? pairs : 65535);
-  hipLaunchKernelGGL(reset_kernel, dim3(16, gy), dim3(256), 0, s, pt, rm, st, ord, step, cnt, g.L, g.n, first, count,
+  hipLaunchKernelGGL(reset_kernel, dim3(16, gy), dim3(256), 0, s, pt, rm, st, ord, step, fresh, g.L, g.n, first, count,
                      g.cap, g.B);
   return hipGetLastError();
 }

@@ -146,6 +146,37 @@ hs_status hs_resolve_tables(hs_handle* h, int32_t layer, int32_t n_req, const in
 hs_status hs_fetch_misses(hs_handle* h, int32_t layer, int32_t n_req, void* stream);
 
 /*
+ * Write-through append of newly generated tokens (the note's introduction: KV not in use is
+ * actively offloaded to host memory; paper abstract: each request's full KV history lives in
+ * host memory).  For each request r < n_req with d_pos[r] >= 0:
+ *   - the row at d_rows + r * row_stride (entry_bytes bytes, device memory) is written to
+ *     position d_pos[r] of the request's history in the host pool;
+ *   - the token becomes resident before the next resolve: it keeps its slot if it has one,
+ *     otherwise it takes the first slot in (stamp, slot) order -- empty slots first -- whose
+ *     token leaves the page table; the slot's bytes become the row and its stamp the step
+ *     number the next resolve will use (the step counter does not move).
+ *   d_pos      [n_req] int32 token positions, -1 = no token for this request
+ *   d_rows     device rows, 16-byte aligned; row_stride >= entry bytes, a multiple of 16
+ *   d_slot_out [n_req] int32 out: the slot now holding the token (-1 if none), or NULL
+ * A position outside [0, capacity) is skipped and sets HS_DEVERR_TOKEN_RANGE.  With
+ * HS_FLAG_NO_IO the tables change but no row moves.  Enqueue-only, graph-capturable.
+ * A selection that names the token in the next resolve finds it resident (a hit).
+ */
+hs_status hs_append(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* d_pos, const void* d_rows,
+                    int64_t row_stride, int32_t* d_slot_out, void* stream);
+
+/*
+ * Prefill offload: copies count rows (device memory, row_stride bytes apart) into positions
+ * first .. first + count - 1 of request `request`'s history in the host pool (the note's
+ * introduction: KV is actively offloaded to host memory).  Device tables are untouched: the
+ * tokens arrive on the device as misses when a selection names them.  A stream-ordered copy
+ * (hipMemcpy2DAsync, device to pinned host); HS_ERR_INVALID_ARG for a range outside
+ * [0, capacity) or row_stride < entry bytes.
+ */
+hs_status hs_offload(hs_handle* h, int32_t layer, int32_t request, int64_t first, int64_t count,
+                     const void* d_rows, int64_t row_stride, void* stream);
+
+/*
  * Sparse MLA decode attention over the resolved slots (paper abstract: each
  * step reads only the selected KV entries; only placement changes, so the
  * result equals attention over the selected tokens of the full history).
