@@ -376,6 +376,7 @@ def bench_attend(args, torch, hsa, w):
     del gn
     hs_noio.close()
     res_ms = [region_ms / args.steps - float(np.mean(att_ms))]
+    append = bench_append_leg(args, torch, hsa, w, d_trace, miss, stream, timed)
     K = args.steps
     att_s = float(np.mean(att_ms)) / 1e3
     valid = (slots[args.warmup:] >= 0).sum().item() / K
@@ -394,6 +395,7 @@ def bench_attend(args, torch, hsa, w):
         "resolve_us_per_step": float(np.mean(res_ms)) * 1e3,
         "resolve_noio_us_per_step": noio_us,
         "misses_per_selection": float(m.mean()),
+        "append": append,
         # resolution (table work, no row copies) + attention against HBM, over the sum of their
         # times: per selection 16k + 4B + 16m bytes of tables plus the attention bytes
         "hbm_resolve_plus_attend": {
@@ -407,6 +409,92 @@ def bench_attend(args, torch, hsa, w):
     }
     hs.close()
     return out_line
+
+
+def measure_d2h_peak(torch, nbytes=1 << 30, reps=5):
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src, non_blocking=True)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return nbytes / ms / 1e6
+
+
+def bench_append_leg(args, torch, hsa, w, d_trace, miss_plain, stream, timed):
+    """Write-through append of each step's newest token before its resolve (the growing
+    context's guaranteed miss), and bulk prefill offload into the pinned history."""
+    from synth import kv as skv
+    T = args.warmup + args.steps
+    hs = hsa.HiSparse(w.k, w.B, w.ratio, w.n, 1, w.layout, 0, 0)
+    for r in range(w.n):
+        ptr, cap, stride = hs.host_kv_ptr(0, r)
+        skv.fill_rows(w.seed, r, 0, 0, cap, w.layout, ptr, stride)
+    # the newest position of step t is ctx + t - 1; its row is the synthetic row of that position
+    pos = torch.from_numpy(np.stack([np.full(w.n, w.ctx + t - 1, dtype=np.int32) for t in range(T)])).cuda()
+    rows = torch.from_numpy(np.stack([np.stack([skv.rows_at(w.seed, r, 0, np.array([w.ctx + t - 1]), w.layout)[0]
+                                                for r in range(w.n)]) for t in range(T)])).cuda()
+    slots = torch.empty(w.n, w.k, dtype=torch.int32, device="cuda")
+    miss = torch.zeros(T, w.n, dtype=torch.int32, device="cuda")
+    with torch.cuda.stream(stream):
+        for t in range(args.warmup):
+            hs.append(0, pos[t], rows[t], stream=stream)
+            hs.resolve(0, d_trace[t], slots, miss[t], stream=stream)
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(args.steps):
+                t = args.warmup + i
+                hs.append(0, pos[t], rows[t], stream=stream)
+                hs.resolve(0, d_trace[t], slots, miss[t], stream=stream)
+    step_ms = timed(g) / args.steps
+    ga = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(ga, stream=stream):
+            for i in range(args.steps):
+                hs.append(0, pos[args.warmup + i], rows[args.warmup + i], stream=stream)
+    append_ms = timed(ga) / args.steps
+    m_app = miss[args.warmup:].double().mean().item()
+    m_plain = miss_plain[args.warmup:].double().mean().item()
+    assert hs.device_error() == 0
+    # prefill offload: 8 requests' 32768-token prompts, device rows -> pinned history
+    nreq, count = 8, min(32768, w.cap)
+    src = torch.randint(0, 256, (count, w.entry_bytes), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        a.record(stream)
+        for r in range(nreq):
+            hs.offload(0, r, 0, src, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    off_ms = a.elapsed_time(b)
+    ok = bool((hs.host_kv(0, nreq - 1)[:count] == src.cpu().numpy()).all())
+    padded = torch.randint(0, 256, (count, w.entry_bytes + 112), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        a.record(stream)
+        for r in range(nreq):
+            hs.offload(0, r, 0, padded, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    off_pad_ms = a.elapsed_time(b)
+    ok = ok and bool((hs.host_kv(0, 0)[:count] == padded[:, :w.entry_bytes].cpu().numpy()).all())
+    d2h = measure_d2h_peak(torch)
+    hs.close()
+    return {"misses_per_selection": m_app, "misses_per_selection_without_append": m_plain,
+            "append_plus_resolve_us_per_step": step_ms * 1e3, "append_us_per_step": append_ms * 1e3,
+            "offload_GBps": nreq * count * w.entry_bytes / (off_ms / 1e3) / 1e9,
+            "offload_padded_rows_GBps": nreq * count * w.entry_bytes / (off_pad_ms / 1e3) / 1e9,
+            "d2h_peak_GBps_measured": d2h, "offload_rows_verified": ok,
+            "offload_sample": f"{nreq} requests x {count} rows of {w.entry_bytes} B"}
 
 
 def bench_prefetch(args, torch, hsa, w):

@@ -43,10 +43,35 @@ struct AppendArgs {
 
 __global__ __launch_bounds__(AT) void append_kernel(AppendArgs a) {
   extern __shared__ int32_t ord_lds[];  // [B]
-  __shared__ int32_t s_pj, s_c;
+  __shared__ int32_t s_pj, s_c, s_more;
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
+  const int B = a.B;
+  int32_t* pt = a.pt + (int64_t)r * a.cap;
+  int32_t* rm = a.rm + (int64_t)r * B;
+  int32_t* st = a.st + (int64_t)r * B;
+  int32_t* ord = a.ord + (int64_t)r * B;
+  // Round trip 1: the position, the step, this thread's 16 bytes of the row and the order
+  // array -- none depends on another.  Batches of order loads are all issued before any is
+  // stored (a loop of load-store pairs would wait for each load in turn).
   const int32_t p = a.pos[r];
+  const int32_t t = a.step[r];
+  v4i rowv = {0, 0, 0, 0};
+  if (a.io && tid < a.chunks) rowv = ((const v4i*)(a.rows + (int64_t)r * a.row_stride))[tid];
+  constexpr int BATCH = 16;
+  for (int i0 = 0; i0 < B; i0 += AT * BATCH) {
+    int32_t v[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int i = i0 + u * AT + tid;
+      v[u] = (i < B) ? ord[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int i = i0 + u * AT + tid;
+      if (i < B) ord_lds[i] = v[u];
+    }
+  }
   if (p == -1) {
     if (tid == 0 && a.slot_out) a.slot_out[r] = -1;
     return;
@@ -58,26 +83,42 @@ __global__ __launch_bounds__(AT) void append_kernel(AppendArgs a) {
     }
     return;
   }
-  const int B = a.B;
-  int32_t* pt = a.pt + (int64_t)r * a.cap;
-  int32_t* rm = a.rm + (int64_t)r * B;
-  int32_t* st = a.st + (int64_t)r * B;
-  int32_t* ord = a.ord + (int64_t)r * B;
-  const int32_t t = a.step[r];
-  const int32_t jr = pt[p];
-  const bool resident = jr >= 0;
-  const int32_t j = resident ? jr : ord[0];  // least recently used: first in (stamp, slot) order
-
-  if (tid == 0) s_c = 0;
+  if (tid == 0) {
+    s_pj = 0;
+    s_c = 0;
+  }
   __syncthreads();
-  // stage the order array; find j's position; count the slots of stamp t above j, which stay
-  // behind it
-  int c = 0;
-  for (int i = tid; i < B; i += AT) {
-    const int32_t s = ord[i];
-    ord_lds[i] = s;
-    if (s == j) s_pj = i;
-    else if (s > j && st[s] == t) ++c;
+  // Round trip 2: the page-table entry, the first slot's owner (the victim's, if the token
+  // is not resident) and the stamps of the last AT slots of the order.  Slots stamped t
+  // (appended since the last resolve) form the tail of the order.
+  const int32_t jr = pt[p];
+  const int32_t lru = ord_lds[0];
+  const int32_t lru_owner = rm[lru];
+  int32_t tail_slot = -1;
+  bool newest = false;
+  if (tid < B) {
+    tail_slot = ord_lds[B - 1 - tid];
+    newest = st[tail_slot] == t;
+  }
+  const bool resident = jr >= 0;
+  const int32_t j = resident ? jr : lru;  // least recently used: first in (stamp, slot) order
+  if (resident)
+    for (int i = tid; i < B; i += AT)
+      if (ord_lds[i] == j) s_pj = i;
+  // the slots of stamp t above j stay behind it
+  int c = (newest && tail_slot > j) ? 1 : 0;
+  if (__syncthreads_and(tid >= B || newest)) {
+    // the tail is longer than one chunk (many appends since the last resolve): walk on
+    for (int base = B - 1 - AT; base >= 0; base -= AT) {
+      const int i = base - tid;
+      bool nw = false;
+      if (i >= 0) {
+        const int32_t sl = ord_lds[i];
+        nw = st[sl] == t;
+        if (nw && sl > j) ++c;
+      }
+      if (!__syncthreads_and(i < 0 || nw)) break;
+    }
   }
   if (c) atomicAdd(&s_c, c);
   __syncthreads();
@@ -87,8 +128,7 @@ __global__ __launch_bounds__(AT) void append_kernel(AppendArgs a) {
   if (tid == 0) {
     ord[q] = j;
     if (!resident) {
-      const int32_t old = rm[j];
-      if (old >= 0) pt[old] = -1;
+      if (lru_owner >= 0) pt[lru_owner] = -1;
       pt[p] = j;
       rm[j] = p;
     }
@@ -97,19 +137,51 @@ __global__ __launch_bounds__(AT) void append_kernel(AppendArgs a) {
     atomicOr(a.fresh + (int64_t)r * ((B + 31) >> 5) + (j >> 5), 1u << (j & 31));
     if (a.slot_out) a.slot_out[r] = j;
   }
-  if (a.io) {
-    const v4i* src = (const v4i*)(a.rows + (int64_t)r * a.row_stride);
-    v4i* dev = (v4i*)(a.buf + (int64_t)r * a.req_stride + (int64_t)j * a.slot_stride);
-    v4i* hst = (v4i*)(a.host + ((int64_t)r * a.cap + p) * a.host_stride);
-    for (int i = tid; i < a.chunks; i += AT) {
-      const v4i v = src[i];
-      dev[i] = v;
-      hst[i] = v;
+  if (a.io && tid < a.chunks) {
+    ((v4i*)(a.buf + (int64_t)r * a.req_stride + (int64_t)j * a.slot_stride))[tid] = rowv;
+    ((v4i*)(a.host + ((int64_t)r * a.cap + p) * a.host_stride))[tid] = rowv;
+  }
+}
+
+// Prefill offload of rows that are not contiguous (a padded row stride): a grid of small
+// workgroups copies 16-byte chunks from the device rows to the pinned history with
+// zero-copy stores, four chunks in flight per thread.
+constexpr int OT = 256;
+
+__global__ __launch_bounds__(OT) void offload_kernel(const uint8_t* __restrict__ src, int64_t src_stride,
+                                                     uint8_t* __restrict__ dst, int64_t count, int32_t chunks) {
+  const int64_t total = count * chunks;
+  const int64_t step = (int64_t)gridDim.x * OT;
+  constexpr int U = 4;
+  for (int64_t base = (int64_t)blockIdx.x * OT + threadIdx.x; base < total; base += step * U) {
+    v4i v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t idx = base + u * step;
+      if (idx < total) {
+        const int64_t row = idx / chunks;
+        v[u] = ((const v4i*)(src + row * src_stride))[idx - row * chunks];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t idx = base + u * step;
+      if (idx < total) ((v4i*)dst)[idx] = v[u];
     }
   }
 }
 
 }  // namespace
+
+hipError_t launch_offload(const void* src, int64_t src_stride, uint8_t* dst_mapped, int64_t count, int64_t entry_bytes,
+                          hipStream_t s) {
+  const int32_t chunks = (int32_t)(entry_bytes / 16);
+  const int64_t total = count * chunks;
+  const int64_t blocks = (total + OT * 4 - 1) / (OT * 4);
+  hipLaunchKernelGGL(offload_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(OT), 0, s,
+                     (const uint8_t*)src, src_stride, dst_mapped, count, chunks);
+  return hipGetLastError();
+}
 
 void prepare_append() {
   (void)hipFuncSetAttribute((const void*)append_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -169,9 +169,10 @@ hs_status hs_append(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* d
  * Prefill offload: copies count rows (device memory, row_stride bytes apart) into positions
  * first .. first + count - 1 of request `request`'s history in the host pool (the note's
  * introduction: KV is actively offloaded to host memory).  Device tables are untouched: the
- * tokens arrive on the device as misses when a selection names them.  A stream-ordered copy
- * (hipMemcpy2DAsync, device to pinned host); HS_ERR_INVALID_ARG for a range outside
- * [0, capacity) or row_stride < entry bytes.
+ * tokens arrive on the device as misses when a selection names them.  Stream-ordered: one
+ * flat device-to-host copy when row_stride equals the entry size, a zero-copy store kernel
+ * for 16-byte-aligned padded rows, a 2-D copy otherwise.  HS_ERR_INVALID_ARG for a range
+ * outside [0, capacity) or row_stride < entry bytes.
  */
 hs_status hs_offload(hs_handle* h, int32_t layer, int32_t request, int64_t first, int64_t count,
                      const void* d_rows, int64_t row_stride, void* stream);

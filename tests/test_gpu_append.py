@@ -171,7 +171,7 @@ def test_append_and_resolve_in_a_graph_replay_like_eager():
         hs.close()
 
 
-@pytest.mark.parametrize("pad", [0, 48])
+@pytest.mark.parametrize("pad", [0, 48, 5])  # flat copy, store kernel, 2-D copy
 def test_offload_writes_history_rows(pad):
     n, B, k, ratio = 2, 64, 16, 8
     cap = ratio * B
