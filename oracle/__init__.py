@@ -28,7 +28,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "liboracle.so")
 _SRC = os.path.join(_HERE, "hs_oracle.c")
 
-OK, BAD_TOKEN, DUPLICATE, NO_ROOM, NOMEM = 0, -1, -2, -3, -4
+OK, BAD_TOKEN, DUPLICATE, NO_ROOM, NOMEM, BAD_POLICY = 0, -1, -2, -3, -4, -5
+LRU, FIFO, RANDOM = 0, 1, 2     # eviction policies (hs_oracle.c)
 ENTRY_BYTES = {0: 1152, 1: 656}
 
 
@@ -52,11 +53,15 @@ def lib():
     L = ctypes.CDLL(_SO)
     p, i64 = ctypes.c_void_p, ctypes.c_int64
     L.orc_resolve.restype = ctypes.c_int
-    L.orc_resolve.argtypes = [i64, i64, i64, p, p, p, i64, p, p, p, p, p, i64]
+    u64 = ctypes.c_uint64
+    L.orc_resolve.argtypes = [i64, i64, i64, p, p, p, i64, p, p, p, p, p, i64, ctypes.c_int, u64, i64]
     L.orc_resolve_batch.restype = ctypes.c_int
-    L.orc_resolve_batch.argtypes = [i64, i64, i64, i64, p, p, p, p, p, p, p, p, p, i64, ctypes.c_int]
+    L.orc_resolve_batch.argtypes = [i64, i64, i64, i64, p, p, p, p, p, p, p, p, p, i64, ctypes.c_int, ctypes.c_int,
+                                    u64, i64, i64]
+    L.orc_random_perm.restype = ctypes.c_uint32
+    L.orc_random_perm.argtypes = [u64, i64, i64, ctypes.c_uint32, ctypes.c_uint32]
     L.orc_append.restype = ctypes.c_int
-    L.orc_append.argtypes = [i64, i64, p, p, p, i64, ctypes.c_int32, p, p, p, i64, p]
+    L.orc_append.argtypes = [i64, i64, p, p, p, i64, ctypes.c_int32, p, p, p, i64, p, ctypes.c_int]
     L.orc_e4m3_decode.restype = ctypes.c_double
     L.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
     L.orc_attend.restype = ctypes.c_int
@@ -75,6 +80,11 @@ def e4m3_decode(code: int) -> float:
     return lib().orc_e4m3_decode(code)
 
 
+def random_perm(seed: int, rl: int, t: int, N: int, x: int) -> int:
+    """The RANDOM policy's permutation of [0, N) for request-layer rl at step t, at x."""
+    return lib().orc_random_perm(seed, rl, t, N, x)
+
+
 def default_threads() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
@@ -84,11 +94,12 @@ class OracleCache:
 
     host: optional [n][L][cap][E] uint8 array holding each request's full KV
     history; when given, the oracle also keeps the device-slot bytes
-    ``dev[n][L][B][E]`` and fills them on every miss.
+    ``dev[n][L][B][E]`` and fills them on every miss.  policy: LRU (the method), or FIFO /
+    RANDOM (seeded) for the eviction-policy study.
     """
 
     def __init__(self, n: int, L: int, B: int, cap: int, layout: int = 0, host: np.ndarray | None = None,
-                 threads: int | None = None):
+                 threads: int | None = None, policy: int = LRU, seed: int = 0):
         if B <= 0 or cap <= 0 or n <= 0 or L <= 0:
             raise OracleError("bad shape")
         self.n, self.L, self.B, self.cap, self.layout = n, L, B, cap, layout
@@ -104,6 +115,7 @@ class OracleCache:
         else:
             self.dev = None
         self.threads = threads or default_threads()
+        self.policy, self.seed = policy, seed
 
     def resolve(self, layer: int, S: np.ndarray, requests: int | None = None):
         """Resolve S[n_req][k] for layer ``layer``; returns (slots[n_req][k] int32, miss[n_req] int64)."""
@@ -121,7 +133,8 @@ class OracleCache:
             dev = np.ascontiguousarray(self.dev[:nr, layer])
             host = np.ascontiguousarray(self.host[:nr, layer])
         rc = lib().orc_resolve_batch(nr, self.B, self.cap, k, _ptr(PT), _ptr(RM), _ptr(ST), _ptr(t), _ptr(S),
-                                     _ptr(slots), _ptr(miss), _ptr(dev), _ptr(host), self.E, self.threads)
+                                     _ptr(slots), _ptr(miss), _ptr(dev), _ptr(host), self.E, self.threads,
+                                     self.policy, self.seed, self.L, layer)
         if rc != OK:
             raise OracleError(f"invalid selection (code {rc})")
         self.PT[:nr, layer] = PT
@@ -152,7 +165,7 @@ class OracleCache:
             host = None if self.host is None else np.ascontiguousarray(self.host[r, layer])
             slot = ctypes.c_int32(-1)
             rc = lib().orc_append(self.B, self.cap, _ptr(PT), _ptr(RM), _ptr(ST), int(self.t[r, layer]), int(pos[r]),
-                                  _ptr(rows[r]), _ptr(dev), _ptr(host), self.E, ctypes.byref(slot))
+                                  _ptr(rows[r]), _ptr(dev), _ptr(host), self.E, ctypes.byref(slot), self.policy)
             if rc != OK:
                 raise OracleError(f"invalid append (code {rc})")
             self.PT[r, layer], self.RM[r, layer], self.ST[r, layer] = PT, RM, ST

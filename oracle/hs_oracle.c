@@ -36,8 +36,49 @@
 #define ORC_DUPLICATE -2
 #define ORC_NO_ROOM -3
 #define ORC_NOMEM -4
+#define ORC_BAD_POLICY -5
+
+/* Eviction policies (the note, section 3: the miss-count experiment compares buffer sizes
+ * and eviction policies; LRU is steadier than a policy that does not exploit locality). */
+#define ORC_LRU 0     /* candidates by (last-selection stamp, slot)                        */
+#define ORC_FIFO 1    /* candidates by (fill stamp, slot): a hit does not refresh a slot    */
+#define ORC_RANDOM 2  /* candidates in slot order, taken through a keyed random permutation */
 
 /* ------------------------------------------------------------------ resolve */
+
+/* The c-th output of SplitMix64 seeded with s (Steele, Lea and Flood, "Fast splittable
+ * pseudorandom number generators", OOPSLA 2014): state s + (c + 1) * golden gamma, then the
+ * generator's output mix. */
+static uint64_t splitmix64_at(uint64_t s, uint64_t c) {
+  uint64_t z = s + (c + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+/* The RANDOM policy's permutation of [0, N) for one (request-layer rl, step t): a balanced
+ * 4-round Feistel network on 2h-bit values, 4^h the smallest power of four >= N, whose round
+ * function i maps the right half R to the low h bits of splitmix64_at(key, i * 2^32 + R)
+ * with key = splitmix64_at(seed, rl * 2^32 + t); values that land outside [0, N) are
+ * encrypted again (cycle walking, Black and Rogaway, "Ciphers with arbitrary finite
+ * domains", CT-RSA 2002) until they land inside. */
+uint32_t orc_random_perm(uint64_t seed, int64_t rl, int64_t t, uint32_t N, uint32_t x) {
+  const uint64_t key = splitmix64_at(seed, ((uint64_t)rl << 32) | (uint32_t)t);
+  int h = 1;
+  while (((uint64_t)1 << (2 * h)) < N) ++h;
+  const uint32_t mask = (1u << h) - 1u;
+  do {
+    uint32_t L = x >> h, R = x & mask;
+    for (uint32_t i = 0; i < 4; ++i) {
+      const uint32_t F = (uint32_t)splitmix64_at(key, ((uint64_t)i << 32) | R) & mask;
+      const uint32_t nl = R;
+      R = L ^ F;
+      L = nl;
+    }
+    x = (L << h) | R;
+  } while (x >= N);
+  return x;
+}
 
 static int cmp_i32(const void* a, const void* b) {
   int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
@@ -55,7 +96,9 @@ static int cmp_cand(const void* a, const void* b) {
 
 /*
  * Resolve one selection S[k] (entries in [0, cap) or -1 for padding) against
- * the state of one (request, layer):
+ * the state of one (request, layer) under eviction policy `policy` (ORC_LRU
+ * unless a policy study asks otherwise; rl = request * layers + layer and seed
+ * key the RANDOM permutation):
  *   PT[cap]  token -> slot, -1 = not resident
  *   RM[B]    slot -> token, -1 = empty
  *   ST[B]    slot recency stamp, -1 = never used
@@ -67,7 +110,8 @@ static int cmp_cand(const void* a, const void* b) {
  */
 int orc_resolve(int64_t B, int64_t cap, int64_t k, int32_t* PT, int32_t* RM, int64_t* ST, int64_t t,
                 const int32_t* S, int32_t* slots, int64_t* miss, uint8_t* DEV, const uint8_t* HOST,
-                int64_t E) {
+                int64_t E, int policy, uint64_t seed, int64_t rl) {
+  if (policy != ORC_LRU && policy != ORC_FIFO && policy != ORC_RANDOM) return ORC_BAD_POLICY;
   int32_t* sorted = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k > 0 ? k : 1));
   int32_t* M = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k > 0 ? k : 1));
   unsigned char* is_hit = (unsigned char*)calloc((size_t)B, 1);
@@ -98,24 +142,28 @@ int orc_resolve(int64_t B, int64_t cap, int64_t k, int32_t* PT, int32_t* RM, int
     else M[m++] = s;
   }
 
-  /* 3. candidates: every slot not holding a hit, ordered by (stamp, slot) */
+  /* 3. candidates: every slot not holding a hit, ordered by (stamp, slot) -- LRU and FIFO
+   *    (their stamps differ) -- or, for RANDOM, left in slot order */
   int64_t nc = 0;
   for (int64_t j = 0; j < B; ++j)
     if (!is_hit[j]) { C[nc].stamp = ST[j]; C[nc].slot = (int32_t)j; ++nc; }
   if (nc < m) { rc = ORC_NO_ROOM; goto done; }
-  qsort(C, (size_t)nc, sizeof(cand_t), cmp_cand);
+  if (policy != ORC_RANDOM) qsort(C, (size_t)nc, sizeof(cand_t), cmp_cand);
 
-  /* 4. assign the i-th miss to the i-th candidate: evict, update both maps, fetch */
+  /* 4. assign the i-th miss to the i-th candidate (RANDOM: candidate perm(i)): evict,
+   *    update both maps, fetch; a filled slot is stamped with this step */
   for (int64_t i = 0; i < m; ++i) {
-    int32_t j = C[i].slot;
+    int32_t j = policy == ORC_RANDOM ? C[orc_random_perm(seed, rl, t, (uint32_t)nc, (uint32_t)i)].slot : C[i].slot;
+    ST[j] = t;
     if (RM[j] >= 0) PT[RM[j]] = -1;
     PT[M[i]] = j;
     RM[j] = M[i];
     if (DEV && HOST) memcpy(DEV + (size_t)j * (size_t)E, HOST + (size_t)M[i] * (size_t)E, (size_t)E);
   }
 
-  /* 5. stamp every selected token's slot with this step */
-  for (int64_t i = 0; i < nv; ++i) ST[PT[sorted[i]]] = t;
+  /* 5. LRU and RANDOM: stamp every selected token's slot with this step (FIFO: fills only) */
+  if (policy != ORC_FIFO)
+    for (int64_t i = 0; i < nv; ++i) ST[PT[sorted[i]]] = t;
 
   /* 6. outputs in selection order */
   for (int64_t i = 0; i < k; ++i) slots[i] = (S[i] == -1) ? -1 : PT[S[i]];
@@ -129,6 +177,7 @@ done:
 /* Batch over n independent request states laid out back to back. */
 typedef struct {
   int64_t B, cap, k, E;
+  int policy; uint64_t seed; int64_t L, l;
   int32_t* PT; int32_t* RM; int64_t* ST; const int64_t* t;
   const int32_t* S; int32_t* slots; int64_t* miss;
   uint8_t* DEV; const uint8_t* HOST;
@@ -143,7 +192,8 @@ static void* rjob_run(void* p) {
     int rc = orc_resolve(j->B, j->cap, j->k, j->PT + r * j->cap, j->RM + r * j->B, j->ST + r * j->B, j->t[r],
                          j->S + r * j->k, j->slots + r * j->k, j->miss + r,
                          j->DEV ? j->DEV + r * j->B * j->E : NULL,
-                         j->HOST ? j->HOST + r * j->cap * j->E : NULL, j->E);
+                         j->HOST ? j->HOST + r * j->cap * j->E : NULL, j->E, j->policy, j->seed,
+                         r * j->L + j->l);
     if (rc != ORC_OK && j->rc == ORC_OK) j->rc = rc;
   }
   return NULL;
@@ -151,14 +201,15 @@ static void* rjob_run(void* p) {
 
 int orc_resolve_batch(int64_t n, int64_t B, int64_t cap, int64_t k, int32_t* PT, int32_t* RM, int64_t* ST,
                       const int64_t* t, const int32_t* S, int32_t* slots, int64_t* miss, uint8_t* DEV,
-                      const uint8_t* HOST, int64_t E, int nthreads) {
+                      const uint8_t* HOST, int64_t E, int nthreads, int policy, uint64_t seed, int64_t L,
+                      int64_t l) {
   if (nthreads < 1) nthreads = 1;
   if (nthreads > 256) nthreads = 256;
   if (nthreads > n) nthreads = (int)(n > 0 ? n : 1);
   pthread_t th[256];
   rjob_t jobs[256];
   for (int i = 0; i < nthreads; ++i) {
-    jobs[i] = (rjob_t){B, cap, k, E, PT, RM, ST, t, S, slots, miss, DEV, HOST,
+    jobs[i] = (rjob_t){B, cap, k, E, policy, seed, L, l, PT, RM, ST, t, S, slots, miss, DEV, HOST,
                        n * i / nthreads, n * (i + 1) / nthreads, ORC_OK};
   }
   for (int i = 1; i < nthreads; ++i) pthread_create(&th[i], NULL, rjob_run, &jobs[i]);
@@ -179,12 +230,15 @@ int orc_resolve_batch(int64_t n, int64_t B, int64_t cap, int64_t k, int32_t* PT,
  *   - a resident token keeps its slot;
  *   - otherwise it takes the first slot in (stamp, slot) order over all slots --
  *     empty slots first -- evicting that slot's token from the page table;
- * the slot's stamp becomes t, the step number the next resolve will use, and
- * with DEV non-NULL the slot's bytes become R.  *slot_out gets the slot.
- * Returns ORC_OK, or ORC_BAD_TOKEN (state untouched) when p is not in [0, cap).
+ * the slot's stamp becomes t, the step number the next resolve will use (under
+ * FIFO only when the token is placed), and with DEV non-NULL the slot's bytes
+ * become R.  *slot_out gets the slot.  Returns ORC_OK, ORC_BAD_TOKEN (state
+ * untouched) when p is not in [0, cap), or ORC_BAD_POLICY for RANDOM, whose
+ * candidate order exists only within a resolve.
  */
 int orc_append(int64_t B, int64_t cap, int32_t* PT, int32_t* RM, int64_t* ST, int64_t t, int32_t p,
-               const uint8_t* R, uint8_t* DEV, uint8_t* HOST, int64_t E, int32_t* slot_out) {
+               const uint8_t* R, uint8_t* DEV, uint8_t* HOST, int64_t E, int32_t* slot_out, int policy) {
+  if (policy != ORC_LRU && policy != ORC_FIFO) return ORC_BAD_POLICY;
   if (p < 0 || p >= cap) return ORC_BAD_TOKEN;
   int32_t j = PT[p];
   if (j < 0) {
@@ -194,8 +248,10 @@ int orc_append(int64_t B, int64_t cap, int32_t* PT, int32_t* RM, int64_t* ST, in
     if (RM[j] >= 0) PT[RM[j]] = -1;
     PT[p] = j;
     RM[j] = p;
+    ST[j] = t;
+  } else if (policy == ORC_LRU) {
+    ST[j] = t;  /* FIFO: rewriting a resident token is a use, which does not refresh its slot */
   }
-  ST[j] = t;
   if (DEV) memcpy(DEV + (size_t)j * (size_t)E, R, (size_t)E);
   if (HOST) memcpy(HOST + (size_t)p * (size_t)E, R, (size_t)E);
   *slot_out = j;

@@ -310,8 +310,10 @@ def test_invariants_random_traces(B, k, cap, steps):
         resident = _check_invariants(oc, S, slots, m, resident, last_use, t, host)
 
 
-def test_relabelled_steps_give_same_placement():
-    # Any strictly increasing step numbering gives the same placement.
+@pytest.mark.parametrize("policy", [oracle.LRU, oracle.FIFO])
+def test_relabelled_steps_give_same_placement(policy):
+    # Any strictly increasing step numbering gives the same placement (for the stamp-ordered
+    # policies; RANDOM keys its permutation by the step number itself).
     rng = np.random.default_rng(9)
     B, cap, k = 20, 90, 9
     seq = [np.asarray(rng.choice(cap, k, replace=False), dtype=np.int32) for _ in range(50)]
@@ -322,7 +324,8 @@ def test_relabelled_steps_give_same_placement():
         slots = np.empty(k, np.int32); miss = np.empty(1, np.int64)
         for t, S in enumerate(seq):
             assert L.orc_resolve(B, cap, k, PT.ctypes.data, RM.ctypes.data, ST.ctypes.data, 100 + t * stride,
-                                 S.ctypes.data, slots.ctypes.data, miss.ctypes.data, None, None, 1152) == 0
+                                 S.ctypes.data, slots.ctypes.data, miss.ctypes.data, None, None, 1152,
+                                 policy, 0, 0) == 0
         states.append((PT.copy(), RM.copy()))
     assert (states[0][0] == states[1][0]).all() and (states[0][1] == states[1][1]).all()
 
