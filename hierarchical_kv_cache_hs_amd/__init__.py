@@ -27,6 +27,7 @@ LAYOUT_BF16 = 0      # HS_KV_BF16_576
 LAYOUT_FP8 = 1       # HS_KV_FP8_MLA_656
 ENTRY_BYTES = {LAYOUT_BF16: 1152, LAYOUT_FP8: 656}
 FLAG_NO_IO = 0x1
+EVICT_LRU, EVICT_FIFO, EVICT_RANDOM = 0, 1, 2   # hs_eviction
 DEVERR_TOKEN_RANGE = 0x1
 DEVERR_DUPLICATE = 0x2
 
@@ -43,7 +44,8 @@ class Config(ctypes.Structure):
     _fields_ = [("top_k", ctypes.c_int32), ("device_buffer_size", ctypes.c_int32),
                 ("host_to_device_ratio", ctypes.c_int32), ("max_requests", ctypes.c_int32),
                 ("num_layers", ctypes.c_int32), ("layout", ctypes.c_int32), ("num_heads", ctypes.c_int32),
-                ("flags", ctypes.c_uint32), ("device_mem", ctypes.c_void_p), ("device_mem_bytes", ctypes.c_size_t)]
+                ("flags", ctypes.c_uint32), ("device_mem", ctypes.c_void_p), ("device_mem_bytes", ctypes.c_size_t),
+                ("eviction", ctypes.c_int32), ("eviction_seed", ctypes.c_uint64)]
 
 
 class StateView(ctypes.Structure):
@@ -103,9 +105,9 @@ def _check(status: int):
 
 
 def make_config(top_k, device_buffer_size, host_to_device_ratio, max_requests, num_layers=1, layout=LAYOUT_BF16,
-                num_heads=0, flags=0) -> Config:
+                num_heads=0, flags=0, eviction=0, eviction_seed=0) -> Config:
     return Config(top_k, device_buffer_size, host_to_device_ratio, max_requests, num_layers, layout, num_heads,
-                  flags, None, 0)
+                  flags, None, 0, eviction, eviction_seed)
 
 
 def device_bytes(cfg: Config) -> int:
@@ -130,9 +132,9 @@ class HiSparse:
 
     def __init__(self, top_k: int, device_buffer_size: int, host_to_device_ratio: int, max_requests: int,
                  num_layers: int = 1, layout: int = LAYOUT_BF16, num_heads: int = 0, flags: int = 0,
-                 device: str | torch.device = "cuda"):
+                 device: str | torch.device = "cuda", eviction: int = 0, eviction_seed: int = 0):
         self.cfg = make_config(top_k, device_buffer_size, host_to_device_ratio, max_requests, num_layers, layout,
-                               num_heads, flags)
+                               num_heads, flags, eviction, eviction_seed)
         nbytes = device_bytes(self.cfg)
         self.device = torch.device(device)
         # torch owns the device block; the library lays its tables out inside it

@@ -1,4 +1,5 @@
-// Write-through append of newly generated tokens.
+// Write-through append of newly generated tokens (LRU and FIFO eviction; under FIFO a token
+// that is already resident only has its row rewritten).
 //
 // What is computed (the HiSparse note's introduction: KV that is not in use is actively
 // offloaded to host memory; paper abstract: each request keeps its full KV history in host
@@ -38,7 +39,7 @@ struct AppendArgs {
   uint8_t* host;          // the layer's host pool, device-mapped address
   int32_t* err;
   int64_t cap, host_stride, slot_stride, req_stride;
-  int32_t B, chunks, io;
+  int32_t B, chunks, io, fifo;
 };
 
 __global__ __launch_bounds__(AT) void append_kernel(AppendArgs a) {
@@ -102,6 +103,15 @@ __global__ __launch_bounds__(AT) void append_kernel(AppendArgs a) {
   }
   const bool resident = jr >= 0;
   const int32_t j = resident ? jr : lru;  // least recently used: first in (stamp, slot) order
+  if (a.fifo && resident) {
+    // FIFO: rewriting a resident token is no refill -- its slot keeps its stamp and place
+    if (tid == 0 && a.slot_out) a.slot_out[r] = j;
+    if (a.io && tid < a.chunks) {
+      ((v4i*)(a.buf + (int64_t)r * a.req_stride + (int64_t)j * a.slot_stride))[tid] = rowv;
+      ((v4i*)(a.host + ((int64_t)r * a.cap + p) * a.host_stride))[tid] = rowv;
+    }
+    return;
+  }
   if (resident)
     for (int i = tid; i < B; i += AT)
       if (ord_lds[i] == j) s_pj = i;
@@ -213,6 +223,7 @@ hipError_t launch_append(const Geometry& g, const LayerTables& t, uint8_t* host_
   a.B = g.B;
   a.chunks = (int32_t)(g.entry_bytes / 16);
   a.io = (g.flags & HS_FLAG_NO_IO) ? 0 : 1;
+  a.fifo = g.policy == HS_EVICT_FIFO ? 1 : 0;
   hipLaunchKernelGGL(append_kernel, dim3(n_req), dim3(AT), (size_t)g.B * sizeof(int32_t), s, a);
   return hipGetLastError();
 }

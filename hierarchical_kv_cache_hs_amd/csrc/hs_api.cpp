@@ -96,6 +96,8 @@ hs_status plan(const hs_config* cfg, hs::Geometry* g, Layout* lay) {
     return fail(HS_ERR_INVALID_ARG, "unknown KV layout");
   if (cfg->num_heads < 0 || cfg->num_heads > 16) return fail(HS_ERR_INVALID_ARG, "num_heads must lie in [0, 16]");
   if (cfg->flags & ~HS_FLAG_NO_IO) return fail(HS_ERR_INVALID_ARG, "unknown flag bits");
+  if (cfg->eviction != HS_EVICT_LRU && cfg->eviction != HS_EVICT_FIFO && cfg->eviction != HS_EVICT_RANDOM)
+    return fail(HS_ERR_INVALID_ARG, "unknown eviction policy");
   if (cfg->top_k > hs::kMaxTopK) return fail(HS_ERR_UNSUPPORTED, "top_k above 8192");
   if (cfg->device_buffer_size > hs::kMaxBuffer) return fail(HS_ERR_UNSUPPORTED, "device_buffer_size above 16384");
   const int64_t cap = (int64_t)cfg->host_to_device_ratio * (int64_t)cfg->device_buffer_size;
@@ -115,6 +117,8 @@ hs_status plan(const hs_config* cfg, hs::Geometry* g, Layout* lay) {
   g->slot_stride = g->entry_bytes;  // packed: scattered 656-byte rows gather faster packed than padded to 768
   g->req_stride = ((int64_t)g->B + 1) * g->slot_stride;
   g->flags = cfg->flags;
+  g->policy = cfg->eviction;
+  g->seed = cfg->eviction_seed;
 
   const size_t LN = (size_t)g->L * (size_t)g->n;
   size_t off = 0, sz = 0, t = 0;
@@ -277,7 +281,7 @@ hs_status resolve_impl(hs_handle* h, int32_t layer, int32_t n_req, const int32_t
   if (!d_sel || !d_slots) return fail(HS_ERR_INVALID_ARG, "selection or slot pointer is NULL");
   hs::LayerTables t = layer_tables(h, layer);
   const uint8_t* host_layer = h->host_pool_dev + (size_t)layer * h->g.n * (size_t)h->g.cap * h->g.host_stride;
-  hipError_t e = hs::launch_resolve(h->g, t, host_layer, n_req, d_sel, d_slots, d_miss, h->err, list_only,
+  hipError_t e = hs::launch_resolve(h->g, t, layer, host_layer, n_req, d_sel, d_slots, d_miss, h->err, list_only,
                                     (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "resolve launch");
   return HS_OK;
@@ -362,6 +366,8 @@ hs_status hs_append(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* d
   if (!h) return fail(HS_ERR_INVALID_ARG, "handle is NULL");
   if (layer < 0 || layer >= h->g.L) return fail(HS_ERR_INVALID_ARG, "layer out of range");
   if (n_req < 0 || n_req > h->g.n) return fail(HS_ERR_INVALID_ARG, "n_req out of range");
+  if (h->g.policy == HS_EVICT_RANDOM)
+    return fail(HS_ERR_UNSUPPORTED, "append needs a stamp-ordered eviction policy (LRU or FIFO)");
   if (n_req == 0) return HS_OK;
   if (!d_pos || !d_rows) return fail(HS_ERR_INVALID_ARG, "position or row pointer is NULL");
   if (row_stride < h->g.entry_bytes || row_stride % 16 || ((uintptr_t)d_rows) % 16)

@@ -39,6 +39,8 @@ struct Geometry {
   int64_t slot_stride;
   int64_t req_stride;   // bytes per request in the slot buffer: B slot rows, then one row of zeros
   uint32_t flags;
+  int32_t policy;       // hs_eviction
+  uint64_t seed;        // HS_EVICT_RANDOM key
 };
 
 // Once per process, before the first launch (outside any graph capture).
@@ -48,9 +50,9 @@ void prepare_resolve();
 size_t resolve_lds_bytes(int64_t cap, int32_t k, int32_t B);
 
 // list_only: write the miss lists instead of copying the rows (launch_fetch copies them).
-hipError_t launch_resolve(const Geometry& g, const LayerTables& t, const uint8_t* host_layer, int32_t n_req,
-                          const int32_t* sel, int32_t* slots, int32_t* miss, int32_t* err, bool list_only,
-                          hipStream_t s);
+hipError_t launch_resolve(const Geometry& g, const LayerTables& t, int32_t layer, const uint8_t* host_layer,
+                          int32_t n_req, const int32_t* sel, int32_t* slots, int32_t* miss, int32_t* err,
+                          bool list_only, hipStream_t s);
 
 hipError_t launch_fetch(const Geometry& g, const LayerTables& t, const uint8_t* host_layer, int32_t n_req,
                         hipStream_t s);

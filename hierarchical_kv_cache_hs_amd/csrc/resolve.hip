@@ -64,10 +64,43 @@ struct ResolveArgs {
   int64_t host_stride;
   int64_t slot_stride;
   int64_t req_stride;  // bytes per request in buf
+  uint64_t seed;       // HS_EVICT_RANDOM key
   int32_t k;
   int32_t B;
   int32_t chunks;  // 16-byte chunks per row
+  int32_t policy;  // hs_eviction
+  int32_t layer, nlayers;
 };
+
+// Output number c of SplitMix64 started from state s (Steele, Lea and Flood, OOPSLA 2014).
+__device__ __forceinline__ uint64_t splitmix64_at(uint64_t s, uint64_t c) {
+  uint64_t z = s + (c + 1ull) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// HS_EVICT_RANDOM: image of x under the keyed permutation of [0, n) -- four Feistel rounds on
+// halves of h bits (4^h >= n), round i mixing the right half into the left with SplitMix64
+// output (i << 32 | right) under `key`, repeated while the value lies outside [0, n) (cycle
+// walking; it returns because the network permutes [0, 4^h)).
+__device__ uint32_t random_rank(uint64_t key, uint32_t n, uint32_t x) {
+  int h = 1;
+  while ((1ull << (2 * h)) < (uint64_t)n) ++h;
+  const uint32_t mask = (1u << h) - 1u;
+  do {
+    uint32_t lo = x & mask, hi = x >> h;
+#pragma unroll
+    for (uint32_t i = 0; i < 4; ++i) {
+      const uint32_t f = (uint32_t)splitmix64_at(key, ((uint64_t)i << 32) | lo) & mask;
+      const uint32_t t = hi ^ f;
+      hi = lo;
+      lo = t;
+    }
+    x = (hi << h) | lo;
+  } while (x >= n);
+  return x;
+}
 
 // Exclusive block-wide prefix sum of v; *total gets the block sum.  Every thread must call.
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
@@ -210,32 +243,72 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
   }
 
   // ---- P3
-  {
-    int rank = (int)(pre & 0xFFFFu);
+  const int policy = a.policy;
+  if (policy == HS_EVICT_RANDOM) {
+    // Candidates are the non-hit slots in slot order; the q-th miss takes candidate
+    // random_rank(q), found through per-word candidate counts (one bitmap word per thread)
+    // and a select within the word.  The LRU order array is not maintained.
+    uint32_t* cpre = freshmap;  // no appends under RANDOM: the fresh bitmap is free
+    uint32_t cand = 0;
+    if (tid < HB) {
+      cand = ~hitmap[tid];
+      if (tid == HB - 1 && (B & 31)) cand &= (1u << (B & 31)) - 1u;
+    }
+    uint32_t ncand;
+    const uint32_t below = block_scan((uint32_t)__popc(cand), wsum, &ncand);
+    if (tid < HB) cpre[tid] = below;
+    __syncthreads();
+    const uint64_t key =
+        splitmix64_at(a.seed, ((uint64_t)((int64_t)r * a.nlayers + a.layer) << 32) | (uint32_t)t);
+    for (int q = tid; q < m && q < (int)ncand; q += NT) {
+      const uint32_t x = random_rank(key, ncand, (uint32_t)q);
+      int lo = 0, hi = HB - 1;  // the last word whose prefix is <= x holds candidate x
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cpre[mid] <= x) lo = mid;
+        else hi = mid - 1;
+      }
+      uint32_t bits = ~hitmap[lo];
+      if (lo == HB - 1 && (B & 31)) bits &= (1u << (B & 31)) - 1u;
+      for (uint32_t z = cpre[lo]; z < x; ++z) bits &= bits - 1u;
+      victims[q] = (uint32_t)(lo * 32 + __ffs(bits) - 1);
+    }
+  } else {
+    // LRU and FIFO: the first m non-hit slots in order are the victims.  Slots stamped with
+    // this step after the resolve -- victims, appended slots and, under LRU, hits -- form the
+    // back of the new order (the bitmap `back`); every other slot keeps its relative order
+    // and moves up past the back-group slots before it.
+    uint32_t* back = (policy == HS_EVICT_FIFO) ? freshmap : hitmap;
+    int rank = (int)(pre & 0xFFFFu);  // non-hit slots before this thread's entries
 #pragma unroll
     for (int x = 0; x < OPT; ++x) {
+      const int32_t j = ordv[x];
+      if (j < 0 || j >= B) continue;
+      const bool fresh_j = (freshmap[j >> 5] >> (j & 31)) & 1u;
       if (nhmask & (1u << x)) {
-        const int32_t j = ordv[x];
         if (rank < m) {
           victims[rank] = (uint32_t)j;
-          atomicOr(&hitmap[j >> 5], 1u << (j & 31));
-        } else if ((freshmap[j >> 5] >> (j & 31)) & 1u) {
-          // appended since the last resolve: its stamp is already this step's, so it joins
-          // the back of the order with the hit and victim slots (appended slots come last in
-          // LRU order, so the slots before them keep their positions rank - m)
-          atomicOr(&hitmap[j >> 5], 1u << (j & 31));
+          atomicOr(&back[j >> 5], 1u << (j & 31));
+        } else if (fresh_j) {
+          // appended since the last resolve: its stamp is already this step's (appended
+          // slots come last in the order, so no slot before them shifts)
+          atomicOr(&back[j >> 5], 1u << (j & 31));
         } else {
-          ord[rank - m] = j;
+          // LRU: hit slots all go to the back, so the untouched slots are exactly the
+          // non-hit ones; FIFO: hits stay, and only the m victims before this slot leave
+          ord[(policy == HS_EVICT_FIFO ? o0 + x : rank) - m] = j;
         }
         ++rank;
+      } else if (policy == HS_EVICT_FIFO && !fresh_j) {
+        ord[o0 + x - min(m, rank)] = j;  // a hit keeps its fill stamp and its place
       }
     }
   }
   __syncthreads();
 
   // ---- P4
-  {
-    uint32_t word = (tid < HB) ? hitmap[tid] : 0u;
+  if (policy != HS_EVICT_RANDOM) {
+    uint32_t word = (tid < HB) ? ((policy == HS_EVICT_FIFO) ? freshmap : hitmap)[tid] : 0u;
     uint32_t touched;
     const uint32_t below = block_scan((uint32_t)__popc(word), wsum, &touched);
     int pos = B - (int)touched + (int)below;
@@ -252,7 +325,7 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
       const int32_t p = ptv[j];
       int32_t out = -1;
       if (p >= 0) {
-        st[p] = t;
+        if (policy != HS_EVICT_FIFO) st[p] = t;  // FIFO: a hit does not refresh its slot
         out = p;
       } else if (p == -1) {
         const int32_t s = selv[j];
@@ -424,9 +497,9 @@ size_t resolve_lds_bytes(int64_t cap, int32_t k, int32_t B) {
   return (bytes + 15) & ~(size_t)15;
 }
 
-hipError_t launch_resolve(const Geometry& g, const LayerTables& t, const uint8_t* host_layer, int32_t n_req,
-                          const int32_t* sel, int32_t* slots, int32_t* miss, int32_t* err, bool list_only,
-                          hipStream_t s) {
+hipError_t launch_resolve(const Geometry& g, const LayerTables& t, int32_t layer, const uint8_t* host_layer,
+                          int32_t n_req, const int32_t* sel, int32_t* slots, int32_t* miss, int32_t* err,
+                          bool list_only, hipStream_t s) {
   ResolveArgs a;
   a.sel = sel;
   a.slots = slots;
@@ -444,6 +517,10 @@ hipError_t launch_resolve(const Geometry& g, const LayerTables& t, const uint8_t
   a.host_stride = g.host_stride;
   a.slot_stride = g.slot_stride;
   a.req_stride = g.req_stride;
+  a.seed = g.seed;
+  a.policy = g.policy;
+  a.layer = layer;
+  a.nlayers = g.L;
   a.k = g.k;
   a.B = g.B;
   a.chunks = (int32_t)(g.entry_bytes / 16);

@@ -56,6 +56,24 @@ typedef enum hs_kv_layout {
 #define HS_FLAG_NO_IO 0x1u /* resolve updates every table but moves no row: measures the
                               resolution cost alone (the paper's no-IO oracle) */
 
+/*
+ * Eviction policies.  LRU is the method (paper abstract; note, section 2); the others exist
+ * for the policy study the note describes (section 3: LRU is steadier than a policy that does
+ * not exploit locality).
+ *   HS_EVICT_LRU     candidates by (stamp of last selection, slot)
+ *   HS_EVICT_FIFO    candidates by (stamp of the fill, slot): a hit does not refresh a slot
+ *   HS_EVICT_RANDOM  the non-hit slots in slot order; the i-th miss (ascending token) takes
+ *                    candidate perm(i), perm a pseudo-random permutation of the candidate
+ *                    ranks: a 4-round Feistel network on 2h-bit values (4^h the smallest
+ *                    power of four >= the candidate count), round i XORing the left half
+ *                    with the low h bits of SplitMix64 output (i << 32 | right half) under
+ *                    key = SplitMix64 output ((request * layers + layer) << 32 | step) of
+ *                    eviction_seed, re-encrypting values outside the range (cycle walking).
+ *                    Stamps follow LRU; lru_order is not maintained; hs_append is
+ *                    unsupported.
+ */
+typedef enum hs_eviction { HS_EVICT_LRU = 0, HS_EVICT_FIFO = 1, HS_EVICT_RANDOM = 2 } hs_eviction;
+
 /* Device error bits, accumulated (OR) until read by hs_get_device_error. */
 #define HS_DEVERR_TOKEN_RANGE 0x1 /* a selected token outside [0, capacity) and not -1 */
 #define HS_DEVERR_DUPLICATE 0x2   /* a token selected twice in one row */
@@ -77,6 +95,8 @@ typedef struct hs_config {
   void* device_mem;             /* optional caller-owned device block of hs_device_bytes()
                                    bytes, 256-byte aligned; NULL: the library allocates     */
   size_t device_mem_bytes;      /* size of device_mem                                        */
+  int32_t eviction;             /* hs_eviction; 0 = LRU                                      */
+  uint64_t eviction_seed;       /* HS_EVICT_RANDOM: key of its permutation                   */
 } hs_config;
 
 typedef struct hs_handle hs_handle;
@@ -87,6 +107,7 @@ typedef struct hs_state_view {
   int32_t* slot_owner;   /* [max_requests][B] slot -> token, -1 = empty               */
   int32_t* slot_stamp;   /* [max_requests][B] step of last selection, -1 = never       */
   int32_t* lru_order;    /* [max_requests][B] slots sorted by (stamp, slot) ascending  */
+                         /* (not maintained under HS_EVICT_RANDOM)                     */
   int32_t* step;         /* [max_requests] resolves done so far (the next stamp)        */
   uint8_t* kv_buffer;    /* per request (request_stride bytes apart): B slot rows of    */
                          /* slot_stride bytes, then one row of zeros the attention     */

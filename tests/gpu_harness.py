@@ -50,15 +50,16 @@ class Pair:
     """A device handle and the oracle, fed the same trace."""
 
     def __init__(self, n, L, k, B, ratio, layout, seed, heads=0, flags=0, oracle_rows=True, requests=None,
-                 split=False):
-        self.split = split
+                 split=False, policy=0, policy_seed=0):
+        self.split, self.policy = split, policy
         self.hs = hsa.HiSparse(top_k=k, device_buffer_size=B, host_to_device_ratio=ratio, max_requests=n,
-                               num_layers=L, layout=layout, num_heads=heads, flags=flags)
+                               num_layers=L, layout=layout, num_heads=heads, flags=flags, eviction=policy,
+                               eviction_seed=policy_seed)
         self.seed, self.n, self.L, self.k, self.B, self.layout = seed, n, L, k, B, layout
         self.cap = ratio * B
         fill_host_pool(self.hs, seed)
         host = oracle_host(seed, n, L, self.cap, layout) if oracle_rows else None
-        self.orc = oracle.OracleCache(n, L, B, self.cap, layout=layout, host=host)
+        self.orc = oracle.OracleCache(n, L, B, self.cap, layout=layout, host=host, policy=policy, seed=policy_seed)
         self.E = skv.ENTRY_BYTES[layout]
 
     def step(self, layer: int, S: np.ndarray, check_state: bool):
@@ -84,7 +85,8 @@ class Pair:
         assert (rm == self.orc.RM[:nr, layer]).all(), "slot owners differ"
         assert (stamp.astype(np.int64) == self.orc.ST[:nr, layer]).all(), "stamps differ"
         assert (st["step"][:nr].cpu().numpy() == self.orc.t[:nr, layer]).all(), "step counters differ"
-        assert lru_order_ok(stamp, order), "LRU order is not (stamp, slot) sorted"
+        if self.policy != hsa.EVICT_RANDOM:     # RANDOM keeps no order array
+            assert lru_order_ok(stamp, order), "LRU order is not (stamp, slot) sorted"
         if rows:
             buf = st["kv_buffer"][:nr, :, : self.E].cpu().numpy()
             for r in range(nr):

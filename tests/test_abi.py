@@ -47,6 +47,8 @@ def _cfg(**kw):
     (dict(num_heads=17), hsa.HS_ERR_INVALID_ARG),
     (dict(num_heads=-1), hsa.HS_ERR_INVALID_ARG),
     (dict(flags=0x80), hsa.HS_ERR_INVALID_ARG),
+    (dict(eviction=3), hsa.HS_ERR_INVALID_ARG),
+    (dict(eviction=-1), hsa.HS_ERR_INVALID_ARG),
     (dict(top_k=8193, device_buffer_size=9000), hsa.HS_ERR_UNSUPPORTED),
     (dict(device_buffer_size=16385), hsa.HS_ERR_UNSUPPORTED),
     (dict(device_buffer_size=4096, host_to_device_ratio=600000), hsa.HS_ERR_INVALID_ARG),
