@@ -20,6 +20,8 @@ host-link peak measured in the same run.  The JSON line also carries:
 entries) instead and reports attention throughput against the HBM roofline.
 --workload prefetch times whole decode steps over 8 layers sharing one selection (128
 requests, fp8), in serial order and with layer-wise prefetch.
+--workload sweep is the miss-count study: misses per selection for device buffers of 2048,
+4096 and 6144 slots under LRU, FIFO and RANDOM eviction (32 requests, 131072 tokens).
 """
 from __future__ import annotations
 
@@ -497,6 +499,80 @@ def bench_append_leg(args, torch, hsa, w, d_trace, miss_plain, stream, timed):
             "offload_sample": f"{nreq} requests x {count} rows of {w.entry_bytes} B"}
 
 
+def bench_sweep(args, torch, hsa):
+    """Misses per selection against device buffer size and eviction policy on the 32-request,
+    131072-token workload (the note's miss-count experiment, section 3 and Fig. 3), plus the
+    fetching LRU resolver's rate per buffer size."""
+    from synth import configs as C
+    from synth import kv as skv
+    from synth import trace as tr
+
+    w0 = C.SWEEP
+    steps = w0.steps
+    trace = tr.generate(w0.trace_spec(), steps=steps)      # one trace for every buffer size
+    d_trace = torch.from_numpy(trace).cuda()
+    warm = min(10, steps - 1)
+    stream = torch.cuda.Stream()
+    policies = (("lru", hsa.EVICT_LRU), ("fifo", hsa.EVICT_FIFO), ("random", hsa.EVICT_RANDOM))
+    study, fetch = {}, {}
+    for B in C.SWEEP_BUFFERS:
+        w = C.sweep_point(B)
+        study[B] = {}
+        for name, pol in policies:
+            hs = hsa.HiSparse(w.k, w.B, w.ratio, w.n, 1, w.layout, 0, hsa.FLAG_NO_IO, eviction=pol,
+                              eviction_seed=12345)
+            slots = torch.empty(w.n, w.k, dtype=torch.int32, device="cuda")
+            miss = torch.zeros(steps, w.n, dtype=torch.int32, device="cuda")
+            with torch.cuda.stream(stream):
+                for t in range(steps):
+                    hs.resolve(0, d_trace[t], slots, miss[t], stream=stream)
+            stream.synchronize()
+            m = miss.double()
+            study[B][name] = {"all_steps": m.mean().item(), "steady": m[warm:].mean().item()}
+            hs.close()
+            log(f"B {B} {name}: {study[B][name]}")
+        # the method's fetching resolver on the same trace: graph of the steady steps
+        hs = hsa.HiSparse(w.k, w.B, w.ratio, w.n, 1, w.layout, 0, 0)
+        for r in range(w.n):
+            ptr, cap, stride = hs.host_kv_ptr(0, r)
+            skv.fill_rows(w.seed, r, 0, 0, cap, w.layout, ptr, stride)
+        slots = torch.empty(w.n, w.k, dtype=torch.int32, device="cuda")
+        miss = torch.zeros(steps, w.n, dtype=torch.int32, device="cuda")
+        with torch.cuda.stream(stream):
+            for t in range(warm):
+                hs.resolve(0, d_trace[t], slots, miss[t], stream=stream)
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for t in range(warm, steps):
+                    hs.resolve(0, d_trace[t], slots, miss[t], stream=stream)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / (steps - warm)
+        mb = miss[warm:].double().sum().item() * w.entry_bytes / (steps - warm)
+        fetch[B] = {"us_per_step": ms * 1e3, "miss_fetch_GBps": mb / (ms / 1e3) / 1e9,
+                    "misses_per_selection": miss[warm:].double().mean().item()}
+        assert abs(fetch[B]["misses_per_selection"] - study[B]["lru"]["steady"]) < 1e-9
+        del g
+        hs.close()
+    return {
+        "metric": "misses per selection vs device buffer size and eviction policy, 1 MI355X",
+        "value": study[4096]["lru"]["steady"], "unit": "misses/selection (LRU, B 4096, steps >= 10)",
+        "n_gpus": 1, "steps": steps - warm, "warmup": warm, "ms_per_step": fetch[4096]["us_per_step"] / 1e3,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "i32", "data": "synthetic",
+        "config": {"workload": w0.description, "global_batch": w0.n, "seq_len": w0.ctx, "top_k": w0.k,
+                   "device_buffer_size": list(C.SWEEP_BUFFERS), "eviction_seed": 12345},
+        "study": {str(B): v for B, v in study.items()},
+        "lru_fetch": {str(B): v for B, v in fetch.items()},
+    }
+
+
 def bench_prefetch(args, torch, hsa, w):
     """Decode steps over 8 layers sharing a selection: serial order vs layer-wise prefetch."""
     from hierarchical_kv_cache_hs_amd.decode_step import DecodeSteps
@@ -585,7 +661,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=190)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="batch64", choices=["batch64", "fp8_256", "prefetch"])
+    ap.add_argument("--workload", default="batch64", choices=["batch64", "fp8_256", "prefetch", "sweep"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--summarize-profile", action="store_true",
@@ -636,6 +712,8 @@ def main():
             line["cpu_baseline"] = None
     elif args.workload == "prefetch":
         line = bench_prefetch(args, torch, hsa, C.PREFETCH)
+    elif args.workload == "sweep":
+        line = bench_sweep(args, torch, hsa)
     else:
         line = bench_attend(args, torch, hsa, C.FP8_256)
         line["cpu_baseline"] = None if args.no_cpu_baseline else \
