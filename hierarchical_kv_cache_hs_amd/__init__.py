@@ -34,7 +34,7 @@ DEVERR_DUPLICATE = 0x2
 HS_OK, HS_ERR_INVALID_ARG, HS_ERR_OUT_OF_MEMORY, HS_ERR_UNSUPPORTED, HS_ERR_HIP, HS_ERR_DEVICE = range(6)
 
 SYMBOLS = ("hs_create", "hs_resolve", "hs_resolve_tables", "hs_fetch_misses", "hs_attend", "hs_destroy",
-           "hs_append", "hs_offload",
+           "hs_append", "hs_offload", "hs_topk",
            "hs_device_bytes", "hs_host_bytes", "hs_host_kv",
            "hs_device_state", "hs_reset_requests", "hs_get_device_error", "hs_status_string",
            "hs_last_error_message")
@@ -79,6 +79,7 @@ def lib():
         L.hs_resolve_tables.argtypes = [p, i32, i32, p, p, p, p]
         L.hs_fetch_misses.argtypes = [p, i32, i32, p]
         L.hs_append.argtypes = [p, i32, i32, p, p, ctypes.c_int64, p, p]
+        L.hs_topk.argtypes = [p, i32, p, ctypes.c_int64, p, p, p]
         L.hs_offload.argtypes = [p, i32, i32, ctypes.c_int64, ctypes.c_int64, p, ctypes.c_int64, p]
         L.hs_attend.argtypes = [p, i32, i32, p, p, ctypes.c_float, p, p, p]
         L.hs_destroy.argtypes = [p]
@@ -230,6 +231,18 @@ class HiSparse:
         _check(lib().hs_append(self._h, layer, n_req, pos.data_ptr(), rows.data_ptr(), rows.stride(0),
                                slot_out.data_ptr(), _stream_ptr(stream)))
         return slot_out
+
+    def topk(self, scores: torch.Tensor, lens: torch.Tensor, sel: torch.Tensor | None = None, stream=None):
+        """hs_topk: scores float32 [n_req][stride] (stride % 4 == 0), lens int32 [n_req] -> sel [n_req][top_k]."""
+        n_req = scores.shape[0]
+        assert scores.dtype == torch.float32 and scores.dim() == 2 and scores.stride(1) == 1
+        assert lens.dtype == torch.int32 and lens.is_contiguous() and lens.shape[0] == n_req
+        if sel is None:
+            sel = torch.empty(n_req, self.top_k, dtype=torch.int32, device=scores.device)
+        assert sel.shape == (n_req, self.top_k) and sel.dtype == torch.int32 and sel.is_contiguous()
+        _check(lib().hs_topk(self._h, n_req, scores.data_ptr(), scores.stride(0), lens.data_ptr(), sel.data_ptr(),
+                             _stream_ptr(stream)))
+        return sel
 
     def offload(self, layer: int, request: int, first: int, rows: torch.Tensor, stream=None):
         """hs_offload: rows uint8 [count][>= entry bytes] on the device -> history positions first.."""

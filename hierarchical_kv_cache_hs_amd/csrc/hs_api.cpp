@@ -406,6 +406,19 @@ hs_status hs_offload(hs_handle* h, int32_t layer, int32_t request, int64_t first
   return HS_OK;
 }
 
+hs_status hs_topk(hs_handle* h, int32_t n_req, const float* d_scores, int64_t score_stride, const int32_t* d_len,
+                  int32_t* d_sel, void* stream) {
+  if (!h) return fail(HS_ERR_INVALID_ARG, "handle is NULL");
+  if (n_req < 0 || n_req > h->g.n) return fail(HS_ERR_INVALID_ARG, "n_req out of range");
+  if (n_req == 0) return HS_OK;
+  if (!d_scores || !d_len || !d_sel) return fail(HS_ERR_INVALID_ARG, "score, length or output pointer is NULL");
+  if (score_stride < 4 || score_stride % 4 || ((uintptr_t)d_scores) % 16)
+    return fail(HS_ERR_INVALID_ARG, "scores must be 16-byte aligned with a row stride that is a multiple of 4");
+  hipError_t e = hs::launch_topk(h->g, n_req, d_scores, score_stride, d_len, d_sel, h->err, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "top-k launch");
+  return HS_OK;
+}
+
 hs_status hs_reset_requests(hs_handle* h, int32_t first, int32_t count, void* stream) {
   if (!h) return fail(HS_ERR_INVALID_ARG, "handle is NULL");
   if (first < 0 || count < 0 || (int64_t)first + count > h->g.n) return fail(HS_ERR_INVALID_ARG, "request range");

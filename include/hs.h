@@ -187,6 +187,23 @@ hs_status hs_append(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* d
                     int64_t row_stride, int32_t* d_slot_out, void* stream);
 
 /*
+ * Top-k selection from indexer scores, the step that feeds hs_resolve (the note, section 2:
+ * the backend's indexer decides the selected set; paper abstract: indexer-agnostic).  For
+ * each request r < n_req, among positions 0 .. d_len[r]-1 of its score row (fp32, row r at
+ * d_scores + r * score_stride), the top_k positions of largest score, a tie going to the
+ * smaller position, are written to d_sel[r][0 .. top_k) in ascending position order; when
+ * d_len[r] < top_k every position is selected and the row is padded with -1.  The output is
+ * a valid hs_resolve selection.
+ *   d_scores  16-byte aligned; score_stride a multiple of 4, >= every d_len[r]; no NaN
+ *   d_len     [n_req] int32 in [0, min(capacity, score_stride)]; otherwise the row is all -1
+ *             and HS_DEVERR_TOKEN_RANGE is set
+ *   d_sel     [n_req][top_k] int32 out
+ * Enqueue-only, graph-capturable; touches no table.
+ */
+hs_status hs_topk(hs_handle* h, int32_t n_req, const float* d_scores, int64_t score_stride, const int32_t* d_len,
+                  int32_t* d_sel, void* stream);
+
+/*
  * Prefill offload: copies count rows (device memory, row_stride bytes apart) into positions
  * first .. first + count - 1 of request `request`'s history in the host pool (the note's
  * introduction: KV is actively offloaded to host memory).  Device tables are untouched: the
