@@ -20,6 +20,8 @@ host-link peak measured in the same run.  The JSON line also carries:
 entries) instead and reports attention throughput against the HBM roofline.
 --workload prefetch times whole decode steps over 8 layers sharing one selection (128
 requests, fp8), in serial order and with layer-wise prefetch.
+--workload topk runs the on-GPU top-k from synthetic indexer scores into the resolver, one
+selection per layer (128 requests, 8 layers, 65536 tokens).
 --workload sweep is the miss-count study: misses per selection for device buffers of 2048,
 4096 and 6144 slots under LRU, FIFO and RANDOM eviction (32 requests, 131072 tokens).
 """
@@ -573,6 +575,97 @@ def bench_sweep(args, torch, hsa):
     }
 
 
+def bench_topk(args, torch, hsa):
+    """On-GPU top-k from synthetic indexer scores feeding the resolver, one selection per layer
+    (128 requests, 8 layers, 65536-token contexts, k 2048, B 4096, fp8 entries).  Scores follow
+    the recipe of synth/scores.py -- per-(request, layer) importance, per-step noise 0.08,
+    +100 on the last 128 positions -- drawn on the device from a seeded generator."""
+    import oracle
+    from oracle.topk import topk as topk_oracle
+    n, L, ctx, k, B, W = 128, 8, 65536, 2048, 4096, 128
+    K, warm = min(args.steps, 10), min(args.warmup, 3)
+    T = warm + K
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4242)
+    imp = torch.randn(L, n, ctx, device="cuda", generator=gen)
+    scores = torch.empty(T, L, n, ctx, device="cuda")
+    for t in range(T):
+        scores[t] = imp + 0.08 * torch.randn(L, n, ctx, device="cuda", generator=gen)
+    scores[:, :, :, ctx - W:] += 100.0
+    del imp
+    lens = torch.full((n,), ctx, dtype=torch.int32, device="cuda")
+    hs = hsa.HiSparse(k, B, ctx // B, n, L, hsa.LAYOUT_FP8, 0, hsa.FLAG_NO_IO)
+    sel = torch.empty(T, L, n, k, dtype=torch.int32, device="cuda")
+    slots = torch.empty(L, n, k, dtype=torch.int32, device="cuda")
+    miss = torch.zeros(T, L, n, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+
+    def step(t):
+        for l in range(L):
+            hs.topk(scores[t, l], lens, sel[t, l], stream=stream)
+            hs.resolve(l, sel[t, l], slots[l], miss[t, l], stream=stream)
+
+    def timed(g):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    with torch.cuda.stream(stream):
+        for t in range(warm):
+            step(t)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for t in range(warm, T):
+                step(t)
+    step_ms = timed(g) / K
+    gt = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(gt, stream=stream):
+            for t in range(warm, T):
+                for l in range(L):
+                    hs.topk(scores[t, l], lens, sel[t, l], stream=stream)
+    topk_us = timed(gt) / (K * L) * 1e3
+    # a sampled check against the oracle, and the oracle's own rate on the same rows
+    rows = scores[T - 1, 3, :8].cpu().numpy()
+    t0 = time.perf_counter()
+    want = topk_oracle(rows, np.full(8, ctx), k)
+    cpu_s = time.perf_counter() - t0
+    ok = bool((sel[T - 1, 3, :8].cpu().numpy() == want).all())
+    bytes_launch = n * (ctx * 4 + k * 4 + 4)
+    achieved = bytes_launch / (topk_us * 1e-6) / 1e9
+    m = miss[warm:].double()
+    s_prev, s_last = sel[T - 2].cpu().numpy(), sel[T - 1].cpu().numpy()
+    churn = float(np.mean([k - np.intersect1d(s_prev[l, r], s_last[l, r]).size for l in range(L) for r in range(0, n, 16)]))
+    hs.close()
+    return {
+        "metric": "top-k selections/s from indexer scores (per layer) feeding the resolver, 1 MI355X",
+        "value": n * L / (step_ms / 1e3), "unit": "selections/s (top-k + resolve, no IO)",
+        "n_gpus": 1, "steps": K, "warmup": warm, "ms_per_step": step_ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{n} requests, {L} layers with their own selections, ctx {ctx}, k {k}, B {B}, "
+                               "fp8 656 B, indexer scores: importance + 0.08 noise + recency 128",
+                   "global_batch": n, "layers": L, "seq_len": ctx, "top_k": k},
+        "topk_us_per_launch": topk_us,
+        "resolve_noio_plus_topk_us_per_layer": step_ms * 1e3 / L,
+        "misses_per_selection": m.mean().item(),
+        "history_churn_per_step": churn,
+        "topk_verified_rows": ok,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": recorded_traffic("topk_c4", "topk.hip"),
+                     "kernel": "topk_kernel", "avg_kernel_us": topk_us, "algorithmic_bytes_per_launch": bytes_launch},
+        "cpu_baseline": {"value": 8 * k / cpu_s, "unit": "selected positions/s", "cores": 1, "kind": "oracle",
+                         "sample": f"oracle top-k (numpy stable sort) of 8 rows of {ctx} scores"},
+    }
+
+
 def bench_prefetch(args, torch, hsa, w):
     """Decode steps over 8 layers sharing a selection: serial order vs layer-wise prefetch."""
     from hierarchical_kv_cache_hs_amd.decode_step import DecodeSteps
@@ -661,7 +754,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=190)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="batch64", choices=["batch64", "fp8_256", "prefetch", "sweep"])
+    ap.add_argument("--workload", default="batch64", choices=["batch64", "fp8_256", "prefetch", "sweep", "topk"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--summarize-profile", action="store_true",
@@ -714,6 +807,8 @@ def main():
         line = bench_prefetch(args, torch, hsa, C.PREFETCH)
     elif args.workload == "sweep":
         line = bench_sweep(args, torch, hsa)
+    elif args.workload == "topk":
+        line = bench_topk(args, torch, hsa)
     else:
         line = bench_attend(args, torch, hsa, C.FP8_256)
         line["cpu_baseline"] = None if args.no_cpu_baseline else \

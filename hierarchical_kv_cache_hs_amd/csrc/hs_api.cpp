@@ -139,7 +139,9 @@ hs_status plan(const hs_config* cfg, hs::Geometry* g, Layout* lay) {
   ok = ok && take(LN * 4, &lay->ml_cnt);
   ok = ok && mul_ok(LN, (size_t)g->req_stride, &sz) && take(sz, &lay->buf);
   lay->total = off;
-  ok = ok && mul_ok(LN, (size_t)cap, &t) && mul_ok(t, (size_t)g->host_stride, &lay->host_total);
+  // no rows ever move in no-IO mode, so no host pool is allocated
+  lay->host_total = 0;
+  if (!(g->flags & HS_FLAG_NO_IO)) ok = ok && mul_ok(LN, (size_t)cap, &t) && mul_ok(t, (size_t)g->host_stride, &lay->host_total);
   if (!ok) return fail(HS_ERR_INVALID_ARG, "configuration sizes overflow");
   return HS_OK;
 }
@@ -230,16 +232,18 @@ hs_status hs_create(const hs_config* cfg, hs_handle** out) {
     release(h);
     return fail(HS_ERR_OUT_OF_MEMORY, "pinned host allocation failed (injected)");
   }
-  e = hipHostMalloc((void**)&h->host_pool, lay.host_total, hipHostMallocMapped | hipHostMallocPortable);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    h->host_pool = nullptr;
-    release(h);
-    return fail(HS_ERR_OUT_OF_MEMORY, "pinned host allocation failed");
+  if (lay.host_total > 0) {
+    e = hipHostMalloc((void**)&h->host_pool, lay.host_total, hipHostMallocMapped | hipHostMallocPortable);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      h->host_pool = nullptr;
+      release(h);
+      return fail(HS_ERR_OUT_OF_MEMORY, "pinned host allocation failed");
+    }
+    h->host_bytes = lay.host_total;
+    e = hipHostGetDevicePointer((void**)&h->host_pool_dev, h->host_pool, 0);
+    if (e != hipSuccess) { release(h); return fail_hip(e, "hipHostGetDevicePointer"); }
   }
-  h->host_bytes = lay.host_total;
-  e = hipHostGetDevicePointer((void**)&h->host_pool_dev, h->host_pool, 0);
-  if (e != hipSuccess) { release(h); return fail_hip(e, "hipHostGetDevicePointer"); }
 
   uint8_t* b = h->dev_block;
   h->err = (int32_t*)(b + lay.err);
@@ -258,6 +262,7 @@ hs_status hs_create(const hs_config* cfg, hs_handle** out) {
   hs::prepare_resolve();
   hs::prepare_attend();
   hs::prepare_append();
+  hs::prepare_topk();
   e = hipMemset(h->err, 0, sizeof(int32_t));
   if (e == hipSuccess)  // the zero row after each request's slots
     e = hipMemset2D(h->buf + (size_t)g.B * (size_t)g.slot_stride, (size_t)g.req_stride, 0, (size_t)g.slot_stride,
@@ -272,6 +277,12 @@ hs_status hs_create(const hs_config* cfg, hs_handle** out) {
 
 namespace {
 
+// Device-mapped address of a layer's host rows (null without a host pool, i.e. no-IO mode).
+uint8_t* host_layer_of(const hs_handle* h, int32_t layer) {
+  if (!h->host_pool_dev) return nullptr;
+  return h->host_pool_dev + (size_t)layer * h->g.n * (size_t)h->g.cap * (size_t)h->g.host_stride;
+}
+
 hs_status resolve_impl(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* d_sel, int32_t* d_slots,
                        int32_t* d_miss, bool list_only, void* stream) {
   if (!h) return fail(HS_ERR_INVALID_ARG, "handle is NULL");
@@ -280,7 +291,7 @@ hs_status resolve_impl(hs_handle* h, int32_t layer, int32_t n_req, const int32_t
   if (n_req == 0) return HS_OK;
   if (!d_sel || !d_slots) return fail(HS_ERR_INVALID_ARG, "selection or slot pointer is NULL");
   hs::LayerTables t = layer_tables(h, layer);
-  const uint8_t* host_layer = h->host_pool_dev + (size_t)layer * h->g.n * (size_t)h->g.cap * h->g.host_stride;
+  const uint8_t* host_layer = host_layer_of(h, layer);
   hipError_t e = hs::launch_resolve(h->g, t, layer, host_layer, n_req, d_sel, d_slots, d_miss, h->err, list_only,
                                     (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "resolve launch");
@@ -305,7 +316,7 @@ hs_status hs_fetch_misses(hs_handle* h, int32_t layer, int32_t n_req, void* stre
   if (n_req < 0 || n_req > h->g.n) return fail(HS_ERR_INVALID_ARG, "n_req out of range");
   if (n_req == 0) return HS_OK;
   hs::LayerTables t = layer_tables(h, layer);
-  const uint8_t* host_layer = h->host_pool_dev + (size_t)layer * h->g.n * (size_t)h->g.cap * h->g.host_stride;
+  const uint8_t* host_layer = host_layer_of(h, layer);
   hipError_t e = hs::launch_fetch(h->g, t, host_layer, n_req, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "fetch launch");
   return HS_OK;
@@ -337,6 +348,7 @@ hs_status hs_host_kv(hs_handle* h, int32_t layer, int32_t request, void** ptr, i
   if (!h || !ptr) return fail(HS_ERR_INVALID_ARG, "handle or ptr is NULL");
   if (layer < 0 || layer >= h->g.L || request < 0 || request >= h->g.n)
     return fail(HS_ERR_INVALID_ARG, "layer or request out of range");
+  if (!h->host_pool) return fail(HS_ERR_UNSUPPORTED, "no host pool in no-IO mode");
   const size_t rows = ((size_t)layer * h->g.n + (size_t)request) * (size_t)h->g.cap;
   *ptr = h->host_pool + rows * (size_t)h->g.host_stride;
   if (capacity) *capacity = h->g.cap;
@@ -373,7 +385,7 @@ hs_status hs_append(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* d
   if (row_stride < h->g.entry_bytes || row_stride % 16 || ((uintptr_t)d_rows) % 16)
     return fail(HS_ERR_INVALID_ARG, "rows must be 16-byte aligned, row_stride >= entry bytes and a multiple of 16");
   hs::LayerTables t = layer_tables(h, layer);
-  uint8_t* host_layer = h->host_pool_dev + (size_t)layer * h->g.n * (size_t)h->g.cap * h->g.host_stride;
+  uint8_t* host_layer = host_layer_of(h, layer);
   hipError_t e = hs::launch_append(h->g, t, host_layer, n_req, d_pos, d_rows, row_stride, d_slot_out, h->err,
                                    (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "append launch");
@@ -386,6 +398,7 @@ hs_status hs_offload(hs_handle* h, int32_t layer, int32_t request, int64_t first
   if (layer < 0 || layer >= h->g.L) return fail(HS_ERR_INVALID_ARG, "layer out of range");
   if (request < 0 || request >= h->g.n) return fail(HS_ERR_INVALID_ARG, "request out of range");
   if (first < 0 || count < 0 || first > h->g.cap - count) return fail(HS_ERR_INVALID_ARG, "positions out of range");
+  if (!h->host_pool) return fail(HS_ERR_UNSUPPORTED, "no host pool in no-IO mode");
   if (count == 0) return HS_OK;
   if (!d_rows) return fail(HS_ERR_INVALID_ARG, "row pointer is NULL");
   if (row_stride < h->g.entry_bytes) return fail(HS_ERR_INVALID_ARG, "row_stride below the entry size");

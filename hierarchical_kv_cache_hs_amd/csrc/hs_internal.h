@@ -74,6 +74,9 @@ hipError_t launch_append(const Geometry& g, const LayerTables& t, uint8_t* host_
 hipError_t launch_offload(const void* src, int64_t src_stride, uint8_t* dst_mapped, int64_t count, int64_t entry_bytes,
                           hipStream_t s);
 
+// Once per process, before the first top-k launch.
+void prepare_topk();
+
 // Top-k selection from indexer scores: for each request, the top_k positions of largest
 // score in [0, len[r]) (ties to the smaller position), ascending; -1 padding when len < k.
 hipError_t launch_topk(const Geometry& g, int32_t n_req, const float* scores, int64_t stride, const int32_t* len,

@@ -6,56 +6,140 @@
 // score -- a tie going to the smaller position -- written in ascending position order; when
 // len[r] < k every position is selected and the row is padded with -1.
 //
-// Design for gfx950.  One 1024-thread workgroup per request.  Scores map to 32-bit keys whose
-// unsigned order is the float order (-0 folded onto +0, so equal floats give equal keys).  A
-// most-significant-digit radix select finds the k-th largest key in three histogram passes
-// (12, 12 and 8 bits; LDS histograms, one digit group per thread for the search) and with it
-// how many of the keys equal to it are taken.  A last pass walks the positions in order; two
-// block scans per tile give each tied key its rank among ties and each selected position its
-// output index, so the output comes out sorted with no sort.  Four reads of the score row;
-// after the first they come from the L2 / last-level cache for the row sizes here.
+// Design for gfx950.  One 512-thread workgroup per request; rows of up to 2^18 positions.
+// Scores map to 32-bit keys whose unsigned order is the float order (-0 folded onto +0, so
+// equal floats give equal keys).  A most-significant-digit radix select, reading the row
+// twice:
+//   pass A   histogram of the top 12 key bits -> the digit d holding the k-th largest key;
+//   pass B   positions whose top digit exceeds d are set in an LDS selection bitmap; those
+//            whose top digit equals d (for scores like these, a percent or so of the row)
+//            are appended to an LDS candidate list (key, position), one wave scan and one
+//            LDS atomic per wave and batch;
+//   list     the next 12 and the last 8 key bits are resolved by histograms over the list,
+//            giving the k-th largest key exactly and how many keys equal to it are taken;
+//            candidates above it join the selection bitmap, those equal to it a tie bitmap;
+//   output   one block scan of (selected, tied) bit counts gives every thread its output
+//            offset -- ties before it that are taken = min(ties before it, ties needed) -- and
+//            the positions come out in order with no sort.
+// If the candidate list would overflow (many equal scores), the last two digits are resolved
+// with re-reads of the row instead.  Reads are batched: eight 16-byte loads per thread are in
+// flight before any is used.
 
 #include "hs_internal.h"
 
 namespace hs {
 namespace {
 
-constexpr int TT = 1024;       // threads per workgroup
-constexpr int TW = TT / 64;    // waves
-constexpr int V = 4;           // positions per thread per tile (one 16-byte load)
+constexpr int TT = 512;                   // threads per workgroup
+constexpr int TW = TT / 64;               // waves
+constexpr int V = 4;                      // positions per thread per tile (one 16-byte load)
 constexpr int TILE = TT * V;
-constexpr int NBIN = 4096;     // 12-bit digits
-static_assert(NBIN == 4 * TT, "one group of four bins per thread");
+constexpr int U = 8;                      // tiles per batch
+constexpr int NBIN = 4096;                // 12-bit digits
+constexpr int BPT = NBIN / TT;            // digits per thread in the search
+constexpr int MAXLEN = 1 << 18;           // positions per row
+constexpr int MAXW = MAXLEN / 32;         // bitmap words
+constexpr int CMAX = 8192;                // candidate list entries (the list also stages the output)
+static_assert(NBIN % TT == 0, "whole groups of digits per thread");
+static_assert(kMaxTopK <= 2 * CMAX, "the candidate list stages a row of output");
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr size_t topk_lds_bytes() {
+  return (NBIN + 2 * MAXW + 2 * CMAX) * sizeof(uint32_t);
+}
 
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t b = __float_as_uint(f);
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// key of a float given by its bits
+__device__ __forceinline__ uint32_t order_key(uint32_t b) {
   if (b == 0x80000000u) b = 0u;  // -0 equals +0
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
 // Inclusive scan of v over the workgroup; *total gets the sum.  Every thread must call.
-__device__ uint32_t block_scan_incl(uint32_t v, uint32_t* wtot, uint32_t* total) {
+template <typename T>
+__device__ T block_scan_incl(T v, T* wtot, T* total) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(v, o);
+    const T y = __shfl_up(v, o);
     if (lane >= o) v += y;
   }
   if (lane == 63) wtot[w] = v;
   __syncthreads();
-  uint32_t base = 0, tot = 0;
+  T base = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < TW; ++i) {
-    const uint32_t x = wtot[i];
-    base += (i < w) ? x : 0u;
+    const T x = wtot[i];
+    base += (i < w) ? x : (T)0;
     tot += x;
   }
   __syncthreads();
   *total = tot;
   return v + base;
+}
+
+// Calls batch(key, b0) for every batch of U tiles of the row, the loads of a batch all issued
+// first; this thread's key[j][e] is that of position b0 + j * TILE + 4 tid + e.  Positions
+// past the row get key 0, below every score's key (-inf maps to 0x007FFFFF).
+template <typename F>
+__device__ __forceinline__ void for_each_batch(const uint32_t* row, int n, F batch) {
+  const int tid = threadIdx.x;
+  for (int b0 = 0; b0 < n; b0 += TILE * U) {
+    u32x4 key[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {  // in bounds: p < n <= stride, p and stride multiples of 4
+      const int p = b0 + j * TILE + 4 * tid;
+      key[j] = p < n ? *(const u32x4*)(row + p) : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int p = b0 + j * TILE + 4 * tid;
+#pragma unroll
+      for (int e = 0; e < V; ++e) key[j][e] = (p + e < n) ? order_key(key[j][e]) : 0u;
+    }
+    batch(key, b0);
+  }
+}
+
+// for_each_batch, one key at a time: f(key, position)
+template <typename F>
+__device__ __forceinline__ void for_each_key(const uint32_t* row, int n, F f) {
+  const int tid = threadIdx.x;
+  for_each_batch(row, n, [&](u32x4 (&key)[U], int b0) {
+#pragma unroll
+    for (int j = 0; j < U; ++j)
+#pragma unroll
+      for (int e = 0; e < V; ++e) f(key[j][e], b0 + j * TILE + 4 * tid + e);
+  });
+}
+
+// The digit of histogram h holding the need-th largest key (counting from the top) and the
+// number of keys above that digit.  Every thread must call.
+__device__ __forceinline__ void find_digit(const uint32_t* h, int dtop, uint32_t need, uint32_t* wtot,
+                                           uint32_t* s_digit, uint32_t* s_above) {
+  const int tid = threadIdx.x;
+  uint32_t cnt[BPT], csum = 0;
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) {
+    const int d = dtop - BPT * tid - q;  // this thread's digits, descending
+    cnt[q] = d >= 0 ? h[d] : 0u;
+    csum += cnt[q];
+  }
+  uint32_t total;
+  const uint32_t incl = block_scan_incl<uint32_t>(csum, wtot, &total);
+  uint32_t run = incl - csum;
+  if (run < need && need <= incl) {
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+      if (run < need && need <= run + cnt[q]) {
+        *s_digit = (uint32_t)(dtop - BPT * tid - q);
+        *s_above = run;
+      }
+      run += cnt[q];
+    }
+  }
+  __syncthreads();
 }
 
 struct TopkArgs {
@@ -69,15 +153,22 @@ struct TopkArgs {
 };
 
 __global__ __launch_bounds__(TT) void topk_kernel(TopkArgs a) {
-  __shared__ uint32_t hist[NBIN];
+  extern __shared__ uint32_t lds[];
+  uint32_t* hist = lds;                  // [NBIN]
+  uint32_t* selmap = hist + NBIN;        // [MAXW] positions taken for sure
+  uint32_t* tiemap = selmap + MAXW;      // [MAXW] positions holding the k-th largest key
+  uint32_t* ckey = tiemap + MAXW;        // [CMAX] candidates: keys
+  uint32_t* cpos = ckey + CMAX;          //        and positions
   __shared__ uint32_t wtot[TW];
-  __shared__ uint32_t s_digit, s_above;
+  __shared__ uint64_t wtot64[TW];
+  __shared__ uint32_t s_digit, s_above, s_ncand;
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int k = a.k;
   int32_t* out = a.sel + (int64_t)r * k;
-  int64_t len = a.len[r];
-  if (len < 0 || len > a.cap || len > a.stride) {
+  const int64_t len = a.len[r];
+  if (len < 0 || len > a.cap || len > a.stride || len > MAXLEN) {
     if (tid == 0) atomicOr(a.err, (int32_t)HS_DEVERR_TOKEN_RANGE);
     for (int i = tid; i < k; i += TT) out[i] = -1;
     return;
@@ -86,56 +177,90 @@ __global__ __launch_bounds__(TT) void topk_kernel(TopkArgs a) {
     for (int i = tid; i < k; i += TT) out[i] = (i < len) ? i : -1;
     return;
   }
-  const float* row = a.scores + (int64_t)r * a.stride;
+  const int n = (int)len;
+  const int nw = (n + 31) >> 5;
+  const uint32_t* row = (const uint32_t*)(a.scores + (int64_t)r * a.stride);
 
-  // ---- radix select: digits of 12, 12 and 8 bits from the top
-  uint32_t prefix = 0;  // key bits fixed so far
-  uint32_t need = (uint32_t)k;  // keys still to take among those matching the prefix
-  int fixed = 0;        // number of fixed bits
-  for (int level = 0; level < 3; ++level) {
-    const int bits = level < 2 ? 12 : 8;
+  // ---- pass A: top digit
+  for (int i = tid; i < NBIN; i += TT) hist[i] = 0u;
+  for (int i = tid; i < nw; i += TT) {
+    selmap[i] = 0u;
+    tiemap[i] = 0u;
+  }
+  if (tid == 0) s_ncand = 0;
+  __syncthreads();
+  // padding (key 0) lands in digit 0, which the search never reaches since len > k
+  for_each_key(row, n, [&](uint32_t u, int) { atomicAdd(&hist[u >> 20], 1u); });
+  __syncthreads();
+  find_digit(hist, NBIN - 1, (uint32_t)k, wtot, &s_digit, &s_above);
+  const uint32_t d1 = s_digit;
+  uint32_t need = (uint32_t)k - s_above;  // keys to take among those with top digit d1
+
+  // ---- pass B: above d1 -> selection bitmap; equal to d1 -> candidate list.  A thread masks
+  // its candidates in a batch; one wave scan and one LDS atomic per wave place them.
+  for_each_batch(row, n, [&](u32x4 (&key)[U], int b0) {
+    uint32_t cmask = 0;
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      // a thread's four positions of a tile share one bitmap word: one atomic per tile
+      const int p = b0 + j * TILE + 4 * tid;
+      uint32_t nib = 0;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const uint32_t u = key[j][e];
+        nib |= ((u >> 20) > d1 ? 1u : 0u) << e;
+        cmask |= ((u >> 20) == d1 && u != 0u ? 1u : 0u) << (j * V + e);
+      }
+      if (nib) atomicOr(&selmap[p >> 5], nib << (p & 31));
+    }
+    const uint32_t c = __popc(cmask);
+    uint32_t incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    uint32_t base = 0;
+    if (lane == 63 && incl) base = atomicAdd(&s_ncand, incl);
+    uint32_t idx = __shfl(base, 63) + incl - c;
+    // candidates are rare: walk the set bits and take each score again (an L2 hit) rather
+    // than branching over every slot of the batch
+    while (cmask) {
+      const int sb = __ffs(cmask) - 1;
+      cmask &= cmask - 1u;
+      const int p = b0 + (sb / V) * TILE + 4 * tid + (sb % V);
+      if (idx < (uint32_t)CMAX) {
+        ckey[idx] = order_key(row[p]);
+        cpos[idx] = (uint32_t)p;
+      }
+      ++idx;
+    }
+  });
+  __syncthreads();
+  const uint32_t ncand = s_ncand;
+  const bool overflow = ncand > (uint32_t)CMAX;
+
+  // ---- the next 12 bits, then the last 8: over the list, or over the row on overflow
+  uint32_t prefix = d1;
+  int fixed = 12;
+  for (int level = 0; level < 2; ++level) {
+    const int bits = level == 0 ? 12 : 8;
     const int shift = 32 - fixed - bits;
     const uint32_t dmask = (1u << bits) - 1u;
     for (int i = tid; i < NBIN; i += TT) hist[i] = 0u;
     __syncthreads();
-    for (int64_t base = 0; base < len; base += TILE) {
-      const int64_t p0 = base + (int64_t)tid * V;
-      if (p0 < len) {
-        const f32x4 v = *(const f32x4*)(row + p0);
-#pragma unroll
-        for (int e = 0; e < V; ++e) {
-          if (p0 + e < len) {
-            const uint32_t u = order_key(v[e]);
-            const bool match = fixed == 0 || (u >> (32 - fixed)) == prefix;
-            if (match) atomicAdd(&hist[(u >> shift) & dmask], 1u);
-          }
-        }
+    if (!overflow) {
+      for (uint32_t i = tid; i < ncand; i += TT) {
+        const uint32_t u = ckey[i];
+        if ((u >> (32 - fixed)) == prefix) atomicAdd(&hist[(u >> shift) & dmask], 1u);
       }
+    } else {
+      for_each_key(row, n, [&](uint32_t u, int) {
+        if (u != 0u && (u >> (32 - fixed)) == prefix) atomicAdd(&hist[(u >> shift) & dmask], 1u);
+      });
     }
     __syncthreads();
-    // thread t owns digits dtop-4t .. dtop-4t-3 (descending); counts from the top digit down
-    const int dtop = (int)dmask;
-    uint32_t c[4], csum = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int d = dtop - 4 * tid - q;
-      c[q] = d >= 0 ? hist[d] : 0u;
-      csum += c[q];
-    }
-    uint32_t total;
-    const uint32_t incl = block_scan_incl(csum, wtot, &total);
-    uint32_t run = incl - csum;  // keys with a larger digit than this thread's first
-    if (run < need && need <= incl) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (run < need && need <= run + c[q]) {
-          s_digit = (uint32_t)(dtop - 4 * tid - q);
-          s_above = run;
-        }
-        run += c[q];
-      }
-    }
-    __syncthreads();
+    find_digit(hist, (int)dmask, need, wtot, &s_digit, &s_above);
     prefix = (prefix << bits) | s_digit;
     need -= s_above;
     fixed += bits;
@@ -143,53 +268,80 @@ __global__ __launch_bounds__(TT) void topk_kernel(TopkArgs a) {
   }
   const uint32_t thr = prefix;  // the k-th largest key; `need` of the keys equal to it are taken
 
-  // ---- positions in order: ties ranked by position, selected positions compacted
-  uint32_t eq_run = 0, sel_run = 0;
-  for (int64_t base = 0; base < len; base += TILE) {
-    const int64_t p0 = base + (int64_t)tid * V;
-    uint32_t u[V];
-    bool ok[V];
-    if (p0 < len) {
-      const f32x4 v = *(const f32x4*)(row + p0);
-#pragma unroll
-      for (int e = 0; e < V; ++e) {
-        ok[e] = p0 + e < len;
-        u[e] = order_key(v[e]);
+  // ---- candidates above thr are taken; those equal to it are ties
+  if (!overflow) {
+    for (uint32_t i = tid; i < ncand; i += TT) {
+      const uint32_t u = ckey[i], p = cpos[i];
+      if (u > thr) atomicOr(&selmap[p >> 5], 1u << (p & 31));
+      else if (u == thr) atomicOr(&tiemap[p >> 5], 1u << (p & 31));
+    }
+  } else {
+    for_each_key(row, n, [&](uint32_t u, int p) {
+      if ((u >> 20) == d1 && u > thr) atomicOr(&selmap[p >> 5], 1u << (p & 31));
+      else if (u == thr) atomicOr(&tiemap[p >> 5], 1u << (p & 31));
+    });
+  }
+  __syncthreads();
+
+  // ---- output: each thread's consecutive bitmap words, in position order (the words are
+  // spread over all threads: ceil(words / threads) each), staged in LDS (the candidate list
+  // is no longer needed) and stored in whole rows
+  uint32_t* obuf = ckey;  // [k] <= 2 CMAX entries
+  const int wpt = (nw + TT - 1) / TT;
+  const int w0 = tid * wpt;
+  const int w1 = min(nw, w0 + wpt);
+  uint32_t ns = 0, nt = 0;
+  for (int w = w0; w < w1; ++w) {
+    ns += __popc(selmap[w]);
+    nt += __popc(tiemap[w]);
+  }
+  const uint64_t mine = ((uint64_t)ns << 32) | nt;
+  uint64_t tot;
+  const uint64_t excl = block_scan_incl<uint64_t>(mine, wtot64, &tot) - mine;
+  uint32_t tie_before = (uint32_t)excl;
+  uint32_t o = (uint32_t)(excl >> 32) + min(tie_before, need);
+  for (int w = w0; w < w1; ++w) {
+    uint32_t t = tiemap[w];
+    // ties are taken in position order while fewer than `need` came before
+    const uint32_t room = need > tie_before ? need - tie_before : 0u;
+    const uint32_t nt_w = __popc(t);
+    tie_before += nt_w;
+    if (nt_w > room) {  // keep the first `room` set bits of t
+      uint32_t keep = 0;
+      for (uint32_t q = 0; q < room; ++q) {
+        keep |= t & (~t + 1u);  // lowest set bit
+        t &= t - 1u;
       }
+      t = keep;
+    }
+    const uint32_t m = selmap[w] | t;
+    // every selected position of the word at once: offset = selected positions below it
+#pragma unroll
+    for (int b = 0; b < 32; ++b) {
+      const uint32_t idx = o + __popc(m & ((1u << b) - 1u));
+      if (((m >> b) & 1u) && idx < (uint32_t)k) obuf[idx] = (uint32_t)(w * 32 + b);
+    }
+    o += __popc(m);
+  }
+  __syncthreads();
+  // the whole row of k positions leaves in 16-byte stores when it is aligned
+  const bool vec = (k & 3) == 0 && ((uintptr_t)out & 15u) == 0;
+  for (int i = 4 * tid; i < k; i += 4 * TT) {
+    if (vec) {
+      *(u32x4*)(out + i) = *(const u32x4*)(obuf + i);
     } else {
-#pragma unroll
-      for (int e = 0; e < V; ++e) {
-        ok[e] = false;
-        u[e] = 0u;
-      }
+      for (int e = i; e < min(k, i + 4); ++e) out[e] = (int32_t)obuf[e];
     }
-    uint32_t neq = 0;
-#pragma unroll
-    for (int e = 0; e < V; ++e) neq += (ok[e] && u[e] == thr) ? 1u : 0u;
-    uint32_t teq;
-    uint32_t tie = eq_run + block_scan_incl(neq, wtot, &teq) - neq;  // ties before this thread's
-    bool take[V];
-    uint32_t nsel = 0;
-#pragma unroll
-    for (int e = 0; e < V; ++e) {
-      take[e] = false;
-      if (ok[e]) {
-        if (u[e] > thr) take[e] = true;
-        else if (u[e] == thr) take[e] = tie++ < need;
-      }
-      nsel += take[e] ? 1u : 0u;
-    }
-    uint32_t tsel;
-    uint32_t o = sel_run + block_scan_incl(nsel, wtot, &tsel) - nsel;
-#pragma unroll
-    for (int e = 0; e < V; ++e)
-      if (take[e] && o < (uint32_t)k) out[o++] = (int32_t)(p0 + e);
-    eq_run += teq;
-    sel_run += tsel;
   }
 }
 
 }  // namespace
+
+void prepare_topk() {
+  (void)hipFuncSetAttribute((const void*)topk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)topk_lds_bytes());
+  (void)hipGetLastError();
+}
 
 hipError_t launch_topk(const Geometry& g, int32_t n_req, const float* scores, int64_t stride, const int32_t* len,
                        int32_t* sel, int32_t* err, hipStream_t s) {
@@ -201,7 +353,7 @@ hipError_t launch_topk(const Geometry& g, int32_t n_req, const float* scores, in
   a.err = err;
   a.cap = g.cap;
   a.k = g.k;
-  hipLaunchKernelGGL(topk_kernel, dim3(n_req), dim3(TT), 0, s, a);
+  hipLaunchKernelGGL(topk_kernel, dim3(n_req), dim3(TT), topk_lds_bytes(), s, a);
   return hipGetLastError();
 }
 

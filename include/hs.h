@@ -54,7 +54,9 @@ typedef enum hs_kv_layout {
 
 /* Handle flags (hs_config.flags). */
 #define HS_FLAG_NO_IO 0x1u /* resolve updates every table but moves no row: measures the
-                              resolution cost alone (the paper's no-IO oracle) */
+                              resolution cost alone (the paper's no-IO oracle); no host
+                              pool is allocated (hs_host_bytes reports 0, hs_host_kv and
+                              hs_offload return HS_ERR_UNSUPPORTED) */
 
 /*
  * Eviction policies.  LRU is the method (paper abstract; note, section 2); the others exist
@@ -121,7 +123,7 @@ typedef struct hs_state_view {
 /* Bytes the device block must have for this configuration (0 and an error if invalid). */
 hs_status hs_device_bytes(const hs_config* cfg, size_t* bytes);
 
-/* Bytes of the pinned host pool for this configuration. */
+/* Bytes of the pinned host pool for this configuration (0 with HS_FLAG_NO_IO). */
 hs_status hs_host_bytes(const hs_config* cfg, size_t* bytes);
 
 /*
@@ -195,8 +197,8 @@ hs_status hs_append(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* d
  * d_len[r] < top_k every position is selected and the row is padded with -1.  The output is
  * a valid hs_resolve selection.
  *   d_scores  16-byte aligned; score_stride a multiple of 4, >= every d_len[r]; no NaN
- *   d_len     [n_req] int32 in [0, min(capacity, score_stride)]; otherwise the row is all -1
- *             and HS_DEVERR_TOKEN_RANGE is set
+ *   d_len     [n_req] int32 in [0, min(capacity, score_stride, 2^18)]; otherwise the row is
+ *             all -1 and HS_DEVERR_TOKEN_RANGE is set
  *   d_sel     [n_req][top_k] int32 out
  * Enqueue-only, graph-capturable; touches no table.
  */
@@ -237,8 +239,9 @@ hs_status hs_destroy(hs_handle* h);
 /*
  * Host rows of (layer, request): *ptr = first of `*capacity` rows, `*row_stride`
  * bytes apart, in pinned memory owned by the handle (valid until hs_destroy).
- * The caller writes a token's row before any selection names it (prefill
- * offload / decode append); the library only reads this memory.
+ * The caller writes a token's row before any selection names it, directly or
+ * through hs_offload / hs_append; resolves read it for misses.
+ * HS_ERR_UNSUPPORTED with HS_FLAG_NO_IO (no host pool).
  */
 hs_status hs_host_kv(hs_handle* h, int32_t layer, int32_t request, void** ptr, int64_t* capacity,
                      int64_t* row_stride);

@@ -75,6 +75,11 @@ def test_sizes_for_the_batch64_workload():
     assert slots + tables <= dev <= slots + tables + 64 * 1024
 
 
+def test_no_io_mode_has_no_host_pool():
+    assert hsa.host_bytes(_cfg(flags=hsa.FLAG_NO_IO)) == 0
+    assert hsa.host_bytes(_cfg()) == 2 * 128 * 32 * 1152
+
+
 def test_null_arguments():
     L = hsa.lib()
     assert L.hs_destroy(None) == hsa.HS_OK

@@ -137,7 +137,8 @@ def test_no_io_mode_same_tables_no_rows():
     b = hsa.HiSparse(64, 128, 32, 3, flags=hsa.FLAG_NO_IO)
     try:
         fill_host_pool(a, w.seed)
-        fill_host_pool(b, w.seed)
+        with pytest.raises(hsa.HSError):          # no host pool in no-IO mode
+            b.host_kv_ptr(0, 0)
         b.state(0)["kv_buffer"].zero_()
         for t in range(x.shape[0]):
             sel = torch.from_numpy(x[t]).cuda()
