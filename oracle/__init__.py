@@ -14,6 +14,15 @@ method defines it: page table, slot owner map, recency stamps, step counter and
 Pinned by tests/test_oracle_pins.py (closed forms, brute force over
 presentation orders, a textbook LRU for k = 1, torch fp64 attention, the
 torch E4M3FN decode table, and the exactness property of the paper abstract).
+
+Page-granular selections (paper abstract: the method is evaluated with the NSA and
+Quest families, which select blocks of consecutive tokens): with ``page_tokens`` P > 1
+the cached unit is a page of P consecutive tokens -- the page table maps page -> slot,
+a slot holds the P rows of its page, a miss fetches the whole page, and the same
+replacement rule applies to pages.  Attention then runs over every token of the
+resolved pages (:meth:`OracleCache.attend`), or over those before each request's
+context length (:meth:`OracleCache.attend_pages`).  Pinned by
+tests/test_oracle_page_pins.py.
 """
 from __future__ import annotations
 
@@ -92,25 +101,30 @@ def default_threads() -> int:
 class OracleCache:
     """Per-(request, layer) cache states, resolved and attended by the C oracle.
 
-    host: optional [n][L][cap][E] uint8 array holding each request's full KV
-    history; when given, the oracle also keeps the device-slot bytes
-    ``dev[n][L][B][E]`` and fills them on every miss.  policy: LRU (the method), or FIFO /
-    RANDOM (seeded) for the eviction-policy study.
+    host: optional [n][L][cap * page_tokens][E] uint8 array holding each request's
+    full KV history, one row per token; when given, the oracle also keeps the device-slot
+    bytes ``dev[n][L][B][page_tokens * E]`` and fills them on every miss.  policy: LRU
+    (the method), or FIFO / RANDOM (seeded) for the eviction-policy study.
+
+    page_tokens P: tokens per cached unit.  With P > 1, selections, B and cap count pages
+    (page c = tokens cP .. cP + P - 1) and every table entry is a page.
     """
 
     def __init__(self, n: int, L: int, B: int, cap: int, layout: int = 0, host: np.ndarray | None = None,
-                 threads: int | None = None, policy: int = LRU, seed: int = 0):
-        if B <= 0 or cap <= 0 or n <= 0 or L <= 0:
+                 threads: int | None = None, policy: int = LRU, seed: int = 0, page_tokens: int = 1):
+        if B <= 0 or cap <= 0 or n <= 0 or L <= 0 or page_tokens <= 0:
             raise OracleError("bad shape")
         self.n, self.L, self.B, self.cap, self.layout = n, L, B, cap, layout
-        self.E = ENTRY_BYTES[layout]
+        self.P = page_tokens
+        self.E_tok = ENTRY_BYTES[layout]
+        self.E = self.E_tok * self.P          # bytes of one cached unit: the P rows of a page, in order
         self.PT = np.full((n, L, cap), -1, dtype=np.int32)
         self.RM = np.full((n, L, B), -1, dtype=np.int32)
         self.ST = np.full((n, L, B), -1, dtype=np.int64)
         self.t = np.zeros((n, L), dtype=np.int64)
         self.host = host
         if host is not None:
-            assert host.shape == (n, L, cap, self.E) and host.dtype == np.uint8 and host.flags.c_contiguous
+            assert host.shape == (n, L, cap * self.P, self.E_tok) and host.dtype == np.uint8 and host.flags.c_contiguous
             self.dev = np.zeros((n, L, B, self.E), dtype=np.uint8)
         else:
             self.dev = None
@@ -151,6 +165,8 @@ class OracleCache:
         Each row goes to the host history (``host``, when kept) and the token becomes
         resident (``orc_append``); returns the slot of each appended token (-1 for none).
         The step counters do not move: the stamp given is the next resolve's step."""
+        if self.P != 1:
+            raise OracleError("append is defined for token-granular caches only")
         pos = np.ascontiguousarray(pos, dtype=np.int32)
         rows = np.ascontiguousarray(rows, dtype=np.uint8)
         assert rows.shape == (pos.shape[0], self.E)
@@ -177,7 +193,11 @@ class OracleCache:
         return out
 
     def attend(self, layer: int, q: np.ndarray, slots: np.ndarray, scale: float):
-        """q[n_req][H][576] bf16 bits (uint16) -> (out[n_req][H][512] f64, lse[n_req][H] f64)."""
+        """q[n_req][H][576] bf16 bits (uint16) -> (out[n_req][H][512] f64, lse[n_req][H] f64).
+
+        With pages, every token of every resolved page takes part."""
+        if self.P != 1:
+            return self.attend_pages(layer, q, slots, None, None, scale)
         if self.dev is None:
             raise OracleError("attention needs the slot bytes (construct with host=...)")
         q = np.ascontiguousarray(q, dtype=np.uint16)
@@ -185,6 +205,41 @@ class OracleCache:
         nr, H = q.shape[0], q.shape[1]
         dev = np.ascontiguousarray(self.dev[:nr, layer])
         return attend_rows(q, slots, dev, self.layout, scale, self.threads)
+
+    def attend_pages(self, layer: int, q: np.ndarray, slots: np.ndarray, sel: np.ndarray | None,
+                     lens: np.ndarray | None, scale: float):
+        """Attention over the tokens of the resolved pages: slots[n_req][k] page slots (-1
+        skipped); with sel (the page selection) and lens (context length in tokens per
+        request), only tokens at positions < lens[r] take part."""
+        if self.dev is None:
+            raise OracleError("attention needs the slot bytes (construct with host=...)")
+        q = np.ascontiguousarray(q, dtype=np.uint16)
+        nr = q.shape[0]
+        idx = page_token_rows(slots, sel, lens, self.P)
+        rows = np.ascontiguousarray(self.dev[:nr, layer]).reshape(nr, self.B * self.P, self.E_tok)
+        return attend_rows(q, idx, rows, self.layout, scale, self.threads)
+
+
+def page_token_rows(slots: np.ndarray, sel: np.ndarray | None, lens: np.ndarray | None, P: int) -> np.ndarray:
+    """Token rows of the resolved pages, in selection order: entry i * P + o is row
+    slots[r][i] * P + o of the request's slot rows (a slot holds its page's P rows in
+    position order), or -1 when the page is padding or, given sel and lens, when its
+    position sel[r][i] * P + o is not below lens[r]."""
+    slots = np.asarray(slots)
+    n, k = slots.shape
+    idx = np.full((n, k * P), -1, dtype=np.int32)
+    for r in range(n):
+        for i in range(k):
+            j = int(slots[r, i])
+            if j < 0:
+                continue
+            for o in range(P):
+                if sel is not None:
+                    c = int(sel[r, i])
+                    if c < 0 or c * P + o >= int(lens[r]):
+                        continue
+                idx[r, i * P + o] = j * P + o
+    return idx
 
 
 def attend_rows(q: np.ndarray, idx: np.ndarray, rows: np.ndarray, layout: int, scale: float,
