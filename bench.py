@@ -22,6 +22,8 @@ entries) instead and reports attention throughput against the HBM roofline.
 requests, fp8), in serial order and with layer-wise prefetch.
 --workload topk runs the on-GPU top-k from synthetic indexer scores into the resolver, one
 selection per layer (128 requests, 8 layers, 65536 tokens).
+--workload pages runs page-granular selections (pages of 16 tokens, 128 pages selected, 256
+page slots, 256 requests, fp8): whole steps of resolve + attention cut at the context length.
 --workload sweep is the miss-count study: misses per selection for device buffers of 2048,
 4096 and 6144 slots under LRU, FIFO and RANDOM eviction (32 requests, 131072 tokens).
 """
@@ -666,6 +668,171 @@ def bench_topk(args, torch, hsa):
     }
 
 
+def cpu_baseline_pages(w, trace, warm, budget_s=15.0, requests=16):
+    """The oracle, as it stands, on whole steps of the page workload for a sample of requests:
+    page resolve (tables + page copies) then fp64 attention cut at the context length."""
+    import oracle
+    from synth import kv as skv
+    P = w.page_tokens
+    n = min(requests, w.n)
+    host = np.empty((n, 1, w.cap * P, w.entry_bytes), dtype=np.uint8)
+    for r in range(n):
+        skv.fill_rows(w.seed, r, 0, 0, w.cap * P, w.layout, host[r, 0].ctypes.data, w.entry_bytes)
+    threads = oracle.default_threads()
+    oc = oracle.OracleCache(n, 1, w.B, w.cap, layout=w.layout, host=host, threads=threads, page_tokens=P)
+    for t in range(warm):
+        oc.resolve(0, trace[t, :n])
+    done, el, t = 0, 0.0, warm
+    while (done == 0 or el < budget_s) and t < trace.shape[0]:
+        q = skv.queries(w.seed, t % 8, n, 0, 16)
+        lens = np.full(n, w.len_tokens(t))
+        t0 = time.perf_counter()
+        slots, _ = oc.resolve(0, trace[t, :n])
+        oc.attend_pages(0, q, slots, trace[t, :n], lens, 1.0 / math.sqrt(576))
+        el += time.perf_counter() - t0
+        done += 1
+        t += 1
+    return {"value": n * done * w.k * P / el, "unit": "attended tokens/s (resolve + attention)", "cores": threads,
+            "kind": "oracle",
+            "sample": f"oracle page resolve + fp64 attention of requests 0..{n - 1} on steps {warm}..{t - 1} "
+                      f"({done} steps, {el:.1f} s)"}
+
+
+def bench_pages(args, torch, hsa, w):
+    """Page-granular selections: whole steps of resolve + attention cut at the context length."""
+    from synth import kv as skv
+    from synth import trace as tr
+
+    P = w.page_tokens
+    K = args.steps
+    T = args.warmup + K
+    trace = tr.generate(w.with_(steps=max(T, w.steps)).trace_spec(), steps=T)
+    d_trace = torch.from_numpy(trace).cuda()
+    lens = torch.tensor([[w.len_tokens(t)] * w.n for t in range(T)], dtype=torch.int32, device="cuda")
+    hs = hsa.HiSparse(w.k, w.B, w.ratio, w.n, 1, w.layout, 16, 0, page_tokens=P)
+    t0 = time.perf_counter()
+    for r in range(w.n):
+        ptr, cap, stride = hs.host_kv_ptr(0, r)
+        skv.fill_rows(w.seed, r, 0, 0, cap, w.layout, ptr, stride)
+    log(f"host pool {hsa.host_bytes(hs.cfg) / 2**30:.2f} GiB filled in {time.perf_counter() - t0:.1f}s")
+    qs = torch.from_numpy(np.stack([skv.queries(w.seed, t % 8, w.n, 0, 16) for t in range(8)]).view(np.int16)) \
+        .cuda().view(torch.bfloat16)
+    slots = torch.empty(T, w.n, w.k, dtype=torch.int32, device="cuda")
+    miss = torch.zeros(T, w.n, dtype=torch.int32, device="cuda")
+    miss_r = torch.zeros(T, w.n, dtype=torch.int32, device="cuda")
+    out = torch.empty(w.n, 16, 512, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(w.n, 16, dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(576)
+    stream = torch.cuda.Stream()
+
+    def timed(g):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    def warm(h, m, attend):
+        with torch.cuda.stream(stream):
+            for t in range(args.warmup):
+                h.resolve(0, d_trace[t], slots[t], m[t], stream=stream)
+                if attend:
+                    h.attend_pages(0, qs[t % 8], slots[t], d_trace[t], lens[t], scale, out, lse, stream=stream)
+        stream.synchronize()
+
+    # resolve alone (the fused kernel: tables and page copies), from an empty cache
+    warm(hs, miss_r, False)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for t in range(args.warmup, T):
+                hs.resolve(0, d_trace[t], slots[t], miss_r[t], stream=stream)
+    resolve_us = timed(g) / K * 1e3
+    del g
+    # whole steps, from an empty cache again
+    hs.reset_requests(0, w.n)
+    torch.cuda.synchronize()
+    warm(hs, miss, True)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for t in range(args.warmup, T):
+                hs.resolve(0, d_trace[t], slots[t], miss[t], stream=stream)
+                hs.attend_pages(0, qs[t % 8], slots[t], d_trace[t], lens[t], scale, out, lse, stream=stream)
+    region_ms = timed(g)
+    del g
+    assert torch.equal(miss, miss_r)
+    # attention alone, cold (a 1 GiB read before each launch evicts the rows from the caches)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    att_ms = []
+    with torch.cuda.stream(stream):
+        for t in range(args.warmup, T):
+            flush.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            hs.attend_pages(0, qs[t % 8], slots[t], d_trace[t], lens[t], scale, out, lse, stream=stream)
+            b.record(stream)
+            b.synchronize()
+            att_ms.append(a.elapsed_time(b))
+    del flush
+    # resolution alone: a handle that moves no rows
+    hs_noio = hsa.HiSparse(w.k, w.B, w.ratio, w.n, 1, w.layout, 0, hsa.FLAG_NO_IO, page_tokens=P)
+    miss_n = torch.zeros(T, w.n, dtype=torch.int32, device="cuda")
+    slots_n = torch.empty(w.n, w.k, dtype=torch.int32, device="cuda")
+    with torch.cuda.stream(stream):
+        for t in range(args.warmup):
+            hs_noio.resolve(0, d_trace[t], slots_n, miss_n[t], stream=stream)
+    stream.synchronize()
+    gn = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(gn, stream=stream):
+            for t in range(args.warmup, T):
+                hs_noio.resolve(0, d_trace[t], slots_n, miss_n[t], stream=stream)
+    noio_us = timed(gn) / K * 1e3
+    del gn
+    assert torch.equal(miss_n[args.warmup:], miss[args.warmup:])
+    hs_noio.close()
+
+    att_s = float(np.mean(att_ms)) / 1e3
+    # attended rows per launch: valid pages' tokens below the context length
+    S = d_trace[args.warmup:].long()
+    off = torch.arange(P, device="cuda")
+    tok = S[..., None] * P + off
+    ok = (S[..., None] >= 0) & (tok < lens[args.warmup:, :, None, None])
+    rows_per_launch = ok.sum().item() / K
+    att_bytes = w.n * (8 * w.k + 4) + rows_per_launch * w.entry_bytes + w.n * 16 * (576 * 2 + 512 * 2 + 4)
+    achieved = att_bytes / att_s / 1e9
+    m = miss[args.warmup:].double().mean().item()
+    page_bytes = P * w.entry_bytes
+    fetch_Bps = m * w.n * page_bytes / (resolve_us * 1e-6)
+    step_tokens = w.n * w.k * P
+    line = {
+        "metric": "attended tokens/s through resolve + attention over page selections, 1 MI355X",
+        "value": step_tokens * K / (region_ms / 1e3),
+        "unit": "attended tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": region_ms / K,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.description, "global_batch": w.n, "page_tokens": P, "seq_len": w.len_tokens(0),
+                   "top_k_pages": w.k, "device_buffer_pages": w.B, "heads": 16, "graph": True},
+        "page_selections_per_s": w.n * K / (region_ms / 1e3),
+        "resolve_us_per_step": resolve_us,
+        "resolve_noio_us_per_step": noio_us,
+        "misses_per_selection_pages": m,
+        "miss_fetch_GBps": fetch_Bps / 1e9,
+        "miss_fetch_frac_of_link": fetch_Bps / 1e9 / PCIE_GEN5_X16_GBPS,
+        "attention_us": att_s * 1e6,
+        "attention_tokens_per_s": rows_per_launch / att_s,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": recorded_traffic("attend_pages", "attend.hip"),
+                     "kernel": "attend_kernel", "avg_kernel_us": att_s * 1e6, "algorithmic_bytes_per_launch": att_bytes},
+    }
+    hs.close()
+    return line, trace
+
+
 def bench_prefetch(args, torch, hsa, w):
     """Decode steps over 8 layers sharing a selection: serial order vs layer-wise prefetch."""
     from hierarchical_kv_cache_hs_amd.decode_step import DecodeSteps
@@ -754,7 +921,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=190)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="batch64", choices=["batch64", "fp8_256", "prefetch", "sweep", "topk"])
+    ap.add_argument("--workload", default="batch64", choices=["batch64", "fp8_256", "prefetch", "sweep", "topk", "pages"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--summarize-profile", action="store_true",
@@ -809,6 +976,10 @@ def main():
         line = bench_sweep(args, torch, hsa)
     elif args.workload == "topk":
         line = bench_topk(args, torch, hsa)
+    elif args.workload == "pages":
+        line, trace = bench_pages(args, torch, hsa, C.PAGES)
+        line["cpu_baseline"] = None if args.no_cpu_baseline else \
+            cpu_baseline_pages(C.PAGES, trace, args.warmup, args.cpu_budget)
     else:
         line = bench_attend(args, torch, hsa, C.FP8_256)
         line["cpu_baseline"] = None if args.no_cpu_baseline else \

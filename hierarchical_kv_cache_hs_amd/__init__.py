@@ -11,6 +11,10 @@ fallback: if libhs.so is missing the import fails.
     hs.host_kv(layer, request)[:] = rows           # pinned host history
     slots, miss = hs.resolve(layer, sel)           # sel: int32 cuda [n_req][top_k]
     out, lse = hs.attend(layer, q, slots, scale)   # q: bf16 cuda [n_req][H][576]
+
+With page_tokens=P > 1 the cached unit is a page of P consecutive tokens: selections,
+top_k, the buffer size and the capacity count pages; the host history stays one row
+per token, and attend / attend_pages read every token of the resolved pages.
 """
 from __future__ import annotations
 
@@ -33,7 +37,8 @@ DEVERR_DUPLICATE = 0x2
 
 HS_OK, HS_ERR_INVALID_ARG, HS_ERR_OUT_OF_MEMORY, HS_ERR_UNSUPPORTED, HS_ERR_HIP, HS_ERR_DEVICE = range(6)
 
-SYMBOLS = ("hs_create", "hs_resolve", "hs_resolve_tables", "hs_fetch_misses", "hs_attend", "hs_destroy",
+SYMBOLS = ("hs_create", "hs_resolve", "hs_resolve_tables", "hs_fetch_misses", "hs_attend", "hs_attend_pages",
+           "hs_destroy",
            "hs_append", "hs_offload", "hs_topk",
            "hs_device_bytes", "hs_host_bytes", "hs_host_kv",
            "hs_device_state", "hs_reset_requests", "hs_get_device_error", "hs_status_string",
@@ -45,14 +50,14 @@ class Config(ctypes.Structure):
                 ("host_to_device_ratio", ctypes.c_int32), ("max_requests", ctypes.c_int32),
                 ("num_layers", ctypes.c_int32), ("layout", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("flags", ctypes.c_uint32), ("device_mem", ctypes.c_void_p), ("device_mem_bytes", ctypes.c_size_t),
-                ("eviction", ctypes.c_int32), ("eviction_seed", ctypes.c_uint64)]
+                ("eviction", ctypes.c_int32), ("eviction_seed", ctypes.c_uint64), ("page_tokens", ctypes.c_int32)]
 
 
 class StateView(ctypes.Structure):
     _fields_ = [("page_table", ctypes.c_void_p), ("slot_owner", ctypes.c_void_p), ("slot_stamp", ctypes.c_void_p),
                 ("lru_order", ctypes.c_void_p), ("step", ctypes.c_void_p), ("kv_buffer", ctypes.c_void_p),
                 ("capacity", ctypes.c_int64), ("slot_stride", ctypes.c_int64), ("entry_bytes", ctypes.c_int64),
-                ("request_stride", ctypes.c_int64)]
+                ("request_stride", ctypes.c_int64), ("page_tokens", ctypes.c_int64)]
 
 
 class HSError(RuntimeError):
@@ -82,6 +87,7 @@ def lib():
         L.hs_topk.argtypes = [p, i32, p, ctypes.c_int64, p, p, p]
         L.hs_offload.argtypes = [p, i32, i32, ctypes.c_int64, ctypes.c_int64, p, ctypes.c_int64, p]
         L.hs_attend.argtypes = [p, i32, i32, p, p, ctypes.c_float, p, p, p]
+        L.hs_attend_pages.argtypes = [p, i32, i32, p, p, p, p, ctypes.c_float, p, p, p]
         L.hs_destroy.argtypes = [p]
         L.hs_host_kv.argtypes = [p, i32, i32, ctypes.POINTER(p), ctypes.POINTER(ctypes.c_int64),
                                  ctypes.POINTER(ctypes.c_int64)]
@@ -93,7 +99,7 @@ def lib():
         L.hs_last_error_message.argtypes = []
         L.hs_last_error_message.restype = ctypes.c_char_p
         for name in ("hs_device_bytes", "hs_host_bytes", "hs_create", "hs_resolve", "hs_resolve_tables",
-                     "hs_fetch_misses", "hs_attend", "hs_destroy",
+                     "hs_fetch_misses", "hs_attend", "hs_attend_pages", "hs_destroy",
                      "hs_host_kv", "hs_device_state", "hs_reset_requests", "hs_get_device_error"):
             getattr(L, name).restype = ctypes.c_int
         _lib_cache = L
@@ -106,9 +112,9 @@ def _check(status: int):
 
 
 def make_config(top_k, device_buffer_size, host_to_device_ratio, max_requests, num_layers=1, layout=LAYOUT_BF16,
-                num_heads=0, flags=0, eviction=0, eviction_seed=0) -> Config:
+                num_heads=0, flags=0, eviction=0, eviction_seed=0, page_tokens=1) -> Config:
     return Config(top_k, device_buffer_size, host_to_device_ratio, max_requests, num_layers, layout, num_heads,
-                  flags, None, 0, eviction, eviction_seed)
+                  flags, None, 0, eviction, eviction_seed, page_tokens)
 
 
 def device_bytes(cfg: Config) -> int:
@@ -133,9 +139,10 @@ class HiSparse:
 
     def __init__(self, top_k: int, device_buffer_size: int, host_to_device_ratio: int, max_requests: int,
                  num_layers: int = 1, layout: int = LAYOUT_BF16, num_heads: int = 0, flags: int = 0,
-                 device: str | torch.device = "cuda", eviction: int = 0, eviction_seed: int = 0):
+                 device: str | torch.device = "cuda", eviction: int = 0, eviction_seed: int = 0,
+                 page_tokens: int = 1):
         self.cfg = make_config(top_k, device_buffer_size, host_to_device_ratio, max_requests, num_layers, layout,
-                               num_heads, flags, eviction, eviction_seed)
+                               num_heads, flags, eviction, eviction_seed, page_tokens)
         nbytes = device_bytes(self.cfg)
         self.device = torch.device(device)
         # torch owns the device block; the library lays its tables out inside it
@@ -150,7 +157,8 @@ class HiSparse:
         self.top_k, self.B, self.n, self.L = top_k, device_buffer_size, max_requests, num_layers
         self.layout, self.heads = layout, num_heads
         self.entry_bytes = ENTRY_BYTES[layout]
-        self.capacity = host_to_device_ratio * device_buffer_size
+        self.capacity = host_to_device_ratio * device_buffer_size     # page-table entries
+        self.page_tokens = page_tokens
 
     # -- lifetime ------------------------------------------------------------------------------
     def close(self):
@@ -177,7 +185,7 @@ class HiSparse:
 
     # -- host pool -----------------------------------------------------------------------------
     def host_kv(self, layer: int, request: int) -> np.ndarray:
-        """[capacity][entry_bytes] uint8 view of the pinned host rows of (layer, request)."""
+        """[capacity * page_tokens][entry_bytes] uint8 view of the pinned host rows (one per token)."""
         ptr = ctypes.c_void_p()
         cap = ctypes.c_int64()
         stride = ctypes.c_int64()
@@ -263,6 +271,24 @@ class HiSparse:
                                lse.data_ptr(), _stream_ptr(stream)))
         return out, lse
 
+    def attend_pages(self, layer: int, q: torch.Tensor, slots: torch.Tensor, sel: torch.Tensor,
+                     lens: torch.Tensor, scale: float, out: torch.Tensor | None = None,
+                     lse: torch.Tensor | None = None, stream=None):
+        """hs_attend_pages: attend cut at lens[r] tokens (sel: the selection slots came from)."""
+        n_req = q.shape[0]
+        assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.shape[2] == 576
+        assert slots.dtype == torch.int32 and slots.is_contiguous() and slots.shape == (n_req, self.top_k)
+        assert sel.dtype == torch.int32 and sel.is_contiguous() and sel.shape == (n_req, self.top_k)
+        assert lens.dtype == torch.int32 and lens.is_contiguous() and lens.shape[0] >= n_req
+        if out is None:
+            out = torch.empty(n_req, q.shape[1], 512, dtype=torch.bfloat16, device=q.device)
+        if lse is None:
+            lse = torch.empty(n_req, q.shape[1], dtype=torch.float32, device=q.device)
+        _check(lib().hs_attend_pages(self._h, layer, n_req, q.data_ptr(), slots.data_ptr(), sel.data_ptr(),
+                                     lens.data_ptr(), float(scale), out.data_ptr(), lse.data_ptr(),
+                                     _stream_ptr(stream)))
+        return out, lse
+
     # -- state -----------------------------------------------------------------------------------
     def state(self, layer: int) -> dict:
         """Torch views (no copies) of one layer's device tables and slot buffer."""
@@ -288,6 +314,7 @@ class HiSparse:
             "kv_buffer": rows[:, :B],
             "zero_row": rows[:, B],
             "entry_bytes": v.entry_bytes,
+            "page_tokens": v.page_tokens,
         }
 
     def reset_requests(self, first: int, count: int, stream=None):

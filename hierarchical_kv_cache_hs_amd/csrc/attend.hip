@@ -7,6 +7,9 @@
 // over the valid slots j of the request (slot -1 skipped), with K_j the 576 decoded values
 // of the slot's entry (512 latent + 64 rope) and V_j its first 512 values (MLA form).
 // FP8 entries decode as e4m3 code * fp32 block scale (one scale per 128 latent values).
+// With pages of P tokens (paper abstract: NSA and Quest select blocks of tokens), a slot holds
+// P rows and the attended tokens are the rows of the valid slots, optionally cut at each
+// request's context length; the slot list is expanded to rows once, in the prologue.
 //
 // Design for gfx950.  The kernel is bound by HBM (about 1.3 MB of rows per request at
 // k = 2048 against 71 MFLOP), so the design is about keeping rows in flight:
@@ -60,15 +63,18 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 struct AttendArgs {
-  const uint8_t* buf;     // layer's slot rows [n][B][stride]
-  const int32_t* slots;   // [n_req][k]
+  const uint8_t* buf;     // layer's rows [n][B][stride]
+  const int32_t* slots;   // [n_req][k >> lgP] slots of the selected units
+  const int32_t* sel;     // [n_req][k >> lgP] the selection, or null (no length cut)
+  const int32_t* len;     // [n_req] context length in tokens (with sel)
   const uint16_t* q;      // [n_req][heads][576] bf16
   uint16_t* out;          // [n_req][heads][512] bf16
   float* lse;             // [n_req][heads] or null
   float* part;            // [n][splits][PART]
-  int64_t stride;         // bytes between slot rows
-  int64_t rstride;        // bytes between requests: B slot rows, then a row of zeros
-  int32_t k, B, heads, chunk, splits;
+  int64_t stride;         // bytes between token rows
+  int64_t rstride;        // bytes between requests: B token rows, then zero rows
+  int32_t k, B, heads, chunk, splits;   // k and B count token rows (units times P)
+  int32_t lgP;            // log2 of the rows per slot
   float scale_log2;       // softmax scale * log2(e)
 };
 
@@ -239,12 +245,28 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
   const int ntiles = (ntok + G::T - 1) / G::T;
   const uint8_t* rbase = a.buf + (int64_t)r * a.rstride;
 
-  // ---- this workgroup's slot list (invalid or missing -> -1) and this wave's Q operands
+  // ---- this workgroup's row list (invalid, cut or missing -> -1) and this wave's Q operands
   {
-    const int32_t* sl = a.slots + (int64_t)r * a.k + tok0;
+    const int lg = a.lgP;
+    const int ku = a.k >> lg, bu = a.B >> lg;
+    const int32_t* su = a.slots + (int64_t)r * ku;
+    const int32_t* cu = a.sel ? a.sel + (int64_t)r * ku : nullptr;
+    const int64_t len = a.sel ? (int64_t)a.len[r] : 0;
     for (int i = tid; i < ntiles * G::T; i += NT) {
-      const int32_t v = (i < ntok) ? sl[i] : -1;
-      slot_lds[i] = (v >= 0 && v < a.B) ? v : -1;
+      int32_t v = -1;
+      if (i < ntok) {
+        const int tok = tok0 + i;
+        const int u = tok >> lg, o = tok & ((1 << lg) - 1);
+        const int32_t j = su[u];
+        if (j >= 0 && j < bu) {
+          v = (j << lg) + o;
+          if (cu) {
+            const int32_t c = cu[u];
+            if (c < 0 || ((int64_t)c << lg) + o >= len) v = -1;
+          }
+        }
+      }
+      slot_lds[i] = v;
     }
   }
   u32x4 qreg[KB_HALF];
@@ -587,9 +609,10 @@ int max_chunk(const Geometry& g) {
 int attend_splits(const Geometry& g) {
   // one workgroup per compute unit at full batch (a workgroup's ring fills most of a CU's
   // LDS), at most MAXCHUNK tokens per workgroup, and at least one 64-token tile each
+  const int tokens = (int)attend_tokens(g);
   int s = (256 + g.n - 1) / g.n;
-  const int by_len = (g.k + 63) / 64;
-  const int need = (g.k + max_chunk(g) - 1) / max_chunk(g);
+  const int by_len = (tokens + 63) / 64;
+  const int need = (tokens + max_chunk(g) - 1) / max_chunk(g);
   if (s > by_len) s = by_len;
   if (s > 16) s = 16;
   if (s < need) s = need;
@@ -610,21 +633,24 @@ void prepare_attend() {
 }
 
 hipError_t launch_attend(const Geometry& g, const LayerTables& t, int32_t n_req, const void* q, const int32_t* slots,
-                         float scale, void* out, float* lse, hipStream_t st) {
+                         const int32_t* sel, const int32_t* len, float scale, void* out, float* lse, hipStream_t st) {
   AttendArgs a;
   a.buf = t.buf;
   a.slots = slots;
+  a.sel = sel;
+  a.len = len;
   a.q = (const uint16_t*)q;
   a.out = (uint16_t*)out;
   a.lse = lse;
   a.part = t.part;
-  a.stride = g.slot_stride;
+  a.stride = g.entry_bytes;
   a.rstride = g.req_stride;
-  a.k = g.k;
-  a.B = g.B;
+  a.k = (int32_t)attend_tokens(g);
+  a.B = g.B * g.P;
+  a.lgP = g.lgP;
   a.heads = g.heads;
   a.splits = attend_splits(g);
-  const int per = (g.k + a.splits - 1) / a.splits;
+  const int per = (a.k + a.splits - 1) / a.splits;
   a.chunk = (per + 15) / 16 * 16;
   a.scale_log2 = scale * kLog2e;
   if (a.splits > 1 && !a.part) return hipErrorInvalidValue;

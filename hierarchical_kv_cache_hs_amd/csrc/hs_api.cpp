@@ -98,10 +98,15 @@ hs_status plan(const hs_config* cfg, hs::Geometry* g, Layout* lay) {
   if (cfg->flags & ~HS_FLAG_NO_IO) return fail(HS_ERR_INVALID_ARG, "unknown flag bits");
   if (cfg->eviction != HS_EVICT_LRU && cfg->eviction != HS_EVICT_FIFO && cfg->eviction != HS_EVICT_RANDOM)
     return fail(HS_ERR_INVALID_ARG, "unknown eviction policy");
+  const int32_t P = cfg->page_tokens == 0 ? 1 : cfg->page_tokens;
+  if (P < 1 || P > 256 || (P & (P - 1)))
+    return fail(HS_ERR_INVALID_ARG, "page_tokens must be 0, 1 or a power of two <= 256");
+  if (cfg->num_heads > 0 && (int64_t)cfg->top_k * P > 65536)
+    return fail(HS_ERR_UNSUPPORTED, "attention over more than 65536 tokens (top_k * page_tokens)");
   if (cfg->top_k > hs::kMaxTopK) return fail(HS_ERR_UNSUPPORTED, "top_k above 8192");
   if (cfg->device_buffer_size > hs::kMaxBuffer) return fail(HS_ERR_UNSUPPORTED, "device_buffer_size above 16384");
   const int64_t cap = (int64_t)cfg->host_to_device_ratio * (int64_t)cfg->device_buffer_size;
-  if (cap > INT32_MAX) return fail(HS_ERR_INVALID_ARG, "capacity (ratio * B) exceeds 2^31-1 tokens");
+  if (cap * P > INT32_MAX) return fail(HS_ERR_INVALID_ARG, "capacity (ratio * B * page_tokens) exceeds 2^31-1 tokens");
   if (hs::resolve_lds_bytes(cap, cfg->top_k, cfg->device_buffer_size) > hs::kLdsLimit)
     return fail(HS_ERR_UNSUPPORTED, "capacity too large for the resolver's on-chip token bitmap");
 
@@ -111,11 +116,17 @@ hs_status plan(const hs_config* cfg, hs::Geometry* g, Layout* lay) {
   g->L = cfg->num_layers;
   g->layout = cfg->layout;
   g->heads = cfg->num_heads;
+  g->P = P;
+  g->lgP = 0;
+  while ((1 << g->lgP) < P) ++g->lgP;
   g->cap = cap;
   g->entry_bytes = cfg->layout == HS_KV_BF16_576 ? 1152 : 656;
-  g->host_stride = g->entry_bytes;
-  g->slot_stride = g->entry_bytes;  // packed: scattered 656-byte rows gather faster packed than padded to 768
+  g->unit_bytes = (int64_t)P * g->entry_bytes;
+  g->host_stride = g->unit_bytes;
+  g->slot_stride = g->unit_bytes;  // packed: scattered 656-byte rows gather faster packed than padded to 768
   g->req_stride = ((int64_t)g->B + 1) * g->slot_stride;
+  // the attention kernel addresses a request's rows with 32-bit offsets
+  if (g->req_stride > (int64_t)UINT32_MAX) return fail(HS_ERR_UNSUPPORTED, "a request's slot rows exceed 4 GiB");
   g->flags = cfg->flags;
   g->policy = cfg->eviction;
   g->seed = cfg->eviction_seed;
@@ -331,7 +342,25 @@ hs_status hs_attend(hs_handle* h, int32_t layer, int32_t n_req, const void* d_q,
   if (n_req == 0) return HS_OK;
   if (!d_q || !d_slots || !d_out) return fail(HS_ERR_INVALID_ARG, "query, slot or output pointer is NULL");
   hs::LayerTables t = layer_tables(h, layer);
-  hipError_t e = hs::launch_attend(h->g, t, n_req, d_q, d_slots, scale, d_out, d_lse, (hipStream_t)stream);
+  hipError_t e =
+      hs::launch_attend(h->g, t, n_req, d_q, d_slots, nullptr, nullptr, scale, d_out, d_lse, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "attend launch");
+  return HS_OK;
+}
+
+hs_status hs_attend_pages(hs_handle* h, int32_t layer, int32_t n_req, const void* d_q, const int32_t* d_slots,
+                          const int32_t* d_sel, const int32_t* d_len, float scale, void* d_out, float* d_lse,
+                          void* stream) {
+  if (!h) return fail(HS_ERR_INVALID_ARG, "handle is NULL");
+  if (h->g.heads == 0) return fail(HS_ERR_UNSUPPORTED, "handle created with num_heads = 0");
+  if (layer < 0 || layer >= h->g.L) return fail(HS_ERR_INVALID_ARG, "layer out of range");
+  if (n_req < 0 || n_req > h->g.n) return fail(HS_ERR_INVALID_ARG, "n_req out of range");
+  if (n_req == 0) return HS_OK;
+  if (!d_q || !d_slots || !d_out) return fail(HS_ERR_INVALID_ARG, "query, slot or output pointer is NULL");
+  if (!d_sel || !d_len) return fail(HS_ERR_INVALID_ARG, "selection or length pointer is NULL");
+  hs::LayerTables t = layer_tables(h, layer);
+  hipError_t e =
+      hs::launch_attend(h->g, t, n_req, d_q, d_slots, d_sel, d_len, scale, d_out, d_lse, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "attend launch");
   return HS_OK;
 }
@@ -349,10 +378,10 @@ hs_status hs_host_kv(hs_handle* h, int32_t layer, int32_t request, void** ptr, i
   if (layer < 0 || layer >= h->g.L || request < 0 || request >= h->g.n)
     return fail(HS_ERR_INVALID_ARG, "layer or request out of range");
   if (!h->host_pool) return fail(HS_ERR_UNSUPPORTED, "no host pool in no-IO mode");
-  const size_t rows = ((size_t)layer * h->g.n + (size_t)request) * (size_t)h->g.cap;
-  *ptr = h->host_pool + rows * (size_t)h->g.host_stride;
-  if (capacity) *capacity = h->g.cap;
-  if (row_stride) *row_stride = h->g.host_stride;
+  const size_t units = ((size_t)layer * h->g.n + (size_t)request) * (size_t)h->g.cap;
+  *ptr = h->host_pool + units * (size_t)h->g.host_stride;
+  if (capacity) *capacity = h->g.cap * h->g.P;   // token rows
+  if (row_stride) *row_stride = h->g.entry_bytes;
   return HS_OK;
 }
 
@@ -370,6 +399,7 @@ hs_status hs_device_state(hs_handle* h, int32_t layer, hs_state_view* v) {
   v->slot_stride = h->g.slot_stride;
   v->entry_bytes = h->g.entry_bytes;
   v->request_stride = h->g.req_stride;
+  v->page_tokens = h->g.P;
   return HS_OK;
 }
 
@@ -380,6 +410,7 @@ hs_status hs_append(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* d
   if (n_req < 0 || n_req > h->g.n) return fail(HS_ERR_INVALID_ARG, "n_req out of range");
   if (h->g.policy == HS_EVICT_RANDOM)
     return fail(HS_ERR_UNSUPPORTED, "append needs a stamp-ordered eviction policy (LRU or FIFO)");
+  if (h->g.P != 1) return fail(HS_ERR_UNSUPPORTED, "append is token-granular (page_tokens must be 1)");
   if (n_req == 0) return HS_OK;
   if (!d_pos || !d_rows) return fail(HS_ERR_INVALID_ARG, "position or row pointer is NULL");
   if (row_stride < h->g.entry_bytes || row_stride % 16 || ((uintptr_t)d_rows) % 16)
@@ -397,13 +428,14 @@ hs_status hs_offload(hs_handle* h, int32_t layer, int32_t request, int64_t first
   if (!h) return fail(HS_ERR_INVALID_ARG, "handle is NULL");
   if (layer < 0 || layer >= h->g.L) return fail(HS_ERR_INVALID_ARG, "layer out of range");
   if (request < 0 || request >= h->g.n) return fail(HS_ERR_INVALID_ARG, "request out of range");
-  if (first < 0 || count < 0 || first > h->g.cap - count) return fail(HS_ERR_INVALID_ARG, "positions out of range");
+  const int64_t cap_tokens = h->g.cap * h->g.P;
+  if (first < 0 || count < 0 || first > cap_tokens - count) return fail(HS_ERR_INVALID_ARG, "positions out of range");
   if (!h->host_pool) return fail(HS_ERR_UNSUPPORTED, "no host pool in no-IO mode");
   if (count == 0) return HS_OK;
   if (!d_rows) return fail(HS_ERR_INVALID_ARG, "row pointer is NULL");
   if (row_stride < h->g.entry_bytes) return fail(HS_ERR_INVALID_ARG, "row_stride below the entry size");
   const size_t E = (size_t)h->g.entry_bytes;
-  const size_t off = (((size_t)layer * h->g.n + (size_t)request) * (size_t)h->g.cap + (size_t)first) * E;
+  const size_t off = (((size_t)layer * h->g.n + (size_t)request) * (size_t)cap_tokens + (size_t)first) * E;
   // Contiguous rows go as one flat copy (the DMA engine's fast path, no compute units);
   // 16-byte-aligned padded rows through a zero-copy store kernel (a 2-D copy of small rows
   // runs at about a third of the link); anything else as a 2-D copy.

@@ -33,10 +33,13 @@ struct LayerTables {
 
 struct Geometry {
   int32_t k, B, n, L, layout, heads;
+  int32_t P;            // tokens per cached unit (1, or a page of P tokens); k, B and cap count units
+  int32_t lgP;          // log2 P
   int64_t cap;
-  int64_t entry_bytes;
-  int64_t host_stride;
-  int64_t slot_stride;
+  int64_t entry_bytes;  // bytes of one token's row
+  int64_t unit_bytes;   // bytes of one cached unit: P rows
+  int64_t host_stride;  // bytes between units in the host history (= unit_bytes)
+  int64_t slot_stride;  // bytes between slots (= unit_bytes)
   int64_t req_stride;   // bytes per request in the slot buffer: B slot rows, then one row of zeros
   uint32_t flags;
   int32_t policy;       // hs_eviction
@@ -89,7 +92,12 @@ void prepare_attend();
 int attend_splits(const Geometry& g);
 size_t attend_partial_floats(const Geometry& g);
 
+// Tokens attended per request: every row of the k selected units.
+inline int64_t attend_tokens(const Geometry& g) { return (int64_t)g.k * g.P; }
+
+// sel and len (both or neither): cut each request's tokens at its context length len[r],
+// token o of unit i taking part iff sel[r][i] >= 0 and sel[r][i] * P + o < len[r].
 hipError_t launch_attend(const Geometry& g, const LayerTables& t, int32_t n_req, const void* q, const int32_t* slots,
-                         float scale, void* out, float* lse, hipStream_t s);
+                         const int32_t* sel, const int32_t* len, float scale, void* out, float* lse, hipStream_t s);
 
 }  // namespace hs

@@ -523,7 +523,7 @@ hipError_t launch_resolve(const Geometry& g, const LayerTables& t, int32_t layer
   a.nlayers = g.L;
   a.k = g.k;
   a.B = g.B;
-  a.chunks = (int32_t)(g.entry_bytes / 16);
+  a.chunks = (int32_t)(g.unit_bytes / 16);
   a.ml_tok = t.ml_tok;
   a.ml_slot = t.ml_slot;
   a.ml_cnt = t.ml_cnt;
@@ -545,7 +545,7 @@ hipError_t launch_fetch(const Geometry& g, const LayerTables& t, const uint8_t* 
   // enough fetch workgroups for ~512 in total, whatever the batch
   const int per_req = (512 + n_req - 1) / n_req < 16 ? (512 + n_req - 1) / n_req : 16;
   hipLaunchKernelGGL(fetch_kernel, dim3(per_req, n_req), dim3(FT), 0, s, t.ml_tok, t.ml_slot, t.ml_cnt, host_layer,
-                     t.buf, g.cap, g.host_stride, g.slot_stride, g.req_stride, g.k, g.B, (int32_t)(g.entry_bytes / 16));
+                     t.buf, g.cap, g.host_stride, g.slot_stride, g.req_stride, g.k, g.B, (int32_t)(g.unit_bytes / 16));
   return hipGetLastError();
 }
 

@@ -15,6 +15,16 @@
  * least recent first, ties to the lower slot index; missing tokens are served
  * in ascending token order, the i-th missing token taking the i-th candidate.
  *
+ * Page-granular selections (paper abstract: the method serves the NSA and Quest
+ * families, whose indexers select blocks of consecutive tokens): with
+ * hs_config.page_tokens = P > 1 the cached unit is a page of P consecutive
+ * tokens (page c = tokens cP .. cP + P - 1).  Selections, top_k,
+ * device_buffer_size, capacity and the page table then count pages, a slot holds
+ * the P rows of its page in position order, a miss fetches the whole page, and
+ * the same replacement rule applies with "page" for "token".  The host history
+ * stays one row per token (hs_host_kv, hs_offload), and hs_attend /
+ * hs_attend_pages read every token of the resolved pages.
+ *
  * Conventions for every function:
  *   - device pointers ("d_" prefix) are HIP device addresses; host pointers are
  *     ordinary process addresses;
@@ -88,7 +98,7 @@ typedef enum hs_eviction { HS_EVICT_LRU = 0, HS_EVICT_FIFO = 1, HS_EVICT_RANDOM 
 typedef struct hs_config {
   int32_t top_k;                /* k: selections per request and step, >= 1                  */
   int32_t device_buffer_size;   /* B: device slots per (request, layer), B >= top_k           */
-  int32_t host_to_device_ratio; /* >= 1; capacity = ratio * B tokens of history              */
+  int32_t host_to_device_ratio; /* >= 1; capacity = ratio * B tokens (pages) of history      */
   int32_t max_requests;         /* request slots 0..max_requests-1                           */
   int32_t num_layers;           /* layers, each with its own buffer and tables               */
   int32_t layout;               /* hs_kv_layout                                              */
@@ -99,14 +109,17 @@ typedef struct hs_config {
   size_t device_mem_bytes;      /* size of device_mem                                        */
   int32_t eviction;             /* hs_eviction; 0 = LRU                                      */
   uint64_t eviction_seed;       /* HS_EVICT_RANDOM: key of its permutation                   */
+  int32_t page_tokens;          /* tokens per cached unit: 0 or 1 = token-granular; P > 1, a
+                                   power of two <= 256, = pages of P tokens (see above);
+                                   with num_heads > 0, top_k * P <= 65536                    */
 } hs_config;
 
 typedef struct hs_handle hs_handle;
 
 /* Device-side state of one layer; all pointers are device addresses owned by the handle. */
 typedef struct hs_state_view {
-  int32_t* page_table;   /* [max_requests][capacity] token -> slot, -1 = not resident  */
-  int32_t* slot_owner;   /* [max_requests][B] slot -> token, -1 = empty               */
+  int32_t* page_table;   /* [max_requests][capacity] token (page) -> slot, -1 = not resident */
+  int32_t* slot_owner;   /* [max_requests][B] slot -> token (page), -1 = empty         */
   int32_t* slot_stamp;   /* [max_requests][B] step of last selection, -1 = never       */
   int32_t* lru_order;    /* [max_requests][B] slots sorted by (stamp, slot) ascending  */
                          /* (not maintained under HS_EVICT_RANDOM)                     */
@@ -114,10 +127,11 @@ typedef struct hs_state_view {
   uint8_t* kv_buffer;    /* per request (request_stride bytes apart): B slot rows of    */
                          /* slot_stride bytes, then one row of zeros the attention     */
                          /* kernel reads for padded selection entries (never written)  */
-  int64_t capacity;      /* host tokens per (request, layer)                            */
-  int64_t slot_stride;   /* bytes between slots in kv_buffer (>= entry_bytes)           */
-  int64_t entry_bytes;   /* bytes of one KV entry                                       */
+  int64_t capacity;      /* page-table entries per (request, layer): tokens, or pages    */
+  int64_t slot_stride;   /* bytes between slots in kv_buffer (page_tokens * entry_bytes) */
+  int64_t entry_bytes;   /* bytes of one token's KV entry                               */
   int64_t request_stride; /* bytes between requests in kv_buffer ((B + 1) * slot_stride) */
+  int64_t page_tokens;   /* tokens per slot (1 = token-granular)                        */
 } hs_state_view;
 
 /* Bytes the device block must have for this configuration (0 and an error if invalid). */
@@ -184,6 +198,8 @@ hs_status hs_fetch_misses(hs_handle* h, int32_t layer, int32_t n_req, void* stre
  * A position outside [0, capacity) is skipped and sets HS_DEVERR_TOKEN_RANGE.  With
  * HS_FLAG_NO_IO the tables change but no row moves.  Enqueue-only, graph-capturable.
  * A selection that names the token in the next resolve finds it resident (a hit).
+ * HS_ERR_UNSUPPORTED with page_tokens > 1 (a new token's page would need the rest of its
+ * rows fetched) or HS_EVICT_RANDOM.
  */
 hs_status hs_append(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* d_pos, const void* d_rows,
                     int64_t row_stride, int32_t* d_slot_out, void* stream);
@@ -207,12 +223,13 @@ hs_status hs_topk(hs_handle* h, int32_t n_req, const float* d_scores, int64_t sc
 
 /*
  * Prefill offload: copies count rows (device memory, row_stride bytes apart) into positions
- * first .. first + count - 1 of request `request`'s history in the host pool (the note's
+ * first .. first + count - 1 (token positions, also with pages) of request `request`'s
+ * history in the host pool (the note's
  * introduction: KV is actively offloaded to host memory).  Device tables are untouched: the
  * tokens arrive on the device as misses when a selection names them.  Stream-ordered: one
  * flat device-to-host copy when row_stride equals the entry size, a zero-copy store kernel
  * for 16-byte-aligned padded rows, a 2-D copy otherwise.  HS_ERR_INVALID_ARG for a range
- * outside [0, capacity) or row_stride < entry bytes.
+ * outside [0, capacity * page_tokens) or row_stride < entry bytes.
  */
 hs_status hs_offload(hs_handle* h, int32_t layer, int32_t request, int64_t first, int64_t count,
                      const void* d_rows, int64_t row_stride, void* stream);
@@ -228,17 +245,33 @@ hs_status hs_offload(hs_handle* h, int32_t layer, int32_t request, int64_t first
  *           with K_j all 576 decoded values of slot j and V_j its first 512
  *   d_lse   [n_req][num_heads] fp32 log-sum-exp of the scaled scores, or NULL
  * A row with no valid slot gives out = 0 and lse = -inf.  HS_ERR_UNSUPPORTED
- * when the handle was created with num_heads = 0.
+ * when the handle was created with num_heads = 0.  With page_tokens = P > 1,
+ * d_slots holds page slots and the attended tokens are the P rows of each valid
+ * page slot (top_k * P tokens).
  */
 hs_status hs_attend(hs_handle* h, int32_t layer, int32_t n_req, const void* d_q, const int32_t* d_slots,
                     float scale, void* d_out, float* d_lse, void* stream);
+
+/*
+ * hs_attend cut at each request's context length, for page-granular selections whose last
+ * page is partly written (paper abstract: NSA and Quest select blocks of tokens; a block past
+ * the newest token holds no KV yet).  Token o of the i-th selected page takes part iff its
+ * page slot is valid, d_sel[r][i] >= 0 and d_sel[r][i] * page_tokens + o < d_len[r].
+ *   d_sel   [n_req][top_k] int32, the selection d_slots was resolved from
+ *   d_len   [n_req] int32 context length in tokens
+ * Other arguments and errors as hs_attend; valid for token-granular handles too.
+ */
+hs_status hs_attend_pages(hs_handle* h, int32_t layer, int32_t n_req, const void* d_q, const int32_t* d_slots,
+                          const int32_t* d_sel, const int32_t* d_len, float scale, void* d_out, float* d_lse,
+                          void* stream);
 
 /* Synchronise the device and free everything the handle owns.  NULL is accepted. */
 hs_status hs_destroy(hs_handle* h);
 
 /*
- * Host rows of (layer, request): *ptr = first of `*capacity` rows, `*row_stride`
- * bytes apart, in pinned memory owned by the handle (valid until hs_destroy).
+ * Host rows of (layer, request): *ptr = first of `*capacity` token rows (the
+ * page-table capacity times page_tokens), `*row_stride` bytes apart, in pinned
+ * memory owned by the handle (valid until hs_destroy).
  * The caller writes a token's row before any selection names it, directly or
  * through hs_offload / hs_append; resolves read it for misses.
  * HS_ERR_UNSUPPORTED with HS_FLAG_NO_IO (no host pool).

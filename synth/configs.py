@@ -36,6 +36,7 @@ class Workload:
     heads: int = 16
     shared_layers: bool = True
     description: str = ""
+    page_tokens: int = 1   # tokens per selected unit; with P > 1, ctx, k, B, window count pages of P tokens
 
     @property
     def seed(self) -> int:
@@ -51,7 +52,12 @@ class Workload:
 
     def trace_spec(self) -> TraceSpec:
         return TraceSpec(n=self.n, k=self.k, ctx=self.ctx, window=self.window, zipf_s=self.zipf_s,
-                         churn=self.churn, steps=self.steps, grow=self.grow, seed=self.seed)
+                         churn=self.churn, steps=self.steps, grow=self.grow, seed=self.seed,
+                         grow_per=self.page_tokens)
+
+    def len_tokens(self, t: int) -> int:
+        """Context length in tokens at step t (one new token per step when growing)."""
+        return self.ctx * self.page_tokens + (t if self.grow else 0)
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -86,7 +92,17 @@ PREFETCH = Workload("prefetch", 4, n=128, layers=8, ctx=65536, k=2048, B=4096, r
                     description="128 requests, 8 layers sharing a selection, ctx 65536, fp8 656 B, k 2048, "
                                 "B 4096, layer-wise prefetch")
 
-ALL = (TINY, BATCH64, FP8_256, SWEEP, PREFETCH)
+# Page-granular selections (paper abstract: the NSA and Quest families select blocks of
+# tokens): Quest-sized pages of 16 tokens with the token budget of the fp8 workload --
+# 128 pages = 2048 tokens selected, 256 pages = 4096 token rows of device buffer -- over a
+# 32768-token context that grows a token per step, so the newest page is partly written.
+PAGES = Workload("pages", 5, n=256, layers=1, ctx=2048, k=128, B=256, ratio=9, layout=LAYOUT_FP8,
+                 steps=200, window=8, zipf_s=1.05, churn=0.10, grow=True, attend=True, page_tokens=16,
+                 description="256 requests, pages of 16 tokens, ctx 32768 tokens + 1/step, fp8 656 B, "
+                             "k 128 pages (2048 tokens), B 256 pages (4096 rows), resolve + MLA attention "
+                             "cut at the context length (16 heads)")
+
+ALL = (TINY, BATCH64, FP8_256, SWEEP, PREFETCH, PAGES)
 
 
 def sweep_point(B: int) -> Workload:

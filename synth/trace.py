@@ -13,6 +13,11 @@ Attention" note, section 3 and Fig. 3):
   not tied to distance), of which a fraction ``churn`` is dropped and redrawn at
   each step.
 
+With pages (the NSA and Quest families of the paper abstract select blocks of
+consecutive tokens) the same recipe runs over page indices: ``grow_per`` tokens
+per page, so a context growing by a token per step gains a page every
+``grow_per`` steps and its newest page is partly written in between.
+
 The set is emitted in a shuffled order on purpose: consumers must not rely on
 sorted input.  Everything is seeded from (seed, request), so a trace is the
 same on every machine and for every buffer size of a sweep.
@@ -35,10 +40,14 @@ class TraceSpec:
     steps: int
     grow: bool        # context grows by one token per step
     seed: int
+    grow_per: int = 1  # tokens per unit: with grow, the context at step t is ctx + ceil(t / grow_per) units
+
+    def ctx_at(self, t: int) -> int:
+        return self.ctx + (-(-t // self.grow_per) if self.grow else 0)
 
     @property
     def ctx_max(self) -> int:
-        return self.ctx + (self.steps if self.grow else 0)
+        return self.ctx_at(self.steps)
 
     @property
     def hist(self) -> int:
@@ -77,7 +86,7 @@ class _Req:
 
     def step(self, t: int) -> np.ndarray:
         sp = self.spec
-        L_t = sp.ctx + (t if sp.grow else 0)
+        L_t = sp.ctx_at(t)
         limit = L_t - sp.window
         if t == 0:
             self.hist = self._draw(sp.hist, limit)

@@ -50,17 +50,18 @@ class Pair:
     """A device handle and the oracle, fed the same trace."""
 
     def __init__(self, n, L, k, B, ratio, layout, seed, heads=0, flags=0, oracle_rows=True, requests=None,
-                 split=False, policy=0, policy_seed=0):
-        self.split, self.policy = split, policy
+                 split=False, policy=0, policy_seed=0, page_tokens=1):
+        self.split, self.policy, self.P = split, policy, page_tokens
         self.hs = hsa.HiSparse(top_k=k, device_buffer_size=B, host_to_device_ratio=ratio, max_requests=n,
                                num_layers=L, layout=layout, num_heads=heads, flags=flags, eviction=policy,
-                               eviction_seed=policy_seed)
+                               eviction_seed=policy_seed, page_tokens=page_tokens)
         self.seed, self.n, self.L, self.k, self.B, self.layout = seed, n, L, k, B, layout
         self.cap = ratio * B
         fill_host_pool(self.hs, seed)
-        host = oracle_host(seed, n, L, self.cap, layout) if oracle_rows else None
-        self.orc = oracle.OracleCache(n, L, B, self.cap, layout=layout, host=host, policy=policy, seed=policy_seed)
-        self.E = skv.ENTRY_BYTES[layout]
+        host = oracle_host(seed, n, L, self.cap * page_tokens, layout) if oracle_rows else None
+        self.orc = oracle.OracleCache(n, L, B, self.cap, layout=layout, host=host, policy=policy, seed=policy_seed,
+                                      page_tokens=page_tokens)
+        self.E = skv.ENTRY_BYTES[layout] * page_tokens     # bytes of a slot: the P rows of a page
 
     def step(self, layer: int, S: np.ndarray, check_state: bool):
         sel = torch.from_numpy(np.ascontiguousarray(S, dtype=np.int32)).cuda()
@@ -96,7 +97,9 @@ class Pair:
                 if self.orc.dev is not None:
                     assert (buf[r, occ] == self.orc.dev[r, layer, occ]).all(), f"slot bytes differ (request {r})"
                 else:
-                    expect = skv.rows_at(self.seed, r, layer, rm[r, occ], self.layout)
+                    P = self.P
+                    tokens = (rm[r, occ][:, None].astype(np.int64) * P + np.arange(P)).reshape(-1)
+                    expect = skv.rows_at(self.seed, r, layer, tokens, self.layout).reshape(occ.size, self.E)
                     assert (buf[r, occ] == expect).all(), f"slot bytes differ (request {r})"
 
     def close(self):

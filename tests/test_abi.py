@@ -53,6 +53,12 @@ def _cfg(**kw):
     (dict(device_buffer_size=16385), hsa.HS_ERR_UNSUPPORTED),
     (dict(device_buffer_size=4096, host_to_device_ratio=600000), hsa.HS_ERR_INVALID_ARG),
     (dict(device_buffer_size=4096, host_to_device_ratio=300), hsa.HS_ERR_UNSUPPORTED),
+    (dict(page_tokens=3), hsa.HS_ERR_INVALID_ARG),
+    (dict(page_tokens=-4), hsa.HS_ERR_INVALID_ARG),
+    (dict(page_tokens=512), hsa.HS_ERR_INVALID_ARG),
+    (dict(top_k=2048, device_buffer_size=2048, page_tokens=64), hsa.HS_ERR_UNSUPPORTED),   # 131072 tokens
+    (dict(device_buffer_size=16384, host_to_device_ratio=1, page_tokens=256), hsa.HS_ERR_UNSUPPORTED),  # > 4 GiB
+    (dict(device_buffer_size=4096, host_to_device_ratio=4096, page_tokens=256), hsa.HS_ERR_INVALID_ARG),  # 2^32 tokens
 ])
 def test_create_rejects_bad_config_before_hip(kw, status):
     cfg = _cfg(**kw)
@@ -80,11 +86,27 @@ def test_no_io_mode_has_no_host_pool():
     assert hsa.host_bytes(_cfg()) == 2 * 128 * 32 * 1152
 
 
+def test_page_sizes():
+    # pages of 16: 256 slots of 16 rows, 32 pages of history per slot; the host pool keeps a row per token
+    cfg = _cfg(top_k=128, device_buffer_size=256, host_to_device_ratio=8, max_requests=4, num_heads=0,
+               layout=hsa.LAYOUT_FP8, page_tokens=16)
+    assert hsa.host_bytes(cfg) == 4 * 256 * 8 * 16 * 656
+    slots = 4 * (256 + 1) * 16 * 656
+    tables = 4 * 2048 * 4 + 3 * 4 * 256 * 4 + 2 * 4 * 128 * 4
+    assert slots + tables <= hsa.device_bytes(cfg) <= slots + tables + 64 * 1024
+    tok = _cfg(top_k=128, device_buffer_size=256, host_to_device_ratio=8, max_requests=4, num_heads=0,
+               layout=hsa.LAYOUT_FP8, page_tokens=1)
+    assert hsa.device_bytes(_cfg(top_k=128, device_buffer_size=256, host_to_device_ratio=8, max_requests=4,
+                                 num_heads=0, layout=hsa.LAYOUT_FP8, page_tokens=0)) == hsa.device_bytes(tok)
+
+
 def test_null_arguments():
     L = hsa.lib()
     assert L.hs_destroy(None) == hsa.HS_OK
     assert L.hs_resolve(None, 0, 1, None, None, None, None) == hsa.HS_ERR_INVALID_ARG
     assert L.hs_attend(None, 0, 1, None, None, ctypes.c_float(1.0), None, None, None) == hsa.HS_ERR_INVALID_ARG
+    assert L.hs_attend_pages(None, 0, 1, None, None, None, None, ctypes.c_float(1.0), None, None,
+                             None) == hsa.HS_ERR_INVALID_ARG
     assert L.hs_create(None, None) == hsa.HS_ERR_INVALID_ARG
     bits = ctypes.c_int32()
     assert L.hs_get_device_error(None, ctypes.byref(bits)) == hsa.HS_ERR_INVALID_ARG
