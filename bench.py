@@ -363,7 +363,23 @@ def bench_attend(args, torch, hsa, w):
             b.record(stream)
             b.synchronize()
             att_ms.append(a.elapsed_time(b))
-    del flush
+    # the fp32-output mode on the same rows and slots (a no-IO handle given a copy of the buffer)
+    hs_f32 = hsa.HiSparse(w.k, w.B, w.ratio, w.n, 1, w.layout, 16, hsa.FLAG_NO_IO | hsa.FLAG_ATTN_OUT_F32)
+    hs_f32.state(0)["kv_buffer"].copy_(hs.state(0)["kv_buffer"])
+    out32 = torch.empty(w.n, 16, 512, dtype=torch.float32, device="cuda")
+    f32_ms = []
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            t = args.warmup + i
+            flush.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            hs_f32.attend(0, qs[t % 8], slots[t], scale, out32, lse, stream=stream)
+            b.record(stream)
+            b.synchronize()
+            f32_ms.append(a.elapsed_time(b))
+    hs_f32.close()
+    del flush, out32
     # resolution alone: a handle that moves no rows, the same selections, one graph of K launches
     hs_noio = hsa.HiSparse(w.k, w.B, w.ratio, w.n, 1, w.layout, 0, hsa.FLAG_NO_IO)
     slots_n = torch.empty(w.n, w.k, dtype=torch.int32, device="cuda")
@@ -400,6 +416,7 @@ def bench_attend(args, torch, hsa, w):
                    "top_k": w.k, "heads": 16, "graph": True},
         "resolve_us_per_step": float(np.mean(res_ms)) * 1e3,
         "resolve_noio_us_per_step": noio_us,
+        "attention_f32_output_us": float(np.mean(f32_ms)) * 1e3,
         "misses_per_selection": float(m.mean()),
         "append": append,
         # resolution (table work, no row copies) + attention against HBM, over the sum of their

@@ -31,6 +31,7 @@ LAYOUT_BF16 = 0      # HS_KV_BF16_576
 LAYOUT_FP8 = 1       # HS_KV_FP8_MLA_656
 ENTRY_BYTES = {LAYOUT_BF16: 1152, LAYOUT_FP8: 656}
 FLAG_NO_IO = 0x1
+FLAG_ATTN_OUT_F32 = 0x2   # attention output in fp32 (P carried in fp32)
 EVICT_LRU, EVICT_FIFO, EVICT_RANDOM = 0, 1, 2   # hs_eviction
 DEVERR_TOKEN_RANGE = 0x1
 DEVERR_DUPLICATE = 0x2
@@ -156,6 +157,7 @@ class HiSparse:
         self._h = h
         self.top_k, self.B, self.n, self.L = top_k, device_buffer_size, max_requests, num_layers
         self.layout, self.heads = layout, num_heads
+        self.out_dtype = torch.float32 if flags & FLAG_ATTN_OUT_F32 else torch.bfloat16
         self.entry_bytes = ENTRY_BYTES[layout]
         self.capacity = host_to_device_ratio * device_buffer_size     # page-table entries
         self.page_tokens = page_tokens
@@ -264,7 +266,8 @@ class HiSparse:
         assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.shape[2] == 576
         assert slots.dtype == torch.int32 and slots.is_contiguous() and slots.shape == (n_req, self.top_k)
         if out is None:
-            out = torch.empty(n_req, q.shape[1], 512, dtype=torch.bfloat16, device=q.device)
+            out = torch.empty(n_req, q.shape[1], 512, dtype=self.out_dtype, device=q.device)
+        assert out.dtype == self.out_dtype and out.is_contiguous() and out.shape == (n_req, q.shape[1], 512)
         if lse is None:
             lse = torch.empty(n_req, q.shape[1], dtype=torch.float32, device=q.device)
         _check(lib().hs_attend(self._h, layer, n_req, q.data_ptr(), slots.data_ptr(), float(scale), out.data_ptr(),
@@ -281,7 +284,8 @@ class HiSparse:
         assert sel.dtype == torch.int32 and sel.is_contiguous() and sel.shape == (n_req, self.top_k)
         assert lens.dtype == torch.int32 and lens.is_contiguous() and lens.shape[0] >= n_req
         if out is None:
-            out = torch.empty(n_req, q.shape[1], 512, dtype=torch.bfloat16, device=q.device)
+            out = torch.empty(n_req, q.shape[1], 512, dtype=self.out_dtype, device=q.device)
+        assert out.dtype == self.out_dtype and out.is_contiguous() and out.shape == (n_req, q.shape[1], 512)
         if lse is None:
             lse = torch.empty(n_req, q.shape[1], dtype=torch.float32, device=q.device)
         _check(lib().hs_attend_pages(self._h, layer, n_req, q.data_ptr(), slots.data_ptr(), sel.data_ptr(),

@@ -35,7 +35,11 @@
 //    product of that block;
 //  * four token groups merge through LDS at the end; with splits > 1 each workgroup writes
 //    an unnormalised partial (max, sum, 16 x 512 values) and a second kernel combines them in
-//    split order.  (A last-arriving-workgroup combine needs a device-scope fence in every
+//    split order;
+//  * fp32-output mode: P enters the P V product as a sum of three bf16 terms (hi, mid, lo:
+//    each the round-to-nearest-even of what the previous ones leave), which carries P to 2^-27
+//    relative -- below fp32 rounding -- so the output is fp32 attention; it costs two more
+//    MFMAs per P V block.  (A last-arriving-workgroup combine needs a device-scope fence in every
 //    workgroup; on this chip each such fence writes back an XCD's L2, and they serialize.)
 
 #include <math.h>
@@ -68,7 +72,7 @@ struct AttendArgs {
   const int32_t* sel;     // [n_req][k >> lgP] the selection, or null (no length cut)
   const int32_t* len;     // [n_req] context length in tokens (with sel)
   const uint16_t* q;      // [n_req][heads][576] bf16
-  uint16_t* out;          // [n_req][heads][512] bf16
+  void* out;              // [n_req][heads][512] bf16, or fp32 in fp32-output mode
   float* lse;             // [n_req][heads] or null
   float* part;            // [n][splits][PART]
   int64_t stride;         // bytes between token rows
@@ -105,6 +109,9 @@ __device__ __forceinline__ s16x4 pack4_exact(const f32x4 x) {
   return __builtin_bit_cast(s16x4, v);
 }
 
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t packed) { return __uint_as_float(packed & 0xFFFF0000u); }
+
 // Four fp32 -> packed bf16, round to nearest even (two v_cvt_pk_bf16_f32).
 __device__ __forceinline__ s16x4 pack4_rne(float a, float b, float c, float d) {
   typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -113,6 +120,19 @@ __device__ __forceinline__ s16x4 pack4_rne(float a, float b, float c, float d) {
   v[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
   v[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){c, d}, bf16x2));
   return __builtin_bit_cast(s16x4, v);
+}
+
+// x[j] -> three packed bf16 terms with hi + mid + lo = x to 2^-27 relative: each term is the
+// round-to-nearest-even of the remainder the previous terms leave (subtractions exact in fp32).
+__device__ __forceinline__ void split3(const float (&x)[4], s16x4& hi, s16x4& mid, s16x4& lo) {
+  hi = pack4_rne(x[0], x[1], x[2], x[3]);
+  const u32x2 h = __builtin_bit_cast(u32x2, hi);
+  float r[4] = {x[0] - bf16_lo_to_f32(h[0]), x[1] - bf16_hi_to_f32(h[0]), x[2] - bf16_lo_to_f32(h[1]),
+                x[3] - bf16_hi_to_f32(h[1])};
+  mid = pack4_rne(r[0], r[1], r[2], r[3]);
+  const u32x2 m = __builtin_bit_cast(u32x2, mid);
+  lo = pack4_rne(r[0] - bf16_lo_to_f32(m[0]), r[1] - bf16_hi_to_f32(m[0]), r[2] - bf16_lo_to_f32(m[1]),
+                 r[3] - bf16_hi_to_f32(m[1]));
 }
 
 // Value offset (within the 576) of reduction block kb (0..17) for lane group g: latent
@@ -215,7 +235,7 @@ static_assert(attend_lds_bytes<0>() + kStaticLds <= kLdsLimit, "bf16 LDS budget"
 static_assert(attend_lds_bytes<1>() + kStaticLds <= kLdsLimit, "fp8 LDS budget");
 static_assert(kParkBytes <= attend_lds_bytes<0>() && kParkBytes <= attend_lds_bytes<1>(), "parking fits");
 
-template <int LAYOUT>
+template <int LAYOUT, bool F32>
 __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
   using G = TileGeo<LAYOUT>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -460,14 +480,20 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
         for (int j = 0; j < 4; ++j) O[tau][j] *= aj[j];
     }
 
-    s16x4 pa[2];
+    s16x4 pa[2], pm[2], pl[2];  // P (fp32-output mode: its hi, mid and lo bf16 terms)
     if (LAYOUT == 0) {
-      pa[0] = pack4_rne(p[0], p[1], p[2], p[3]);
+      if (F32) split3(p, pa[0], pm[0], pl[0]);
+      else pa[0] = pack4_rne(p[0], p[1], p[2], p[3]);
       pa[1] = pa[0];
+      pm[1] = pm[0];
+      pl[1] = pl[0];
     } else {
 #pragma unroll
-      for (int bb = 0; bb < 2; ++bb)
-        pa[bb] = pack4_rne(p[0] * sccur[0][bb], p[1] * sccur[1][bb], p[2] * sccur[2][bb], p[3] * sccur[3][bb]);
+      for (int bb = 0; bb < 2; ++bb) {
+        const float x[4] = {p[0] * sccur[0][bb], p[1] * sccur[1][bb], p[2] * sccur[2][bb], p[3] * sccur[3][bb]};
+        if (F32) split3(x, pa[bb], pm[bb], pl[bb]);
+        else pa[bb] = pack4_rne(x[0], x[1], x[2], x[3]);
+      }
     }
 
     // ---- tile t + 1's operands (its bytes landed before the last barrier); the last
@@ -485,8 +511,15 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
       const s16x4 P = pa[i >> 2];
       const f32x4 t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, sel0, zero, 0, 0, 0);
       const f32x4 t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, sel1, zero, 0, 0, 0);
-      O[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(P, pack4_exact(t0), O[2 * i], 0, 0, 0);
-      O[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(P, pack4_exact(t1), O[2 * i + 1], 0, 0, 0);
+      const s16x4 v0 = pack4_exact(t0), v1 = pack4_exact(t1);
+      if (F32) {  // smallest terms first
+        O[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl[i >> 2], v0, O[2 * i], 0, 0, 0);
+        O[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl[i >> 2], v1, O[2 * i + 1], 0, 0, 0);
+        O[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pm[i >> 2], v0, O[2 * i], 0, 0, 0);
+        O[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pm[i >> 2], v1, O[2 * i + 1], 0, 0, 0);
+      }
+      O[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(P, v0, O[2 * i], 0, 0, 0);
+      O[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(P, v1, O[2 * i + 1], 0, 0, 0);
     }
 
     const f32x4 partnext = qk(knext, scnext);
@@ -554,8 +587,11 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
     if (splits == 1) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (h0 + j < heads)
-          a.out[((int64_t)r * heads + h0 + j) * DV + col] = (uint16_t)bf16_rne(acc[j] * inv_l[h0 + j]);
+        if (h0 + j < heads) {
+          const int64_t o = ((int64_t)r * heads + h0 + j) * DV + col;
+          if (F32) ((float*)a.out)[o] = acc[j] * inv_l[h0 + j];
+          else ((uint16_t*)a.out)[o] = (uint16_t)bf16_rne(acc[j] * inv_l[h0 + j]);
+        }
     } else {
       // an unnormalised partial (per-head max and sum, 16 x 512 values); the combine kernel
       // that follows on the stream merges the splits (the kernel boundary makes these stores
@@ -573,8 +609,9 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
 constexpr int COMBINE_THREADS = 256;
 constexpr int COMBINE_BLOCKS = HMAX * DV / 4 / COMBINE_THREADS;
 
+template <bool F32>
 __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(const float* __restrict__ part, int splits, int heads,
-                                                                  uint16_t* __restrict__ out, float* __restrict__ lse) {
+                                                                  void* __restrict__ out, float* __restrict__ lse) {
   const int r = blockIdx.y;
   const int i4 = blockIdx.x * COMBINE_THREADS + threadIdx.x;   // float4 index within 16 x 512
   const int h = (4 * i4) / DV;
@@ -593,10 +630,15 @@ __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(const float* _
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  uint2 packed;
-  packed.x = bf16_rne(acc[0] * inv) | (bf16_rne(acc[1] * inv) << 16);
-  packed.y = bf16_rne(acc[2] * inv) | (bf16_rne(acc[3] * inv) << 16);
-  *(uint2*)(out + ((int64_t)r * heads + h) * DV + (4 * i4) % DV) = packed;
+  const int64_t o = ((int64_t)r * heads + h) * DV + (4 * i4) % DV;
+  if (F32) {
+    *(f32x4*)((float*)out + o) = acc * inv;
+  } else {
+    uint2 packed;
+    packed.x = bf16_rne(acc[0] * inv) | (bf16_rne(acc[1] * inv) << 16);
+    packed.y = bf16_rne(acc[2] * inv) | (bf16_rne(acc[3] * inv) << 16);
+    *(uint2*)((uint16_t*)out + o) = packed;
+  }
   if ((4 * i4) % DV == 0 && lse) lse[(int64_t)r * heads + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
@@ -625,9 +667,13 @@ size_t attend_partial_floats(const Geometry& g) {
 }
 
 void prepare_attend() {
-  (void)hipFuncSetAttribute((const void*)attend_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize,
+  (void)hipFuncSetAttribute((const void*)attend_kernel<0, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)attend_lds_bytes<0>());
-  (void)hipFuncSetAttribute((const void*)attend_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize,
+  (void)hipFuncSetAttribute((const void*)attend_kernel<1, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)attend_lds_bytes<1>());
+  (void)hipFuncSetAttribute((const void*)attend_kernel<0, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)attend_lds_bytes<0>());
+  (void)hipFuncSetAttribute((const void*)attend_kernel<1, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)attend_lds_bytes<1>());
   (void)hipGetLastError();
 }
@@ -640,7 +686,7 @@ hipError_t launch_attend(const Geometry& g, const LayerTables& t, int32_t n_req,
   a.sel = sel;
   a.len = len;
   a.q = (const uint16_t*)q;
-  a.out = (uint16_t*)out;
+  a.out = out;
   a.lse = lse;
   a.part = t.part;
   a.stride = g.entry_bytes;
@@ -656,14 +702,22 @@ hipError_t launch_attend(const Geometry& g, const LayerTables& t, int32_t n_req,
   if (a.splits > 1 && !a.part) return hipErrorInvalidValue;
   if (a.chunk > max_chunk(g)) return hipErrorInvalidValue;
   dim3 grid(a.splits, n_req);
-  if (g.layout == HS_KV_BF16_576)
-    hipLaunchKernelGGL(attend_kernel<0>, grid, dim3(NT), attend_lds_bytes<0>(), st, a);
-  else
-    hipLaunchKernelGGL(attend_kernel<1>, grid, dim3(NT), attend_lds_bytes<1>(), st, a);
+  const bool f32 = (g.flags & HS_FLAG_ATTN_OUT_F32) != 0;
+  if (g.layout == HS_KV_BF16_576) {
+    if (f32) hipLaunchKernelGGL((attend_kernel<0, true>), grid, dim3(NT), attend_lds_bytes<0>(), st, a);
+    else hipLaunchKernelGGL((attend_kernel<0, false>), grid, dim3(NT), attend_lds_bytes<0>(), st, a);
+  } else {
+    if (f32) hipLaunchKernelGGL((attend_kernel<1, true>), grid, dim3(NT), attend_lds_bytes<1>(), st, a);
+    else hipLaunchKernelGGL((attend_kernel<1, false>), grid, dim3(NT), attend_lds_bytes<1>(), st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(COMBINE_BLOCKS, n_req), dim3(COMBINE_THREADS), 0, st, t.part, a.splits, g.heads,
-                     (uint16_t*)out, lse);
+  if (f32)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(COMBINE_BLOCKS, n_req), dim3(COMBINE_THREADS), 0, st, t.part,
+                       a.splits, g.heads, out, lse);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(COMBINE_BLOCKS, n_req), dim3(COMBINE_THREADS), 0, st, t.part,
+                       a.splits, g.heads, out, lse);
   return hipGetLastError();
 }
 

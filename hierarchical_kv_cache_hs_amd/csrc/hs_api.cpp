@@ -95,7 +95,7 @@ hs_status plan(const hs_config* cfg, hs::Geometry* g, Layout* lay) {
   if (cfg->layout != HS_KV_BF16_576 && cfg->layout != HS_KV_FP8_MLA_656)
     return fail(HS_ERR_INVALID_ARG, "unknown KV layout");
   if (cfg->num_heads < 0 || cfg->num_heads > 16) return fail(HS_ERR_INVALID_ARG, "num_heads must lie in [0, 16]");
-  if (cfg->flags & ~HS_FLAG_NO_IO) return fail(HS_ERR_INVALID_ARG, "unknown flag bits");
+  if (cfg->flags & ~(HS_FLAG_NO_IO | HS_FLAG_ATTN_OUT_F32)) return fail(HS_ERR_INVALID_ARG, "unknown flag bits");
   if (cfg->eviction != HS_EVICT_LRU && cfg->eviction != HS_EVICT_FIFO && cfg->eviction != HS_EVICT_RANDOM)
     return fail(HS_ERR_INVALID_ARG, "unknown eviction policy");
   const int32_t P = cfg->page_tokens == 0 ? 1 : cfg->page_tokens;

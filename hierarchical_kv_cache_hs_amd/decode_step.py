@@ -38,7 +38,7 @@ class DecodeSteps:
         H = qs[0].shape[2]
         self.slots = torch.empty(L, n, k, dtype=torch.int32, device=dev)
         self.miss = torch.zeros(len(sels), L, n, dtype=torch.int32, device=dev)
-        self.out = torch.empty(L, n, H, 512, dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty(L, n, H, 512, dtype=hs.out_dtype, device=dev)
         self.lse = torch.empty(L, n, H, dtype=torch.float32, device=dev)
         self.stream = torch.cuda.Stream(device=dev)
         self.side = torch.cuda.Stream(device=dev)

@@ -67,6 +67,9 @@ typedef enum hs_kv_layout {
                               resolution cost alone (the paper's no-IO oracle); no host
                               pool is allocated (hs_host_bytes reports 0, hs_host_kv and
                               hs_offload return HS_ERR_UNSUPPORTED) */
+#define HS_FLAG_ATTN_OUT_F32 0x2u /* hs_attend / hs_attend_pages write fp32 output, with P
+                                     carried in fp32 through the P V product (the 1e-5 tier)
+                                     instead of rounded to bf16 */
 
 /*
  * Eviction policies.  LRU is the method (paper abstract; note, section 2); the others exist
@@ -241,8 +244,9 @@ hs_status hs_offload(hs_handle* h, int32_t layer, int32_t request, int64_t first
  *   d_q     [n_req][num_heads][576] bf16 queries (512 latent + 64 rope)
  *   d_slots [n_req][top_k] int32 slots from hs_resolve (-1 entries skipped)
  *   scale   softmax scale applied to q.K
- *   d_out   [n_req][num_heads][512] bf16: sum_j softmax_j(scale q.K_j) V_j,
- *           with K_j all 576 decoded values of slot j and V_j its first 512
+ *   d_out   [n_req][num_heads][512] bf16 (fp32 with HS_FLAG_ATTN_OUT_F32):
+ *           sum_j softmax_j(scale q.K_j) V_j, with K_j all 576 decoded values of
+ *           slot j and V_j its first 512
  *   d_lse   [n_req][num_heads] fp32 log-sum-exp of the scaled scores, or NULL
  * A row with no valid slot gives out = 0 and lse = -inf.  HS_ERR_UNSUPPORTED
  * when the handle was created with num_heads = 0.  With page_tokens = P > 1,

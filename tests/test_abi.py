@@ -81,6 +81,11 @@ def test_sizes_for_the_batch64_workload():
     assert slots + tables <= dev <= slots + tables + 64 * 1024
 
 
+def test_fp32_output_flag_is_accepted():
+    assert hsa.device_bytes(_cfg(flags=hsa.FLAG_ATTN_OUT_F32)) == hsa.device_bytes(_cfg())
+    assert hsa.device_bytes(_cfg(flags=hsa.FLAG_ATTN_OUT_F32 | hsa.FLAG_NO_IO)) > 0
+
+
 def test_no_io_mode_has_no_host_pool():
     assert hsa.host_bytes(_cfg(flags=hsa.FLAG_NO_IO)) == 0
     assert hsa.host_bytes(_cfg()) == 2 * 128 * 32 * 1152
