@@ -11,17 +11,22 @@
 //       load this thread's contiguous chunk of the LRU order into registers;
 //   P1  gather the page-table entry of every selected token (coalesced selection read,
 //       random 4-byte table reads); hits set their slot bit, misses their token bit
-//       (LDS atomics; a bit already set flags a repeated token);
+//       (LDS atomics; a bit already set flags a repeated token).  The same round trip reads
+//       the owners of the first k slots in LRU order, which hold every possible victim (the
+//       m-th non-hit slot lies at most k - m hits deep);
 //   P2  one packed block scan gives (a) for each word of the token bitmap the number of
 //       misses below it, so a miss's ascending-token rank is prefix[word] +
-//       popcount(lower bits of the word), and (b) each non-hit slot's rank in LRU order;
+//       popcount(lower bits of the word), and (b) each non-hit slot's rank in LRU order; the
+//       miss list (token of rank q) goes to LDS, and the fusing workgroup starts reading
+//       the first rows of its misses from host memory here, so the link is busy while the
+//       tables are finished (barriers from here on wait for LDS only);
 //   P3  the first m non-hit slots in LRU order are the victims; the remaining non-hit
 //       slots keep their order and move to position rank - m of the new order;
 //   P4  hit and victim slots, all stamped with this step, form the back of the new
 //       order in ascending slot index (a scan over the slot bitmap), together with any slot
-//       appended since the last resolve (hs_append stamps it with this step); the i-th miss takes
-//       victim i: evict its owner from the page table, install the token, stamp, and
-//       write the output slot;
+//       appended since the last resolve (hs_append stamps it with this step); the stamps are
+//       written in one coalesced pass over that bitmap; the i-th miss takes victim i: evict
+//       its owner from the page table, install the token and write the output slot;
 //   P5  the missing rows are copied from pinned host memory (zero-copy 16-byte loads over
 //       PCIe, row-major over the miss list so a wave reads ~1 KiB runs) into the victim
 //       slots.  hs_resolve does this inside the resolving workgroup (each request's copy
@@ -102,6 +107,11 @@ __device__ uint32_t random_rank(uint64_t key, uint32_t n, uint32_t x) {
   return x;
 }
 
+// A workgroup barrier that waits for this wave's LDS operations only.  From P2 on no thread
+// reads global memory another thread of the workgroup writes, so the global fence that
+// __syncthreads() adds is not needed -- and it would stall on the host reads in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Exclusive block-wide prefix sum of v; *total gets the block sum.  Every thread must call.
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63;
@@ -113,7 +123,7 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint3
     if (lane >= o) x += y;
   }
   if (lane == 63) wsum[wid] = x;
-  __syncthreads();
+  lds_barrier();
   uint32_t before = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
@@ -121,7 +131,7 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint3
     before += (w < wid) ? s : 0u;
     tot += s;
   }
-  __syncthreads();
+  lds_barrier();
   *total = tot;
   return before + x - v;
 }
@@ -148,7 +158,8 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
   uint32_t* missmap = hitmap + HB;              // [W]   missing tokens
   uint32_t* victims = missmap + W;              // [k]   victim slot of the i-th miss
   uint32_t* misstok = victims + k;              // [k]   token of the i-th miss (-1: none)
-  uint32_t* wsum = misstok + k;                 // [NW]  scan scratch
+  uint32_t* vowner = misstok + k;               // [k]   token held by victim i before the step (-1: none)
+  uint32_t* wsum = vowner + k;                  // [NW]  scan scratch
   uint32_t* freshmap = wsum + NW;               // [HB]  slots appended since the last resolve
   uint16_t* prefix = (uint16_t*)(freshmap + HB);  // [W] misses below each bitmap word
 
@@ -193,6 +204,16 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
       else p = pt[s];
     }
     ptv[j] = p;
+  }
+  const int policy = a.policy;
+  // A fusing workgroup under LRU or FIFO reads its first rows early (P2); it then takes the
+  // victims' owners from registers, since a global load after those reads would wait for them.
+  const bool early = MODE == FUSED && policy != HS_EVICT_RANDOM;
+  int32_t rmv[OPT];  // owners of this thread's LRU-order slots among the first k
+#pragma unroll
+  for (int x = 0; x < OPT; ++x) {
+    const int32_t j = ordv[x];
+    rmv[x] = (early && o0 + x < k && j >= 0 && j < B) ? rm[j] : -1;
   }
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
@@ -241,9 +262,42 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
       run += __popc(missmap[w]);
     }
   }
+  // rank q of a missing token = misses below it (ascending token order)
+  auto miss_rank = [&](int32_t s) -> int {
+    const int w = s >> 5;
+    return (int)prefix[w] + __popc(missmap[w] & ((1u << (s & 31)) - 1u));
+  };
+  constexpr int U = 4;
+  const int C = a.chunks;
+  const int total = m * C;
+  const uint8_t* host = a.host + (int64_t)r * cap * a.host_stride;
+  int qv[KPT];
+  v4i v0[U];
+  if (early) {
+    // the miss list, then the first rows of the misses, read while the tables are finished
+    // (no global load follows these reads before P5)
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      qv[j] = -1;
+      if (ptv[j] == -1) {
+        qv[j] = miss_rank(selv[j]);
+        if (qv[j] < k) misstok[qv[j]] = (uint32_t)selv[j];
+      }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = tid + u * NT;
+      if (idx < total) {
+        const int q = idx / C;
+        const int c = idx - q * C;
+        v0[u] = __builtin_nontemporal_load((const v4i*)(host + (int64_t)misstok[q] * a.host_stride) + c);
+      }
+    }
+  }
 
   // ---- P3
-  const int policy = a.policy;
   if (policy == HS_EVICT_RANDOM) {
     // Candidates are the non-hit slots in slot order; the q-th miss takes candidate
     // random_rank(q), found through per-word candidate counts (one bitmap word per thread)
@@ -257,7 +311,7 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
     uint32_t ncand;
     const uint32_t below = block_scan((uint32_t)__popc(cand), wsum, &ncand);
     if (tid < HB) cpre[tid] = below;
-    __syncthreads();
+    lds_barrier();
     const uint64_t key =
         splitmix64_at(a.seed, ((uint64_t)((int64_t)r * a.nlayers + a.layer) << 32) | (uint32_t)t);
     for (int q = tid; q < m && q < (int)ncand; q += NT) {
@@ -288,6 +342,7 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
       if (nhmask & (1u << x)) {
         if (rank < m) {
           victims[rank] = (uint32_t)j;
+          if (early) vowner[rank] = (uint32_t)rmv[x];
           atomicOr(&back[j >> 5], 1u << (j & 31));
         } else if (fresh_j) {
           // appended since the last resolve: its stamp is already this step's (appended
@@ -304,7 +359,7 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- P4
   if (policy != HS_EVICT_RANDOM) {
@@ -318,6 +373,14 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
       ord[pos++] = tid * 32 + b;
     }
   }
+  // stamps, coalesced: LRU -- hits, victims and appended slots (all in the hit bitmap by
+  // now); FIFO -- victims and appended slots (the fresh bitmap); RANDOM -- hits (its victims
+  // are stamped below)
+  {
+    const uint32_t* stampmap = (policy == HS_EVICT_FIFO) ? freshmap : hitmap;
+    for (int j = tid; j < B; j += NT)
+      if ((stampmap[j >> 5] >> (j & 31)) & 1u) st[j] = t;
+  }
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int i = tid + j * NT;
@@ -325,20 +388,18 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
       const int32_t p = ptv[j];
       int32_t out = -1;
       if (p >= 0) {
-        if (policy != HS_EVICT_FIFO) st[p] = t;  // FIFO: a hit does not refresh its slot
         out = p;
       } else if (p == -1) {
         const int32_t s = selv[j];
-        const int w = s >> 5;
-        const int q = (int)prefix[w] + __popc(missmap[w] & ((1u << (s & 31)) - 1u));
+        const int q = early ? qv[j] : miss_rank(s);
         const int32_t v = (q < m && q < nonhit) ? (int32_t)victims[q] : -1;
         int32_t tok = -1;
         if (v >= 0 && v < B) {
-          const int32_t old = rm[v];
+          const int32_t old = early ? (int32_t)vowner[q] : rm[v];
           if (old >= 0 && (int64_t)old < cap) pt[old] = -1;
           pt[s] = v;
           rm[v] = s;
-          st[v] = t;
+          if (policy == HS_EVICT_RANDOM) st[v] = t;
           out = v;
           tok = s;
         }
@@ -357,16 +418,25 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
     if (MODE == LIST) a.ml_cnt[r] = m;
   }
   if (MODE != FUSED) return;
-  __syncthreads();
+  lds_barrier();
 
   // ---- P5
   if (m == 0) return;
-  const int C = a.chunks;
-  const int total = m * C;
-  const uint8_t* host = a.host + (int64_t)r * cap * a.host_stride;
   uint8_t* buf = a.buf + (int64_t)r * a.req_stride;
-  constexpr int U = 4;
-  for (int base = tid; base < total; base += NT * U) {
+  int base0 = tid;
+  if (early) {  // the batch read in P2
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = tid + u * NT;
+      if (idx < total) {
+        const int q = idx / C;
+        const int c = idx - q * C;
+        if ((int32_t)misstok[q] >= 0) ((v4i*)(buf + (int64_t)victims[q] * a.slot_stride))[c] = v0[u];
+      }
+    }
+    base0 += NT * U;
+  }
+  for (int base = base0; base < total; base += NT * U) {
     v4i v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -492,7 +562,7 @@ void prepare_resolve() {
 size_t resolve_lds_bytes(int64_t cap, int32_t k, int32_t B) {
   const size_t W = (size_t)((cap + 31) >> 5);
   const size_t HB = (size_t)((B + 31) >> 5);
-  size_t words = 2 * HB + W + 2 * (size_t)k + NW;
+  size_t words = 2 * HB + W + 3 * (size_t)k + NW;
   size_t bytes = words * 4 + W * 2;
   return (bytes + 15) & ~(size_t)15;
 }
