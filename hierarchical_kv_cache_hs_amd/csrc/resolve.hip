@@ -17,9 +17,9 @@
 //   P2  one packed block scan gives (a) for each word of the token bitmap the number of
 //       misses below it, so a miss's ascending-token rank is prefix[word] +
 //       popcount(lower bits of the word), and (b) each non-hit slot's rank in LRU order; the
-//       miss list (token of rank q) goes to LDS, and the fusing workgroup starts reading
-//       the first rows of its misses from host memory here, so the link is busy while the
-//       tables are finished (barriers from here on wait for LDS only);
+//       miss list (token of rank q) goes to LDS, and with few requests the fusing workgroup
+//       starts reading the first rows of its misses from host memory here, so the link is
+//       busy while the tables are finished (barriers from here on wait for LDS only);
 //   P3  the first m non-hit slots in LRU order are the victims; the remaining non-hit
 //       slots keep their order and move to position rank - m of the new order;
 //   P4  hit and victim slots, all stamped with this step, form the back of the new
@@ -75,6 +75,7 @@ struct ResolveArgs {
   int32_t chunks;  // 16-byte chunks per row
   int32_t policy;  // hs_eviction
   int32_t layer, nlayers;
+  int32_t early_reads;  // FUSED: start the host reads in P2 (see launch_resolve)
 };
 
 // Output number c of SplitMix64 started from state s (Steele, Lea and Flood, OOPSLA 2014).
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
   const int policy = a.policy;
   // A fusing workgroup under LRU or FIFO reads its first rows early (P2); it then takes the
   // victims' owners from registers, since a global load after those reads would wait for them.
-  const bool early = MODE == FUSED && policy != HS_EVICT_RANDOM;
+  const bool early = MODE == FUSED && policy != HS_EVICT_RANDOM && a.early_reads;
   int32_t rmv[OPT];  // owners of this thread's LRU-order slots among the first k
 #pragma unroll
   for (int x = 0; x < OPT; ++x) {
@@ -598,6 +599,11 @@ hipError_t launch_resolve(const Geometry& g, const LayerTables& t, int32_t layer
   a.ml_slot = t.ml_slot;
   a.ml_cnt = t.ml_cnt;
   const int mode = (g.flags & HS_FLAG_NO_IO) ? TABLES : list_only ? LIST : FUSED;
+  // Early host reads pay off while the link would idle during the table phase: measured on
+  // the 2048-of-4096 workloads, they save 4-6 us per launch at 32-128 requests of 656-byte
+  // rows and ~4 us at 64 requests of 1152-byte rows, but cost 2-4 us from 128 requests of
+  // 1152-byte rows and 192 of 656-byte rows on, where other workgroups keep the link busy.
+  a.early_reads = n_req <= 96;
   const size_t lds = resolve_lds_bytes(g.cap, g.k, g.B);
   const int kpt = (g.k + NT - 1) / NT;
   const int opt = (g.B + NT - 1) / NT;
