@@ -58,7 +58,8 @@ class StateView(ctypes.Structure):
     _fields_ = [("page_table", ctypes.c_void_p), ("slot_owner", ctypes.c_void_p), ("slot_stamp", ctypes.c_void_p),
                 ("lru_order", ctypes.c_void_p), ("step", ctypes.c_void_p), ("kv_buffer", ctypes.c_void_p),
                 ("capacity", ctypes.c_int64), ("slot_stride", ctypes.c_int64), ("entry_bytes", ctypes.c_int64),
-                ("request_stride", ctypes.c_int64), ("page_tokens", ctypes.c_int64)]
+                ("request_stride", ctypes.c_int64), ("page_tokens", ctypes.c_int64),
+                ("fresh_slots", ctypes.c_void_p)]
 
 
 class HSError(RuntimeError):
@@ -314,6 +315,7 @@ class HiSparse:
             "slot_stamp": view(v.slot_stamp, n * B, torch.int32, (n, B)),
             "lru_order": view(v.lru_order, n * B, torch.int32, (n, B)),
             "step": view(v.step, n, torch.int32, (n,)),
+            "fresh_slots": view(v.fresh_slots, n * ((B + 31) // 32), torch.int32, (n, (B + 31) // 32)),
             # per request: B slot rows, then a row of zeros that padded attention entries read
             "kv_buffer": rows[:, :B],
             "zero_row": rows[:, B],

@@ -400,6 +400,7 @@ hs_status hs_device_state(hs_handle* h, int32_t layer, hs_state_view* v) {
   v->entry_bytes = h->g.entry_bytes;
   v->request_stride = h->g.req_stride;
   v->page_tokens = h->g.P;
+  v->fresh_slots = t.fresh;
   return HS_OK;
 }
 

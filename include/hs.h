@@ -135,6 +135,8 @@ typedef struct hs_state_view {
   int64_t entry_bytes;   /* bytes of one token's KV entry                               */
   int64_t request_stride; /* bytes between requests in kv_buffer ((B + 1) * slot_stride) */
   int64_t page_tokens;   /* tokens per slot (1 = token-granular)                        */
+  uint32_t* fresh_slots; /* [max_requests][(B + 31) / 32] bits: slots appended since the  */
+                         /* last resolve (their stamp is already the next step's)        */
 } hs_state_view;
 
 /* Bytes the device block must have for this configuration (0 and an error if invalid). */
@@ -283,7 +285,9 @@ hs_status hs_destroy(hs_handle* h);
 hs_status hs_host_kv(hs_handle* h, int32_t layer, int32_t request, void** ptr, int64_t* capacity,
                      int64_t* row_stride);
 
-/* Device pointers of one layer's tables and slot buffer. */
+/* Device pointers of one layer's tables and slot buffer.  Together with the host rows
+ * (hs_host_kv) they are the whole state carried from one step to the next: copying them
+ * into another handle of the same configuration, between steps, resumes the run there. */
 hs_status hs_device_state(hs_handle* h, int32_t layer, hs_state_view* view);
 
 /* Return requests first..first+count-1 of every layer to the empty state (enqueued on stream). */
