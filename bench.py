@@ -960,7 +960,7 @@ def main():
         summarize_profile(args)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0:
