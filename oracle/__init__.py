@@ -166,7 +166,7 @@ class OracleCache:
         resident (``orc_append``); returns the slot of each appended token (-1 for none).
         The step counters do not move: the stamp given is the next resolve's step."""
         if self.P != 1:
-            raise OracleError("append is defined for token-granular caches only")
+            return self._append_pages(layer, pos, rows)
         pos = np.ascontiguousarray(pos, dtype=np.int32)
         rows = np.ascontiguousarray(rows, dtype=np.uint8)
         assert rows.shape == (pos.shape[0], self.E)
@@ -190,6 +190,31 @@ class OracleCache:
             if host is not None:
                 self.host[r, layer] = host
             out[r] = slot.value
+        return out
+
+    def _append_pages(self, layer: int, pos: np.ndarray, rows: np.ndarray) -> np.ndarray:
+        """Write-through append with pages: each new token's row goes to its history position,
+        and into its page's slot when that page is resident (at row offset pos mod P).  No
+        table changes: a page that is not resident is fetched whole, new row included, when a
+        selection names it.  Returns the page's slot (-1 when not resident or no token)."""
+        pos = np.asarray(pos, dtype=np.int64)
+        rows = np.ascontiguousarray(rows, dtype=np.uint8)
+        assert rows.shape == (pos.shape[0], self.E_tok)
+        out = np.full(pos.shape[0], -1, dtype=np.int32)
+        for r in range(pos.shape[0]):
+            p = int(pos[r])
+            if p == -1:
+                continue
+            if p < 0 or p >= self.cap * self.P:
+                raise OracleError("append position out of range")
+            if self.host is not None:
+                self.host[r, layer, p] = rows[r]
+            c, o = p // self.P, p % self.P
+            j = int(self.PT[r, layer, c])
+            if j >= 0:
+                if self.dev is not None:
+                    self.dev[r, layer, j, o * self.E_tok:(o + 1) * self.E_tok] = rows[r]
+                out[r] = j
         return out
 
     def attend(self, layer: int, q: np.ndarray, slots: np.ndarray, scale: float):

@@ -11,7 +11,9 @@ tests/test_oracle_pins.py pins on its own:
   * a resident page's slot holds the P history rows of that page;
   * attention over pages equals attention over the same positions gathered straight from
     the history (only placement changes), cut at the context length, and it is the
-    log-sum-exp merge of the attentions over each page alone.
+    log-sum-exp merge of the attentions over each page alone;
+  * append writes the new row through to the history and to its resident page's slot,
+    leaves every table alone, and a page that was not resident arrives with the row.
 Each fails for a plausible slip: the page's rows taken from the wrong offset, a slot
 indexed in tokens instead of pages, a dropped or extra token at the length cut (< vs <=),
 a page counted once instead of P times.
@@ -177,7 +179,30 @@ def test_page_attention_is_lse_merge_of_single_pages():
     assert np.allclose(merged, out, rtol=0, atol=1e-12)
 
 
-def test_page_mode_rejects_append():
-    oc = oracle.OracleCache(1, 1, 4, 8, page_tokens=4)
+def test_page_append_writes_through_and_keeps_tables():
+    # a resident page takes the new row at its offset; a page that is not resident is left to
+    # the next miss, which fetches it whole with the new row; tables never change
+    rng = np.random.default_rng(12)
+    P, n, B, cap_pages, k = 4, 2, 5, 12, 3
+    host = rng.integers(0, 256, size=(n, 1, cap_pages * P, 1152), dtype=np.uint8)
+    oc = oracle.OracleCache(n, 1, B, cap_pages, host=host.copy(), page_tokens=P)
+    oc.resolve(0, np.array([[2, 7, 9], [0, 1, -1]], dtype=np.int32))
+    tables = (oc.PT.copy(), oc.RM.copy(), oc.ST.copy(), oc.t.copy())
+    rows = rng.integers(0, 256, size=(n, 1152), dtype=np.uint8)
+    slots = oc.append(0, np.array([7 * P + 3, 5 * P + 1]), rows)         # page 7 resident, page 5 not
+    assert slots[0] == oc.PT[0, 0, 7] and slots[1] == -1
+    for a, b in zip(tables, (oc.PT, oc.RM, oc.ST, oc.t)):
+        assert (a == b).all()
+    j = int(slots[0])
+    assert (oc.dev[0, 0, j].reshape(P, 1152)[3] == rows[0]).all()
+    assert (oc.host[0, 0, 7 * P + 3] == rows[0]).all() and (oc.host[1, 0, 5 * P + 1] == rows[1]).all()
+    for r in range(n):                                                    # resident pages = history pages
+        for jj in np.nonzero(oc.RM[r, 0] >= 0)[0]:
+            c = int(oc.RM[r, 0, jj])
+            assert (oc.dev[r, 0, jj] == oc.host[r, 0, c * P:(c + 1) * P].reshape(-1)).all()
+    oc.resolve(0, np.array([[2, 7, 9], [5, 0, -1]], dtype=np.int32))     # page 5 now fetched with its new row
+    j5 = int(oc.PT[1, 0, 5])
+    assert (oc.dev[1, 0, j5].reshape(P, 1152)[1] == rows[1]).all()
     with pytest.raises(oracle.OracleError):
-        oc.append(0, np.array([3], dtype=np.int32), np.zeros((1, 1152), dtype=np.uint8))
+        oc.append(0, np.array([cap_pages * P, -1]), rows)
+    assert oc.append(0, np.array([-1, -1]), rows).tolist() == [-1, -1]
