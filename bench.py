@@ -23,7 +23,8 @@ requests, fp8), in serial order and with layer-wise prefetch.
 --workload topk runs the on-GPU top-k from synthetic indexer scores into the resolver, one
 selection per layer (128 requests, 8 layers, 65536 tokens).
 --workload pages runs page-granular selections (pages of 16 tokens, 128 pages selected, 256
-page slots, 256 requests, fp8): whole steps of resolve + attention cut at the context length.
+page slots, 256 requests, fp8): whole steps of write-through append of the newest token, resolve,
+and attention cut at the context length.
 --workload sweep is the miss-count study: misses per selection for device buffers of 2048,
 4096 and 6144 slots under LRU, FIFO and RANDOM eviction (32 requests, 131072 tokens).
 """
@@ -687,7 +688,8 @@ def bench_topk(args, torch, hsa):
 
 def cpu_baseline_pages(w, trace, warm, budget_s=15.0, requests=16):
     """The oracle, as it stands, on whole steps of the page workload for a sample of requests:
-    page resolve (tables + page copies) then fp64 attention cut at the context length."""
+    append of the newest token, page resolve (tables + page copies), then fp64 attention cut
+    at the context length."""
     import oracle
     from synth import kv as skv
     P = w.page_tokens
@@ -703,20 +705,24 @@ def cpu_baseline_pages(w, trace, warm, budget_s=15.0, requests=16):
     while (done == 0 or el < budget_s) and t < trace.shape[0]:
         q = skv.queries(w.seed, t % 8, n, 0, 16)
         lens = np.full(n, w.len_tokens(t))
+        pos = lens - 1
+        new = np.stack([skv.rows_at(w.seed, r, 0, pos[r:r + 1], w.layout)[0] for r in range(n)])
         t0 = time.perf_counter()
+        oc.append(0, pos, new)
         slots, _ = oc.resolve(0, trace[t, :n])
         oc.attend_pages(0, q, slots, trace[t, :n], lens, 1.0 / math.sqrt(576))
         el += time.perf_counter() - t0
         done += 1
         t += 1
-    return {"value": n * done * w.k * P / el, "unit": "attended tokens/s (resolve + attention)", "cores": threads,
+    return {"value": n * done * w.k * P / el, "unit": "attended tokens/s (append + resolve + attention)", "cores": threads,
             "kind": "oracle",
-            "sample": f"oracle page resolve + fp64 attention of requests 0..{n - 1} on steps {warm}..{t - 1} "
+            "sample": f"oracle append + page resolve + fp64 attention of requests 0..{n - 1} on steps {warm}..{t - 1} "
                       f"({done} steps, {el:.1f} s)"}
 
 
 def bench_pages(args, torch, hsa, w):
-    """Page-granular selections: whole steps of resolve + attention cut at the context length."""
+    """Page-granular selections: whole steps of write-through append of the newest token,
+    resolve, and attention cut at the context length."""
     from synth import kv as skv
     from synth import trace as tr
 
@@ -734,6 +740,12 @@ def bench_pages(args, torch, hsa, w):
     log(f"host pool {hsa.host_bytes(hs.cfg) / 2**30:.2f} GiB filled in {time.perf_counter() - t0:.1f}s")
     qs = torch.from_numpy(np.stack([skv.queries(w.seed, t % 8, w.n, 0, 16) for t in range(8)]).view(np.int16)) \
         .cuda().view(torch.bfloat16)
+    # each step's newest token (position len - 1), appended before the step's resolve; its row
+    # is the history's own, so the appends keep history and device pages consistent
+    newest = np.array([w.len_tokens(t) - 1 for t in range(T)], dtype=np.int64)
+    d_pos = torch.from_numpy(np.repeat(newest[:, None], w.n, axis=1).astype(np.int32)).cuda()
+    d_new = torch.from_numpy(np.stack([skv.rows_at(w.seed, r, 0, newest, w.layout) for r in range(w.n)], axis=1)).cuda()
+    slot_new = torch.empty(w.n, dtype=torch.int32, device="cuda")
     slots = torch.empty(T, w.n, w.k, dtype=torch.int32, device="cuda")
     miss = torch.zeros(T, w.n, dtype=torch.int32, device="cuda")
     miss_r = torch.zeros(T, w.n, dtype=torch.int32, device="cuda")
@@ -755,6 +767,8 @@ def bench_pages(args, torch, hsa, w):
     def warm(h, m, attend):
         with torch.cuda.stream(stream):
             for t in range(args.warmup):
+                if attend:
+                    h.append(0, d_pos[t], d_new[t], slot_new, stream=stream)
                 h.resolve(0, d_trace[t], slots[t], m[t], stream=stream)
                 if attend:
                     h.attend_pages(0, qs[t % 8], slots[t], d_trace[t], lens[t], scale, out, lse, stream=stream)
@@ -777,11 +791,20 @@ def bench_pages(args, torch, hsa, w):
     with torch.cuda.stream(stream):
         with torch.cuda.graph(g, stream=stream):
             for t in range(args.warmup, T):
+                hs.append(0, d_pos[t], d_new[t], slot_new, stream=stream)
                 hs.resolve(0, d_trace[t], slots[t], miss[t], stream=stream)
                 hs.attend_pages(0, qs[t % 8], slots[t], d_trace[t], lens[t], scale, out, lse, stream=stream)
     region_ms = timed(g)
     del g
-    assert torch.equal(miss, miss_r)
+    assert torch.equal(miss, miss_r)      # appends change no table
+    # the appends alone, on the final state (write-through into resident pages and the history)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for t in range(args.warmup, T):
+                hs.append(0, d_pos[t], d_new[t], slot_new, stream=stream)
+    append_us = timed(g) / K * 1e3
+    del g
     # attention alone, cold (a 1 GiB read before each launch evicts the rows from the caches)
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     att_ms = []
@@ -827,7 +850,7 @@ def bench_pages(args, torch, hsa, w):
     fetch_Bps = m * w.n * page_bytes / (resolve_us * 1e-6)
     step_tokens = w.n * w.k * P
     line = {
-        "metric": "attended tokens/s through resolve + attention over page selections, 1 MI355X",
+        "metric": "attended tokens/s through append + resolve + attention over page selections, 1 MI355X",
         "value": step_tokens * K / (region_ms / 1e3),
         "unit": "attended tokens/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": region_ms / K,
@@ -835,6 +858,7 @@ def bench_pages(args, torch, hsa, w):
         "config": {"workload": w.description, "global_batch": w.n, "page_tokens": P, "seq_len": w.len_tokens(0),
                    "top_k_pages": w.k, "device_buffer_pages": w.B, "heads": 16, "graph": True},
         "page_selections_per_s": w.n * K / (region_ms / 1e3),
+        "append_us_per_step": append_us,
         "resolve_us_per_step": resolve_us,
         "resolve_noio_us_per_step": noio_us,
         "misses_per_selection_pages": m,

@@ -14,6 +14,11 @@
 // slots of the same (newest) stamp with a smaller index.  The victim of a non-resident token
 // is the array's first entry.  One workgroup per request; the array is staged in LDS for the
 // shift.
+//
+// With pages of P tokens (paper abstract: NSA and Quest select blocks of tokens) the append
+// writes through only: the row goes to the history, and into its page's slot at row offset
+// p mod P when that page is resident.  No table changes -- a page that is not resident is
+// fetched whole, new row included, the next time a selection names it.
 
 #include "hs_internal.h"
 
@@ -181,7 +186,50 @@ __global__ __launch_bounds__(OT) void offload_kernel(const uint8_t* __restrict__
   }
 }
 
+// Page-granular write-through: one wave per request, 16 bytes per lane and step.
+constexpr int PT_THREADS = 64;
+
+__global__ __launch_bounds__(PT_THREADS) void append_pages_kernel(
+    const int32_t* __restrict__ pos, const uint8_t* __restrict__ rows, int64_t row_stride,
+    const int32_t* __restrict__ pt, int64_t cap, int32_t lgP, int32_t B, uint8_t* __restrict__ buf, int64_t req_stride,
+    int64_t slot_stride, uint8_t* __restrict__ host, int64_t entry_bytes, int32_t* __restrict__ slot_out,
+    int32_t* __restrict__ err) {
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int32_t p = pos[r];
+  const int64_t cap_tokens = cap << lgP;
+  int32_t j = -1;
+  if (p >= 0 && (int64_t)p < cap_tokens) {
+    const int32_t c = p >> lgP;
+    const int32_t o = p & ((1 << lgP) - 1);
+    const int32_t v = pt[(int64_t)r * cap + c];
+    j = (v >= 0 && v < B) ? v : -1;
+    const int chunks = (int)(entry_bytes / 16);
+    const v4i* src = (const v4i*)(rows + (int64_t)r * row_stride);
+    v4i* hdst = host ? (v4i*)(host + ((int64_t)r * cap_tokens + p) * entry_bytes) : nullptr;
+    v4i* ddst = j >= 0 ? (v4i*)(buf + (int64_t)r * req_stride + (int64_t)j * slot_stride + (int64_t)o * entry_bytes)
+                       : nullptr;
+    for (int i = tid; i < chunks; i += PT_THREADS) {
+      const v4i x = src[i];
+      if (hdst) hdst[i] = x;
+      if (ddst) ddst[i] = x;
+    }
+  } else if (p != -1 && tid == 0) {
+    atomicOr(err, HS_DEVERR_TOKEN_RANGE);
+  }
+  if (tid == 0 && slot_out) slot_out[r] = j;
+}
+
 }  // namespace
+
+hipError_t launch_append_pages(const Geometry& g, const LayerTables& t, uint8_t* host_layer, int32_t n_req,
+                               const int32_t* pos, const void* rows, int64_t row_stride, int32_t* slot_out,
+                               int32_t* err, hipStream_t s) {
+  hipLaunchKernelGGL(append_pages_kernel, dim3(n_req), dim3(PT_THREADS), 0, s, pos, (const uint8_t*)rows, row_stride,
+                     t.pt, g.cap, g.lgP, g.B, t.buf, g.req_stride, g.slot_stride,
+                     (g.flags & HS_FLAG_NO_IO) ? nullptr : host_layer, g.entry_bytes, slot_out, err);
+  return hipGetLastError();
+}
 
 hipError_t launch_offload(const void* src, int64_t src_stride, uint8_t* dst_mapped, int64_t count, int64_t entry_bytes,
                           hipStream_t s) {

@@ -409,17 +409,18 @@ hs_status hs_append(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* d
   if (!h) return fail(HS_ERR_INVALID_ARG, "handle is NULL");
   if (layer < 0 || layer >= h->g.L) return fail(HS_ERR_INVALID_ARG, "layer out of range");
   if (n_req < 0 || n_req > h->g.n) return fail(HS_ERR_INVALID_ARG, "n_req out of range");
-  if (h->g.policy == HS_EVICT_RANDOM)
+  if (h->g.policy == HS_EVICT_RANDOM && h->g.P == 1)
     return fail(HS_ERR_UNSUPPORTED, "append needs a stamp-ordered eviction policy (LRU or FIFO)");
-  if (h->g.P != 1) return fail(HS_ERR_UNSUPPORTED, "append is token-granular (page_tokens must be 1)");
   if (n_req == 0) return HS_OK;
   if (!d_pos || !d_rows) return fail(HS_ERR_INVALID_ARG, "position or row pointer is NULL");
   if (row_stride < h->g.entry_bytes || row_stride % 16 || ((uintptr_t)d_rows) % 16)
     return fail(HS_ERR_INVALID_ARG, "rows must be 16-byte aligned, row_stride >= entry bytes and a multiple of 16");
   hs::LayerTables t = layer_tables(h, layer);
   uint8_t* host_layer = host_layer_of(h, layer);
-  hipError_t e = hs::launch_append(h->g, t, host_layer, n_req, d_pos, d_rows, row_stride, d_slot_out, h->err,
-                                   (hipStream_t)stream);
+  hipError_t e = h->g.P == 1 ? hs::launch_append(h->g, t, host_layer, n_req, d_pos, d_rows, row_stride, d_slot_out,
+                                                 h->err, (hipStream_t)stream)
+                             : hs::launch_append_pages(h->g, t, host_layer, n_req, d_pos, d_rows, row_stride,
+                                                       d_slot_out, h->err, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "append launch");
   return HS_OK;
 }

@@ -72,6 +72,12 @@ hipError_t launch_append(const Geometry& g, const LayerTables& t, uint8_t* host_
                          const int32_t* pos, const void* rows, int64_t row_stride, int32_t* slot_out, int32_t* err,
                          hipStream_t s);
 
+// Page-granular write-through append: each row goes to its history position and, when its
+// page is resident, into the page's slot at row offset pos mod P; no table changes.
+hipError_t launch_append_pages(const Geometry& g, const LayerTables& t, uint8_t* host_layer, int32_t n_req,
+                               const int32_t* pos, const void* rows, int64_t row_stride, int32_t* slot_out,
+                               int32_t* err, hipStream_t s);
+
 // Prefill offload of 16-byte-aligned rows with a padded stride into the pinned history
 // (dst_mapped: device-mapped address of the first destination row, rows packed).
 hipError_t launch_offload(const void* src, int64_t src_stride, uint8_t* dst_mapped, int64_t count, int64_t entry_bytes,

@@ -203,8 +203,11 @@ hs_status hs_fetch_misses(hs_handle* h, int32_t layer, int32_t n_req, void* stre
  * A position outside [0, capacity) is skipped and sets HS_DEVERR_TOKEN_RANGE.  With
  * HS_FLAG_NO_IO the tables change but no row moves.  Enqueue-only, graph-capturable.
  * A selection that names the token in the next resolve finds it resident (a hit).
- * HS_ERR_UNSUPPORTED with page_tokens > 1 (a new token's page would need the rest of its
- * rows fetched) or HS_EVICT_RANDOM.
+ * HS_ERR_UNSUPPORTED under HS_EVICT_RANDOM (token-granular handles).
+ * With page_tokens = P > 1 the append writes through only: the row goes to the history and,
+ * when its page d_pos[r] / P is resident, into that page's slot at row offset d_pos[r] mod P;
+ * no table changes (a page that is not resident arrives whole, new row included, when a
+ * selection names it), and d_slot_out gets the page's slot or -1.  Any eviction policy.
  */
 hs_status hs_append(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* d_pos, const void* d_rows,
                     int64_t row_stride, int32_t* d_slot_out, void* stream);

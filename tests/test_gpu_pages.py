@@ -3,7 +3,8 @@ families select blocks of consecutive tokens).  Bit-exact: page table, owners, s
 counters, output slots, miss counts and every byte of the resident pages, fused and split
 resolves, LRU / FIFO / RANDOM.  Attention within the fp64 oracle's tolerance (max abs 2e-2 on
 the bf16 output, 1e-3 on lse): over whole pages (hs_attend) and cut at the context length
-(hs_attend_pages), with padding pages, ragged lengths and the full-size page workload."""
+(hs_attend_pages), with padding pages, ragged lengths and the full-size page workload.  The
+page-granular append writes through to the history and to resident pages, bit-exact."""
 import math
 
 import numpy as np
@@ -232,13 +233,47 @@ def test_page_workload_full_size_sampled():
         p.close()
 
 
-def test_page_append_is_rejected_and_offload_is_per_token():
+@pytest.mark.parametrize("policy", [hsa.EVICT_LRU, hsa.EVICT_RANDOM])
+def test_page_append_writes_through(policy):
+    """Page-mode append against the oracle: rows land in the history and in resident pages'
+    slots, tables stay, pages brought in later carry the new rows, out-of-range positions flag."""
+    P, n, B, k, ratio = 8, 3, 24, 10, 5
+    say(f"pages append: P {P}, n {n}, B {B}, k {k}, policy {policy}")
+    rng = np.random.default_rng(70 + policy)
+    p = Pair(n, 1, k, B, ratio, hsa.LAYOUT_FP8, seed=19, policy=policy, policy_seed=4, page_tokens=P)
+    cap_tok = ratio * B * P
+    try:
+        for t in range(12):
+            pos = rng.integers(0, cap_tok, size=n).astype(np.int32)
+            if t % 3 == 0:
+                pos[0] = -1
+            sel = _page_trace(rng, n, ratio * B, k, 0.0)
+            for r in range(n):                    # half the time the new token's page is selected
+                if pos[r] >= 0 and rng.random() < 0.5 and pos[r] // P not in sel[r]:
+                    sel[r, 0] = pos[r] // P
+            rows = rng.integers(0, 256, size=(n, 656), dtype=np.uint8)
+            s_o = p.orc.append(0, pos, rows)
+            s_d = p.hs.append(0, torch.from_numpy(pos).cuda(), torch.from_numpy(rows).cuda())
+            torch.cuda.synchronize()
+            assert (s_d.cpu().numpy() == s_o).all(), f"step {t}: append slots"
+            for r in range(n):
+                assert (p.hs.host_kv(0, r) == p.orc.host[r, 0]).all(), f"step {t}: history rows"
+            p.check_state(0, n)                   # tables unchanged and slot bytes equal the oracle's
+            p.step(0, sel, check_state=True)
+        bad = np.array([cap_tok, -1, -1], dtype=np.int32)
+        s_d = p.hs.append(0, torch.from_numpy(bad).cuda(), torch.zeros(n, 656, dtype=torch.uint8, device="cuda"))
+        torch.cuda.synchronize()
+        assert (s_d.cpu().numpy() == -1).all()
+        assert p.hs.device_error() & hsa.DEVERR_TOKEN_RANGE
+        p.check_state(0, n)
+    finally:
+        p.close()
+
+
+def test_page_offload_is_per_token():
     P, n, B, k = 8, 2, 16, 4
     hs = hsa.HiSparse(k, B, 4, n, 1, hsa.LAYOUT_FP8, num_heads=16, page_tokens=P)
     try:
-        with pytest.raises(hsa.HSError):
-            hs.append(0, torch.zeros(n, dtype=torch.int32, device="cuda"),
-                      torch.zeros(n, 656, dtype=torch.uint8, device="cuda"))
         assert hs.host_kv(0, 1).shape == (4 * B * P, 656)
         rows = torch.from_numpy(skv.rows_at(2, 1, 0, np.arange(4 * B * P), hsa.LAYOUT_FP8)).cuda()
         hs.offload(0, 1, 0, rows)
