@@ -80,11 +80,11 @@ def test_page_resolve_policies(policy):
 
 @pytest.mark.parametrize("layout", [hsa.LAYOUT_BF16, hsa.LAYOUT_FP8])
 @pytest.mark.parametrize("P,k,B,heads,n", [(4, 50, 80, 16, 3), (16, 20, 40, 5, 2), (64, 6, 12, 16, 2),
-                                           (16, 128, 256, 16, 2)])
+                                           (16, 128, 256, 16, 2), (64, 256, 320, 16, 2)])
 def test_page_attention_matches_oracle(layout, P, k, B, heads, n):
     say(f"pages attend: P {P}, k {k}, B {B}, heads {heads}, n {n}, layout {layout}")
     rng = np.random.default_rng(P + k + heads + layout)
-    ratio = 4
+    ratio = 4 if k * P <= 8192 else 2          # 16384 attended tokens: 8 or 16 splits
     cap = ratio * B
     p = Pair(n, 1, k, B, ratio, layout, seed=23, heads=heads, page_tokens=P)
     try:
