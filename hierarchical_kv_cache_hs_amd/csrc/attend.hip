@@ -247,6 +247,7 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
   __shared__ float wl[GROUPS][HMAX];
   __shared__ float fac[GROUPS][HMAX];
   __shared__ float inv_l[HMAX];
+  __shared__ int wlast[WAVES];
 
   const int s = blockIdx.x;
   const int r = blockIdx.y;
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
   const int tok0 = s * a.chunk;
   const int tok1 = min(a.k, tok0 + a.chunk);
   const int ntok = tok1 > tok0 ? tok1 - tok0 : 0;
-  const int ntiles = (ntok + G::T - 1) / G::T;
+  const int ntiles_all = (ntok + G::T - 1) / G::T;
   const uint8_t* rbase = a.buf + (int64_t)r * a.rstride;
 
   // ---- this workgroup's row list (invalid, cut or missing -> -1) and this wave's Q operands
@@ -272,7 +273,8 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
     const int32_t* su = a.slots + (int64_t)r * ku;
     const int32_t* cu = a.sel ? a.sel + (int64_t)r * ku : nullptr;
     const int64_t len = a.sel ? (int64_t)a.len[r] : 0;
-    for (int i = tid; i < ntiles * G::T; i += NT) {
+    int last = 0;  // one past this thread's last valid entry
+    for (int i = tid; i < ntiles_all * G::T; i += NT) {
       int32_t v = -1;
       if (i < ntok) {
         const int tok = tok0 + i;
@@ -287,7 +289,11 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
         }
       }
       slot_lds[i] = v;
+      if (v >= 0) last = i + 1;
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o));
+    if (lane == 0) wlast[w] = last;
   }
   u32x4 qreg[KB_HALF];
 #pragma unroll
@@ -298,6 +304,11 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
   }
   __syncthreads();
   __builtin_amdgcn_s_waitcnt(0);
+  // tiles past the last valid entry (trailing padding: short contexts, cut pages) are skipped
+  int nvalid = 0;
+#pragma unroll
+  for (int v = 0; v < WAVES; ++v) nvalid = max(nvalid, wlast[v]);
+  const int ntiles = (nvalid + G::T - 1) / G::T;
 
   const int wu = __builtin_amdgcn_readfirstlane(w) & (WAVES - 1);  // the wave index, scalar and known < WAVES
   const int per = dma_per_tile<LAYOUT>(wu);

@@ -114,6 +114,30 @@ def test_ragged_shapes_and_padding(layout, heads, k, B, n):
         p.close()
 
 
+@pytest.mark.parametrize("layout", [hsa.LAYOUT_BF16, hsa.LAYOUT_FP8])
+@pytest.mark.parametrize("n", [4, 300])
+def test_trailing_padding(layout, n):
+    """Selections valid only in a prefix (short contexts): requests with 0, 1, 63, 64, 65, 300 and
+    all 2048 valid entries in one batch, one split and several; the tiles past the last valid
+    entry are skipped, which must not change the result."""
+    k, B, heads = 2048, 4096, 16
+    say(f"attend trailing padding: layout {layout}, n {n}")
+    rng = np.random.default_rng(5 + n + layout)
+    p = Pair(n, 1, k, B, 2, layout, seed=43, heads=heads)
+    try:
+        S = np.stack([rng.choice(2 * B, k, replace=False) for _ in range(n)]).astype(np.int32)
+        valid = [0, 1, 63, 64, 65, 300, k]
+        for r in range(n):
+            S[r, valid[r % len(valid)]:] = -1
+        slots, _ = p.step(0, S, check_state=False)
+        qb = skv.queries(43, 0, n, 0, heads)
+        out, lse, out_o, lse_o = _attend_pair(p, 0, qb, slots, heads)
+        _compare(out, lse, out_o, lse_o, "trailing padding")
+        assert (out[0].float() == 0).all() and torch.isneginf(lse[0]).all()
+    finally:
+        p.close()
+
+
 @pytest.mark.parametrize("layout,k,n", [(hsa.LAYOUT_FP8, 200, 3), (hsa.LAYOUT_BF16, 70, 2)])
 def test_padding_ignores_nan_rows(layout, k, n):
     """Padded (-1) and out-of-range slot entries contribute nothing even when every slot that
