@@ -659,11 +659,12 @@ int max_chunk(const Geometry& g) {
 
 }  // namespace
 
-int attend_splits(const Geometry& g) {
-  // one workgroup per compute unit at full batch (a workgroup's ring fills most of a CU's
-  // LDS), at most MAXCHUNK tokens per workgroup, and at least one 64-token tile each
+int attend_splits(const Geometry& g, int n_req) {
+  // A workgroup's ring fills most of a compute unit's LDS, so one runs per CU: the splits keep
+  // n_req * splits within the 256 CUs (one round -- a second, partial round costs more than the
+  // idle CUs of a floor), with at most MAXCHUNK tokens and at least one 64-token tile each.
   const int tokens = (int)attend_tokens(g);
-  int s = (256 + g.n - 1) / g.n;
+  int s = 256 / (n_req > 0 ? n_req : 1);
   const int by_len = (tokens + 63) / 64;
   const int need = (tokens + max_chunk(g) - 1) / max_chunk(g);
   if (s > by_len) s = by_len;
@@ -673,8 +674,13 @@ int attend_splits(const Geometry& g) {
 }
 
 size_t attend_partial_floats(const Geometry& g) {
-  const int s = attend_splits(g);
-  return s > 1 ? (size_t)s * PART : 0;
+  // per request slot: room for the largest n * splits(n) over the launch sizes the handle allows
+  int64_t most = 0;
+  for (int n = 1; n <= g.n; ++n) {
+    const int s = attend_splits(g, n);
+    if (s > 1 && (int64_t)n * s > most) most = (int64_t)n * s;
+  }
+  return most > 0 ? (size_t)((most + g.n - 1) / g.n) * PART : 0;
 }
 
 void prepare_attend() {
@@ -706,7 +712,7 @@ hipError_t launch_attend(const Geometry& g, const LayerTables& t, int32_t n_req,
   a.B = g.B * g.P;
   a.lgP = g.lgP;
   a.heads = g.heads;
-  a.splits = attend_splits(g);
+  a.splits = attend_splits(g, n_req);
   const int per = (a.k + a.splits - 1) / a.splits;
   a.chunk = (per + 15) / 16 * 16;
   a.scale_log2 = scale * kLog2e;

@@ -95,7 +95,7 @@ hipError_t launch_topk(const Geometry& g, int32_t n_req, const float* scores, in
 void prepare_attend();
 
 // Attention: split factor and partial-buffer floats per request.
-int attend_splits(const Geometry& g);
+int attend_splits(const Geometry& g, int n_req);
 size_t attend_partial_floats(const Geometry& g);
 
 // Tokens attended per request: every row of the k selected units.

@@ -114,6 +114,27 @@ def test_ragged_shapes_and_padding(layout, heads, k, B, n):
         p.close()
 
 
+def test_launch_sizes_below_the_handle_size():
+    """Splits follow each launch's request count (n_req * splits within the 256 compute units):
+    launches of 1, 17, 100, 129 and 200 requests on a 256-request handle, against the oracle."""
+    n, k, B, heads = 256, 512, 1024, 16
+    say("attend launch sizes: handle of 256 requests, launches of 1, 17, 100, 129, 200")
+    rng = np.random.default_rng(77)
+    p = Pair(n, 1, k, B, 2, hsa.LAYOUT_FP8, seed=53, heads=heads)
+    try:
+        S = np.stack([rng.choice(2 * B, k, replace=False) for _ in range(n)]).astype(np.int32)
+        slots, _ = p.step(0, S, check_state=False)
+        for nr in (1, 17, 100, 129, 200):
+            qb = skv.queries(53, nr, nr, 0, heads)
+            q = torch.from_numpy(qb.view(np.int16)).cuda().view(torch.bfloat16)
+            out, lse = p.hs.attend(0, q, torch.from_numpy(slots[:nr]).cuda(), SCALE)
+            torch.cuda.synchronize()
+            out_o, lse_o = p.orc.attend(0, qb, slots[:nr], SCALE)
+            _compare(out, lse, out_o, lse_o, f"{nr} requests")
+    finally:
+        p.close()
+
+
 @pytest.mark.parametrize("layout", [hsa.LAYOUT_BF16, hsa.LAYOUT_FP8])
 @pytest.mark.parametrize("n", [4, 300])
 def test_trailing_padding(layout, n):
