@@ -11,22 +11,25 @@
 //       load this thread's contiguous chunk of the LRU order into registers;
 //   P1  gather the page-table entry of every selected token (coalesced selection read,
 //       random 4-byte table reads); hits set their slot bit, misses their token bit
-//       (LDS atomics; a bit already set flags a repeated token).  The same round trip reads
-//       the owners of the first k slots in LRU order, which hold every possible victim (the
-//       m-th non-hit slot lies at most k - m hits deep);
+//       (LDS atomics; a bit already set flags a repeated token).  With early reads (P2) the
+//       same round trip reads the owners of the first k slots in LRU order, which hold every
+//       possible victim (the m-th non-hit slot lies at most k - m hits deep);
 //   P2  one packed block scan gives (a) for each word of the token bitmap the number of
 //       misses below it, so a miss's ascending-token rank is prefix[word] +
 //       popcount(lower bits of the word), and (b) each non-hit slot's rank in LRU order; the
 //       miss list (token of rank q) goes to LDS, and with few requests the fusing workgroup
 //       starts reading the first rows of its misses from host memory here, so the link is
 //       busy while the tables are finished (barriers from here on wait for LDS only);
-//   P3  the first m non-hit slots in LRU order are the victims; the remaining non-hit
-//       slots keep their order and move to position rank - m of the new order;
-//   P4  hit and victim slots, all stamped with this step, form the back of the new
-//       order in ascending slot index (a scan over the slot bitmap), together with any slot
-//       appended since the last resolve (hs_append stamps it with this step); the stamps are
-//       written in one coalesced pass over that bitmap; the i-th miss takes victim i: evict
-//       its owner from the page table, install the token and write the output slot;
+//   P3  LRU: the first m non-hit slots in LRU order are the victims; the remaining non-hit
+//       slots keep their order and move to position rank - m of the new order (FIFO: the
+//       order is by fill step, so hits keep their places too; RANDOM: the q-th miss takes
+//       the non-hit slot of rank perm(q), a keyed permutation, and no order is kept);
+//   P4  the slots stamped with this step -- under LRU hits and victims, under FIFO victims,
+//       and any slot appended since the last resolve (hs_append stamps it with this step) --
+//       form the back of the new order in ascending slot index (a scan over their bitmap);
+//       the stamps are written in one coalesced pass over that bitmap; the i-th miss takes
+//       victim i: evict its owner from the page table, install the token and write the
+//       output slot;
 //   P5  the missing rows are copied from pinned host memory (zero-copy 16-byte loads over
 //       PCIe, row-major over the miss list so a wave reads ~1 KiB runs) into the victim
 //       slots.  hs_resolve does this inside the resolving workgroup (each request's copy
