@@ -17,7 +17,7 @@ def test_trace_deterministic_and_seed_sensitive():
 
 
 @pytest.mark.parametrize("w", [C.TINY, C.BATCH64.with_(n=3, steps=30), C.FP8_256.with_(n=2, steps=40),
-                               C.SWEEP.with_(n=2, steps=20)])
+                               C.SWEEP.with_(n=2, steps=20), C.PAGES.with_(n=2, steps=40)])
 def test_trace_shape(w):
     sp = w.trace_spec()
     x = tr.generate(sp)
@@ -29,7 +29,7 @@ def test_trace_shape(w):
         prev = None
         for t in range(T):
             S = x[t, r]
-            L_t = sp.ctx + (t if sp.grow else 0)
+            L_t = sp.ctx + (-(-t // w.page_tokens) if sp.grow else 0)   # units: tokens or pages
             assert len(set(S.tolist())) == k
             assert S.min() >= 0 and S.max() < L_t
             window = set(range(L_t - sp.window, L_t))
@@ -42,6 +42,21 @@ def test_trace_shape(w):
             prev = hist
         # the emitted order is shuffled, not sorted
         assert not (np.diff(x[0, r]) > 0).all()
+
+
+def test_page_trace_tracks_a_token_growing_context():
+    # pages of P tokens over a context growing a token per step: at step t the context holds
+    # len_tokens(t) tokens, the newest (partly written) page is ceil(len / P) - 1, and the
+    # recency window always holds it
+    w = C.PAGES.with_(n=3, steps=50)
+    P = w.page_tokens
+    x = tr.generate(w.trace_spec())
+    for t in range(w.steps):
+        L = w.len_tokens(t)
+        assert L == w.ctx * P + t
+        newest = -(-L // P) - 1
+        assert (x[t].max(axis=1) == newest).all()
+        assert all(newest in set(x[t, r].tolist()) for r in range(w.n))
 
 
 def test_trace_prefix_is_stable():
