@@ -142,6 +142,34 @@ def measure_h2d_peak(torch, nbytes=1 << 30, reps=5):
     return nbytes / ms / 1e6
 
 
+def measure_hbm_peak(torch, hsa, nbytes=1 << 32, reps=5):
+    """Measured HBM rates on this GPU: the library's dense streaming read (16-byte loads over
+    4 GiB, far beyond the caches) and a device-to-device copy (bytes read + written over the
+    time).  The larger one is the measured peak the resolve + attention fraction is also
+    given against."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    hsa.stream_read(src, sink, stream)
+    half = src[: nbytes // 8]
+    dst = torch.empty_like(half)
+    dst.copy_(half)
+    torch.cuda.synchronize()
+    a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    a.record(stream)
+    for _ in range(reps):
+        hsa.stream_read(src, sink, stream)
+    b.record(stream)
+    for _ in range(reps):
+        dst.copy_(half)
+    c.record(stream)
+    torch.cuda.synchronize()
+    read = nbytes / (a.elapsed_time(b) / reps) / 1e6
+    copy = nbytes / (b.elapsed_time(c) / reps) / 1e6
+    del src, dst, half, sink
+    return {"read_GBps": read, "copy_GBps": copy, "peak_GBps": max(copy, read)}
+
+
 def cpu_baseline_resolve(w, trace, warm, budget_s=15.0):
     """The oracle, as it stands, on the timed steps of the same trace.
 
@@ -399,6 +427,7 @@ def bench_attend(args, torch, hsa, w):
     del gn
     hs_noio.close()
     res_ms = [region_ms / args.steps - float(np.mean(att_ms))]
+    overlap = bench_overlap_leg(args, torch, hsa, w, hs, d_trace, qs, miss, stream, timed, scale, region_ms)
     append = bench_append_leg(args, torch, hsa, w, d_trace, miss, stream, timed)
     K = args.steps
     att_s = float(np.mean(att_ms)) / 1e3
@@ -407,6 +436,9 @@ def bench_attend(args, torch, hsa, w):
     achieved = att_bytes / att_s / 1e9
     m = miss[args.warmup:].cpu().numpy().astype(np.int64)
     traffic = recorded_traffic("attend_fp8_256", "attend.hip")
+    ra_bytes = w.n * (16 * w.k + 4 * w.B + 16 * float(m.mean())) + att_bytes
+    hbm = measure_hbm_peak(torch, hsa)
+    log(f"HBM measured: copy {hbm['copy_GBps']:.0f} GB/s, read {hbm['read_GBps']:.0f} GB/s")
     out_line = {
         "metric": "attention tokens/s over resolved slots, 1 MI355X",
         "value": w.n * w.k / att_s,
@@ -420,16 +452,19 @@ def bench_attend(args, torch, hsa, w):
         "attention_f32_output_us": float(np.mean(f32_ms)) * 1e3,
         "misses_per_selection": float(m.mean()),
         "append": append,
+        "attend_while_fetching": overlap,
         # resolution (table work, no row copies) + attention against HBM, over the sum of their
         # times: per selection 16k + 4B + 16m bytes of tables plus the attention bytes
         "hbm_resolve_plus_attend": {
-            "bytes": w.n * (16 * w.k + 4 * w.B + 16 * float(m.mean())) + att_bytes,
+            "bytes": ra_bytes,
             "us": noio_us + att_s * 1e6,
-            "frac": (w.n * (16 * w.k + 4 * w.B + 16 * float(m.mean())) + att_bytes)
-                    / ((noio_us * 1e-6 + att_s) * HBM_PEAK_GBPS * 1e9)},
+            "frac": ra_bytes / ((noio_us * 1e-6 + att_s) * HBM_PEAK_GBPS * 1e9),
+            "hbm_measured": hbm,
+            "frac_of_measured_peak": ra_bytes / ((noio_us * 1e-6 + att_s) * hbm["peak_GBps"] * 1e9)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic, "kernel": "attend_kernel",
-                     "avg_kernel_us": att_s * 1e6, "algorithmic_bytes_per_launch": att_bytes},
+                     "avg_kernel_us": att_s * 1e6, "algorithmic_bytes_per_launch": att_bytes,
+                     "frac_of_measured_peak": achieved / hbm["peak_GBps"]},
     }
     hs.close()
     return out_line
@@ -449,6 +484,41 @@ def measure_d2h_peak(torch, nbytes=1 << 30, reps=5):
     ms = a.elapsed_time(b) / reps
     del src, dst
     return nbytes / ms / 1e6
+
+
+def bench_overlap_leg(args, torch, hsa, w, hs, d_trace, qs, miss_serial, stream, timed, scale, serial_ms):
+    """The same steps with the attention of the resident tokens overlapping the miss copy:
+    list-only resolve, then the copy on a second stream beside the resident part of the
+    attention, then the fetched part and the merge; captured in one graph with the fork and
+    join of the two streams.  The handle is reset to the empty state and replays the trace."""
+    from hierarchical_kv_cache_hs_amd.decode_step import attend_while_fetching
+    T = args.warmup + args.steps
+    side = torch.cuda.Stream()
+    slots = torch.empty(w.n, w.k, dtype=torch.int32, device="cuda")
+    miss = torch.zeros(T, w.n, dtype=torch.int32, device="cuda")
+    out = torch.empty(w.n, 16, 512, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(w.n, 16, dtype=torch.float32, device="cuda")
+    hs.reset_requests(0, w.n, stream=stream)
+    with torch.cuda.stream(stream):
+        for t in range(args.warmup):
+            attend_while_fetching(hs, 0, d_trace[t], qs[t % 8], scale, slots, miss[t], out, lse, stream, side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(args.steps):
+                t = args.warmup + i
+                attend_while_fetching(hs, 0, d_trace[t], qs[t % 8], scale, slots, miss[t], out, lse, stream, side)
+    ms = timed(g)
+    assert torch.equal(miss[args.warmup:], miss_serial[args.warmup:])
+    # the fused resolve (tables and copy in one kernel) then the attention, as timed above
+    step_us = ms / args.steps * 1e3
+    log(f"attend while fetching: {step_us:.1f} us per step against {serial_ms / args.steps * 1e3:.1f} serial")
+    del g
+    return {"us_per_step": step_us, "serial_us_per_step": serial_ms / args.steps * 1e3,
+            "saved_frac": 1.0 - ms / serial_ms,
+            "attended_tokens_per_s_whole_step": w.n * w.k / (step_us * 1e-6),
+            "selections_per_s_whole_step": w.n / (step_us * 1e-6)}
 
 
 def bench_append_leg(args, torch, hsa, w, d_trace, miss_plain, stream, timed):

@@ -43,7 +43,7 @@ SYMBOLS = ("hs_create", "hs_resolve", "hs_resolve_tables", "hs_fetch_misses", "h
            "hs_append", "hs_offload", "hs_topk",
            "hs_device_bytes", "hs_host_bytes", "hs_host_kv",
            "hs_device_state", "hs_reset_requests", "hs_get_device_error", "hs_status_string",
-           "hs_last_error_message")
+           "hs_last_error_message", "hs_stream_read", "hs_attend_resident", "hs_attend_fetched")
 
 
 class Config(ctypes.Structure):
@@ -91,6 +91,9 @@ def lib():
         L.hs_attend.argtypes = [p, i32, i32, p, p, ctypes.c_float, p, p, p]
         L.hs_attend_pages.argtypes = [p, i32, i32, p, p, p, p, ctypes.c_float, p, p, p]
         L.hs_destroy.argtypes = [p]
+        L.hs_stream_read.argtypes = [p, ctypes.c_size_t, p, p]
+        L.hs_attend_resident.argtypes = [p, i32, i32, p, p, p, p, ctypes.c_float, p]
+        L.hs_attend_fetched.argtypes = [p, i32, i32, p, p, ctypes.c_float, p, p, p]
         L.hs_host_kv.argtypes = [p, i32, i32, ctypes.POINTER(p), ctypes.POINTER(ctypes.c_int64),
                                  ctypes.POINTER(ctypes.c_int64)]
         L.hs_device_state.argtypes = [p, i32, ctypes.POINTER(StateView)]
@@ -102,7 +105,8 @@ def lib():
         L.hs_last_error_message.restype = ctypes.c_char_p
         for name in ("hs_device_bytes", "hs_host_bytes", "hs_create", "hs_resolve", "hs_resolve_tables",
                      "hs_fetch_misses", "hs_attend", "hs_attend_pages", "hs_destroy",
-                     "hs_host_kv", "hs_device_state", "hs_reset_requests", "hs_get_device_error"):
+                     "hs_host_kv", "hs_device_state", "hs_reset_requests", "hs_get_device_error",
+                     "hs_stream_read", "hs_attend_resident", "hs_attend_fetched"):
             getattr(L, name).restype = ctypes.c_int
         _lib_cache = L
     return _lib_cache
@@ -129,6 +133,14 @@ def host_bytes(cfg: Config) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().hs_host_bytes(ctypes.byref(cfg), ctypes.byref(n)))
     return n.value
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Enqueue the library's dense streaming read of `src` (a measurement helper, not a step
+    of the method); `sink` is a one-element int32 cuda tensor the kernel may overwrite."""
+    assert src.is_cuda and src.is_contiguous() and sink.is_cuda and sink.dtype == torch.int32
+    _check(lib().hs_stream_read(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(),
+                                _stream_ptr(stream)))
 
 
 def _stream_ptr(stream) -> int:
@@ -292,6 +304,39 @@ class HiSparse:
         _check(lib().hs_attend_pages(self._h, layer, n_req, q.data_ptr(), slots.data_ptr(), sel.data_ptr(),
                                      lens.data_ptr(), float(scale), out.data_ptr(), lse.data_ptr(),
                                      _stream_ptr(stream)))
+        return out, lse
+
+    def attend_resident(self, layer: int, q: torch.Tensor, slots: torch.Tensor, scale: float,
+                        sel: torch.Tensor | None = None, lens: torch.Tensor | None = None, stream=None):
+        """hs_attend_resident: after resolve_tables, attend the entries outside this step's victim
+        slots into the handle's partials (may run beside fetch_misses of the same layer)."""
+        n_req = q.shape[0]
+        assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.shape[2] == 576
+        assert slots.dtype == torch.int32 and slots.is_contiguous() and slots.shape == (n_req, self.top_k)
+        assert (sel is None) == (lens is None)
+        if sel is not None:
+            assert sel.dtype == torch.int32 and sel.is_contiguous() and sel.shape == (n_req, self.top_k)
+            assert lens.dtype == torch.int32 and lens.is_contiguous() and lens.shape[0] >= n_req
+        _check(lib().hs_attend_resident(self._h, layer, n_req, q.data_ptr(), slots.data_ptr(),
+                                        None if sel is None else sel.data_ptr(),
+                                        None if lens is None else lens.data_ptr(), float(scale),
+                                        _stream_ptr(stream)))
+
+    def attend_fetched(self, layer: int, q: torch.Tensor, scale: float, out: torch.Tensor | None = None,
+                       lse: torch.Tensor | None = None, lens: torch.Tensor | None = None, stream=None):
+        """hs_attend_fetched: after fetch_misses and attend_resident, attend the misses and merge."""
+        n_req = q.shape[0]
+        assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.shape[2] == 576
+        if lens is not None:
+            assert lens.dtype == torch.int32 and lens.is_contiguous() and lens.shape[0] >= n_req
+        if out is None:
+            out = torch.empty(n_req, q.shape[1], 512, dtype=self.out_dtype, device=q.device)
+        assert out.dtype == self.out_dtype and out.is_contiguous() and out.shape == (n_req, q.shape[1], 512)
+        if lse is None:
+            lse = torch.empty(n_req, q.shape[1], dtype=torch.float32, device=q.device)
+        _check(lib().hs_attend_fetched(self._h, layer, n_req, q.data_ptr(),
+                                       None if lens is None else lens.data_ptr(), float(scale), out.data_ptr(),
+                                       lse.data_ptr(), _stream_ptr(stream)))
         return out, lse
 
     # -- state -----------------------------------------------------------------------------------

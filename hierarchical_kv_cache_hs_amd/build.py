@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhs.so")
 
-SOURCES = ["hs_api.cpp", "resolve.hip", "attend.hip", "append.hip", "topk.hip"]
+SOURCES = ["hs_api.cpp", "resolve.hip", "attend.hip", "append.hip", "topk.hip", "calibrate.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -36,6 +36,11 @@
 //  * four token groups merge through LDS at the end; with splits > 1 each workgroup writes
 //    an unnormalised partial (max, sum, 16 x 512 values) and a second kernel combines them in
 //    split order;
+//  * a step whose misses are still being copied (hs_fetch_misses) can attend in two parts:
+//    the resident part skips the step's victim slots (an LDS bitmap of the miss list, built
+//    in the prologue inside the then idle ring) and may run while the copy writes those
+//    slots; the fetched part walks the compact miss list once the rows have landed; both
+//    write split partials and the combine kernel merges them in fixed order;
 //  * fp32-output mode: P enters the P V product as a sum of three bf16 terms (hi, mid, lo:
 //    each the round-to-nearest-even of what the previous ones leave), which carries P to 2^-27
 //    relative -- below fp32 rounding -- so the output is fp32 attention; it costs two more
@@ -74,12 +79,26 @@ struct AttendArgs {
   const uint16_t* q;      // [n_req][heads][576] bf16
   void* out;              // [n_req][heads][512] bf16, or fp32 in fp32-output mode
   float* lse;             // [n_req][heads] or null
-  float* part;            // [n][splits][PART]
+  float* part;            // [n][part_stride][PART]
+  const int32_t* ml_slot; // [n_req][k >> lgP] this step's victim slots, miss list order (parts)
+  const int32_t* ml_tok;  // [n_req][k >> lgP] the units fetched into them
+  const int32_t* ml_cnt;  // [n_req] misses of this step
   int64_t stride;         // bytes between token rows
   int64_t rstride;        // bytes between requests: B token rows, then zero rows
   int32_t k, B, heads, chunk, splits;   // k and B count token rows (units times P)
   int32_t lgP;            // log2 of the rows per slot
+  int32_t part_mode;      // ATT_ALL, ATT_RESIDENT or ATT_FETCHED
+  int32_t part_stride;    // partials per request in `part`
+  int32_t part0;          // this launch's first partial
+  int32_t to_part;        // write partials even with one split
   float scale_log2;       // softmax scale * log2(e)
+};
+
+// Which entries a launch attends.
+enum PartMode : int {
+  ATT_ALL = 0,       // every valid entry of the slot list
+  ATT_RESIDENT = 1,  // the entries whose slot is not one of this step's victims
+  ATT_FETCHED = 2,   // the miss list: the rows just copied into the victim slots
 };
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *(const u32x4*)p; }
@@ -270,17 +289,36 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
   {
     const int lg = a.lgP;
     const int ku = a.k >> lg, bu = a.B >> lg;
-    const int32_t* su = a.slots + (int64_t)r * ku;
-    const int32_t* cu = a.sel ? a.sel + (int64_t)r * ku : nullptr;
-    const int64_t len = a.sel ? (int64_t)a.len[r] : 0;
+    const int mode = a.part_mode;
+    const int32_t* su = (mode == ATT_FETCHED ? a.ml_slot : a.slots) + (int64_t)r * ku;
+    const int32_t* cu = nullptr;  // the units, where the context length cuts
+    if (a.len) cu = (mode == ATT_FETCHED ? a.ml_tok : a.sel) + (int64_t)r * ku;
+    const int64_t len = a.len ? (int64_t)a.len[r] : 0;
+    int units = ku;  // entries of the list
+    uint32_t* vbits = (uint32_t*)ring;  // ATT_RESIDENT: this step's victim slots (prologue only)
+    if (mode != ATT_ALL) {
+      const int m = a.ml_cnt[r];
+      units = m < 0 ? 0 : (m < ku ? m : ku);
+    }
+    if (mode == ATT_RESIDENT) {
+      for (int x = tid; x < (bu + 31) >> 5; x += NT) vbits[x] = 0u;
+      __syncthreads();
+      const int32_t* vs = a.ml_slot + (int64_t)r * ku;
+      for (int q = tid; q < units; q += NT) {
+        const int32_t j = vs[q];
+        if (j >= 0 && j < bu) atomicOr(&vbits[j >> 5], 1u << (j & 31));
+      }
+      __syncthreads();
+      units = ku;
+    }
     int last = 0;  // one past this thread's last valid entry
     for (int i = tid; i < ntiles_all * G::T; i += NT) {
       int32_t v = -1;
       if (i < ntok) {
         const int tok = tok0 + i;
         const int u = tok >> lg, o = tok & ((1 << lg) - 1);
-        const int32_t j = su[u];
-        if (j >= 0 && j < bu) {
+        const int32_t j = u < units ? su[u] : -1;
+        if (j >= 0 && j < bu && !(mode == ATT_RESIDENT && ((vbits[j >> 5] >> (j & 31)) & 1u))) {
           v = (j << lg) + o;
           if (cu) {
             const int32_t c = cu[u];
@@ -559,8 +597,8 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) o_park[((tg * 2 + hf) * 16 + i) * 64 + lane] = O[i];
   __syncthreads();
-  const int splits = a.splits;
-  float* mypart = a.part + ((int64_t)r * splits + s) * PART;  // used when splits > 1
+  const bool direct = a.splits == 1 && !a.to_part;  // else write partials for the combine kernel
+  float* mypart = a.part + ((int64_t)r * a.part_stride + a.part0 + s) * PART;
   if (tid < HMAX) {
     const int h = tid;
     float M = wm[0][h];
@@ -573,7 +611,7 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
       fac[v][h] = f;
       L += f * wl[v][h];
     }
-    if (splits == 1) {
+    if (direct) {
       inv_l[h] = L > 0.f ? 1.f / L : 0.f;
       if (a.lse && h < heads) a.lse[(int64_t)r * heads + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
     } else {
@@ -595,7 +633,7 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
       for (int j = 0; j < 4; ++j) acc[j] += fac[v][h0 + j] * o[j];
     }
     const int col = out_col(16 * he + tau, ln & 15);
-    if (splits == 1) {
+    if (direct) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (h0 + j < heads) {
@@ -673,14 +711,22 @@ int attend_splits(const Geometry& g, int n_req) {
   return s < 1 ? 1 : s;
 }
 
+// Splits of the fetched part: the whole miss list may fill the selection, MAXCHUNK tokens each.
+int fetched_splits(const Geometry& g) {
+  const int tokens = (int)attend_tokens(g);
+  return (tokens + max_chunk(g) - 1) / max_chunk(g);
+}
+
 size_t attend_partial_floats(const Geometry& g) {
-  // per request slot: room for the largest n * splits(n) over the launch sizes the handle allows
+  // per request slot: room for the largest n * (partials per request) over the launch sizes the
+  // handle allows -- a split launch, or a resident part and a fetched part
   int64_t most = 0;
+  const int sf = fetched_splits(g);
   for (int n = 1; n <= g.n; ++n) {
-    const int s = attend_splits(g, n);
-    if (s > 1 && (int64_t)n * s > most) most = (int64_t)n * s;
+    const int s = attend_splits(g, n) + sf;
+    if ((int64_t)n * s > most) most = (int64_t)n * s;
   }
-  return most > 0 ? (size_t)((most + g.n - 1) / g.n) * PART : 0;
+  return (size_t)((most + g.n - 1) / g.n) * PART;
 }
 
 void prepare_attend() {
@@ -695,9 +741,40 @@ void prepare_attend() {
   (void)hipGetLastError();
 }
 
+namespace {
+
+hipError_t launch_combine(const Geometry& g, const LayerTables& t, int32_t n_req, int parts, void* out, float* lse,
+                          hipStream_t st) {
+  if (g.flags & HS_FLAG_ATTN_OUT_F32)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(COMBINE_BLOCKS, n_req), dim3(COMBINE_THREADS), 0, st, t.part, parts,
+                       g.heads, out, lse);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(COMBINE_BLOCKS, n_req), dim3(COMBINE_THREADS), 0, st, t.part,
+                       parts, g.heads, out, lse);
+  return hipGetLastError();
+}
+
+void launch_kernel(const Geometry& g, const AttendArgs& a, int32_t n_req, hipStream_t st) {
+  dim3 grid(a.splits, n_req);
+  const bool f32 = (g.flags & HS_FLAG_ATTN_OUT_F32) != 0;
+  if (g.layout == HS_KV_BF16_576) {
+    if (f32) hipLaunchKernelGGL((attend_kernel<0, true>), grid, dim3(NT), attend_lds_bytes<0>(), st, a);
+    else hipLaunchKernelGGL((attend_kernel<0, false>), grid, dim3(NT), attend_lds_bytes<0>(), st, a);
+  } else {
+    if (f32) hipLaunchKernelGGL((attend_kernel<1, true>), grid, dim3(NT), attend_lds_bytes<1>(), st, a);
+    else hipLaunchKernelGGL((attend_kernel<1, false>), grid, dim3(NT), attend_lds_bytes<1>(), st, a);
+  }
+}
+
+}  // namespace
+
 hipError_t launch_attend(const Geometry& g, const LayerTables& t, int32_t n_req, const void* q, const int32_t* slots,
                          const int32_t* sel, const int32_t* len, float scale, void* out, float* lse, hipStream_t st) {
   AttendArgs a;
+  a.ml_slot = a.ml_tok = a.ml_cnt = nullptr;
+  a.part_mode = ATT_ALL;
+  a.part0 = 0;
+  a.to_part = 0;
   a.buf = t.buf;
   a.slots = slots;
   a.sel = sel;
@@ -713,29 +790,53 @@ hipError_t launch_attend(const Geometry& g, const LayerTables& t, int32_t n_req,
   a.lgP = g.lgP;
   a.heads = g.heads;
   a.splits = attend_splits(g, n_req);
+  a.part_stride = a.splits;
   const int per = (a.k + a.splits - 1) / a.splits;
   a.chunk = (per + 15) / 16 * 16;
   a.scale_log2 = scale * kLog2e;
   if (a.splits > 1 && !a.part) return hipErrorInvalidValue;
   if (a.chunk > max_chunk(g)) return hipErrorInvalidValue;
-  dim3 grid(a.splits, n_req);
-  const bool f32 = (g.flags & HS_FLAG_ATTN_OUT_F32) != 0;
-  if (g.layout == HS_KV_BF16_576) {
-    if (f32) hipLaunchKernelGGL((attend_kernel<0, true>), grid, dim3(NT), attend_lds_bytes<0>(), st, a);
-    else hipLaunchKernelGGL((attend_kernel<0, false>), grid, dim3(NT), attend_lds_bytes<0>(), st, a);
-  } else {
-    if (f32) hipLaunchKernelGGL((attend_kernel<1, true>), grid, dim3(NT), attend_lds_bytes<1>(), st, a);
-    else hipLaunchKernelGGL((attend_kernel<1, false>), grid, dim3(NT), attend_lds_bytes<1>(), st, a);
-  }
+  launch_kernel(g, a, n_req, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  if (f32)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(COMBINE_BLOCKS, n_req), dim3(COMBINE_THREADS), 0, st, t.part,
-                       a.splits, g.heads, out, lse);
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(COMBINE_BLOCKS, n_req), dim3(COMBINE_THREADS), 0, st, t.part,
-                       a.splits, g.heads, out, lse);
-  return hipGetLastError();
+  return launch_combine(g, t, n_req, a.splits, out, lse, st);
+}
+
+hipError_t launch_attend_part(const Geometry& g, const LayerTables& t, int32_t n_req, bool fetched, const void* q,
+                              const int32_t* slots, const int32_t* sel, const int32_t* len, float scale, void* out,
+                              float* lse, hipStream_t st) {
+  AttendArgs a;
+  a.buf = t.buf;
+  a.slots = slots;
+  a.sel = sel;
+  a.len = len;
+  a.q = (const uint16_t*)q;
+  a.out = out;
+  a.lse = lse;
+  a.part = t.part;
+  a.ml_slot = t.ml_slot;
+  a.ml_tok = t.ml_tok;
+  a.ml_cnt = t.ml_cnt;
+  a.stride = g.entry_bytes;
+  a.rstride = g.req_stride;
+  a.k = (int32_t)attend_tokens(g);
+  a.B = g.B * g.P;
+  a.lgP = g.lgP;
+  a.heads = g.heads;
+  a.scale_log2 = scale * kLog2e;
+  a.to_part = 1;
+  const int sr = attend_splits(g, n_req), sf = fetched_splits(g);
+  a.part_stride = sr + sf;
+  a.part_mode = fetched ? ATT_FETCHED : ATT_RESIDENT;
+  a.splits = fetched ? sf : sr;
+  a.part0 = fetched ? sr : 0;
+  const int per = (a.k + a.splits - 1) / a.splits;
+  a.chunk = (per + 15) / 16 * 16;
+  if (!a.part || a.chunk > max_chunk(g)) return hipErrorInvalidValue;
+  launch_kernel(g, a, n_req, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !fetched) return e;
+  return launch_combine(g, t, n_req, a.part_stride, out, lse, st);
 }
 
 }  // namespace hs

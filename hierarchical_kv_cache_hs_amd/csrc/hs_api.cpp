@@ -333,6 +333,16 @@ hs_status hs_fetch_misses(hs_handle* h, int32_t layer, int32_t n_req, void* stre
   return HS_OK;
 }
 
+hs_status hs_stream_read(const void* d_src, size_t bytes, uint32_t* d_sink, void* stream) {
+  if (!d_src || !d_sink) return fail(HS_ERR_INVALID_ARG, "source or sink pointer is NULL");
+  if (bytes % 16 != 0 || ((uintptr_t)d_src & 15u) != 0)
+    return fail(HS_ERR_INVALID_ARG, "bytes must be a multiple of 16 and the source 16-byte aligned");
+  if (bytes == 0) return HS_OK;
+  hipError_t e = hs::launch_stream_read(d_src, bytes, d_sink, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "stream read launch");
+  return HS_OK;
+}
+
 hs_status hs_attend(hs_handle* h, int32_t layer, int32_t n_req, const void* d_q, const int32_t* d_slots, float scale,
                     void* d_out, float* d_lse, void* stream) {
   if (!h) return fail(HS_ERR_INVALID_ARG, "handle is NULL");
@@ -361,6 +371,39 @@ hs_status hs_attend_pages(hs_handle* h, int32_t layer, int32_t n_req, const void
   hs::LayerTables t = layer_tables(h, layer);
   hipError_t e =
       hs::launch_attend(h->g, t, n_req, d_q, d_slots, d_sel, d_len, scale, d_out, d_lse, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "attend launch");
+  return HS_OK;
+}
+
+hs_status hs_attend_resident(hs_handle* h, int32_t layer, int32_t n_req, const void* d_q, const int32_t* d_slots,
+                             const int32_t* d_sel, const int32_t* d_len, float scale, void* stream) {
+  if (!h) return fail(HS_ERR_INVALID_ARG, "handle is NULL");
+  if (h->g.heads == 0) return fail(HS_ERR_UNSUPPORTED, "handle created with num_heads = 0");
+  if (h->g.flags & HS_FLAG_NO_IO) return fail(HS_ERR_UNSUPPORTED, "no miss copy to overlap with HS_FLAG_NO_IO");
+  if (layer < 0 || layer >= h->g.L) return fail(HS_ERR_INVALID_ARG, "layer out of range");
+  if (n_req < 0 || n_req > h->g.n) return fail(HS_ERR_INVALID_ARG, "n_req out of range");
+  if (n_req == 0) return HS_OK;
+  if (!d_q || !d_slots) return fail(HS_ERR_INVALID_ARG, "query or slot pointer is NULL");
+  if (!d_sel != !d_len) return fail(HS_ERR_INVALID_ARG, "selection and length pointers: give both or neither");
+  hs::LayerTables t = layer_tables(h, layer);
+  hipError_t e = hs::launch_attend_part(h->g, t, n_req, false, d_q, d_slots, d_sel, d_len, scale, nullptr, nullptr,
+                                        (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "attend launch");
+  return HS_OK;
+}
+
+hs_status hs_attend_fetched(hs_handle* h, int32_t layer, int32_t n_req, const void* d_q, const int32_t* d_len,
+                            float scale, void* d_out, float* d_lse, void* stream) {
+  if (!h) return fail(HS_ERR_INVALID_ARG, "handle is NULL");
+  if (h->g.heads == 0) return fail(HS_ERR_UNSUPPORTED, "handle created with num_heads = 0");
+  if (h->g.flags & HS_FLAG_NO_IO) return fail(HS_ERR_UNSUPPORTED, "no miss copy to overlap with HS_FLAG_NO_IO");
+  if (layer < 0 || layer >= h->g.L) return fail(HS_ERR_INVALID_ARG, "layer out of range");
+  if (n_req < 0 || n_req > h->g.n) return fail(HS_ERR_INVALID_ARG, "n_req out of range");
+  if (n_req == 0) return HS_OK;
+  if (!d_q || !d_out) return fail(HS_ERR_INVALID_ARG, "query or output pointer is NULL");
+  hs::LayerTables t = layer_tables(h, layer);
+  hipError_t e = hs::launch_attend_part(h->g, t, n_req, true, d_q, nullptr, nullptr, d_len, scale, d_out, d_lse,
+                                        (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "attend launch");
   return HS_OK;
 }

@@ -101,9 +101,22 @@ size_t attend_partial_floats(const Geometry& g);
 // Tokens attended per request: every row of the k selected units.
 inline int64_t attend_tokens(const Geometry& g) { return (int64_t)g.k * g.P; }
 
+// Dense streaming read of `bytes` (a multiple of 16, 16-byte aligned) of device memory.
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
+
 // sel and len (both or neither): cut each request's tokens at its context length len[r],
 // token o of unit i taking part iff sel[r][i] >= 0 and sel[r][i] * P + o < len[r].
 hipError_t launch_attend(const Geometry& g, const LayerTables& t, int32_t n_req, const void* q, const int32_t* slots,
                          const int32_t* sel, const int32_t* len, float scale, void* out, float* lse, hipStream_t s);
+
+// One part of a step's attention split by residency, after a list-only resolve (the miss
+// lists in t): fetched == false attends the entries of `slots` outside this step's victim
+// slots into split partials (it may run while launch_fetch copies the misses); fetched ==
+// true, after the copy and the resident part, attends the miss list and merges every partial
+// into out / lse.  len (with sel for the resident part; the fetched part takes the units from
+// the miss list) cuts at the context length as in launch_attend.
+hipError_t launch_attend_part(const Geometry& g, const LayerTables& t, int32_t n_req, bool fetched, const void* q,
+                              const int32_t* slots, const int32_t* sel, const int32_t* len, float scale, void* out,
+                              float* lse, hipStream_t s);
 
 }  // namespace hs

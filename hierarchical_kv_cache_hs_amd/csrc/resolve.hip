@@ -468,47 +468,56 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
   }
 }
 
-// Copies the rows of the miss lists written by resolve_kernel<..., LIST>: grid (per-request
-// blocks, requests), 16-byte zero-copy loads from pinned host memory, four in flight per
-// thread.  No LDS and few registers, so its workgroups fit beside a running attention kernel.
+// Copies the rows of the miss lists written by resolve_kernel<..., LIST>: grid (blocks per
+// request, request groups); a workgroup copies requests y, y + gridDim.y, ... in turn, its
+// threads covering consecutive 16-byte chunks of the request's rows (zero-copy loads from
+// pinned host memory, four in flight per thread; no LDS, at most 64 VGPRs).  128 workgroups
+// in all keep the link busy and leave half the compute units to an attention kernel running
+// beside the copy: an attention workgroup that shares a unit with the copy's long-latency
+// host reads proceeds at the link's pace.  Measured on 256 requests of 656-byte rows with the
+// attention of the resident tokens alongside (the whole step, in us): 64 workgroups 528-530,
+// 128 512-520, 192 520, 256 567 (blocks the attention's placement); LDS reserved to keep the
+// attention off the copy's units made no difference.
 constexpr int FT = 256;
+constexpr int kFetchGroups = 128;   // workgroups of a launch
 
-__global__ __launch_bounds__(FT) void fetch_kernel(const int32_t* __restrict__ ml_tok, const int32_t* __restrict__ ml_slot,
-                                                   const int32_t* __restrict__ ml_cnt, const uint8_t* __restrict__ host,
-                                                   uint8_t* __restrict__ buf, int64_t cap, int64_t host_stride,
-                                                   int64_t slot_stride, int64_t req_stride, int32_t k, int32_t B,
-                                                   int32_t chunks) {
-  const int r = blockIdx.y;
-  const int m = min(ml_cnt[r], k);
-  const int total = m * chunks;
-  const int32_t* tok = ml_tok + (int64_t)r * k;
-  const int32_t* slot = ml_slot + (int64_t)r * k;
-  const uint8_t* hrow = host + (int64_t)r * cap * host_stride;
-  uint8_t* drow = buf + (int64_t)r * req_stride;
+__global__ __launch_bounds__(FT, 8) void fetch_kernel(const int32_t* __restrict__ ml_tok, const int32_t* __restrict__ ml_slot,
+                                                      const int32_t* __restrict__ ml_cnt, const uint8_t* __restrict__ host,
+                                                      uint8_t* __restrict__ buf, int64_t cap, int64_t host_stride,
+                                                      int64_t slot_stride, int64_t req_stride, int32_t k, int32_t B,
+                                                      int32_t chunks, int32_t n_req) {
   constexpr int U = 4;
   const int step = gridDim.x * FT;
-  for (int base = blockIdx.x * FT + threadIdx.x; base < total; base += step * U) {
-    v4i v[U];
-    int32_t dst[U];
+  for (int r = blockIdx.y; r < n_req; r += gridDim.y) {
+    const int m = min(ml_cnt[r], k);
+    const int total = m * chunks;
+    const int32_t* tok = ml_tok + (int64_t)r * k;
+    const int32_t* slot = ml_slot + (int64_t)r * k;
+    const uint8_t* hrow = host + (int64_t)r * cap * host_stride;
+    uint8_t* drow = buf + (int64_t)r * req_stride;
+    for (int base = blockIdx.x * FT + threadIdx.x; base < total; base += step * U) {
+      v4i v[U];
+      int32_t dst[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int idx = base + u * step;
-      dst[u] = -1;
-      if (idx < total) {
-        const int q = idx / chunks;
-        const int c = idx - q * chunks;
-        const int32_t s = tok[q], j = slot[q];
-        if (s >= 0 && (int64_t)s < cap && j >= 0 && j < B) {
-          v[u] = __builtin_nontemporal_load((const v4i*)(hrow + (int64_t)s * host_stride) + c);
-          dst[u] = j * chunks + c;
+      for (int u = 0; u < U; ++u) {
+        const int idx = base + u * step;
+        dst[u] = -1;
+        if (idx < total) {
+          const int q = idx / chunks;
+          const int c = idx - q * chunks;
+          const int32_t s = tok[q], j = slot[q];
+          if (s >= 0 && (int64_t)s < cap && j >= 0 && j < B) {
+            v[u] = __builtin_nontemporal_load((const v4i*)(hrow + (int64_t)s * host_stride) + c);
+            dst[u] = j * chunks + c;
+          }
         }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (dst[u] >= 0) {
-        const int j = dst[u] / chunks, c = dst[u] - j * chunks;
-        ((v4i*)(drow + (int64_t)j * slot_stride))[c] = v[u];
+      for (int u = 0; u < U; ++u) {
+        if (dst[u] >= 0) {
+          const int j = dst[u] / chunks, c = dst[u] - j * chunks;
+          ((v4i*)(drow + (int64_t)j * slot_stride))[c] = v[u];
+        }
       }
     }
   }
@@ -638,10 +647,14 @@ hipError_t launch_resolve(const Geometry& g, const LayerTables& t, int32_t layer
 hipError_t launch_fetch(const Geometry& g, const LayerTables& t, const uint8_t* host_layer, int32_t n_req,
                         hipStream_t s) {
   if (g.flags & HS_FLAG_NO_IO) return hipSuccess;
-  // enough fetch workgroups for ~512 in total, whatever the batch
-  const int per_req = (512 + n_req - 1) / n_req < 16 ? (512 + n_req - 1) / n_req : 16;
-  hipLaunchKernelGGL(fetch_kernel, dim3(per_req, n_req), dim3(FT), 0, s, t.ml_tok, t.ml_slot, t.ml_cnt, host_layer,
-                     t.buf, g.cap, g.host_stride, g.slot_stride, g.req_stride, g.k, g.B, (int32_t)(g.unit_bytes / 16));
+  // kFetchGroups workgroups in all: one per request group, and with fewer requests several
+  // per request (at most 16)
+  const int groups = n_req < kFetchGroups ? n_req : kFetchGroups;
+  int per_req = (kFetchGroups + n_req - 1) / n_req;
+  if (per_req > 16) per_req = 16;
+  hipLaunchKernelGGL(fetch_kernel, dim3(per_req, groups), dim3(FT), 0, s, t.ml_tok, t.ml_slot, t.ml_cnt,
+                     host_layer, t.buf, g.cap, g.host_stride, g.slot_stride, g.req_stride, g.k, g.B,
+                     (int32_t)(g.unit_bytes / 16), n_req);
   return hipGetLastError();
 }
 

@@ -274,6 +274,39 @@ hs_status hs_attend_pages(hs_handle* h, int32_t layer, int32_t n_req, const void
                           const int32_t* d_sel, const int32_t* d_len, float scale, void* d_out, float* d_lse,
                           void* stream);
 
+/*
+ * Measurement helper, not a step of the method: a dense streaming read of `bytes` bytes of
+ * device memory at d_src (16-byte aligned, bytes a multiple of 16), enqueued on `stream`.
+ * Timing it gives the HBM read rate the attention and resolver kernels are compared with.
+ * d_sink: one device uint32 that the kernel may overwrite (it keeps the loads alive).
+ * HS_ERR_INVALID_ARG for NULL pointers or misaligned sizes; no allocation, no sync.
+ */
+hs_status hs_stream_read(const void* d_src, size_t bytes, uint32_t* d_sink, void* stream);
+
+/*
+ * A step's attention split by residency, so that the attention of the selected tokens
+ * already in the device buffer runs while the misses are still being copied in (paper
+ * abstract: host-device IO is the only price of bounded residency; the note, section 3:
+ * the missing KV is pulled from host memory before the step can attend).  The two parts
+ * together equal hs_attend (or hs_attend_pages, with d_len) over the same slots, up to the
+ * order in which fp32 partial sums are merged.  Order on the caller's streams:
+ *   hs_resolve_tables(l)  ->  { hs_attend_resident(l)  ||  hs_fetch_misses(l) }  ->  hs_attend_fetched(l)
+ * with no other resolve, attend part or append of layer l in between.
+ * hs_attend_resident attends the entries of d_slots (from that hs_resolve_tables) whose slot
+ * is not one of the step's victims -- those rows are resident and the copy does not touch
+ * them -- and leaves split partials in the handle; it reads the handle's miss list.
+ * hs_attend_fetched attends the step's misses (the rows hs_fetch_misses copied), merges them
+ * with the resident partials in a fixed order and writes d_out / d_lse as hs_attend does.
+ *   d_sel, d_len  both NULL (no cut), or as hs_attend_pages (the fetched part takes each
+ *                 miss's unit from the miss list and needs only d_len, the same array)
+ * Other arguments, outputs and errors as hs_attend; HS_ERR_UNSUPPORTED with HS_FLAG_NO_IO
+ * (no rows are copied, so there is nothing to overlap).  Enqueue-only, graph-capturable.
+ */
+hs_status hs_attend_resident(hs_handle* h, int32_t layer, int32_t n_req, const void* d_q, const int32_t* d_slots,
+                             const int32_t* d_sel, const int32_t* d_len, float scale, void* stream);
+hs_status hs_attend_fetched(hs_handle* h, int32_t layer, int32_t n_req, const void* d_q, const int32_t* d_len,
+                            float scale, void* d_out, float* d_lse, void* stream);
+
 /* Synchronise the device and free everything the handle owns.  NULL is accepted. */
 hs_status hs_destroy(hs_handle* h);
 
