@@ -117,3 +117,21 @@ def test_null_arguments():
     assert L.hs_get_device_error(None, ctypes.byref(bits)) == hsa.HS_ERR_INVALID_ARG
     for s in range(6):
         assert L.hs_status_string(s)
+
+
+def test_new_entry_points_reject_bad_arguments_before_hip():
+    L = hsa.lib()
+    f = ctypes.c_float(1.0)
+    assert L.hs_attend_resident(None, 0, 1, None, None, None, None, f, None) == hsa.HS_ERR_INVALID_ARG
+    assert L.hs_attend_fetched(None, 0, 1, None, None, f, None, None, None) == hsa.HS_ERR_INVALID_ARG
+    sink = ctypes.c_uint32()
+    assert L.hs_stream_read(None, 16, ctypes.byref(sink), None) == hsa.HS_ERR_INVALID_ARG
+    buf = (ctypes.c_uint8 * 64)()
+    base = ctypes.addressof(buf)
+    aligned = (base + 15) & ~15
+    assert L.hs_stream_read(aligned, 24, ctypes.byref(sink), None) == hsa.HS_ERR_INVALID_ARG   # not a multiple of 16
+    assert L.hs_stream_read(aligned + 4, 16, ctypes.byref(sink), None) == hsa.HS_ERR_INVALID_ARG  # misaligned
+    assert L.hs_stream_read(aligned, 16, None, None) == hsa.HS_ERR_INVALID_ARG
+    assert L.hs_stream_read(aligned, 0, ctypes.byref(sink), None) == hsa.HS_OK                  # nothing to read
+    assert hsa.lib().hs_last_error_message().decode() != ""
+

@@ -238,3 +238,26 @@ def test_overlap_graph_replay_equals_eager():
     finally:
         eager.close()
         graphed.close()
+
+
+def test_overlap_parts_unsupported_without_io_and_stream_read_runs():
+    hs = hsa.HiSparse(top_k=64, device_buffer_size=128, host_to_device_ratio=4, max_requests=2, num_layers=1,
+                      layout=hsa.LAYOUT_FP8, num_heads=16, flags=hsa.FLAG_NO_IO)
+    try:
+        q = torch.zeros(2, 16, 576, dtype=torch.bfloat16, device="cuda")
+        slots = torch.full((2, 64), -1, dtype=torch.int32, device="cuda")
+        with pytest.raises(hsa.HSError) as e:
+            hs.attend_resident(0, q, slots, SCALE)
+        assert e.value.status == hsa.HS_ERR_UNSUPPORTED
+        with pytest.raises(hsa.HSError) as e:
+            hs.attend_fetched(0, q, SCALE)
+        assert e.value.status == hsa.HS_ERR_UNSUPPORTED
+    finally:
+        hs.close()
+    # the measurement helper: reads the buffer and leaves the sink alone for ordinary data
+    src = torch.ones(1 << 20, dtype=torch.float32, device="cuda")
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    hsa.stream_read(src, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7
+
