@@ -91,6 +91,7 @@ struct AttendArgs {
   int32_t part_stride;    // partials per request in `part`
   int32_t part0;          // this launch's first partial
   int32_t to_part;        // write partials even with one split
+  int32_t merge_prev;     // one split: also merge partials 0 .. part0-1 and write out / lse
   float scale_log2;       // softmax scale * log2(e)
 };
 
@@ -248,7 +249,8 @@ constexpr size_t attend_lds_bytes() {
          TileGeo<LAYOUT>::XCH * WAVES * 64 * sizeof(f32x4);
 }
 
-constexpr size_t kStaticLds = (3 * GROUPS + 1) * HMAX * sizeof(float);  // wm, wl, fac, inv_l
+constexpr int MAXPREV = 16;  // earlier partials a workgroup can merge (the resident part's splits)
+constexpr size_t kStaticLds = (3 * GROUPS + 1 + MAXPREV) * HMAX * sizeof(float);  // wm, wl, fac, inv_l, pfac
 constexpr size_t kParkBytes = (size_t)GROUPS * 2 * 16 * 64 * sizeof(f32x4);   // parked accumulators
 static_assert(attend_lds_bytes<0>() + kStaticLds <= kLdsLimit, "bf16 LDS budget");
 static_assert(attend_lds_bytes<1>() + kStaticLds <= kLdsLimit, "fp8 LDS budget");
@@ -266,6 +268,7 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
   __shared__ float wl[GROUPS][HMAX];
   __shared__ float fac[GROUPS][HMAX];
   __shared__ float inv_l[HMAX];
+  __shared__ float pfac[MAXPREV][HMAX];  // merge_prev: factors of the earlier partials
   __shared__ int wlast[WAVES];
 
   const int s = blockIdx.x;
@@ -597,13 +600,19 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) o_park[((tg * 2 + hf) * 16 + i) * 64 + lane] = O[i];
   __syncthreads();
-  const bool direct = a.splits == 1 && !a.to_part;  // else write partials for the combine kernel
+  // direct: write out / lse (one split, or one split that also merges the earlier partials of
+  // its request, which a kernel earlier on the stream wrote); else a partial for the combine
+  const bool prev = a.merge_prev != 0;
+  const bool direct = a.splits == 1 && (!a.to_part || prev);
   float* mypart = a.part + ((int64_t)r * a.part_stride + a.part0 + s) * PART;
+  const float* prevpart = a.part + (int64_t)r * a.part_stride * PART;  // prev: partials 0 .. part0-1
   if (tid < HMAX) {
     const int h = tid;
     float M = wm[0][h];
 #pragma unroll
     for (int v = 1; v < GROUPS; ++v) M = fmaxf(M, wm[v][h]);
+    if (prev)
+      for (int v = 0; v < a.part0; ++v) M = fmaxf(M, prevpart[v * PART + h]);
     float L = 0.f;
 #pragma unroll
     for (int v = 0; v < GROUPS; ++v) {
@@ -611,6 +620,12 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
       fac[v][h] = f;
       L += f * wl[v][h];
     }
+    if (prev)
+      for (int v = 0; v < a.part0; ++v) {
+        const float f = (M == -INFINITY) ? 0.f : exp2f(prevpart[v * PART + h] - M);
+        pfac[v][h] = f;
+        L += f * prevpart[v * PART + HMAX + h];
+      }
     if (direct) {
       inv_l[h] = L > 0.f ? 1.f / L : 0.f;
       if (a.lse && h < heads) a.lse[(int64_t)r * heads + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
@@ -633,6 +648,11 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
       for (int j = 0; j < 4; ++j) acc[j] += fac[v][h0 + j] * o[j];
     }
     const int col = out_col(16 * he + tau, ln & 15);
+    if (prev)
+      for (int v = 0; v < a.part0; ++v) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] += pfac[v][h0 + j] * prevpart[v * PART + 2 * HMAX + (h0 + j) * DV + col];
+      }
     if (direct) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -775,6 +795,7 @@ hipError_t launch_attend(const Geometry& g, const LayerTables& t, int32_t n_req,
   a.part_mode = ATT_ALL;
   a.part0 = 0;
   a.to_part = 0;
+  a.merge_prev = 0;
   a.buf = t.buf;
   a.slots = slots;
   a.sel = sel;
@@ -826,6 +847,8 @@ hipError_t launch_attend_part(const Geometry& g, const LayerTables& t, int32_t n
   a.scale_log2 = scale * kLog2e;
   a.to_part = 1;
   const int sr = attend_splits(g, n_req), sf = fetched_splits(g);
+  // a single fetched split merges the resident partials itself (no combine launch)
+  a.merge_prev = fetched && sf == 1 && sr <= MAXPREV;
   a.part_stride = sr + sf;
   a.part_mode = fetched ? ATT_FETCHED : ATT_RESIDENT;
   a.splits = fetched ? sf : sr;
@@ -835,7 +858,7 @@ hipError_t launch_attend_part(const Geometry& g, const LayerTables& t, int32_t n
   if (!a.part || a.chunk > max_chunk(g)) return hipErrorInvalidValue;
   launch_kernel(g, a, n_req, st);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !fetched) return e;
+  if (e != hipSuccess || !fetched || a.merge_prev) return e;
   return launch_combine(g, t, n_req, a.part_stride, out, lse, st);
 }
 
