@@ -39,8 +39,10 @@
 //  * a step whose misses are still being copied (hs_fetch_misses) can attend in two parts:
 //    the resident part skips the step's victim slots (an LDS bitmap of the miss list, built
 //    in the prologue inside the then idle ring) and may run while the copy writes those
-//    slots; the fetched part walks the compact miss list once the rows have landed; both
-//    write split partials and the combine kernel merges them in fixed order;
+//    slots; the fetched part walks the compact miss list once the rows have landed.  The
+//    resident part writes split partials; a fetched part of one workgroup per request merges
+//    them in its epilogue (they were written by an earlier kernel on the stream, so no fence
+//    is needed), a fetched part of several leaves the merge to the combine kernel;
 //  * fp32-output mode: P enters the P V product as a sum of three bf16 terms (hi, mid, lo:
 //    each the round-to-nearest-even of what the previous ones leave), which carries P to 2^-27
 //    relative -- below fp32 rounding -- so the output is fp32 attention; it costs two more
