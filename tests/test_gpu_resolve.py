@@ -85,6 +85,64 @@ def test_ragged_shapes_random_traces(k, B, ratio, n, split):
         p.close()
 
 
+@pytest.mark.parametrize("split", [False, True])
+def test_maximum_sizes_with_attention(split):
+    """The largest selection and buffer the library accepts (top_k 8192, 16384 slots): the
+    widest register tiling of the 1024-thread resolver, with hits, misses, evictions and
+    padding over 5 steps, and attention over 8192 tokens (16 splits) against the oracle."""
+    k, B, ratio, n, heads = 8192, 16384, 2, 2, 16
+    say(f"maximum sizes: k {k}, B {B}, ratio {ratio}, n {n}, split {split}, attention on the last step")
+    cap = B * ratio
+    rng = np.random.default_rng(8192 + split)
+    p = Pair(n, 1, k, B, ratio, hsa.LAYOUT_BF16, seed=81, heads=heads, split=split)
+    try:
+        prev = None
+        for t in range(5):
+            rows = []
+            for r in range(n):
+                if prev is None:
+                    rows.append(rng.choice(cap, k, replace=False))
+                else:
+                    keep = prev[r][rng.random(k) < 0.6]
+                    keep = keep[keep >= 0]
+                    pool = np.setdiff1d(np.arange(cap), keep)
+                    rows.append(np.concatenate([keep, rng.choice(pool, k - keep.size, replace=False)]))
+            S = np.stack(rows).astype(np.int32)
+            prev = S.copy()
+            S[rng.random(S.shape) < 0.03] = -1
+            slots, m = p.step(0, S, check_state=(t % 2 == 0 or t == 4))
+            say(f"step {t}: misses {m.tolist()}")
+        qb = skv.queries(81, 4, n, 0, heads)
+        q = torch.from_numpy(qb.view(np.int16)).cuda().view(torch.bfloat16)
+        out, lse = p.hs.attend(0, q, torch.from_numpy(slots).cuda(), 1.0 / 24.0)
+        torch.cuda.synchronize()
+        out_o, lse_o = p.orc.attend(0, qb, slots, 1.0 / 24.0)
+        err = np.abs(out.float().cpu().numpy().astype(np.float64) - out_o).max()
+        lerr = np.abs(lse.cpu().numpy().astype(np.float64) - lse_o).max()
+        say(f"attention max abs error {err:.3e}, lse {lerr:.3e}")
+        assert err <= 2e-2 and lerr <= 1e-3
+    finally:
+        p.close()
+
+
+def test_widest_tiling_of_the_512_thread_resolver():
+    """More than 128 requests copying rows take the 512-thread resolver; with 16384 slots it
+    holds 32 LRU-order entries per thread (its widest tiling)."""
+    k, B, ratio, n = 64, 16384, 2, 130
+    say(f"512-thread resolver: k {k}, B {B}, n {n}, fp8 rows, 4 steps")
+    cap = B * ratio
+    rng = np.random.default_rng(130)
+    p = Pair(n, 1, k, B, ratio, hsa.LAYOUT_FP8, seed=13)
+    try:
+        for t in range(4):
+            S = np.stack([rng.choice(cap if t < 2 else 96, k, replace=False) for _ in range(n)]).astype(np.int32)
+            S[rng.random(S.shape) < 0.05] = -1
+            p.step(0, S, check_state=False)
+        p.check_state(0, n, sample_rows=32)
+    finally:
+        p.close()
+
+
 def test_fewer_requests_than_slots_and_layers_independent():
     say("n_req < max_requests, two layers")
     p = Pair(6, 2, 64, 128, 4, hsa.LAYOUT_FP8, seed=5)
