@@ -316,20 +316,31 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
       __syncthreads();
       units = ku;
     }
+    // A thread's entries are i = tid + e * NT, e < PER (the chunk, rounded up to whole tiles,
+    // is at most MAXCHUNK): all their slot and unit loads are issued before any is used, so the
+    // list costs one global round trip, not one per entry.
+    constexpr int PER = G::MAXCHUNK / NT;
+    static_assert(G::MAXCHUNK % NT == 0, "whole entries per thread");
+    int32_t jv[PER], cv[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int i = tid + e * NT;
+      const int u = (tok0 + i) >> lg;
+      const bool in = i < ntok && u < units;
+      jv[e] = in ? su[u] : -1;
+      cv[e] = (in && cu) ? cu[u] : 0;
+    }
     int last = 0;  // one past this thread's last valid entry
-    for (int i = tid; i < ntiles_all * G::T; i += NT) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int i = tid + e * NT;
+      if (i >= ntiles_all * G::T) break;
+      const int o = (tok0 + i) & ((1 << lg) - 1);
+      const int32_t j = jv[e];
       int32_t v = -1;
-      if (i < ntok) {
-        const int tok = tok0 + i;
-        const int u = tok >> lg, o = tok & ((1 << lg) - 1);
-        const int32_t j = u < units ? su[u] : -1;
-        if (j >= 0 && j < bu && !(mode == ATT_RESIDENT && ((vbits[j >> 5] >> (j & 31)) & 1u))) {
-          v = (j << lg) + o;
-          if (cu) {
-            const int32_t c = cu[u];
-            if (c < 0 || ((int64_t)c << lg) + o >= len) v = -1;
-          }
-        }
+      if (j >= 0 && j < bu && !(mode == ATT_RESIDENT && ((vbits[j >> 5] >> (j & 31)) & 1u))) {
+        v = (j << lg) + o;
+        if (cu && (cv[e] < 0 || ((int64_t)cv[e] << lg) + o >= len)) v = -1;
       }
       slot_lds[i] = v;
       if (v >= 0) last = i + 1;
