@@ -106,6 +106,24 @@ def test_overlap_tiny_every_step(layout):
     say(f"worst abs error {worst:.3e}")
 
 
+@pytest.mark.parametrize("policy", [hsa.EVICT_FIFO, hsa.EVICT_RANDOM])
+def test_overlap_under_other_eviction_policies(policy):
+    """The miss list names the step's victims under every policy, so the resident part skips
+    exactly the slots the copy writes; tiny trace, fp8, every step against the oracle."""
+    w = C.TINY.with_(layout=hsa.LAYOUT_FP8, n=3)
+    say(f"overlap, eviction policy {policy}: 3 requests, k 64, B 128, 32 steps")
+    x = trace_for(w)
+    p = Pair(w.n, 1, w.k, w.B, w.ratio, w.layout, w.seed, heads=16, policy=policy, policy_seed=99)
+    ov = Overlapped(p, 16)
+    try:
+        for t in range(x.shape[0]):
+            out, lse, out_o, lse_o, _ = ov.step(0, x[t], skv.queries(w.seed, t, w.n, 0, 16))
+            _compare(out, lse, out_o, lse_o, 2e-2, 1e-3, f"step {t}")
+        p.check_state(0, w.n)
+    finally:
+        p.close()
+
+
 @pytest.mark.parametrize("layout,heads,k,B,n", [(hsa.LAYOUT_BF16, 16, 100, 160, 3), (hsa.LAYOUT_FP8, 5, 37, 64, 2),
                                                 (hsa.LAYOUT_BF16, 1, 1, 4, 2), (hsa.LAYOUT_FP8, 16, 1000, 1024, 1),
                                                 (hsa.LAYOUT_BF16, 16, 2048, 4096, 300)])
