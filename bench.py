@@ -255,10 +255,14 @@ def bench_resolve(args, torch, hsa, w):
     stream = torch.cuda.Stream()
     results = {}
     for name, hs in handles.items():
+        w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):
+            w0.record(stream)
             for t in range(args.warmup):
                 hs.resolve(0, d_trace[t], slots, miss[t], stream=stream)
+            w1.record(stream)
         stream.synchronize()
+        warm_ms = w0.elapsed_time(w1) if args.warmup else 0.0
         # capture the timed steps; the graph holds only resolver launches, so the region
         # time over the launch count is the kernel's average launch duration
         g = torch.cuda.CUDAGraph()
@@ -276,7 +280,8 @@ def bench_resolve(args, torch, hsa, w):
         torch.cuda.synchronize()
         region_ms = a.elapsed_time(b)
         m = miss[args.warmup:].cpu().numpy().astype(np.int64)
-        results[name] = {"region_ms": region_ms, "kernel_ms": region_ms / args.steps, "miss": m}
+        results[name] = {"region_ms": region_ms, "kernel_ms": region_ms / args.steps, "miss": m, "warm_ms": warm_ms,
+                         "warm_miss": miss[:args.warmup].cpu().numpy().astype(np.int64)}
         log(f"{name}: {region_ms:.3f} ms for {args.steps} steps; {region_ms / args.steps * 1e3:.1f} us per launch")
         del g
 
@@ -317,6 +322,15 @@ def bench_resolve(args, torch, hsa, w):
         "h2d_peak_GBps_measured": h2d,
         "miss_fetch_frac_of_measured_peak": (fetch_bytes / (io["region_ms"] / 1e3) / 1e9) / h2d,
         "split_tables_and_fetch_us_per_step": split["kernel_ms"] * 1e3,
+        # the untimed warmup steps from an empty buffer (step 0 misses every token), launched
+        # one by one, and the mean over every step of the trace
+        "cold_start": {"steps": args.warmup, "ms": io["warm_ms"],
+                       "misses_per_selection": float(io["warm_miss"].mean()) if args.warmup else None,
+                       "step0_misses_per_selection": float(io["warm_miss"][0].mean()) if args.warmup else None,
+                       "miss_fetch_GBps": (float(io["warm_miss"].sum()) * w.entry_bytes / (io["warm_ms"] / 1e3) / 1e9
+                                           if args.warmup and io["warm_ms"] > 0 else None),
+                       "all_steps_misses_per_selection": float(np.concatenate([io["warm_miss"], io["miss"]]).mean()),
+                       "all_steps_selections_per_s": w.n * (args.warmup + K) / ((io["warm_ms"] + io["region_ms"]) / 1e3)},
         "resolve_only": {"us_per_step": avg_kernel_noio_s * 1e6,
                          "selections_per_s": w.n / avg_kernel_noio_s,
                          "share_of_io_step": avg_kernel_noio_s / avg_kernel_s},

@@ -19,6 +19,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "hs_internal.h"
 
@@ -44,6 +45,10 @@ struct hs_handle {
   int32_t* ml_cnt = nullptr;
   uint8_t* buf = nullptr;
   size_t part_floats = 0;  // per request
+  // per layer: requests whose miss lists the last resolve-side call left in the handle (a
+  // list-only resolve); 0 after any other resolve, append or reset.  The attention parts read
+  // those lists and refuse to run without them.
+  std::vector<int32_t> lists_for;
 };
 
 namespace {
@@ -223,6 +228,7 @@ hs_status hs_create(const hs_config* cfg, hs_handle** out) {
   hs_handle* h = new hs_handle();
   h->g = g;
   h->part_floats = lay.part_floats;
+  h->lists_for.assign((size_t)g.L, 0);
   hipError_t e = hipGetDevice(&h->device);
   if (e != hipSuccess) { release(h); return fail_hip(e, "hipGetDevice"); }
   if (cfg->device_mem) {
@@ -306,6 +312,7 @@ hs_status resolve_impl(hs_handle* h, int32_t layer, int32_t n_req, const int32_t
   hipError_t e = hs::launch_resolve(h->g, t, layer, host_layer, n_req, d_sel, d_slots, d_miss, h->err, list_only,
                                     (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "resolve launch");
+  h->lists_for[layer] = (list_only && !(h->g.flags & HS_FLAG_NO_IO)) ? n_req : 0;
   return HS_OK;
 }
 
@@ -382,6 +389,8 @@ hs_status hs_attend_resident(hs_handle* h, int32_t layer, int32_t n_req, const v
   if (h->g.flags & HS_FLAG_NO_IO) return fail(HS_ERR_UNSUPPORTED, "no miss copy to overlap with HS_FLAG_NO_IO");
   if (layer < 0 || layer >= h->g.L) return fail(HS_ERR_INVALID_ARG, "layer out of range");
   if (n_req < 0 || n_req > h->g.n) return fail(HS_ERR_INVALID_ARG, "n_req out of range");
+  if (n_req > h->lists_for[layer])
+    return fail(HS_ERR_INVALID_ARG, "no miss lists for these requests: hs_resolve_tables of this layer must come first");
   if (n_req == 0) return HS_OK;
   if (!d_q || !d_slots) return fail(HS_ERR_INVALID_ARG, "query or slot pointer is NULL");
   if (!d_sel != !d_len) return fail(HS_ERR_INVALID_ARG, "selection and length pointers: give both or neither");
@@ -399,6 +408,8 @@ hs_status hs_attend_fetched(hs_handle* h, int32_t layer, int32_t n_req, const vo
   if (h->g.flags & HS_FLAG_NO_IO) return fail(HS_ERR_UNSUPPORTED, "no miss copy to overlap with HS_FLAG_NO_IO");
   if (layer < 0 || layer >= h->g.L) return fail(HS_ERR_INVALID_ARG, "layer out of range");
   if (n_req < 0 || n_req > h->g.n) return fail(HS_ERR_INVALID_ARG, "n_req out of range");
+  if (n_req > h->lists_for[layer])
+    return fail(HS_ERR_INVALID_ARG, "no miss lists for these requests: hs_resolve_tables of this layer must come first");
   if (n_req == 0) return HS_OK;
   if (!d_q || !d_out) return fail(HS_ERR_INVALID_ARG, "query or output pointer is NULL");
   hs::LayerTables t = layer_tables(h, layer);
@@ -465,6 +476,7 @@ hs_status hs_append(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* d
                              : hs::launch_append_pages(h->g, t, host_layer, n_req, d_pos, d_rows, row_stride,
                                                        d_slot_out, h->err, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "append launch");
+  h->lists_for[layer] = 0;
   return HS_OK;
 }
 
@@ -516,6 +528,7 @@ hs_status hs_reset_requests(hs_handle* h, int32_t first, int32_t count, void* st
   hipError_t e =
       hs::launch_reset(h->g, h->pt, h->rm, h->st, h->ord, h->step, h->fresh, first, count, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "reset launch");
+  h->lists_for.assign((size_t)h->g.L, 0);
   return HS_OK;
 }
 

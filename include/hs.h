@@ -300,7 +300,10 @@ hs_status hs_stream_read(const void* d_src, size_t bytes, uint32_t* d_sink, void
  *   d_sel, d_len  both NULL (no cut), or as hs_attend_pages (the fetched part takes each
  *                 miss's unit from the miss list and needs only d_len, the same array)
  * Other arguments, outputs and errors as hs_attend; HS_ERR_UNSUPPORTED with HS_FLAG_NO_IO
- * (no rows are copied, so there is nothing to overlap).  Enqueue-only, graph-capturable.
+ * (no rows are copied, so there is nothing to overlap); HS_ERR_INVALID_ARG when the layer's
+ * last resolve, append or reset call was not an hs_resolve_tables of at least n_req requests
+ * (the handle tracks the order of the calls, not of the device work).  Enqueue-only,
+ * graph-capturable.
  */
 hs_status hs_attend_resident(hs_handle* h, int32_t layer, int32_t n_req, const void* d_q, const int32_t* d_slots,
                              const int32_t* d_sel, const int32_t* d_len, float scale, void* stream);

@@ -279,3 +279,37 @@ def test_overlap_parts_unsupported_without_io_and_stream_read_runs():
     torch.cuda.synchronize()
     assert int(sink.item()) == 7
 
+
+def test_attention_parts_require_the_layers_miss_lists():
+    """The parts refuse to run unless the layer's last resolve-side call was a list-only
+    resolve of at least as many requests (a fused resolve, an append or a reset in between
+    leaves no lists for this step)."""
+    p = Pair(3, 2, 64, 128, 4, hsa.LAYOUT_FP8, seed=3, heads=16)
+    try:
+        rng = np.random.default_rng(3)
+        S = _selection(rng, 3, 512, 64)
+        sel = torch.from_numpy(S).cuda()
+        q = _q(skv.queries(3, 0, 3, 0, 16))
+        slots = torch.empty_like(sel)
+        miss = torch.empty(3, dtype=torch.int32, device="cuda")
+
+        def refused(fn):
+            with pytest.raises(hsa.HSError) as e:
+                fn()
+            assert e.value.status == hsa.HS_ERR_INVALID_ARG
+
+        refused(lambda: p.hs.attend_resident(0, q, slots, SCALE))          # nothing resolved yet
+        p.hs.resolve(0, sel, slots, miss)                                  # fused: no lists
+        refused(lambda: p.hs.attend_resident(0, q, slots, SCALE))
+        p.hs.resolve_tables(0, sel[:2], slots[:2], miss[:2])
+        refused(lambda: p.hs.attend_resident(0, q, slots, SCALE))          # 3 requests, lists for 2
+        refused(lambda: p.hs.attend_resident(1, q, slots, SCALE))          # other layer
+        p.hs.fetch_misses(0, 2)
+        p.hs.attend_resident(0, q[:2], slots[:2], SCALE)
+        p.hs.attend_fetched(0, q[:2], SCALE)
+        p.hs.reset_requests(0, 3)
+        refused(lambda: p.hs.attend_fetched(0, q[:2], SCALE))
+        torch.cuda.synchronize()
+    finally:
+        p.close()
+
