@@ -981,10 +981,11 @@ def bench_prefetch(args, torch, hsa, w):
     sels = [d_trace[t] for t in range(T)]
     qsteps = [qs[t % 4] for t in range(T)]
 
-    def timed(prefetch, attend):
+    def timed(prefetch, attend, split_attention=False):
         hs.reset_requests(0, w.n)
         DecodeSteps(hs, sels[:args.warmup], qsteps[:args.warmup], scale, prefetch=False, attend=attend).replay()
-        steps = DecodeSteps(hs, sels[args.warmup:], qsteps[args.warmup:], scale, prefetch=prefetch, attend=attend)
+        steps = DecodeSteps(hs, sels[args.warmup:], qsteps[args.warmup:], scale, prefetch=prefetch, attend=attend,
+                            split_attention=split_attention)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(steps.stream):
@@ -996,8 +997,13 @@ def bench_prefetch(args, torch, hsa, w):
 
     t_ser, s_ser = timed(False, True)
     t_pre, s_pre = timed(True, True)
+    t_spl, s_spl = timed(True, True, split_attention=True)
     t_res, _ = timed(False, False)
     same = torch.equal(s_ser.out, s_pre.out) and torch.equal(s_ser.miss, s_pre.miss)
+    # the attention merged from two parts equals the single launch up to fp32 summation order
+    spl_close = torch.equal(s_ser.miss, s_spl.miss) and \
+        (s_ser.out.float() - s_spl.out.float()).abs().max().item() <= 2e-2
+    log(f"serial {t_ser:.3f} ms, prefetch {t_pre:.3f} ms, prefetch + split attention {t_spl:.3f} ms per step")
     t_att = t_ser - t_res
     # attention alone over the 8 layers (each launch reads another layer's rows), K times
     ga = torch.cuda.CUDAGraph()
@@ -1035,6 +1041,10 @@ def bench_prefetch(args, torch, hsa, w):
         "misses_per_selection": misses,
         "miss_GB_per_step": misses * w.n * w.layers * w.entry_bytes / 1e9,
         "prefetch_equals_serial": bool(same),
+        # each layer's attention split by residency: the resident part waits only for the
+        # layer's tables, the fetched part for its copy
+        "prefetch_split_attention_ms_per_step": t_spl,
+        "prefetch_split_attention_within_bf16_tier_of_serial": bool(spl_close),
         "selections_per_s": w.n * w.layers / (t_pre / 1e3),
     }
     hs.close()

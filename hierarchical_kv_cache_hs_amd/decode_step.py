@@ -5,6 +5,10 @@ replacement, table update, host-to-device fetch) and then runs sparse attention
 over the resolved slots.  With ``prefetch=True`` the layers' resolves run back to
 back on a second stream and each attention waits only for its own layer's
 resolve, so resolving (and fetching) layer l + 1 overlaps attention of layer l.
+With ``split_attention=True`` as well, each layer's attention is split by residency: the
+part over the resident tokens waits only for the layer's tables and runs beside the copies,
+the part over the fetched misses waits for the layer's copy, so after the last layer's copy
+only that part remains.
 This is valid when the layers share one selection known at the start of the step
 (HiSparse paper abstract: exact layer-wise prefetching for models that share
 selections across layers); the results are the same as the serial order because
@@ -49,9 +53,11 @@ class DecodeSteps:
     ``miss[i][l][r]`` records every step's miss counts.
     """
 
-    def __init__(self, hs: HiSparse, sels, qs, scale: float, prefetch: bool, attend: bool = True):
+    def __init__(self, hs: HiSparse, sels, qs, scale: float, prefetch: bool, attend: bool = True,
+                 split_attention: bool = False):
         assert len(sels) == len(qs) and len(sels) > 0
-        self.hs, self.prefetch, self.attend = hs, prefetch, attend
+        assert not split_attention or (prefetch and attend)
+        self.hs, self.prefetch, self.attend, self.split_attention = hs, prefetch, attend, split_attention
         n = sels[0].shape[0]
         L, k = hs.L, hs.top_k
         dev = sels[0].device
@@ -80,6 +86,25 @@ class DecodeSteps:
             return
         side = self.side
         side.wait_stream(main)                       # fork
+        if self.split_attention:
+            n = sel.shape[0]
+            tables, copied = [], []
+            for l in range(hs.L):
+                hs.resolve_tables(l, sel, self.slots[l], self.miss[i, l], stream=side)
+                e = torch.cuda.Event()
+                e.record(side)
+                tables.append(e)
+                hs.fetch_misses(l, n, stream=side)
+                e = torch.cuda.Event()
+                e.record(side)
+                copied.append(e)
+            for l in range(hs.L):
+                main.wait_event(tables[l])
+                hs.attend_resident(l, q[l], self.slots[l], scale, stream=main)
+                main.wait_event(copied[l])
+                hs.attend_fetched(l, q[l], scale, self.out[l], self.lse[l], stream=main)
+            main.wait_stream(side)                   # join
+            return
         done = []
         for l in range(hs.L):
             # tables first, then the row copy by the LDS-free kernel, which can run beside the

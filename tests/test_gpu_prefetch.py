@@ -27,11 +27,11 @@ def _queries(w, t, L):
     return torch.from_numpy(q.view(np.int16)).cuda().view(torch.bfloat16)
 
 
-def _run(hs, w, x, qs, prefetch):
+def _run(hs, w, x, qs, prefetch, split_attention=False):
     rec = []
     for t in range(x.shape[0]):
         sel = torch.from_numpy(x[t]).cuda()
-        steps = DecodeSteps(hs, [sel], [qs[t]], SCALE, prefetch=prefetch)
+        steps = DecodeSteps(hs, [sel], [qs[t]], SCALE, prefetch=prefetch, split_attention=split_attention)
         steps.replay()
         torch.cuda.synchronize()
         rec.append((steps.slots.clone(), steps.miss[0].clone(), steps.out.clone(), steps.lse.clone()))
@@ -86,3 +86,42 @@ def test_prefetch_equals_serial_and_oracle(full):
                 assert np.abs(ser[T - 1][3][l, r].cpu().numpy() - l_o[0]).max() <= 1e-3
     finally:
         hs.close()
+
+
+def test_prefetch_with_attention_split_by_residency():
+    """Layer-wise prefetch with each layer's attention split into the resident part (beside
+    the copies) and the fetched part: tables, slots and misses equal the serial run bitwise;
+    the attention, merged from two parts, matches the serial single-launch attention within the
+    bf16 tier and the oracle on sampled requests."""
+    w = C.PREFETCH.with_(n=6, ctx=8192, ratio=2)
+    T = 8
+    say(f"prefetch + split attention: {w.n} requests, {w.layers} layers, cap {w.cap}, fp8, {T} steps")
+    x = trace_for(w, steps=T)
+    hs = hsa.HiSparse(w.k, w.B, w.ratio, w.n, w.layers, w.layout, num_heads=16)
+    try:
+        fill_host_pool(hs, w.seed)
+        qs = [_queries(w, t, w.layers) for t in range(T)]
+        ser, ser_tables = _run(hs, w, x, qs, prefetch=False)
+        hs.reset_requests(0, w.n)
+        torch.cuda.synchronize()
+        spl, spl_tables = _run(hs, w, x, qs, prefetch=True, split_attention=True)
+        for t, (a, b) in enumerate(zip(ser, spl)):
+            assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), f"step {t}: slots or misses differ"
+            err = (a[2].float() - b[2].float()).abs().max().item()
+            lerr = (a[3] - b[3]).abs().max().item()
+            assert err <= 2e-2 and lerr <= 1e-3, f"step {t}: attention differs by {err} (lse {lerr})"
+        for l in range(w.layers):
+            for u, v in zip(ser_tables[l], spl_tables[l]):
+                assert torch.equal(u, v), f"layer {l}: tables differ"
+        qb = np.stack([skv.queries(w.seed, T - 1, w.n, l, 16) for l in range(w.layers)])
+        for l in (0, w.layers - 1):
+            for r in (0, w.n - 1):
+                rows = skv.rows_at(w.seed, r, l, x[T - 1, r], w.layout)[None]
+                o_o, l_o = oracle.attend_rows(qb[l, r][None], np.arange(w.k, dtype=np.int32)[None], rows,
+                                              w.layout, SCALE)
+                err = np.abs(spl[T - 1][2][l, r].float().cpu().numpy() - o_o[0]).max()
+                assert err <= 2e-2, f"layer {l} request {r}: attention error {err}"
+                assert np.abs(spl[T - 1][3][l, r].cpu().numpy() - l_o[0]).max() <= 1e-3
+    finally:
+        hs.close()
+
