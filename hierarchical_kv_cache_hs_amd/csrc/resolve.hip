@@ -8,12 +8,18 @@
 // Design for gfx950.  One workgroup of 1024 or 512 threads (16 or 8 wave64s) per request; a
 // request's tables are private, so workgroups never communicate.
 //   P0  clear two LDS bitmaps (hit slots [B bits], missing tokens [capacity bits]) and
-//       load this thread's contiguous chunk of the LRU order into registers;
-//   P1  gather the page-table entry of every selected token (coalesced selection read,
-//       random 4-byte table reads); hits set their slot bit, misses their token bit
-//       (LDS atomics; a bit already set flags a repeated token).  With early reads (P2) the
-//       same round trip reads the owners of the first k slots in LRU order, which hold every
-//       possible victim (the m-th non-hit slot lies at most k - m hits deep);
+//       load this thread's contiguous chunk of the LRU order into registers.  In launches of
+//       more than 96 requests whose capacity fits (up to ~40 k tokens beside the rest), the
+//       owner array (slot -> token, the inverse of the page table on resident tokens) is read
+//       in the same coalesced round trip and scattered into an LDS token -> slot map (16-bit
+//       entries);
+//   P1  look up every selected token: in the LDS map when it was built, else by a random
+//       4-byte gather of its page-table entry (2048 lookups per request are ~0.5 M separate
+//       cache requests per launch at 256 requests, which the map avoids); hits set their
+//       slot bit, misses their token bit (LDS atomics; a bit already set flags a repeated
+//       token).  Without the map, with early reads (P2) the same round trip reads the owners
+//       of the first k slots in LRU order, which hold every possible victim (the m-th non-hit
+//       slot lies at most k - m hits deep);
 //   P2  one packed block scan gives (a) for each word of the token bitmap the number of
 //       misses below it, so a miss's ascending-token rank is prefix[word] +
 //       popcount(lower bits of the word), and (b) each non-hit slot's rank in LRU order; the
@@ -79,6 +85,7 @@ struct ResolveArgs {
   int32_t policy;  // hs_eviction
   int32_t layer, nlayers;
   int32_t early_reads;  // FUSED: start the host reads in P2 (see launch_resolve)
+  int32_t use_map;      // build the LDS token -> slot map (capacity fits in LDS)
 };
 
 // Output number c of SplitMix64 started from state s (Steele, Lea and Flood, OOPSLA 2014).
@@ -170,6 +177,10 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
   uint32_t* wsum = vowner + k;                  // [NW_MAX] scan scratch
   uint32_t* freshmap = wsum + NW_MAX;           // [HB]  slots appended since the last resolve
   uint16_t* prefix = (uint16_t*)(freshmap + HB);  // [W] misses below each bitmap word
+  const bool map = a.use_map != 0;
+  const int MW = (int)((cap + 1) >> 1);                        // map words (two entries each)
+  int16_t* tmap = (int16_t*)((uint32_t*)prefix + ((W + 1) >> 1));  // [cap] slot of a token, -1 absent
+  int32_t* rml = (int32_t*)((uint32_t*)tmap + (map ? MW : 0));     // [B] owners before the step
 
   int32_t* pt = a.pt + (int64_t)r * cap;
   int32_t* rm = a.rm + (int64_t)r * B;
@@ -188,10 +199,15 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
     if (f) fresh[w] = 0u;  // consumed by this resolve
   }
   for (int w = tid; w < W; w += NT) missmap[w] = 0u;
+  if (map)
+    for (int e = tid; e < MW; e += NT) ((uint32_t*)tmap)[e] = 0xFFFFFFFFu;
   int32_t ordv[OPT];
+  int32_t own[OPT];  // owners of this thread's chunk of slots (the map)
   const int o0 = tid * OPT;
 #pragma unroll
   for (int x = 0; x < OPT; ++x) ordv[x] = (o0 + x < B) ? ord[o0 + x] : -1;
+#pragma unroll
+  for (int x = 0; x < OPT; ++x) own[x] = (map && o0 + x < B) ? rm[o0 + x] : -1;
   int32_t selv[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
@@ -199,6 +215,15 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
     selv[j] = (i < k) ? sel[i] : -1;
   }
   __syncthreads();
+  if (map) {
+#pragma unroll
+    for (int x = 0; x < OPT; ++x) {
+      if (o0 + x >= B) continue;
+      rml[o0 + x] = own[x];
+      if (own[x] >= 0 && (int64_t)own[x] < cap) tmap[own[x]] = (int16_t)(o0 + x);
+    }
+    __syncthreads();
+  }
 
   // ---- P1
   uint32_t err = 0;
@@ -209,7 +234,7 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
     int32_t p = kPad;
     if (s != -1) {
       if (s < 0 || (int64_t)s >= cap) err |= HS_DEVERR_TOKEN_RANGE;
-      else p = pt[s];
+      else p = map ? (int32_t)tmap[s] : pt[s];
     }
     ptv[j] = p;
   }
@@ -221,7 +246,7 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
 #pragma unroll
   for (int x = 0; x < OPT; ++x) {
     const int32_t j = ordv[x];
-    rmv[x] = (early && o0 + x < k && j >= 0 && j < B) ? rm[j] : -1;
+    rmv[x] = (early && !map && o0 + x < k && j >= 0 && j < B) ? rm[j] : -1;
   }
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
@@ -350,7 +375,7 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
       if (nhmask & (1u << x)) {
         if (rank < m) {
           victims[rank] = (uint32_t)j;
-          if (early) vowner[rank] = (uint32_t)rmv[x];
+          if (early && !map) vowner[rank] = (uint32_t)rmv[x];
           atomicOr(&back[j >> 5], 1u << (j & 31));
         } else if (fresh_j) {
           // appended since the last resolve: its stamp is already this step's (appended
@@ -403,7 +428,7 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
         const int32_t v = (q < m && q < nonhit) ? (int32_t)victims[q] : -1;
         int32_t tok = -1;
         if (v >= 0 && v < B) {
-          const int32_t old = early ? (int32_t)vowner[q] : rm[v];
+          const int32_t old = map ? rml[v] : early ? (int32_t)vowner[q] : rm[v];
           if (old >= 0 && (int64_t)old < cap) pt[old] = -1;
           pt[s] = v;
           rm[v] = s;
@@ -595,9 +620,14 @@ void prepare_resolve() {
 size_t resolve_lds_bytes(int64_t cap, int32_t k, int32_t B) {
   const size_t W = (size_t)((cap + 31) >> 5);
   const size_t HB = (size_t)((B + 31) >> 5);
-  size_t words = 2 * HB + W + 3 * (size_t)k + NW_MAX;
-  size_t bytes = words * 4 + W * 2;
-  return (bytes + 15) & ~(size_t)15;
+  size_t words = 2 * HB + W + 3 * (size_t)k + NW_MAX + (W + 1) / 2;
+  return (words * 4 + 15) & ~(size_t)15;
+}
+
+// LDS of the token -> slot map and the owners' copy, when they fit beside the rest.
+static size_t resolve_map_bytes(int64_t cap, int32_t k, int32_t B) {
+  const size_t extra = (size_t)((cap + 1) >> 1) * 4 + (size_t)B * 4;
+  return resolve_lds_bytes(cap, k, B) + extra <= kLdsLimit && B <= 32767 ? extra : 0;
 }
 
 hipError_t launch_resolve(const Geometry& g, const LayerTables& t, int32_t layer, const uint8_t* host_layer,
@@ -636,7 +666,13 @@ hipError_t launch_resolve(const Geometry& g, const LayerTables& t, int32_t layer
   // rows and ~4 us at 64 requests of 1152-byte rows, but cost 2-4 us from 128 requests of
   // 1152-byte rows and 192 of 656-byte rows on, where other workgroups keep the link busy.
   a.early_reads = n_req <= 96;
-  const size_t lds = resolve_lds_bytes(g.cap, g.k, g.B);
+  // The LDS map pays once the page-table gathers of many requests crowd the caches: measured
+  // no-IO, 256 requests 15.5 -> 14.6 us, but 64 requests 10.9 -> 11.8 us (the map's fill and
+  // scatter cost more than a few gathers), so it is built for launches past the early-read
+  // threshold only.
+  const size_t map_bytes = n_req > 96 ? resolve_map_bytes(g.cap, g.k, g.B) : 0;
+  a.use_map = map_bytes > 0;
+  const size_t lds = resolve_lds_bytes(g.cap, g.k, g.B) + map_bytes;
   // The wide (1024-thread) workgroup finishes the tables sooner (measured 10.5 vs 12.9 us for
   // 64 requests and 15.4 vs 18.1 us for 256, no IO); with row copies from more than 128
   // requests the 512-thread one copies faster (473 vs 491 us at 256 requests of 656-byte rows).
