@@ -1049,13 +1049,18 @@ def bench_prefetch(args, torch, hsa, w):
     valid = float((s_ser.slots >= 0).sum().item()) / w.layers
     att_bytes = valid * w.entry_bytes + w.n * (4 * w.k + 16 * (576 * 2 + 512 * 2 + 4))
     misses = float(s_ser.miss.double().mean())
+    # the line's value: the faster of the two prefetch schedules (the split one only if its
+    # attention stayed within the bf16 tier of the serial run)
+    best_split = spl_close and t_spl < t_pre
+    t_best = t_spl if best_split else t_pre
     out = {
         "metric": "decode steps/s, 8 layers sharing a selection, layer-wise prefetch, 1 MI355X",
-        "value": 1e3 / t_pre, "unit": "steps/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
-        "ms_per_step": t_pre, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "value": 1e3 / t_best, "unit": "steps/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": t_best, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.description, "global_batch": w.n, "layers": w.layers, "seq_len": w.ctx,
-                   "top_k": w.k, "graph": True},
+                   "top_k": w.k, "graph": True,
+                   "schedule": "prefetch, attention split by residency" if best_split else "prefetch"},
         "serial_ms_per_step": t_ser, "prefetch_ms_per_step": t_pre, "resolve_only_ms_per_step": t_res,
         "attention_ms_per_step": t_att,
         "attention_alone_ms_per_step": t_att_only,
@@ -1069,7 +1074,7 @@ def bench_prefetch(args, torch, hsa, w):
         # layer's tables, the fetched part for its copy
         "prefetch_split_attention_ms_per_step": t_spl,
         "prefetch_split_attention_within_bf16_tier_of_serial": bool(spl_close),
-        "selections_per_s": w.n * w.layers / (t_pre / 1e3),
+        "selections_per_s": w.n * w.layers / (t_best / 1e3),
     }
     hs.close()
     return out
