@@ -905,6 +905,26 @@ def bench_pages(args, torch, hsa, w):
     region_ms = timed(g)
     del g
     assert torch.equal(miss, miss_r)      # appends change no table
+    out_serial = out.clone()
+    # whole steps again with the attention split by residency: the part over resident pages runs
+    # beside the copy of the missing pages, the part over the fetched pages after it
+    from hierarchical_kv_cache_hs_amd.decode_step import attend_while_fetching
+    side = torch.cuda.Stream()
+    miss_o = torch.zeros(T, w.n, dtype=torch.int32, device="cuda")
+    hs.reset_requests(0, w.n)
+    torch.cuda.synchronize()
+    warm(hs, miss_o, True)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for t in range(args.warmup, T):
+                hs.append(0, d_pos[t], d_new[t], slot_new, stream=stream)
+                attend_while_fetching(hs, 0, d_trace[t], qs[t % 8], scale, slots[t], miss_o[t], out, lse, stream, side,
+                                      lens=lens[t])
+    overlap_ms = timed(g)
+    del g
+    overlap_ok = torch.equal(miss_o, miss) and (out.float() - out_serial.float()).abs().max().item() <= 2e-2
+    log(f"pages: whole step {region_ms / K * 1e3:.1f} us serial, {overlap_ms / K * 1e3:.1f} us with the split attention")
     # the appends alone, on the final state (write-through into resident pages and the history)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
@@ -957,15 +977,24 @@ def bench_pages(args, torch, hsa, w):
     page_bytes = P * w.entry_bytes
     fetch_Bps = m * w.n * page_bytes / (resolve_us * 1e-6)
     step_tokens = w.n * w.k * P
+    # the line's value: the faster of the two step schedules (the split one only if its attention
+    # stayed within the bf16 tier of the serial run)
+    split_best = overlap_ok and overlap_ms < region_ms
+    best_ms = overlap_ms if split_best else region_ms
     line = {
         "metric": "attended tokens/s through append + resolve + attention over page selections, 1 MI355X",
-        "value": step_tokens * K / (region_ms / 1e3),
+        "value": step_tokens * K / (best_ms / 1e3),
         "unit": "attended tokens/s",
-        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": region_ms / K,
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": best_ms / K,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.description, "global_batch": w.n, "page_tokens": P, "seq_len": w.len_tokens(0),
-                   "top_k_pages": w.k, "device_buffer_pages": w.B, "heads": 16, "graph": True},
-        "page_selections_per_s": w.n * K / (region_ms / 1e3),
+                   "top_k_pages": w.k, "device_buffer_pages": w.B, "heads": 16, "graph": True,
+                   "schedule": "attention split by residency" if split_best else "serial"},
+        "page_selections_per_s": w.n * K / (best_ms / 1e3),
+        # the same steps with the attention split by residency (resident pages beside the copy)
+        "attend_while_fetching": {"us_per_step": overlap_ms / K * 1e3, "serial_us_per_step": region_ms / K * 1e3,
+                                  "attended_tokens_per_s": step_tokens * K / (overlap_ms / 1e3),
+                                  "within_bf16_tier_of_serial": bool(overlap_ok)},
         "append_us_per_step": append_us,
         "resolve_us_per_step": resolve_us,
         "resolve_noio_us_per_step": noio_us,
