@@ -828,6 +828,39 @@ def cpu_baseline_pages(w, trace, warm, budget_s=15.0, requests=16):
                       f"({done} steps, {el:.1f} s)"}
 
 
+def cpu_baseline_prefetch(w, trace, warm, budget_s=15.0, requests=4):
+    """The oracle, as it stands, on whole 8-layer decode steps for a sample of requests: every
+    layer resolves the shared selection (tables + row copies), then fp64 attention per layer.
+    The rate is scaled to the whole batch (steps/s of all requests)."""
+    import oracle
+    from synth import kv as skv
+    n = min(requests, w.n)
+    L = w.layers
+    host = np.empty((n, L, w.cap, w.entry_bytes), dtype=np.uint8)
+    for r in range(n):
+        for l in range(L):
+            skv.fill_rows(w.seed, r, l, 0, w.cap, w.layout, host[r, l].ctypes.data, w.entry_bytes)
+    threads = oracle.default_threads()
+    oc = oracle.OracleCache(n, L, w.B, w.cap, layout=w.layout, host=host, threads=threads)
+    for t in range(warm):
+        for l in range(L):
+            oc.resolve(l, trace[t, :n])
+    done, el, t = 0, 0.0, warm
+    while (done == 0 or el < budget_s) and t < trace.shape[0]:
+        qs = [skv.queries(w.seed, t % 4, n, l, 16) for l in range(L)]
+        t0 = time.perf_counter()
+        for l in range(L):
+            slots, _ = oc.resolve(l, trace[t, :n])
+            oc.attend(l, qs[l], slots, 1.0 / math.sqrt(576))
+        el += time.perf_counter() - t0
+        done += 1
+        t += 1
+    return {"value": done * n / w.n / el, "unit": "steps/s (scaled to all requests)", "cores": threads,
+            "kind": "oracle",
+            "sample": f"oracle resolve (tables + row copies) and fp64 attention of {L} layers for requests "
+                      f"0..{n - 1} on steps {warm}..{t - 1} ({done} steps, {el:.1f} s), rate scaled by {n}/{w.n}"}
+
+
 def bench_pages(args, torch, hsa, w):
     """Page-granular selections: whole steps of write-through append of the newest token,
     resolve, and attention cut at the context length."""
@@ -1104,9 +1137,15 @@ def bench_prefetch(args, torch, hsa, w):
         "prefetch_split_attention_ms_per_step": t_spl,
         "prefetch_split_attention_within_bf16_tier_of_serial": bool(spl_close),
         "selections_per_s": w.n * w.layers / (t_best / 1e3),
+        # the step is bound by the miss copies over the host link (the fetch kernels on the
+        # copy stream); whole-step rate against the link, no single-kernel duration here
+        "roofline": {"bound": "host_link", "achieved": misses * w.n * w.layers * w.entry_bytes / (t_best / 1e3) / 1e9,
+                     "peak": PCIE_GEN5_X16_GBPS, "unit": "GB/s",
+                     "frac": misses * w.n * w.layers * w.entry_bytes / (t_best / 1e3) / 1e9 / PCIE_GEN5_X16_GBPS,
+                     "traffic": None, "kernel": "whole step (fetch_kernel copies on the second stream)"},
     }
     hs.close()
-    return out
+    return out, trace
 
 
 def main():
@@ -1164,7 +1203,9 @@ def main():
         else:
             line["cpu_baseline"] = None
     elif args.workload == "prefetch":
-        line = bench_prefetch(args, torch, hsa, C.PREFETCH)
+        line, trace = bench_prefetch(args, torch, hsa, C.PREFETCH)
+        line["cpu_baseline"] = None if args.no_cpu_baseline else \
+            cpu_baseline_prefetch(C.PREFETCH, trace, args.warmup, args.cpu_budget)
     elif args.workload == "sweep":
         line = bench_sweep(args, torch, hsa)
     elif args.workload == "topk":
