@@ -4,7 +4,8 @@ For each layer l the step resolves the layer's selection (hit detection, LRU
 replacement, table update, host-to-device fetch) and then runs sparse attention
 over the resolved slots.  With ``prefetch=True`` the layers' resolves run back to
 back on a second stream and each attention waits only for its own layer's
-resolve, so resolving (and fetching) layer l + 1 overlaps attention of layer l.
+resolve, so resolving (and fetching) layer l + 1 overlaps attention of layer l; the table
+resolves run on their own stream, ahead of the row copies, so the copies follow one another.
 With ``split_attention=True`` as well, each layer's attention is split by residency: the
 part over the resident tokens waits only for the layer's tables and runs beside the copies,
 the part over the fetched misses waits for the layer's copy, so after the last layer's copy
@@ -67,7 +68,8 @@ class DecodeSteps:
         self.out = torch.empty(L, n, H, 512, dtype=hs.out_dtype, device=dev)
         self.lse = torch.empty(L, n, H, dtype=torch.float32, device=dev)
         self.stream = torch.cuda.Stream(device=dev)
-        self.side = torch.cuda.Stream(device=dev)
+        self.side = torch.cuda.Stream(device=dev)    # table resolves
+        self.copy = torch.cuda.Stream(device=dev)    # row copies
         self.graph = torch.cuda.CUDAGraph()
         self.stream.wait_stream(torch.cuda.current_stream(dev))
         with torch.cuda.stream(self.stream):
@@ -84,40 +86,55 @@ class DecodeSteps:
                 if self.attend:
                     hs.attend(l, q[l], self.slots[l], scale, self.out[l], self.lse[l], stream=main)
             return
+        # Attention on the main stream.  With one attention per layer, the table resolves run
+        # on one side stream and the row copies on another: the tables of layer l + 1 (a short,
+        # latency-bound kernel) run while the rows of layer l are copied, so the link does not
+        # idle between layers (128 requests x 8 layers: 2.16 against 2.23-2.28 ms).  With the
+        # attention split by residency, tables and copies alternate on one side stream: tables
+        # running ahead would let the resident parts start early and crowd the copies' compute
+        # units (2.23 against 2.19 ms).
         side = self.side
+        copy = side if self.split_attention else self.copy
         side.wait_stream(main)                       # fork
-        if self.split_attention:
-            n = sel.shape[0]
-            tables, copied = [], []
+        if copy is not side:
+            copy.wait_stream(main)
+        n = sel.shape[0]
+        tables, copied = [None] * hs.L, [None] * hs.L
+
+        def resolve_tables(l):
+            hs.resolve_tables(l, sel, self.slots[l], self.miss[i, l], stream=side)
+            tables[l] = torch.cuda.Event()
+            tables[l].record(side)
+
+        def fetch(l):
+            if copy is not side:
+                copy.wait_event(tables[l])
+            hs.fetch_misses(l, n, stream=copy)
+            copied[l] = torch.cuda.Event()
+            copied[l].record(copy)
+
+        if copy is side:
             for l in range(hs.L):
-                hs.resolve_tables(l, sel, self.slots[l], self.miss[i, l], stream=side)
-                e = torch.cuda.Event()
-                e.record(side)
-                tables.append(e)
-                hs.fetch_misses(l, n, stream=side)
-                e = torch.cuda.Event()
-                e.record(side)
-                copied.append(e)
+                resolve_tables(l)
+                fetch(l)
+        else:
             for l in range(hs.L):
+                resolve_tables(l)
+            for l in range(hs.L):
+                fetch(l)
+        for l in range(hs.L):
+            if self.split_attention:
                 main.wait_event(tables[l])
                 hs.attend_resident(l, q[l], self.slots[l], scale, stream=main)
                 main.wait_event(copied[l])
                 hs.attend_fetched(l, q[l], scale, self.out[l], self.lse[l], stream=main)
-            main.wait_stream(side)                   # join
-            return
-        done = []
-        for l in range(hs.L):
-            # tables first, then the row copy by the LDS-free kernel, which can run beside the
-            # attention of an earlier layer on the main stream
-            hs.resolve(l, sel, self.slots[l], self.miss[i, l], stream=side, split=True)
-            e = torch.cuda.Event()
-            e.record(side)
-            done.append(e)
-        for l in range(hs.L):
-            main.wait_event(done[l])
-            if self.attend:
-                hs.attend(l, q[l], self.slots[l], scale, self.out[l], self.lse[l], stream=main)
+            else:
+                main.wait_event(copied[l])
+                if self.attend:
+                    hs.attend(l, q[l], self.slots[l], scale, self.out[l], self.lse[l], stream=main)
         main.wait_stream(side)                       # join
+        if copy is not side:
+            main.wait_stream(copy)
 
     def replay(self):
         """Runs the captured steps on this object's stream (ordered after the caller's stream)."""
