@@ -36,8 +36,8 @@ def attend_while_fetching(hs: HiSparse, layer: int, sel, q, scale: float, slots,
     n = sel.shape[0]
     hs.resolve_tables(layer, sel, slots, miss, stream=main)
     # the copy is enqueued (and in a graph, captured) first, so that its few workgroups are
-    # placed before the attention's fill the compute units (the other order left the copy
-    # waiting for the attention: 601 against 530 us per step, 256 requests of fp8 rows)
+    # placed before the attention's fill the compute units (256 requests of fp8 rows: 505
+    # against 515 us per step with the attention enqueued first)
     side.wait_stream(main)                       # fork: the copy needs only the miss lists
     hs.fetch_misses(layer, n, stream=side)
     hs.attend_resident(layer, q, slots, scale, sel if lens is not None else None, lens, stream=main)
