@@ -125,3 +125,42 @@ def test_prefetch_with_attention_split_by_residency():
     finally:
         hs.close()
 
+
+@pytest.mark.parametrize("split_attention", [False, True])
+def test_several_steps_in_one_graph(split_attention):
+    """Four steps captured in one graph on the prefetch schedules (tables, copies and attention
+    on three streams, or tables and copies alternating on one): each step's copies must wait
+    for the previous step's attention, whose rows they may overwrite.  Miss counts of every
+    step and the final tables equal the serial run bitwise; the last step's attention equals
+    it bitwise (single launch) or within the bf16 tier (split by residency)."""
+    w = C.PREFETCH.with_(n=6, ctx=8192, ratio=2)
+    T = 4
+    say(f"prefetch, {T} steps in one graph, split attention {split_attention}")
+    x = trace_for(w, steps=T)
+    hs = hsa.HiSparse(w.k, w.B, w.ratio, w.n, w.layers, w.layout, num_heads=16)
+    try:
+        fill_host_pool(hs, w.seed)
+        sels = [torch.from_numpy(x[t]).cuda() for t in range(T)]
+        qs = [_queries(w, t, w.layers) for t in range(T)]
+        ser = DecodeSteps(hs, sels, qs, SCALE, prefetch=False)
+        ser.replay()
+        torch.cuda.synchronize()
+        ser_tables = [tuple(hs.state(l)[k].clone() for k in ("page_table", "slot_owner", "slot_stamp", "step"))
+                      for l in range(w.layers)]
+        hs.reset_requests(0, w.n)
+        torch.cuda.synchronize()
+        pre = DecodeSteps(hs, sels, qs, SCALE, prefetch=True, split_attention=split_attention)
+        pre.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ser.miss, pre.miss) and torch.equal(ser.slots, pre.slots)
+        if split_attention:
+            assert (ser.out.float() - pre.out.float()).abs().max().item() <= 2e-2
+            assert (ser.lse - pre.lse).abs().max().item() <= 1e-3
+        else:
+            assert torch.equal(ser.out, pre.out) and torch.equal(ser.lse, pre.lse)
+        for l in range(w.layers):
+            for u, k in zip(ser_tables[l], ("page_table", "slot_owner", "slot_stamp", "step")):
+                assert torch.equal(u, hs.state(l)[k]), f"layer {l}: {k} differs"
+    finally:
+        hs.close()
+
