@@ -190,17 +190,10 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
   int32_t* slots = a.slots + (int64_t)r * k;
   const int32_t t = a.step[r];
 
-  // ---- P0
+  // ---- P0: every global load first (one round trip), the LDS clears while they are in flight
+  static_assert(kMaxBuffer / 32 <= NT, "one word of the slot bitmaps per thread");
   uint32_t* fresh = a.fresh + (int64_t)r * HB;
-  for (int w = tid; w < HB; w += NT) {
-    hitmap[w] = 0u;
-    const uint32_t f = fresh[w];
-    freshmap[w] = f;
-    if (f) fresh[w] = 0u;  // consumed by this resolve
-  }
-  for (int w = tid; w < W; w += NT) missmap[w] = 0u;
-  if (map)
-    for (int e = tid; e < MW; e += NT) ((uint32_t*)tmap)[e] = 0xFFFFFFFFu;
+  const uint32_t fw = (tid < HB) ? fresh[tid] : 0u;
   int32_t ordv[OPT];
   int32_t own[OPT];  // owners of this thread's chunk of slots (the map)
   const int o0 = tid * OPT;
@@ -213,6 +206,14 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
   for (int j = 0; j < KPT; ++j) {
     const int i = tid + j * NT;
     selv[j] = (i < k) ? sel[i] : -1;
+  }
+  if (tid < HB) hitmap[tid] = 0u;
+  for (int w = tid; w < W; w += NT) missmap[w] = 0u;
+  if (map)
+    for (int e = tid; e < MW; e += NT) ((uint32_t*)tmap)[e] = 0xFFFFFFFFu;
+  if (tid < HB) {
+    freshmap[tid] = fw;
+    if (fw) fresh[tid] = 0u;  // consumed by this resolve
   }
   __syncthreads();
   if (map) {
