@@ -313,3 +313,24 @@ def test_attention_parts_require_the_layers_miss_lists():
     finally:
         p.close()
 
+
+@pytest.mark.parametrize("layout", [hsa.LAYOUT_BF16, hsa.LAYOUT_FP8])
+def test_overlap_parts_empty_on_cold_and_repeated_steps(layout):
+    """Degenerate splits: the first step misses every token (the resident part attends nothing),
+    the same selection again hits every token (the fetched part attends nothing, the miss list
+    is empty); both equal the oracle's attention over the whole selection."""
+    n, k, B, heads = 3, 256, 512, 16
+    say(f"overlap degenerate parts, layout {layout}: all misses, then all hits")
+    rng = np.random.default_rng(5 + layout)
+    p = Pair(n, 1, k, B, 4, layout, seed=41, heads=heads)
+    ov = Overlapped(p, heads)
+    try:
+        S = _selection(rng, n, 4 * B, k)
+        S[1, k // 2:] = -1                                  # a half-padded request
+        for t, want in ((0, k), (1, 0)):
+            out, lse, out_o, lse_o, miss = ov.step(0, S, skv.queries(41, t, n, 0, heads))
+            assert miss[0] == want and miss[2] == want, f"step {t}: misses {miss.tolist()}"
+            _compare(out, lse, out_o, lse_o, 2e-2, 1e-3, f"step {t}")
+    finally:
+        p.close()
+
