@@ -32,7 +32,8 @@
 //       the non-hit slot of rank perm(q), a keyed permutation, and no order is kept);
 //   P4  the slots stamped with this step -- under LRU hits and victims, under FIFO victims,
 //       and any slot appended since the last resolve (hs_append stamps it with this step) --
-//       form the back of the new order in ascending slot index (a scan over their bitmap);
+//       form the back of the new order in ascending slot index (a scan over their bitmap;
+//       each thread then places the back-group slots of its own chunk of slot indices);
 //       the stamps are written in one coalesced pass over that bitmap; the i-th miss takes
 //       victim i: evict its owner from the page table, install the token and write the
 //       output slot;
@@ -176,7 +177,8 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
   uint32_t* vowner = misstok + k;               // [k]   token held by victim i before the step (-1: none)
   uint32_t* wsum = vowner + k;                  // [NW_MAX] scan scratch
   uint32_t* freshmap = wsum + NW_MAX;           // [HB]  slots appended since the last resolve
-  uint16_t* prefix = (uint16_t*)(freshmap + HB);  // [W] misses below each bitmap word
+  uint32_t* backpre = freshmap + HB;            // [HB]  back-group slots below each bitmap word
+  uint16_t* prefix = (uint16_t*)(backpre + HB);  // [W] misses below each bitmap word
   const bool map = a.use_map != 0;
   const int MW = (int)((cap + 1) >> 1);                        // map words (two entries each)
   int16_t* tmap = (int16_t*)((uint32_t*)prefix + ((W + 1) >> 1));  // [cap] slot of a token, -1 absent
@@ -397,14 +399,25 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
 
   // ---- P4
   if (policy != HS_EVICT_RANDOM) {
-    uint32_t word = (tid < HB) ? ((policy == HS_EVICT_FIFO) ? freshmap : hitmap)[tid] : 0u;
+    // The back group, in ascending slot order, fills the end of the new order: every thread
+    // places the back-group slots of its own chunk of slot indices (a back-group slot's place
+    // = the back-group slots below its word + those below it in the word), so the stores of
+    // a wave land on neighbouring entries and all threads share the work.
+    const uint32_t* bmap = (policy == HS_EVICT_FIFO) ? freshmap : hitmap;
+    const uint32_t word = (tid < HB) ? bmap[tid] : 0u;
     uint32_t touched;
     const uint32_t below = block_scan<NT>((uint32_t)__popc(word), wsum, &touched);
-    int pos = B - (int)touched + (int)below;
-    while (word) {
-      const int b = __ffs(word) - 1;
-      word &= word - 1u;
-      ord[pos++] = tid * 32 + b;
+    if (tid < HB) backpre[tid] = below;
+    lds_barrier();
+    const int base = B - (int)touched;
+#pragma unroll
+    for (int x = 0; x < OPT; ++x) {
+      const int j = o0 + x;
+      if (j < B) {
+        const uint32_t wd = bmap[j >> 5];
+        const uint32_t bit = (uint32_t)(j & 31);
+        if ((wd >> bit) & 1u) ord[base + (int)backpre[j >> 5] + __popc(wd & ((1u << bit) - 1u))] = j;
+      }
     }
   }
   // stamps, coalesced: LRU -- hits, victims and appended slots (all in the hit bitmap by
@@ -621,7 +634,7 @@ void prepare_resolve() {
 size_t resolve_lds_bytes(int64_t cap, int32_t k, int32_t B) {
   const size_t W = (size_t)((cap + 31) >> 5);
   const size_t HB = (size_t)((B + 31) >> 5);
-  size_t words = 2 * HB + W + 3 * (size_t)k + NW_MAX + (W + 1) / 2;
+  size_t words = 3 * HB + W + 3 * (size_t)k + NW_MAX + (W + 1) / 2;
   return (words * 4 + 15) & ~(size_t)15;
 }
 
