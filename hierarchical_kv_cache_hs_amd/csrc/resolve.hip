@@ -124,6 +124,20 @@ __device__ uint32_t random_rank(uint64_t key, uint32_t n, uint32_t x) {
 // __syncthreads() adds is not needed -- and it would stall on the host reads in flight.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS round trips):
+// within each 16-lane row by shifts of 1, 2, 4 and 8 (lanes shifted in from outside the row
+// read 0), then lane 15 of each row added to the next row (rows 1 and 3) and lane 31 to the
+// upper half (rows 2 and 3).
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
 // Exclusive block-wide prefix sum of v over NT threads; *total gets the block sum.  Every
 // thread must call.
 template <int NT>
@@ -131,12 +145,7 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint3
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_scan_incl(v);
   if (lane == 63) wsum[wid] = x;
   lds_barrier();
   uint32_t before = 0, tot = 0;
