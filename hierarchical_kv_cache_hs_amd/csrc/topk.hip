@@ -27,6 +27,7 @@
 // flight before any is used.
 
 #include "hs_internal.h"
+#include "hs_wave.h"
 
 namespace hs {
 namespace {
@@ -57,15 +58,18 @@ __device__ __forceinline__ uint32_t order_key(uint32_t b) {
 }
 
 // Inclusive scan of v over the workgroup; *total gets the sum.  Every thread must call.
+// In-wave inclusive scan: 32-bit values on DPP; 64-bit values here are two independent 32-bit
+// counts packed (hi, lo) whose sums stay below 2^32, so each half is scanned on its own.
+__device__ __forceinline__ uint32_t wave_incl(uint32_t v) { return wave_scan_incl(v); }
+__device__ __forceinline__ uint64_t wave_incl(uint64_t v) {
+  return ((uint64_t)wave_scan_incl((uint32_t)(v >> 32)) << 32) | wave_scan_incl((uint32_t)v);
+}
+
 template <typename T>
 __device__ T block_scan_incl(T v, T* wtot, T* total) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const T y = __shfl_up(v, o);
-    if (lane >= o) v += y;
-  }
+  v = wave_incl(v);
   if (lane == 63) wtot[w] = v;
   __syncthreads();
   T base = 0, tot = 0;
@@ -215,12 +219,7 @@ __global__ __launch_bounds__(TT) void topk_kernel(TopkArgs a) {
       if (nib) atomicOr(&selmap[p >> 5], nib << (p & 31));
     }
     const uint32_t c = __popc(cmask);
-    uint32_t incl = c;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
+    const uint32_t incl = wave_scan_incl(c);
     uint32_t base = 0;
     if (lane == 63 && incl) base = atomicAdd(&s_ncand, incl);
     uint32_t idx = __shfl(base, 63) + incl - c;
