@@ -25,6 +25,8 @@ selection per layer (128 requests, 8 layers, 65536 tokens).
 --workload pages runs page-granular selections (pages of 16 tokens, 128 pages selected, 256
 page slots, 256 requests, fp8): whole steps of write-through append of the newest token, resolve,
 and attention cut at the context length.
+--workload attend_cost splits an attention launch's time into a per-tile and a fixed part: k = 64
+.. 2048 rows per request (256 requests, fp8), read from HBM cold and read from the caches.
 --workload sweep is the miss-count study: misses per selection for device buffers of 2048,
 4096 and 6144 slots under LRU, FIFO and RANDOM eviction (32 requests, 131072 tokens).
 """
@@ -1162,12 +1164,80 @@ def bench_prefetch(args, torch, hsa, w):
     return out, trace
 
 
+def bench_attend_cost(args, torch, hsa):
+    """Where a sparse-attention launch spends its time (fp8 rows, 256 requests, 16 heads, one
+    workgroup per request): launches over k = 64 .. 2048 selected rows per request, each timed
+    cold (after a 1 GiB read that evicts the caches) with HIP events on the launch stream, and
+    the same launches over only 64 distinct rows per request, read over and over (they stay in
+    the caches, so the time is the kernel's own tile pipeline).  A least-squares line over k
+    gives the time per 64-token tile and the fixed time per launch, for both."""
+    n, H, B = 256, 16, 2048
+    ks = (64, 256, 512, 1024, 2048)
+    reps = max(5, min(args.steps, 40))
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+    scale = 1.0 / math.sqrt(576)
+    times = {"hbm": {}, "cached": {}}
+    for k in ks:
+        hs = hsa.HiSparse(k, B, 1, n, 1, hsa.LAYOUT_FP8, H, hsa.FLAG_NO_IO)
+        buf = hs.state(0)["kv_buffer"]
+        g = torch.Generator(device="cuda")
+        g.manual_seed(1000 + k)
+        # bytes below 64: finite fp8 codes, bf16 rope values and scales of moderate size
+        buf.copy_(torch.randint(0, 64, buf.shape, dtype=torch.uint8, device="cuda", generator=g))
+        perm = torch.argsort(torch.rand(n, B, device="cuda", generator=g), dim=1).to(torch.int32)
+        q = (torch.randn(n, H, 576, device="cuda", generator=g) * 0.1).to(torch.bfloat16).contiguous()
+        out = torch.empty(n, H, 512, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(n, H, dtype=torch.float32, device="cuda")
+        for kind, slots in (("hbm", perm[:, :k].contiguous()),
+                            ("cached", perm[:, :64].repeat(1, k // 64).contiguous())):
+            assert slots.shape == (n, k) and int(slots.min()) >= 0 and int(slots.max()) < B
+            us = []
+            with torch.cuda.stream(stream):
+                for i in range(args.warmup + reps):
+                    if kind == "hbm":
+                        flush.sum()
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    hs.attend(0, q, slots, scale, out, lse, stream=stream)
+                    b.record(stream)
+                    b.synchronize()
+                    if i >= args.warmup:
+                        us.append(a.elapsed_time(b) * 1e3)
+            assert bool(torch.isfinite(lse).all())
+            times[kind][k] = float(np.median(us))
+            log(f"attend cost k {k} {kind}: {times[kind][k]:.1f} us")
+        hs.close()
+        del buf
+    fit = {}
+    for kind, t in times.items():
+        tiles = np.array([k / 64 for k in ks])
+        slope, icpt = np.polyfit(tiles, np.array([t[k] for k in ks]), 1)
+        fit[kind] = {"us_per_tile": float(slope), "us_fixed": float(icpt)}
+    tile_bytes = n * 64 * 656
+    t2048 = times["hbm"][2048]
+    return {
+        "metric": "sparse MLA attention launch time vs selected rows per request, 1 MI355X",
+        "value": t2048, "unit": "us per launch (k 2048, cold, HIP events)",
+        "n_gpus": 1, "steps": reps, "warmup": args.warmup, "ms_per_step": t2048 / 1e3,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "fp8/bf16 -> f32",
+        "data": "synthetic",
+        "config": {"workload": "256 requests, 16 heads, fp8 656-byte rows, k 64..2048, 2048 slots",
+                   "global_batch": n, "top_k": list(ks)},
+        "us_per_launch": {kind: {str(k): v for k, v in t.items()} for kind, t in times.items()},
+        "fit": fit,
+        "tile_bytes": tile_bytes,
+        "tile_GBps_hbm": tile_bytes / (fit["hbm"]["us_per_tile"] * 1e-6) / 1e9,
+        "cpu_baseline": None,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=190)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="batch64", choices=["batch64", "fp8_256", "prefetch", "sweep", "topk", "pages"])
+    ap.add_argument("--workload", default="batch64", choices=["batch64", "fp8_256", "prefetch", "sweep", "topk", "pages", "attend_cost"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--summarize-profile", action="store_true",
@@ -1224,6 +1294,8 @@ def main():
         line = bench_sweep(args, torch, hsa)
     elif args.workload == "topk":
         line = bench_topk(args, torch, hsa)
+    elif args.workload == "attend_cost":
+        line = bench_attend_cost(args, torch, hsa)
     elif args.workload == "pages":
         line, trace = bench_pages(args, torch, hsa, C.PAGES)
         line["cpu_baseline"] = None if args.no_cpu_baseline else \
