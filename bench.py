@@ -1220,7 +1220,7 @@ def bench_attend_cost(args, torch, hsa):
         "metric": "sparse MLA attention launch time vs selected rows per request, 1 MI355X",
         "value": t2048, "unit": "us per launch (k 2048, cold, HIP events)",
         "n_gpus": 1, "steps": reps, "warmup": args.warmup, "ms_per_step": t2048 / 1e3,
-        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "fp8/bf16 -> f32",
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "256 requests, 16 heads, fp8 656-byte rows, k 64..2048, 2048 slots",
                    "global_batch": n, "top_k": list(ks)},
