@@ -1,25 +1,26 @@
 #!/usr/bin/env python3
 """Benchmark of the HiSparse hot path on one MI355X.
 
-Default workload: 64 requests, 1 layer, context 32768, bf16 576-value entries (1152 B),
-top_k 2048, device buffer 4096 slots, host_to_device_ratio 8, resolve only; the selection
-trace is the seeded 200-step recency-window + Zipf(1.05) history with 10 % churn.  A step is
-one resolve of every request's selection (hit detection, LRU replacement, table update and
-the host-to-device fetch of the missing rows), replayed from a captured hipGraph; the first
---warmup steps run untimed, then exactly --steps steps are timed.
+Default workload (the largest single-GPU one): 128 requests, 8 layers sharing one selection per
+step, context 65536, fp8 656-byte entries, top_k 2048, device buffer 4096 slots, host capacity
+65536 tokens; the selection trace is the seeded recency-window (128) + Zipf(1.05) history with
+10 % churn per step.  A step is a whole decode step: every layer resolves the shared selection
+(hit detection, LRU replacement, table update, host-to-device fetch of the missing rows) and
+runs sparse MLA attention (16 heads) over its resolved slots, with layer-wise prefetch (layer
+l + 1's tables and row copies on other streams beside layer l's attention).  The steps are
+captured in one hipGraph; the first --warmup steps run untimed from an empty buffer, then
+exactly --steps steps are timed.
 
-Metric: resolved top-k selections/s (whole job), with the miss-fetch rate against the
-host-link peak measured in the same run.  The JSON line also carries:
-  roofline     the resolver kernel against the host link (its bound): the timed graph holds
-               only resolver launches, so HIP events around it on the launch stream give the
-               kernel's average launch duration;
-  resolve_only the same steps on a handle that moves no rows (resolution cost alone);
-  cpu_baseline the CPU oracle on a bounded sample of the same trace, on this host's cores.
+Metric: resolved top-k selections/s (whole job: requests x layers x steps over the timed
+region), with the miss-fetch rate against the host-link peak.  The JSON line also carries:
+  roofline       the dominant kernel (the row copies over the host link, fetch_kernel), its
+                 average launch time from HIP events on its stream;
+  other_workloads the 64-request resolve-only and 256-request resolve + attention rates;
+  cpu_baseline   the CPU oracle on a bounded sample of the same trace, on this host's cores.
 
+--workload batch64 times resolve-only steps of 64 requests (bf16 1152-byte rows).
 --workload fp8_256 measures resolve + sparse MLA attention (256 requests, fp8 656-byte
-entries) instead and reports attention throughput against the HBM roofline.
---workload prefetch times whole decode steps over 8 layers sharing one selection (128
-requests, fp8), in serial order and with layer-wise prefetch.
+entries) and reports attention throughput against the HBM roofline.
 --workload topk runs the on-GPU top-k from synthetic indexer scores into the resolver, one
 selection per layer (128 requests, 8 layers, 65536 tokens).
 --workload pages runs page-granular selections (pages of 16 tokens, 128 pages selected, 256
@@ -361,8 +362,9 @@ def bench_resolve(args, torch, hsa, w):
     return out, trace
 
 
-def bench_attend(args, torch, hsa, w):
-    """Resolve + attention on the fp8 256-request workload (attention against HBM)."""
+def bench_attend(args, torch, hsa, w, legs=True):
+    """Resolve + attention on the fp8 256-request workload (attention against HBM).  With
+    legs=False the overlapped-step and append legs are skipped."""
     from synth import kv as skv
     from synth import trace as tr
 
@@ -476,8 +478,9 @@ def bench_attend(args, torch, hsa, w):
     del flush
     hs_noio.close()
     res_ms = [region_ms / args.steps - float(np.mean(att_ms))]
-    overlap = bench_overlap_leg(args, torch, hsa, w, hs, d_trace, qs, miss, stream, timed, scale, region_ms)
-    append = bench_append_leg(args, torch, hsa, w, d_trace, miss, stream, timed)
+    overlap = bench_overlap_leg(args, torch, hsa, w, hs, d_trace, qs, miss, stream, timed, scale, region_ms) \
+        if legs else None
+    append = bench_append_leg(args, torch, hsa, w, d_trace, miss, stream, timed) if legs else None
     K = args.steps
     att_s = float(np.mean(att_ms)) / 1e3
     valid = (slots[args.warmup:] >= 0).sum().item() / K
@@ -847,7 +850,9 @@ def cpu_baseline_pages(w, trace, warm, budget_s=15.0, requests=16):
 def cpu_baseline_prefetch(w, trace, warm, budget_s=15.0, requests=4):
     """The oracle, as it stands, on whole 8-layer decode steps for a sample of requests: every
     layer resolves the shared selection (tables + row copies), then fp64 attention per layer.
-    The rate is scaled to the whole batch (steps/s of all requests)."""
+    The timed steps (warm..) are replayed from an empty cache as many times as fit in about
+    budget_s seconds; the rate is selections (request-layer pairs resolved and attended) per
+    second."""
     import oracle
     from synth import kv as skv
     n = min(requests, w.n)
@@ -857,24 +862,26 @@ def cpu_baseline_prefetch(w, trace, warm, budget_s=15.0, requests=4):
         for l in range(L):
             skv.fill_rows(w.seed, r, l, 0, w.cap, w.layout, host[r, l].ctypes.data, w.entry_bytes)
     threads = oracle.default_threads()
-    oc = oracle.OracleCache(n, L, w.B, w.cap, layout=w.layout, host=host, threads=threads)
-    for t in range(warm):
-        for l in range(L):
-            oc.resolve(l, trace[t, :n])
-    done, el, t = 0, 0.0, warm
-    while (done == 0 or el < budget_s) and t < trace.shape[0]:
-        qs = [skv.queries(w.seed, t % 4, n, l, 16) for l in range(L)]
-        t0 = time.perf_counter()
-        for l in range(L):
-            slots, _ = oc.resolve(l, trace[t, :n])
-            oc.attend(l, qs[l], slots, 1.0 / math.sqrt(576))
-        el += time.perf_counter() - t0
-        done += 1
-        t += 1
-    return {"value": done * n / w.n / el, "unit": "steps/s (scaled to all requests)", "cores": threads,
-            "kind": "oracle",
+    T = trace.shape[0]
+    qs = {t: [skv.queries(w.seed, t, n, l, 16) for l in range(L)] for t in range(warm, T)}
+    done, el, passes = 0, 0.0, 0
+    while passes == 0 or el < budget_s:
+        oc = oracle.OracleCache(n, L, w.B, w.cap, layout=w.layout, host=host, threads=threads)
+        for t in range(warm):
+            for l in range(L):
+                oc.resolve(l, trace[t, :n])
+        for t in range(warm, T):
+            t0 = time.perf_counter()
+            for l in range(L):
+                slots, _ = oc.resolve(l, trace[t, :n])
+                oc.attend(l, qs[t][l], slots, 1.0 / math.sqrt(576))
+            el += time.perf_counter() - t0
+            done += 1
+        passes += 1
+    return {"value": done * n * L / el, "unit": "selections/s", "cores": threads, "kind": "oracle",
             "sample": f"oracle resolve (tables + row copies) and fp64 attention of {L} layers for requests "
-                      f"0..{n - 1} on steps {warm}..{t - 1} ({done} steps, {el:.1f} s), rate scaled by {n}/{w.n}"}
+                      f"0..{n - 1} on steps {warm}..{T - 1} of the same trace, {passes} passes from an empty "
+                      f"cache ({done} steps, {done * n * L} selections, {el:.1f} s)"}
 
 
 def bench_pages(args, torch, hsa, w):
@@ -1061,14 +1068,24 @@ def bench_pages(args, torch, hsa, w):
 
 
 def bench_prefetch(args, torch, hsa, w):
-    """Decode steps over 8 layers sharing a selection: serial order vs layer-wise prefetch."""
+    """Whole decode steps over 8 layers sharing one selection (128 requests, ctx 65536, fp8 rows,
+    k 2048, B 4096): every layer resolves the step's selection (hit detection, LRU replacement,
+    table update, host-to-device fetch of the misses) and attends over its resolved slots.
+    Schedules: serial (resolve and attend layer after layer), layer-wise prefetch (the tables of
+    every layer on one side stream, the row copies on another, each attention waiting for its
+    layer's copy) and prefetch with each attention split by residency.  Each is captured as one
+    hipGraph of exactly --steps steps, replayed after --warmup untimed steps from an empty
+    buffer; the line's value is the fastest schedule whose outputs match the serial run."""
     from hierarchical_kv_cache_hs_amd.decode_step import DecodeSteps
     from synth import kv as skv
     from synth import trace as tr
 
-    K = min(args.steps, w.steps - args.warmup)
-    T = args.warmup + K
+    K, W = args.steps, args.warmup
+    T = W + K
+    w = w.with_(steps=max(w.steps, T))
+    t0 = time.perf_counter()
     trace = tr.generate(w.trace_spec(), steps=T)
+    log(f"trace {trace.shape} in {time.perf_counter() - t0:.1f}s")
     d_trace = torch.from_numpy(trace).cuda()
     hs = hsa.HiSparse(w.k, w.B, w.ratio, w.n, w.layers, w.layout, 16, 0)
     t0 = time.perf_counter()
@@ -1077,16 +1094,22 @@ def bench_prefetch(args, torch, hsa, w):
             ptr, cap, stride = hs.host_kv_ptr(l, r)
             skv.fill_rows(w.seed, r, l, 0, cap, w.layout, ptr, stride)
     log(f"host pool {hsa.host_bytes(hs.cfg) / 2**30:.1f} GiB filled in {time.perf_counter() - t0:.1f}s")
-    qs = [torch.from_numpy(np.stack([skv.queries(w.seed, t, w.n, l, 16) for l in range(w.layers)]).view(np.int16))
-          .cuda().view(torch.bfloat16) for t in range(4)]
+    # every step and layer has its own queries
+    t0 = time.perf_counter()
+    qsteps = [torch.from_numpy(np.stack([skv.queries(w.seed, t, w.n, l, 16) for l in range(w.layers)]).view(np.int16))
+              .cuda().view(torch.bfloat16) for t in range(T)]
+    log(f"queries for {T} steps in {time.perf_counter() - t0:.1f}s")
     scale = 1.0 / math.sqrt(576)
     sels = [d_trace[t] for t in range(T)]
-    qsteps = [qs[t % 4] for t in range(T)]
+
+    def warm(attend):
+        hs.reset_requests(0, w.n)
+        if W:
+            DecodeSteps(hs, sels[:W], qsteps[:W], scale, prefetch=False, attend=attend).replay()
 
     def timed(prefetch, attend, split_attention=False):
-        hs.reset_requests(0, w.n)
-        DecodeSteps(hs, sels[:args.warmup], qsteps[:args.warmup], scale, prefetch=False, attend=attend).replay()
-        steps = DecodeSteps(hs, sels[args.warmup:], qsteps[args.warmup:], scale, prefetch=prefetch, attend=attend,
+        warm(attend)
+        steps = DecodeSteps(hs, sels[W:], qsteps[W:], scale, prefetch=prefetch, attend=attend,
                             split_attention=split_attention)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -1101,13 +1124,44 @@ def bench_prefetch(args, torch, hsa, w):
     t_pre, s_pre = timed(True, True)
     t_spl, s_spl = timed(True, True, split_attention=True)
     t_res, _ = timed(False, False)
-    same = torch.equal(s_ser.out, s_pre.out) and torch.equal(s_ser.miss, s_pre.miss)
+    same = torch.equal(s_ser.out, s_pre.out) and torch.equal(s_ser.miss, s_pre.miss) and \
+        torch.equal(s_ser.lse, s_pre.lse)
     # the attention merged from two parts equals the single launch up to fp32 summation order
     spl_close = torch.equal(s_ser.miss, s_spl.miss) and \
         (s_ser.out.float() - s_spl.out.float()).abs().max().item() <= 2e-2
-    log(f"serial {t_ser:.3f} ms, prefetch {t_pre:.3f} ms, prefetch + split attention {t_spl:.3f} ms per step")
-    t_att = t_ser - t_res
-    # attention alone over the 8 layers (each launch reads another layer's rows), K times
+    log(f"serial {t_ser:.3f} ms, prefetch {t_pre:.3f} ms, prefetch + split attention {t_spl:.3f} ms, "
+        f"resolve only {t_res:.3f} ms per step")
+    best_split = spl_close and t_spl < t_pre
+    t_best = t_spl if best_split else t_pre
+    misses = s_ser.miss.double()                                  # [K][L][n]
+    miss_bytes_step = float(misses.sum()) * w.entry_bytes / K
+
+    # The row-copy kernel (fetch_kernel) timed on its own stream: the same steps again, enqueued
+    # without a graph in the prefetch schedule (a captured graph exposes no per-kernel time on
+    # this platform), with HIP events on the copy stream before each step's first copy launch and
+    # after its last; the layers' copies run back to back there, so the span over the launch
+    # count is the average launch duration (dispatch gaps between the copies included).
+    warm(True)
+    # (the prefetch schedule without the split attention: there the copies have a stream of their
+    # own, so nothing else runs between the step's first and last copy on it)
+    eager = DecodeSteps(hs, sels[W:], qsteps[W:], scale, prefetch=True, attend=True, split_attention=False,
+                        capture=False)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(eager.stream)
+    eager.run_eager(time_fetches=True)
+    e1.record(eager.stream)
+    torch.cuda.synchronize()
+    t_eager = e0.elapsed_time(e1) / K
+    fetch_ms = np.array([a.elapsed_time(b) for a, b in eager.fetch_events])   # per step, L launches
+    assert fetch_ms.size == K and torch.equal(eager.miss, s_ser.miss)
+    fetch_bytes_launch = miss_bytes_step / w.layers
+    fetch_avg_s = float(fetch_ms.sum()) / (K * w.layers) / 1e3
+    fetch_GBps = fetch_bytes_launch / fetch_avg_s / 1e9
+    log(f"fetch_kernel: {fetch_avg_s * 1e6:.1f} us per launch ({K * w.layers} launches), {fetch_GBps:.1f} GB/s; "
+        f"eager step {t_eager:.3f} ms")
+
+    # attention alone over the 8 layers (each launch reads another layer's rows), K steps
     ga = torch.cuda.CUDAGraph()
     st = torch.cuda.Stream()
     st.wait_stream(torch.cuda.current_stream())
@@ -1115,7 +1169,7 @@ def bench_prefetch(args, torch, hsa, w):
         with torch.cuda.graph(ga, stream=st):
             for i in range(K):
                 for l in range(w.layers):
-                    hs.attend(l, qsteps[i][l], s_ser.slots[l], scale, s_ser.out[l], s_ser.lse[l], stream=st)
+                    hs.attend(l, qsteps[W + i][l], s_ser.slots[l], scale, s_ser.out[l], s_ser.lse[l], stream=st)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(st):
@@ -1124,44 +1178,74 @@ def bench_prefetch(args, torch, hsa, w):
         b.record(st)
     torch.cuda.synchronize()
     t_att_only = a.elapsed_time(b) / K
+    del ga
     valid = float((s_ser.slots >= 0).sum().item()) / w.layers
-    att_bytes = valid * w.entry_bytes + w.n * (4 * w.k + 16 * (576 * 2 + 512 * 2 + 4))
-    misses = float(s_ser.miss.double().mean())
-    # the line's value: the faster of the two prefetch schedules (the split one only if its
-    # attention stayed within the bf16 tier of the serial run)
-    best_split = spl_close and t_spl < t_pre
-    t_best = t_spl if best_split else t_pre
+    att_bytes = valid * w.entry_bytes + w.n * (4 * w.k + 16 * (576 * 2 + 512 * 2 + 4))   # per launch
+    h2d = measure_h2d_peak(torch)
+    log(f"H2D memcpy peak {h2d:.1f} GB/s")
+    t_att = t_ser - t_res
+    step_GBps = miss_bytes_step / (t_best / 1e3) / 1e9
+    traffic = recorded_traffic("fetch_prefetch_c4", "resolve.hip")
     out = {
-        "metric": "decode steps/s, 8 layers sharing a selection, layer-wise prefetch, 1 MI355X",
-        "value": 1e3 / t_best, "unit": "steps/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "metric": "resolved top-k selections/s + miss-fetch GB/s vs host-link peak, 1 MI355X",
+        "value": w.n * w.layers / (t_best / 1e3), "unit": "selections/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": t_best, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        # resolution is integer work; the attention computes in bf16 (fp8 rows decoded exactly)
+        # with fp32 accumulation
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.description, "global_batch": w.n, "layers": w.layers, "seq_len": w.ctx,
-                   "top_k": w.k, "graph": True,
+                   "top_k": w.k, "device_buffer_size": w.B, "host_to_device_ratio": w.ratio,
+                   "entry_bytes": w.entry_bytes, "kv_rows": "fp8 e4m3 latent + fp32 scales + bf16 rope",
+                   "graph": True, "steps_timed": f"{W}..{W + K - 1}", "queries": "distinct per step and layer",
                    "schedule": "prefetch, attention split by residency" if best_split else "prefetch"},
-        "serial_ms_per_step": t_ser, "prefetch_ms_per_step": t_pre, "resolve_only_ms_per_step": t_res,
-        "attention_ms_per_step": t_att,
-        "attention_alone_ms_per_step": t_att_only,
-        "attention_alone_GBps": att_bytes * w.layers / (t_att_only / 1e3) / 1e9,
-        "overlap_saved_ms_per_step": t_ser - t_pre,
-        "attention_hidden_fraction": (t_ser - t_pre) / t_att if t_att > 0 else None,
-        "misses_per_selection": misses,
-        "miss_GB_per_step": misses * w.n * w.layers * w.entry_bytes / 1e9,
+        "selected_tokens_per_s": w.n * w.layers * w.k / (t_best / 1e3),
+        "attended_tokens_per_s": w.n * w.layers * w.k / (t_best / 1e3),
+        "misses_per_selection": float(misses.mean()),
+        "miss_GB_per_step": miss_bytes_step / 1e9,
+        # whole-step miss rate: the step's miss bytes over its time
+        "miss_fetch_GBps": step_GBps,
+        "miss_fetch_frac_of_link": step_GBps / PCIE_GEN5_X16_GBPS,
+        "miss_fetch_frac_of_measured_peak": step_GBps / h2d,
+        "h2d_peak_GBps_measured": h2d,
+        "serial_ms_per_step": t_ser, "prefetch_ms_per_step": t_pre, "prefetch_split_attention_ms_per_step": t_spl,
+        "resolve_only_ms_per_step": t_res,
+        "eager_ms_per_step": t_eager,
         "prefetch_equals_serial": bool(same),
-        # each layer's attention split by residency: the resident part waits only for the
-        # layer's tables, the fetched part for its copy
-        "prefetch_split_attention_ms_per_step": t_spl,
         "prefetch_split_attention_within_bf16_tier_of_serial": bool(spl_close),
-        "selections_per_s": w.n * w.layers / (t_best / 1e3),
-        # the step is bound by the miss copies over the host link (the fetch kernels on the
-        # copy stream); whole-step rate against the link, no single-kernel duration here
-        "roofline": {"bound": "host_link", "achieved": misses * w.n * w.layers * w.entry_bytes / (t_best / 1e3) / 1e9,
-                     "peak": PCIE_GEN5_X16_GBPS, "unit": "GB/s",
-                     "frac": misses * w.n * w.layers * w.entry_bytes / (t_best / 1e3) / 1e9 / PCIE_GEN5_X16_GBPS,
-                     "traffic": None, "kernel": "whole step (fetch_kernel copies on the second stream)"},
+        "overlap_saved_ms_per_step": t_ser - t_best,
+        "attention_ms_per_step": t_att,
+        "attention_hidden_fraction": (t_ser - t_best) / t_att if t_att > 0 else None,
+        "attention_alone": {"ms_per_step": t_att_only, "us_per_launch": t_att_only * 1e3 / w.layers,
+                            "bytes_per_launch": att_bytes,
+                            "GBps": att_bytes * w.layers / (t_att_only / 1e3) / 1e9,
+                            "frac_of_hbm": att_bytes * w.layers / (t_att_only / 1e3) / 1e9 / HBM_PEAK_GBPS},
+        # the dominant kernel: the row copies over the host link, timed launch by launch
+        "roofline": {"bound": "host_link", "achieved": fetch_GBps, "peak": PCIE_GEN5_X16_GBPS, "unit": "GB/s",
+                     "frac": fetch_GBps / PCIE_GEN5_X16_GBPS, "traffic": traffic, "kernel": "fetch_kernel",
+                     "avg_kernel_us": fetch_avg_s * 1e6, "launches_timed": int(K * w.layers),
+                     "algorithmic_bytes_per_launch": fetch_bytes_launch,
+                     "frac_of_measured_peak": fetch_GBps / h2d,
+                     "timing": "HIP events on the copy stream around each step's 8 back-to-back copy launches, "
+                               "the timed steps re-run without a graph in the prefetch schedule"},
     }
     hs.close()
     return out, trace
+
+
+def bench_extras(args, torch, hsa):
+    """The 64-request resolve-only and the 256-request resolve + attention workloads, run beside
+    the headline with the same --steps / --warmup: their rates go into the line as extra keys."""
+    from synth import configs as C
+    res, _ = bench_resolve(args, torch, hsa, C.BATCH64)
+    keep = ("value", "ms_per_step", "misses_per_selection", "miss_fetch_GBps", "miss_fetch_frac_of_measured_peak",
+            "resolve_only", "roofline", "config")
+    c1 = {k: res[k] for k in keep}
+    c1["unit"] = res["unit"]
+    att = bench_attend(args, torch, hsa, C.FP8_256, legs=False)
+    keep = ("value", "unit", "ms_per_step", "resolve_noio_us_per_step", "resolve_noio_cold_us_per_step",
+            "attention_f32_output_us", "misses_per_selection", "hbm_resolve_plus_attend", "roofline", "config")
+    c2 = {k: att[k] for k in keep}
+    return {"resolve_64_requests_bf16": c1, "resolve_attend_256_requests_fp8": c2}
 
 
 def bench_attend_cost(args, torch, hsa):
@@ -1237,7 +1321,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=190)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="batch64", choices=["batch64", "fp8_256", "prefetch", "sweep", "topk", "pages", "attend_cost"])
+    ap.add_argument("--workload", default="prefetch",
+                    choices=["prefetch", "batch64", "fp8_256", "sweep", "topk", "pages", "attend_cost"])
+    ap.add_argument("--no-extras", action="store_true",
+                    help="prefetch workload: skip the 64- and 256-request workloads run beside it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--summarize-profile", action="store_true",
@@ -1288,8 +1375,10 @@ def main():
             line["cpu_baseline"] = None
     elif args.workload == "prefetch":
         line, trace = bench_prefetch(args, torch, hsa, C.PREFETCH)
+        if not args.no_extras:
+            line["other_workloads"] = bench_extras(args, torch, hsa)
         line["cpu_baseline"] = None if args.no_cpu_baseline else \
-            cpu_baseline_prefetch(C.PREFETCH, trace, args.warmup, args.cpu_budget)
+            cpu_baseline_prefetch(C.PREFETCH.with_(steps=trace.shape[0]), trace, args.warmup, args.cpu_budget)
     elif args.workload == "sweep":
         line = bench_sweep(args, torch, hsa)
     elif args.workload == "topk":

@@ -226,6 +226,8 @@ class HiSparse:
         if miss is None:
             miss = torch.empty(n_req, dtype=torch.int32, device=sel.device)
         assert slots.shape == sel.shape and slots.dtype == torch.int32 and slots.is_contiguous()
+        assert miss.dtype == torch.int32 and miss.is_contiguous() and miss.numel() >= n_req
+        self._on_device(sel, slots, miss)
         if split:
             self.resolve_tables(layer, sel, slots, miss, stream)
             self.fetch_misses(layer, n_req, stream)
@@ -237,6 +239,8 @@ class HiSparse:
     def resolve_tables(self, layer: int, sel: torch.Tensor, slots: torch.Tensor, miss: torch.Tensor, stream=None):
         assert sel.dtype == torch.int32 and sel.is_contiguous() and sel.shape[1] == self.top_k
         assert slots.shape == sel.shape and slots.dtype == torch.int32 and slots.is_contiguous()
+        assert miss.dtype == torch.int32 and miss.is_contiguous() and miss.numel() >= sel.shape[0]
+        self._on_device(sel, slots, miss)
         _check(lib().hs_resolve_tables(self._h, layer, sel.shape[0], sel.data_ptr(), slots.data_ptr(),
                                        miss.data_ptr(), _stream_ptr(stream)))
 
@@ -251,6 +255,8 @@ class HiSparse:
         assert rows.dtype == torch.uint8 and rows.dim() == 2 and rows.shape[0] == n_req and rows.stride(1) == 1
         if slot_out is None:
             slot_out = torch.empty(n_req, dtype=torch.int32, device=pos.device)
+        assert slot_out.dtype == torch.int32 and slot_out.is_contiguous() and slot_out.numel() >= n_req
+        self._on_device(pos, rows, slot_out)
         _check(lib().hs_append(self._h, layer, n_req, pos.data_ptr(), rows.data_ptr(), rows.stride(0),
                                slot_out.data_ptr(), _stream_ptr(stream)))
         return slot_out
@@ -263,6 +269,7 @@ class HiSparse:
         if sel is None:
             sel = torch.empty(n_req, self.top_k, dtype=torch.int32, device=scores.device)
         assert sel.shape == (n_req, self.top_k) and sel.dtype == torch.int32 and sel.is_contiguous()
+        self._on_device(scores, lens, sel)
         _check(lib().hs_topk(self._h, n_req, scores.data_ptr(), scores.stride(0), lens.data_ptr(), sel.data_ptr(),
                              _stream_ptr(stream)))
         return sel
@@ -273,16 +280,36 @@ class HiSparse:
         _check(lib().hs_offload(self._h, layer, request, first, rows.shape[0], rows.data_ptr(), rows.stride(0),
                                 _stream_ptr(stream)))
 
+    # -- argument checks shared by the attention calls --------------------------------------------
+    def _on_device(self, *ts):
+        for t in ts:
+            if t is not None:
+                assert t.is_cuda and t.device == self.block.device, \
+                    f"tensor on {t.device}, handle on {self.block.device}"
+
+    def _attn_io(self, q: torch.Tensor, out, lse):
+        """Checks q against the handle's head count and sizes out / lse (the kernels index all
+        three with num_heads)."""
+        n_req = q.shape[0]
+        assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.dim() == 3 and q.shape[2] == 576
+        # a handle without heads: the library itself refuses (HS_ERR_UNSUPPORTED)
+        heads = self.heads if self.heads > 0 else q.shape[1]
+        assert q.shape[1] == heads, f"q has {q.shape[1]} heads, the handle {self.heads}"
+        if out is None:
+            out = torch.empty(n_req, heads, 512, dtype=self.out_dtype, device=q.device)
+        assert out.dtype == self.out_dtype and out.is_contiguous() and out.shape == (n_req, heads, 512)
+        if lse is None:
+            lse = torch.empty(n_req, heads, dtype=torch.float32, device=q.device)
+        assert lse.dtype == torch.float32 and lse.is_contiguous() and lse.shape == (n_req, heads)
+        self._on_device(q, out, lse)
+        return out, lse
+
     def attend(self, layer: int, q: torch.Tensor, slots: torch.Tensor, scale: float,
                out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream=None):
         n_req = q.shape[0]
-        assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.shape[2] == 576
         assert slots.dtype == torch.int32 and slots.is_contiguous() and slots.shape == (n_req, self.top_k)
-        if out is None:
-            out = torch.empty(n_req, q.shape[1], 512, dtype=self.out_dtype, device=q.device)
-        assert out.dtype == self.out_dtype and out.is_contiguous() and out.shape == (n_req, q.shape[1], 512)
-        if lse is None:
-            lse = torch.empty(n_req, q.shape[1], dtype=torch.float32, device=q.device)
+        out, lse = self._attn_io(q, out, lse)
+        self._on_device(slots)
         _check(lib().hs_attend(self._h, layer, n_req, q.data_ptr(), slots.data_ptr(), float(scale), out.data_ptr(),
                                lse.data_ptr(), _stream_ptr(stream)))
         return out, lse
@@ -292,15 +319,11 @@ class HiSparse:
                      lse: torch.Tensor | None = None, stream=None):
         """hs_attend_pages: attend cut at lens[r] tokens (sel: the selection slots came from)."""
         n_req = q.shape[0]
-        assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.shape[2] == 576
         assert slots.dtype == torch.int32 and slots.is_contiguous() and slots.shape == (n_req, self.top_k)
         assert sel.dtype == torch.int32 and sel.is_contiguous() and sel.shape == (n_req, self.top_k)
-        assert lens.dtype == torch.int32 and lens.is_contiguous() and lens.shape[0] >= n_req
-        if out is None:
-            out = torch.empty(n_req, q.shape[1], 512, dtype=self.out_dtype, device=q.device)
-        assert out.dtype == self.out_dtype and out.is_contiguous() and out.shape == (n_req, q.shape[1], 512)
-        if lse is None:
-            lse = torch.empty(n_req, q.shape[1], dtype=torch.float32, device=q.device)
+        assert lens.dtype == torch.int32 and lens.is_contiguous() and lens.dim() == 1 and lens.shape[0] >= n_req
+        out, lse = self._attn_io(q, out, lse)
+        self._on_device(slots, sel, lens)
         _check(lib().hs_attend_pages(self._h, layer, n_req, q.data_ptr(), slots.data_ptr(), sel.data_ptr(),
                                      lens.data_ptr(), float(scale), out.data_ptr(), lse.data_ptr(),
                                      _stream_ptr(stream)))
@@ -311,12 +334,14 @@ class HiSparse:
         """hs_attend_resident: after resolve_tables, attend the entries outside this step's victim
         slots into the handle's partials (may run beside fetch_misses of the same layer)."""
         n_req = q.shape[0]
-        assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.shape[2] == 576
+        assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.dim() == 3 and q.shape[2] == 576
+        assert self.heads == 0 or q.shape[1] == self.heads, f"q has {q.shape[1]} heads, the handle {self.heads}"
         assert slots.dtype == torch.int32 and slots.is_contiguous() and slots.shape == (n_req, self.top_k)
         assert (sel is None) == (lens is None)
         if sel is not None:
             assert sel.dtype == torch.int32 and sel.is_contiguous() and sel.shape == (n_req, self.top_k)
-            assert lens.dtype == torch.int32 and lens.is_contiguous() and lens.shape[0] >= n_req
+            assert lens.dtype == torch.int32 and lens.is_contiguous() and lens.dim() == 1 and lens.shape[0] >= n_req
+        self._on_device(q, slots, sel, lens)
         _check(lib().hs_attend_resident(self._h, layer, n_req, q.data_ptr(), slots.data_ptr(),
                                         None if sel is None else sel.data_ptr(),
                                         None if lens is None else lens.data_ptr(), float(scale),
@@ -326,14 +351,10 @@ class HiSparse:
                        lse: torch.Tensor | None = None, lens: torch.Tensor | None = None, stream=None):
         """hs_attend_fetched: after fetch_misses and attend_resident, attend the misses and merge."""
         n_req = q.shape[0]
-        assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.shape[2] == 576
         if lens is not None:
-            assert lens.dtype == torch.int32 and lens.is_contiguous() and lens.shape[0] >= n_req
-        if out is None:
-            out = torch.empty(n_req, q.shape[1], 512, dtype=self.out_dtype, device=q.device)
-        assert out.dtype == self.out_dtype and out.is_contiguous() and out.shape == (n_req, q.shape[1], 512)
-        if lse is None:
-            lse = torch.empty(n_req, q.shape[1], dtype=torch.float32, device=q.device)
+            assert lens.dtype == torch.int32 and lens.is_contiguous() and lens.dim() == 1 and lens.shape[0] >= n_req
+        out, lse = self._attn_io(q, out, lse)
+        self._on_device(lens)
         _check(lib().hs_attend_fetched(self._h, layer, n_req, q.data_ptr(),
                                        None if lens is None else lens.data_ptr(), float(scale), out.data_ptr(),
                                        lse.data_ptr(), _stream_ptr(stream)))

@@ -49,7 +49,7 @@ struct AppendArgs {
 
 __global__ __launch_bounds__(AT) void append_kernel(AppendArgs a) {
   extern __shared__ int32_t ord_lds[];  // [B]
-  __shared__ int32_t s_pj, s_c, s_more;
+  __shared__ int32_t s_pj, s_c;
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int B = a.B;

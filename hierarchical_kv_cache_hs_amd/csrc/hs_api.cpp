@@ -46,9 +46,25 @@ struct hs_handle {
   uint8_t* buf = nullptr;
   size_t part_floats = 0;  // per request
   // per layer: requests whose miss lists the last resolve-side call left in the handle (a
-  // list-only resolve); 0 after any other resolve, append or reset.  The attention parts read
-  // those lists and refuse to run without them.
+  // list-only resolve); 0 after any other resolve, append or reset.  The copy and the attention
+  // parts read those lists and refuse to run without them.
   std::vector<int32_t> lists_for;
+  // per layer: requests whose resident attention part left its split partials in the handle
+  // since the layer's last list-only resolve; 0 after any resolve, append, reset or whole
+  // attention of the layer (which reuse the same partial space).  The fetched part merges
+  // those partials and refuses to run without them.
+  std::vector<int32_t> resident_for;
+  // Streams this handle has enqueued work on outside graph capture, each with an event
+  // recorded after the handle's latest work there: hs_get_device_error and hs_destroy wait for
+  // these events only, not for the whole device.  Past kMaxStreams distinct streams the handle
+  // stops tracking and waits for the whole device instead.
+  struct Mark {
+    hipStream_t stream;
+    hipEvent_t event;
+  };
+  std::vector<Mark> marks;
+  bool untracked = false;
+  hipStream_t aux = nullptr;  // private non-blocking stream: initialisation and error-word reads
 };
 
 namespace {
@@ -182,9 +198,54 @@ hs::LayerTables layer_tables(const hs_handle* h, int32_t layer) {
 
 void release(hs_handle* h) {
   if (!h) return;
+  for (const hs_handle::Mark& m : h->marks) (void)hipEventDestroy(m.event);
+  if (h->aux) (void)hipStreamDestroy(h->aux);
   if (h->host_pool) (void)hipHostFree(h->host_pool);
   if (h->own_dev && h->dev_block) (void)hipFree(h->dev_block);
   delete h;
+}
+
+constexpr size_t kMaxStreams = 16;
+
+// Records, after work just enqueued on `s`, an event that hs_get_device_error / hs_destroy
+// wait for.  Work enqueued during graph capture runs when the graph is launched, on a stream
+// the handle never sees: the caller waits for it (a failure to query the capture state makes
+// the handle fall back to device-wide waits).
+void note_work(hs_handle* h, void* stream) {
+  if (h->untracked) return;
+  hipStream_t s = (hipStream_t)stream;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    h->untracked = true;
+    return;
+  }
+  if (cs != hipStreamCaptureStatusNone) return;
+  hipEvent_t ev = nullptr;
+  for (const hs_handle::Mark& m : h->marks)
+    if (m.stream == s) ev = m.event;
+  if (!ev) {
+    if (h->marks.size() >= kMaxStreams || hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
+      (void)hipGetLastError();
+      h->untracked = true;
+      return;
+    }
+    h->marks.push_back({s, ev});
+  }
+  if (hipEventRecord(ev, s) != hipSuccess) {
+    (void)hipGetLastError();
+    h->untracked = true;
+  }
+}
+
+// Waits for the work this handle enqueued (see note_work).
+hipError_t wait_own_work(hs_handle* h) {
+  if (h->untracked) return hipDeviceSynchronize();
+  for (const hs_handle::Mark& m : h->marks) {
+    hipError_t e = hipEventSynchronize(m.event);
+    if (e != hipSuccess) return e;
+  }
+  return h->aux ? hipStreamSynchronize(h->aux) : hipSuccess;
 }
 
 }  // namespace
@@ -229,8 +290,11 @@ hs_status hs_create(const hs_config* cfg, hs_handle** out) {
   h->g = g;
   h->part_floats = lay.part_floats;
   h->lists_for.assign((size_t)g.L, 0);
+  h->resident_for.assign((size_t)g.L, 0);
   hipError_t e = hipGetDevice(&h->device);
   if (e != hipSuccess) { release(h); return fail_hip(e, "hipGetDevice"); }
+  e = hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking);
+  if (e != hipSuccess) { h->aux = nullptr; release(h); return fail_hip(e, "hipStreamCreateWithFlags"); }
   if (cfg->device_mem) {
     h->dev_block = (uint8_t*)cfg->device_mem;
   } else {
@@ -280,13 +344,15 @@ hs_status hs_create(const hs_config* cfg, hs_handle** out) {
   hs::prepare_attend();
   hs::prepare_append();
   hs::prepare_topk();
-  e = hipMemset(h->err, 0, sizeof(int32_t));
+  // initialisation on the handle's own stream, waited for here: no device-wide synchronisation
+  e = hipMemsetAsync(h->err, 0, sizeof(int32_t), h->aux);
   if (e == hipSuccess)  // the zero row after each request's slots
-    e = hipMemset2D(h->buf + (size_t)g.B * (size_t)g.slot_stride, (size_t)g.req_stride, 0, (size_t)g.slot_stride,
-                    (size_t)g.L * (size_t)g.n);
-  if (e != hipSuccess) { release(h); return fail_hip(e, "hipMemset"); }
-  e = hs::launch_reset(g, h->pt, h->rm, h->st, h->ord, h->step, h->fresh, 0, g.n, nullptr);
-  if (e == hipSuccess) e = hipDeviceSynchronize();
+    e = hipMemset2DAsync(h->buf + (size_t)g.B * (size_t)g.slot_stride, (size_t)g.req_stride, 0,
+                         (size_t)g.slot_stride, (size_t)g.L * (size_t)g.n, h->aux);
+  if (e != hipSuccess) { (void)hipStreamSynchronize(h->aux); release(h); return fail_hip(e, "hipMemset"); }
+  e = hs::launch_reset(g, h->pt, h->rm, h->st, h->ord, h->step, h->fresh, 0, g.n, h->aux);
+  hipError_t e2 = hipStreamSynchronize(h->aux);
+  if (e == hipSuccess) e = e2;
   if (e != hipSuccess) { release(h); return fail_hip(e, "initialising tables"); }
   *out = h;
   return HS_OK;
@@ -313,6 +379,8 @@ hs_status resolve_impl(hs_handle* h, int32_t layer, int32_t n_req, const int32_t
                                     (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "resolve launch");
   h->lists_for[layer] = (list_only && !(h->g.flags & HS_FLAG_NO_IO)) ? n_req : 0;
+  h->resident_for[layer] = 0;
+  note_work(h, stream);
   return HS_OK;
 }
 
@@ -332,11 +400,18 @@ hs_status hs_fetch_misses(hs_handle* h, int32_t layer, int32_t n_req, void* stre
   if (!h) return fail(HS_ERR_INVALID_ARG, "handle is NULL");
   if (layer < 0 || layer >= h->g.L) return fail(HS_ERR_INVALID_ARG, "layer out of range");
   if (n_req < 0 || n_req > h->g.n) return fail(HS_ERR_INVALID_ARG, "n_req out of range");
+  if (h->g.flags & HS_FLAG_NO_IO) return HS_OK;  // no rows move
+  // the lists must be this step's: a fused resolve, an append or a reset since the list-only
+  // resolve has changed the tables, and replaying old lists would write rows into slots the
+  // page table now gives to other tokens
+  if (n_req > h->lists_for[layer])
+    return fail(HS_ERR_INVALID_ARG, "no miss lists for these requests: hs_resolve_tables of this layer must come first");
   if (n_req == 0) return HS_OK;
   hs::LayerTables t = layer_tables(h, layer);
   const uint8_t* host_layer = host_layer_of(h, layer);
   hipError_t e = hs::launch_fetch(h->g, t, host_layer, n_req, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "fetch launch");
+  note_work(h, stream);
   return HS_OK;
 }
 
@@ -362,6 +437,8 @@ hs_status hs_attend(hs_handle* h, int32_t layer, int32_t n_req, const void* d_q,
   hipError_t e =
       hs::launch_attend(h->g, t, n_req, d_q, d_slots, nullptr, nullptr, scale, d_out, d_lse, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "attend launch");
+  h->resident_for[layer] = 0;  // a split launch reuses the layer's partial space
+  note_work(h, stream);
   return HS_OK;
 }
 
@@ -379,6 +456,8 @@ hs_status hs_attend_pages(hs_handle* h, int32_t layer, int32_t n_req, const void
   hipError_t e =
       hs::launch_attend(h->g, t, n_req, d_q, d_slots, d_sel, d_len, scale, d_out, d_lse, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "attend launch");
+  h->resident_for[layer] = 0;  // a split launch reuses the layer's partial space
+  note_work(h, stream);
   return HS_OK;
 }
 
@@ -398,6 +477,8 @@ hs_status hs_attend_resident(hs_handle* h, int32_t layer, int32_t n_req, const v
   hipError_t e = hs::launch_attend_part(h->g, t, n_req, false, d_q, d_slots, d_sel, d_len, scale, nullptr, nullptr,
                                         (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "attend launch");
+  h->resident_for[layer] = n_req;
+  note_work(h, stream);
   return HS_OK;
 }
 
@@ -410,20 +491,26 @@ hs_status hs_attend_fetched(hs_handle* h, int32_t layer, int32_t n_req, const vo
   if (n_req < 0 || n_req > h->g.n) return fail(HS_ERR_INVALID_ARG, "n_req out of range");
   if (n_req > h->lists_for[layer])
     return fail(HS_ERR_INVALID_ARG, "no miss lists for these requests: hs_resolve_tables of this layer must come first");
+  // the partial strides depend on n_req, so the resident part must have covered exactly these requests
+  if (n_req != 0 && n_req != h->resident_for[layer])
+    return fail(HS_ERR_INVALID_ARG,
+                "no resident partials for these requests: hs_attend_resident of this layer with the same n_req must "
+                "come first");
   if (n_req == 0) return HS_OK;
   if (!d_q || !d_out) return fail(HS_ERR_INVALID_ARG, "query or output pointer is NULL");
   hs::LayerTables t = layer_tables(h, layer);
   hipError_t e = hs::launch_attend_part(h->g, t, n_req, true, d_q, nullptr, nullptr, d_len, scale, d_out, d_lse,
                                         (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "attend launch");
+  note_work(h, stream);
   return HS_OK;
 }
 
 hs_status hs_destroy(hs_handle* h) {
   if (!h) return HS_OK;
-  hipError_t e = hipDeviceSynchronize();
+  hipError_t e = wait_own_work(h);
   release(h);
-  if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
+  if (e != hipSuccess) return fail_hip(e, "waiting for the handle's work");
   return HS_OK;
 }
 
@@ -477,6 +564,8 @@ hs_status hs_append(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* d
                                                        d_slot_out, h->err, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "append launch");
   h->lists_for[layer] = 0;
+  h->resident_for[layer] = 0;
+  note_work(h, stream);
   return HS_OK;
 }
 
@@ -505,6 +594,7 @@ hs_status hs_offload(hs_handle* h, int32_t layer, int32_t request, int64_t first
     e = hipMemcpy2DAsync(h->host_pool + off, E, d_rows, (size_t)row_stride, E, (size_t)count, hipMemcpyDeviceToHost,
                          (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "offload copy");
+  note_work(h, stream);
   return HS_OK;
 }
 
@@ -518,6 +608,7 @@ hs_status hs_topk(hs_handle* h, int32_t n_req, const float* d_scores, int64_t sc
     return fail(HS_ERR_INVALID_ARG, "scores must be 16-byte aligned with a row stride that is a multiple of 4");
   hipError_t e = hs::launch_topk(h->g, n_req, d_scores, score_stride, d_len, d_sel, h->err, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "top-k launch");
+  note_work(h, stream);
   return HS_OK;
 }
 
@@ -529,16 +620,23 @@ hs_status hs_reset_requests(hs_handle* h, int32_t first, int32_t count, void* st
       hs::launch_reset(h->g, h->pt, h->rm, h->st, h->ord, h->step, h->fresh, first, count, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "reset launch");
   h->lists_for.assign((size_t)h->g.L, 0);
+  h->resident_for.assign((size_t)h->g.L, 0);
+  note_work(h, stream);
   return HS_OK;
 }
 
 hs_status hs_get_device_error(hs_handle* h, int32_t* bits) {
   if (!h || !bits) return fail(HS_ERR_INVALID_ARG, "handle or bits is NULL");
-  hipError_t e = hipDeviceSynchronize();
-  if (e == hipSuccess) e = hipMemcpy(bits, h->err, sizeof(int32_t), hipMemcpyDeviceToHost);
-  if (e == hipSuccess) e = hipMemset(h->err, 0, sizeof(int32_t));
-  if (e == hipSuccess) e = hipDeviceSynchronize();
+  // waits for the handle's own work only (see note_work), then reads and clears the word on the
+  // handle's private stream
+  int32_t v = 0;
+  hipError_t e = wait_own_work(h);
+  if (e == hipSuccess) e = hipMemcpyAsync(&v, h->err, sizeof(int32_t), hipMemcpyDeviceToHost, h->aux);
+  if (e == hipSuccess) e = hipMemsetAsync(h->err, 0, sizeof(int32_t), h->aux);
+  hipError_t e2 = hipStreamSynchronize(h->aux);
+  if (e == hipSuccess) e = e2;
   if (e != hipSuccess) return fail_hip(e, "reading the device error word");
+  *bits = v;
   return HS_OK;
 }
 

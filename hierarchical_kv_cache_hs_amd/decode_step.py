@@ -55,10 +55,14 @@ class DecodeSteps:
     """
 
     def __init__(self, hs: HiSparse, sels, qs, scale: float, prefetch: bool, attend: bool = True,
-                 split_attention: bool = False):
+                 split_attention: bool = False, capture: bool = True):
+        """With ``capture=False`` nothing is captured: :meth:`run_eager` enqueues the same
+        launches, in the same stream order, one step at a time (used to time single kernels of
+        the schedule with HIP events, which a captured graph does not expose)."""
         assert len(sels) == len(qs) and len(sels) > 0
         assert not split_attention or (prefetch and attend)
         self.hs, self.prefetch, self.attend, self.split_attention = hs, prefetch, attend, split_attention
+        self.fetch_events = None   # run_eager(time_fetches=True): (start, end) per fetch launch
         n = sels[0].shape[0]
         L, k = hs.L, hs.top_k
         dev = sels[0].device
@@ -70,12 +74,29 @@ class DecodeSteps:
         self.stream = torch.cuda.Stream(device=dev)
         self.side = torch.cuda.Stream(device=dev)    # table resolves
         self.copy = torch.cuda.Stream(device=dev)    # row copies
-        self.graph = torch.cuda.CUDAGraph()
+        self.sels, self.qs, self.scale = sels, qs, scale
+        self.graph = None
+        if capture:
+            self.graph = torch.cuda.CUDAGraph()
+            self.stream.wait_stream(torch.cuda.current_stream(dev))
+            with torch.cuda.stream(self.stream):
+                with torch.cuda.graph(self.graph, stream=self.stream):
+                    for i, (sel, q) in enumerate(zip(sels, qs)):
+                        self._one_step(i, sel, q, scale)
+            torch.cuda.current_stream(dev).wait_stream(self.stream)
+
+    def run_eager(self, time_fetches: bool = False):
+        """Enqueues every step without a graph (same kernels, streams and waits as the captured
+        schedule).  With ``time_fetches`` each step's row-copy launches are bracketed by timing
+        events on the stream they run on (one before the first copy, one after the last, so that
+        the layers' copies stay back to back); ``fetch_events`` then holds one (start, end) pair
+        per step."""
+        dev = self.slots.device
+        self.fetch_events = [] if time_fetches else None
         self.stream.wait_stream(torch.cuda.current_stream(dev))
         with torch.cuda.stream(self.stream):
-            with torch.cuda.graph(self.graph, stream=self.stream):
-                for i, (sel, q) in enumerate(zip(sels, qs)):
-                    self._one_step(i, sel, q, scale)
+            for i, (sel, q) in enumerate(zip(self.sels, self.qs)):
+                self._one_step(i, sel, q, self.scale)
         torch.cuda.current_stream(dev).wait_stream(self.stream)
 
     def _one_step(self, i, sel, q, scale):
@@ -109,7 +130,13 @@ class DecodeSteps:
         def fetch(l):
             if copy is not side:
                 copy.wait_event(tables[l])
+            timing = self.fetch_events is not None
+            if timing and l == 0:
+                self.fetch_events.append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+                self.fetch_events[-1][0].record(copy)
             hs.fetch_misses(l, n, stream=copy)
+            if timing and l == hs.L - 1:
+                self.fetch_events[-1][1].record(copy)
             copied[l] = torch.cuda.Event()
             copied[l].record(copy)
 

@@ -181,7 +181,10 @@ hs_status hs_resolve(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* 
  * rows with a kernel that uses no LDS and few registers, so it can share compute units with
  * a running attention kernel.  The pair must run in this order on the caller's streams,
  * with no other resolve of the same layer in between; together they equal hs_resolve.
- * With HS_FLAG_NO_IO, hs_fetch_misses enqueues nothing.
+ * hs_fetch_misses returns HS_ERR_INVALID_ARG (and enqueues nothing) unless the layer's last
+ * resolve, append or reset call was an hs_resolve_tables of at least n_req requests: other
+ * calls change the tables, and copying an older miss list would write rows into slots that
+ * now belong to other tokens.  With HS_FLAG_NO_IO, hs_fetch_misses enqueues nothing.
  */
 hs_status hs_resolve_tables(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* d_sel, int32_t* d_slots,
                             int32_t* d_miss, void* stream);
@@ -302,15 +305,22 @@ hs_status hs_stream_read(const void* d_src, size_t bytes, uint32_t* d_sink, void
  * Other arguments, outputs and errors as hs_attend; HS_ERR_UNSUPPORTED with HS_FLAG_NO_IO
  * (no rows are copied, so there is nothing to overlap); HS_ERR_INVALID_ARG when the layer's
  * last resolve, append or reset call was not an hs_resolve_tables of at least n_req requests
- * (the handle tracks the order of the calls, not of the device work).  Enqueue-only,
- * graph-capturable.
+ * (the handle tracks the order of the calls, not of the device work).  hs_attend_fetched
+ * also returns HS_ERR_INVALID_ARG unless an hs_attend_resident of the same layer and the same
+ * n_req came after that hs_resolve_tables with no hs_attend / hs_attend_pages of the layer in
+ * between (they reuse the space of the resident partials).  Enqueue-only, graph-capturable.
  */
 hs_status hs_attend_resident(hs_handle* h, int32_t layer, int32_t n_req, const void* d_q, const int32_t* d_slots,
                              const int32_t* d_sel, const int32_t* d_len, float scale, void* stream);
 hs_status hs_attend_fetched(hs_handle* h, int32_t layer, int32_t n_req, const void* d_q, const int32_t* d_len,
                             float scale, void* d_out, float* d_lse, void* stream);
 
-/* Synchronise the device and free everything the handle owns.  NULL is accepted. */
+/*
+ * Wait for the work this handle's calls enqueued (not for the rest of the device) and free
+ * everything the handle owns.  NULL is accepted.  Work the caller captured into a graph runs
+ * on whatever stream the graph is launched on, which the handle never sees: the caller
+ * waits for such replays before destroying the handle.
+ */
 hs_status hs_destroy(hs_handle* h);
 
 /*
@@ -332,7 +342,11 @@ hs_status hs_device_state(hs_handle* h, int32_t layer, hs_state_view* view);
 /* Return requests first..first+count-1 of every layer to the empty state (enqueued on stream). */
 hs_status hs_reset_requests(hs_handle* h, int32_t first, int32_t count, void* stream);
 
-/* Synchronise the device, return the accumulated HS_DEVERR_* bits in *bits and clear them. */
+/*
+ * Wait for the work this handle's calls enqueued (as hs_destroy; graph replays are the
+ * caller's to wait for), then return the accumulated HS_DEVERR_* bits in *bits and clear
+ * them.  Other streams of the process are not synchronised.
+ */
 hs_status hs_get_device_error(hs_handle* h, int32_t* bits);
 
 /* Static description of a status code. */

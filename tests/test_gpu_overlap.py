@@ -281,9 +281,10 @@ def test_overlap_parts_unsupported_without_io_and_stream_read_runs():
 
 
 def test_attention_parts_require_the_layers_miss_lists():
-    """The parts refuse to run unless the layer's last resolve-side call was a list-only
-    resolve of at least as many requests (a fused resolve, an append or a reset in between
-    leaves no lists for this step)."""
+    """The copy and the parts refuse to run unless the layer's last resolve-side call was a
+    list-only resolve of at least as many requests (a fused resolve, an append or a reset in
+    between leaves no lists for this step); the fetched part also needs the resident part's
+    partials of the same requests, which a whole attention of the layer overwrites."""
     p = Pair(3, 2, 64, 128, 4, hsa.LAYOUT_FP8, seed=3, heads=16)
     try:
         rng = np.random.default_rng(3)
@@ -299,16 +300,27 @@ def test_attention_parts_require_the_layers_miss_lists():
             assert e.value.status == hsa.HS_ERR_INVALID_ARG
 
         refused(lambda: p.hs.attend_resident(0, q, slots, SCALE))          # nothing resolved yet
+        refused(lambda: p.hs.fetch_misses(0, 3))
         p.hs.resolve(0, sel, slots, miss)                                  # fused: no lists
         refused(lambda: p.hs.attend_resident(0, q, slots, SCALE))
+        refused(lambda: p.hs.fetch_misses(0, 3))                           # stale lists would corrupt slots
         p.hs.resolve_tables(0, sel[:2], slots[:2], miss[:2])
         refused(lambda: p.hs.attend_resident(0, q, slots, SCALE))          # 3 requests, lists for 2
         refused(lambda: p.hs.attend_resident(1, q, slots, SCALE))          # other layer
+        refused(lambda: p.hs.fetch_misses(0, 3))
+        refused(lambda: p.hs.fetch_misses(1, 2))
         p.hs.fetch_misses(0, 2)
+        refused(lambda: p.hs.attend_fetched(0, q[:2], SCALE))             # no resident partials yet
+        p.hs.attend_resident(0, q[:2], slots[:2], SCALE)
+        refused(lambda: p.hs.attend_fetched(0, q[:1], SCALE))             # partials of 2 requests
+        p.hs.attend_fetched(0, q[:2], SCALE)
+        p.hs.attend(0, q[:2], slots[:2], SCALE)                           # reuses the partial space
+        refused(lambda: p.hs.attend_fetched(0, q[:2], SCALE))
         p.hs.attend_resident(0, q[:2], slots[:2], SCALE)
         p.hs.attend_fetched(0, q[:2], SCALE)
         p.hs.reset_requests(0, 3)
         refused(lambda: p.hs.attend_fetched(0, q[:2], SCALE))
+        refused(lambda: p.hs.fetch_misses(0, 2))
         torch.cuda.synchronize()
     finally:
         p.close()
