@@ -28,8 +28,12 @@
 //    accumulator layout a lane holds one head and four consecutive tokens -- exactly the
 //    A-operand layout of v_mfma_f32_16x16x16bf16_1k -- so P needs no data movement;
 //  * V must reach the P V MFMA as four consecutive tokens of one column per lane, the
-//    transpose of how rows are held.  One MFMA of the K operand against a 0/1 selector
-//    (exact: one product per output) produces that layout;
+//    transpose of how rows are held.  gfx950's LDS transpose reads produce that layout
+//    straight from the ring: per 32 value columns, one ds_read_b64_tr_b8 gives a lane the
+//    fp8 codes of its four tokens in two columns (converted exactly to bf16), or two
+//    ds_read_b64_tr_b16 give the bf16 values; they are read with the tile's K operands, so
+//    the ring slot is freed at the same point as before (the reads are one asm block with its
+//    own wait, see read_v_transposed);
 //  * FP8 codes decode with v_cvt_scalef32_pk_bf16_fp8 (exact); block scales are applied per
 //    token to the partial scores of each 128-value block and folded into P for the P V
 //    product of that block;
@@ -61,6 +65,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int WAVES = 8;
 constexpr int NT = WAVES * 64;
@@ -123,11 +128,11 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return v;
 }
 
-// Four fp32 that are bf16 values already (the transposed V) -> packed bf16, by truncation.
-__device__ __forceinline__ s16x4 pack4_exact(const f32x4 x) {
+// Four E4M3FN codes (bytes of w, in order) -> four bf16, exact.
+__device__ __forceinline__ s16x4 e4m3x4_to_bf16x4(uint32_t w) {
   u32x2 v;
-  v[0] = __builtin_amdgcn_perm(__float_as_uint(x[1]), __float_as_uint(x[0]), 0x07060302u);
-  v[1] = __builtin_amdgcn_perm(__float_as_uint(x[3]), __float_as_uint(x[2]), 0x07060302u);
+  v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
   return __builtin_bit_cast(s16x4, v);
 }
 
@@ -164,12 +169,9 @@ __device__ __forceinline__ int kb_offset(int kb, int g) {
   return kb < 16 ? 128 * (kb >> 2) + 32 * g + 8 * (kb & 3) : 512 + 16 * g + 8 * (kb - 16);
 }
 
-// Output column of accumulator tile tau (= 2 kb + sigma over latent kb) at tile column n.
-__device__ __forceinline__ int out_col(int tau, int n) {
-  const int kb = tau >> 1, sigma = tau & 1;
-  const int kappa = 16 * sigma + n;
-  return 128 * (kb >> 2) + 32 * (kappa >> 3) + 8 * (kb & 3) + (kappa & 7);
-}
+// Output column of accumulator tile tau (= 16 value half + 2 block + sigma) at tile column n:
+// block i of half hf covers columns 256 hf + 32 i .. + 31, sigma its 16-column halves.
+__device__ __forceinline__ int out_col(int tau, int n) { return 16 * tau + n; }
 
 // Reductions across the four 16-lane rows of a wave with gfx950's row-swap moves (plain VALU,
 // no LDS round trip).  v_permlane16_swap(x, x) leaves every lane holding its own value and
@@ -202,9 +204,65 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 __device__ __forceinline__ void lds_done_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// 32-bit LDS address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// A tile's transposed V operands for this lane (see voff): fp8, 8 reads of 8 codes at columns
+// 32 i; bf16, 16 reads of 4 values at columns 16 i.  The reads are written out in one asm
+// block that ends by waiting for them: the compiler's own transpose-read builtins are treated
+// as possibly aliasing the ring's in-flight LDS-DMA loads and get a wait for all of them
+// (every tile prefetched behind this one), which serialises the ring.  The tile read here
+// has landed: its DMA completed before the barrier that published it.
+template <int LAYOUT>
+__device__ __forceinline__ void read_v_transposed(uint32_t a, i32x2 (&vr)[LAYOUT == 0 ? 16 : 8]) {
+  if constexpr (LAYOUT == 1) {
+    asm volatile(
+        "ds_read_b64_tr_b8 %0, %8\n\t"
+        "ds_read_b64_tr_b8 %1, %8 offset:32\n\t"
+        "ds_read_b64_tr_b8 %2, %8 offset:64\n\t"
+        "ds_read_b64_tr_b8 %3, %8 offset:96\n\t"
+        "ds_read_b64_tr_b8 %4, %8 offset:128\n\t"
+        "ds_read_b64_tr_b8 %5, %8 offset:160\n\t"
+        "ds_read_b64_tr_b8 %6, %8 offset:192\n\t"
+        "ds_read_b64_tr_b8 %7, %8 offset:224\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]), "=&v"(vr[6]),
+          "=&v"(vr[7])
+        : "v"(a)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16\n\t"
+        "ds_read_b64_tr_b16 %1, %16 offset:32\n\t"
+        "ds_read_b64_tr_b16 %2, %16 offset:64\n\t"
+        "ds_read_b64_tr_b16 %3, %16 offset:96\n\t"
+        "ds_read_b64_tr_b16 %4, %16 offset:128\n\t"
+        "ds_read_b64_tr_b16 %5, %16 offset:160\n\t"
+        "ds_read_b64_tr_b16 %6, %16 offset:192\n\t"
+        "ds_read_b64_tr_b16 %7, %16 offset:224\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:256\n\t"
+        "ds_read_b64_tr_b16 %9, %16 offset:288\n\t"
+        "ds_read_b64_tr_b16 %10, %16 offset:320\n\t"
+        "ds_read_b64_tr_b16 %11, %16 offset:352\n\t"
+        "ds_read_b64_tr_b16 %12, %16 offset:384\n\t"
+        "ds_read_b64_tr_b16 %13, %16 offset:416\n\t"
+        "ds_read_b64_tr_b16 %14, %16 offset:448\n\t"
+        "ds_read_b64_tr_b16 %15, %16 offset:480\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]), "=&v"(vr[6]),
+          "=&v"(vr[7]), "=&v"(vr[8]), "=&v"(vr[9]), "=&v"(vr[10]), "=&v"(vr[11]), "=&v"(vr[12]), "=&v"(vr[13]),
+          "=&v"(vr[14]), "=&v"(vr[15])
+        : "v"(a)
+        : "memory");
+  }
+}
+
 template <int LAYOUT>
 struct TileGeo {
   static constexpr int E = LAYOUT == 0 ? 1152 : 656;      // bytes per row
+  static constexpr int VR = LAYOUT == 0 ? 16 : 8;         // 8-byte transposed V reads per wave and tile
   static constexpr int C = E / 16;                        // 16-byte chunks per row
   static constexpr int NBUF = LAYOUT == 0 ? 2 : 3;        // ring depth
   static constexpr int T = 16 * GROUPS;                   // tokens per tile
@@ -396,15 +454,15 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
     }
   };
 
-  // selector B operands of the V transposition: lane (g, n = c16) holds reduction rows
-  // 8g..8g+7 of column n; sigma = 0 selects row n, sigma = 1 row 16 + n.
-  bf16x8 sel0, sel1;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int kappa = 8 * g + e;
-    sel0[e] = (kappa == c16) ? (__bf16)1.0f : (__bf16)0.0f;
-    sel1[e] = (kappa == 16 + c16) ? (__bf16)1.0f : (__bf16)0.0f;
-  }
+  // This lane's address (bytes into a tile) of its transposed V reads, for block 0 of its half:
+  // fp8 -- source lane s = c16 of lane group g reads the 8 codes at row 4 g + (s/2 mod 4) of
+  // the wave's token group, column 16 (s/8) + 8 (s mod 2); the transpose hands lane (g, n)
+  // tokens 4g..4g+3 of columns n and 16 + n.  bf16 -- source lane s reads the 4 values at
+  // row 4 g + s/4, column 4 (s mod 4) (+16 for the second read); lane (g, n) receives tokens
+  // 4g..4g+3 of column n.  Block i adds 32 i columns.
+  const int voff = (LAYOUT == 1)
+                       ? (16 * tg + 4 * g + ((c16 >> 1) & 3)) * G::E + 256 * hf + 16 * (c16 >> 3) + 8 * (c16 & 1)
+                       : (16 * tg + 4 * g + (c16 >> 2)) * G::E + 2 * (256 * hf + 4 * (c16 & 3));
 
   f32x4 O[16];
 #pragma unroll
@@ -414,10 +472,11 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
   // This wave's K operands (its half of the 576 values of tokens 16 tg .. 16 tg + 15 of
   // tile t, converted to bf16), block scales of tokens 4g + j, and the slots of tokens
   // 4g .. 4g + 3 (-1 = padding).
-  auto load_tile = [&](int t, u32x4 (&kr)[KB_HALF], float (&scl)[4][2], u32x4& vqr) {
+  auto load_tile = [&](int t, u32x4 (&kr)[KB_HALF], float (&scl)[4][2], u32x4& vqr, i32x2 (&vr)[G::VR]) {
     const uint8_t* tile = ring + (t % G::NBUF) * G::TILE;
     const uint8_t* row = tile + (16 * tg + c16) * G::E;  // this lane's token (A-operand row)
     vqr = *(const u32x4*)(slot_lds + t * G::T + 16 * tg + 4 * g);
+    read_v_transposed<LAYOUT>(lds_addr(tile + voff), vr);
     if (LAYOUT == 0) {
 #pragma unroll
       for (int i = 0; i < KB_HALF; ++i) {
@@ -495,15 +554,16 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
   // registers, so all NBUF buffers start in flight.
   for (int u = 0; u < G::NBUF && u < ntiles; ++u) issue(u);
 
-  u32x4 kcur[KB_HALF];
   float sccur[4][2];
   u32x4 vqcur;
   f32x4 partcur;
+  i32x2 vcur[G::VR];  // tile t's V operands (transposed reads)
   if (ntiles > 0) {
+    u32x4 k0[KB_HALF];
     wait_tiles<LAYOUT>(min(G::NBUF - 1, ntiles - 1), per);  // this wave's share of tile 0
     barrier_only();
-    load_tile(0, kcur, sccur, vqcur);
-    partcur = qk(kcur, sccur);
+    load_tile(0, k0, sccur, vqcur, vcur);
+    partcur = qk(k0, sccur);
     publish(0, partcur);
   }
 
@@ -566,17 +626,21 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
     u32x4 knext[KB_HALF];
     float scnext[4][2];
     u32x4 vqnext;
-    load_tile(min(t + 1, ntiles - 1), knext, scnext, vqnext);
+    i32x2 vnext[G::VR];
+    load_tile(min(t + 1, ntiles - 1), knext, scnext, vqnext, vnext);
 
-    // ---- O += P V over this half's 256 columns
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    // ---- O += P V over this half's 256 columns (block i: columns 256 hf + 32 i .. + 31)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const bf16x8 kv = __builtin_bit_cast(bf16x8, kcur[i]);
       const s16x4 P = pa[i >> 2];
-      const f32x4 t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, sel0, zero, 0, 0, 0);
-      const f32x4 t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, sel1, zero, 0, 0, 0);
-      const s16x4 v0 = pack4_exact(t0), v1 = pack4_exact(t1);
+      s16x4 v0, v1;
+      if (LAYOUT == 1) {
+        v0 = e4m3x4_to_bf16x4((uint32_t)vcur[i][0]);
+        v1 = e4m3x4_to_bf16x4((uint32_t)vcur[i][1]);
+      } else {
+        v0 = __builtin_bit_cast(s16x4, vcur[2 * i]);
+        v1 = __builtin_bit_cast(s16x4, vcur[2 * i + 1]);
+      }
       if (F32) {  // smallest terms first
         O[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl[i >> 2], v0, O[2 * i], 0, 0, 0);
         O[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl[i >> 2], v1, O[2 * i + 1], 0, 0, 0);
@@ -589,7 +653,7 @@ __global__ __launch_bounds__(NT, 1) void attend_kernel(AttendArgs a) {
 
     const f32x4 partnext = qk(knext, scnext);
 #pragma unroll
-    for (int i = 0; i < KB_HALF; ++i) kcur[i] = knext[i];
+    for (int i = 0; i < G::VR; ++i) vcur[i] = vnext[i];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       sccur[j][0] = scnext[j][0];
