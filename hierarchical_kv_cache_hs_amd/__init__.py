@@ -43,7 +43,8 @@ SYMBOLS = ("hs_create", "hs_resolve", "hs_resolve_tables", "hs_fetch_misses", "h
            "hs_append", "hs_offload", "hs_topk",
            "hs_device_bytes", "hs_host_bytes", "hs_host_kv",
            "hs_device_state", "hs_reset_requests", "hs_get_device_error", "hs_status_string",
-           "hs_last_error_message", "hs_stream_read", "hs_attend_resident", "hs_attend_fetched")
+           "hs_last_error_message", "hs_stream_read", "hs_attend_resident", "hs_attend_fetched",
+           "hs_attend_noalloc")
 
 
 class Config(ctypes.Structure):
@@ -94,6 +95,7 @@ def lib():
         L.hs_stream_read.argtypes = [p, ctypes.c_size_t, p, p]
         L.hs_attend_resident.argtypes = [p, i32, i32, p, p, p, p, ctypes.c_float, p]
         L.hs_attend_fetched.argtypes = [p, i32, i32, p, p, ctypes.c_float, p, p, p]
+        L.hs_attend_noalloc.argtypes = [p, i32, i32, i32, p, p, ctypes.c_float, p, p, p]
         L.hs_host_kv.argtypes = [p, i32, i32, ctypes.POINTER(p), ctypes.POINTER(ctypes.c_int64),
                                  ctypes.POINTER(ctypes.c_int64)]
         L.hs_device_state.argtypes = [p, i32, ctypes.POINTER(StateView)]
@@ -106,7 +108,7 @@ def lib():
         for name in ("hs_device_bytes", "hs_host_bytes", "hs_create", "hs_resolve", "hs_resolve_tables",
                      "hs_fetch_misses", "hs_attend", "hs_attend_pages", "hs_destroy",
                      "hs_host_kv", "hs_device_state", "hs_reset_requests", "hs_get_device_error",
-                     "hs_stream_read", "hs_attend_resident", "hs_attend_fetched"):
+                     "hs_stream_read", "hs_attend_resident", "hs_attend_fetched", "hs_attend_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         _lib_cache = L
     return _lib_cache
@@ -312,6 +314,26 @@ class HiSparse:
         self._on_device(slots)
         _check(lib().hs_attend(self._h, layer, n_req, q.data_ptr(), slots.data_ptr(), float(scale), out.data_ptr(),
                                lse.data_ptr(), _stream_ptr(stream)))
+        return out, lse
+
+    def attend_noalloc(self, layer: int, q: torch.Tensor, slots: torch.Tensor, scale: float,
+                       out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream=None):
+        """hs_attend_noalloc: hs_attend with q's head count (1..16, any handle) and the split
+        partials in the library's static device array; out / lse are allocated here only when
+        not given."""
+        n_req, heads = q.shape[0], q.shape[1]
+        assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.dim() == 3 and q.shape[2] == 576
+        assert 1 <= heads <= 16
+        assert slots.dtype == torch.int32 and slots.is_contiguous() and slots.shape == (n_req, self.top_k)
+        if out is None:
+            out = torch.empty(n_req, heads, 512, dtype=self.out_dtype, device=q.device)
+        assert out.dtype == self.out_dtype and out.is_contiguous() and out.shape == (n_req, heads, 512)
+        if lse is None:
+            lse = torch.empty(n_req, heads, dtype=torch.float32, device=q.device)
+        assert lse.dtype == torch.float32 and lse.is_contiguous() and lse.shape == (n_req, heads)
+        self._on_device(q, slots, out, lse)
+        _check(lib().hs_attend_noalloc(self._h, layer, n_req, heads, q.data_ptr(), slots.data_ptr(), float(scale),
+                                       out.data_ptr(), lse.data_ptr(), _stream_ptr(stream)))
         return out, lse
 
     def attend_pages(self, layer: int, q: torch.Tensor, slots: torch.Tensor, sel: torch.Tensor,

@@ -55,6 +55,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "hs_internal.h"
 
 namespace hs {
@@ -898,6 +900,52 @@ hipError_t launch_attend(const Geometry& g, const LayerTables& t, int32_t n_req,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   return launch_combine(g, t, n_req, a.splits, out, lse, st);
+}
+
+// Split partials of hs_attend_noalloc: a file-scope device array, one copy on every GPU the
+// library runs on (held until the process ends), so that the call allocates nothing.
+static __device__ __align__(256) float scratch[(size_t)kNoallocPartials * PART];
+
+namespace {
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each GPU, once resolved
+}  // namespace
+
+hipError_t prepare_attend_noalloc(int device) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device]) return hipSuccess;
+  // the array's host-side name is only a stand-in: its address on this device comes from here
+  float* p = nullptr;
+  hipError_t e = hipGetSymbolAddress((void**)&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  g_scratch_ptr[device] = p;
+  return hipSuccess;
+}
+
+int64_t attend_noalloc_partials(const Geometry& g, int32_t n_req, int32_t heads) {
+  Geometry g2 = g;
+  g2.heads = heads;
+  const int splits = attend_splits(g2, n_req);
+  return splits > 1 ? (int64_t)n_req * splits : 0;
+}
+
+hipError_t launch_attend_noalloc(const Geometry& g, const LayerTables& t, int device, int32_t n_req, int32_t heads,
+                                 const void* q, const int32_t* slots, float scale, void* out, float* lse,
+                                 hipStream_t st) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  float* p;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[device];
+  }
+  if (!p) return hipErrorNotInitialized;
+  if (attend_noalloc_partials(g, n_req, heads) > kNoallocPartials) return hipErrorInvalidValue;
+  Geometry g2 = g;
+  g2.heads = heads;
+  LayerTables t2 = t;
+  t2.part = p;  // the handle's own partial space (if any) is left untouched
+  return launch_attend(g2, t2, n_req, q, slots, nullptr, nullptr, scale, out, lse, st);
 }
 
 hipError_t launch_attend_part(const Geometry& g, const LayerTables& t, int32_t n_req, bool fetched, const void* q,

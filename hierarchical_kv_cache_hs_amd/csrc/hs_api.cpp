@@ -65,6 +65,7 @@ struct hs_handle {
   std::vector<Mark> marks;
   bool untracked = false;
   hipStream_t aux = nullptr;  // private non-blocking stream: initialisation and error-word reads
+  hipError_t noalloc_ready = hipErrorNotInitialized;  // hs_attend_noalloc's scratch resolved on `device`
 };
 
 namespace {
@@ -342,6 +343,8 @@ hs_status hs_create(const hs_config* cfg, hs_handle** out) {
 
   hs::prepare_resolve();
   hs::prepare_attend();
+  // hs_attend_noalloc's static partials: their address on this device, resolved once per device
+  h->noalloc_ready = hs::prepare_attend_noalloc(h->device);
   hs::prepare_append();
   hs::prepare_topk();
   // initialisation on the handle's own stream, waited for here: no device-wide synchronisation
@@ -457,6 +460,30 @@ hs_status hs_attend_pages(hs_handle* h, int32_t layer, int32_t n_req, const void
       hs::launch_attend(h->g, t, n_req, d_q, d_slots, d_sel, d_len, scale, d_out, d_lse, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "attend launch");
   h->resident_for[layer] = 0;  // a split launch reuses the layer's partial space
+  note_work(h, stream);
+  return HS_OK;
+}
+
+hs_status hs_attend_noalloc(hs_handle* h, int32_t layer, int32_t n_req, int32_t num_heads, const void* d_q,
+                            const int32_t* d_slots, float scale, void* d_out, float* d_lse, void* stream) {
+  if (!h) return fail(HS_ERR_INVALID_ARG, "handle is NULL");
+  if (layer < 0 || layer >= h->g.L) return fail(HS_ERR_INVALID_ARG, "layer out of range");
+  if (n_req < 0 || n_req > h->g.n) return fail(HS_ERR_INVALID_ARG, "n_req out of range");
+  if (num_heads < 1 || num_heads > 16) return fail(HS_ERR_INVALID_ARG, "num_heads must lie in [1, 16]");
+  if (n_req == 0) return HS_OK;
+  if (!d_q || !d_slots || !d_out) return fail(HS_ERR_INVALID_ARG, "query, slot or output pointer is NULL");
+  if ((int64_t)h->g.k * h->g.P > 65536)
+    return fail(HS_ERR_UNSUPPORTED, "attention over more than 65536 tokens (top_k * page_tokens)");
+  const int64_t need = hs::attend_noalloc_partials(h->g, n_req, num_heads);
+  if (need > hs::kNoallocPartials)
+    return fail(HS_ERR_UNSUPPORTED, "this launch needs " + std::to_string(need) +
+                                        " split partials; the static scratch holds " +
+                                        std::to_string(hs::kNoallocPartials) + " (use fewer requests or hs_attend)");
+  if (h->noalloc_ready != hipSuccess) return fail_hip(h->noalloc_ready, "resolving the static scratch");
+  hs::LayerTables t = layer_tables(h, layer);
+  hipError_t e = hs::launch_attend_noalloc(h->g, t, h->device, n_req, num_heads, d_q, d_slots, scale, d_out, d_lse,
+                                           (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "attend launch");
   note_work(h, stream);
   return HS_OK;
 }

@@ -109,6 +109,19 @@ hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hip
 hipError_t launch_attend(const Geometry& g, const LayerTables& t, int32_t n_req, const void* q, const int32_t* slots,
                          const int32_t* sel, const int32_t* len, float scale, void* out, float* lse, hipStream_t s);
 
+// hs_attend_noalloc: the split partials live in a static device array of kNoallocPartials
+// partials (one copy per GPU, up to kMaxDevices GPUs).  prepare_attend_noalloc resolves the
+// array's address on `device` (current) once; launch_attend_noalloc is launch_attend with
+// `heads` query heads and the partials there (hipErrorInvalidValue if the launch needs more
+// than kNoallocPartials; attend_noalloc_partials gives the count, 0 for a single split).
+constexpr int kNoallocPartials = 256;
+constexpr int kMaxDevices = 64;
+hipError_t prepare_attend_noalloc(int device);
+int64_t attend_noalloc_partials(const Geometry& g, int32_t n_req, int32_t heads);
+hipError_t launch_attend_noalloc(const Geometry& g, const LayerTables& t, int device, int32_t n_req, int32_t heads,
+                                 const void* q, const int32_t* slots, float scale, void* out, float* lse,
+                                 hipStream_t s);
+
 // One part of a step's attention split by residency, after a list-only resolve (the miss
 // lists in t): fetched == false attends the entries of `slots` outside this step's victim
 // slots into split partials (it may run while launch_fetch copies the misses); fetched ==

@@ -287,6 +287,25 @@ hs_status hs_attend_pages(hs_handle* h, int32_t layer, int32_t n_req, const void
 hs_status hs_stream_read(const void* d_src, size_t bytes, uint32_t* d_sink, void* stream);
 
 /*
+ * hs_attend for callers that cannot allocate device memory (code under graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc), also on handles created with
+ * num_heads = 0, which reserve no attention partials: the same computation and kernels as
+ * hs_attend with num_heads (1..16) query heads per call, the split partials of requests
+ * spread over several workgroups kept in a static device array of 256 partials (8.4 MB),
+ * one copy per GPU, held until the process ends, instead of the handle's block.  Its address
+ * on the handle's device is resolved when the handle is created.  Allocates nothing.
+ *   d_q, d_slots, scale, d_out, d_lse   as hs_attend, with num_heads in place of the handle's
+ * HS_ERR_UNSUPPORTED when the launch would need more than 256 partials: it needs n_req x s
+ * of them when hs_attend would spread each request over s > 1 workgroups (s = 256 / n_req,
+ * at most 16 and at most tokens / 64, at least tokens / 2048 for fp8 rows and tokens / 1024
+ * for bf16 rows, tokens = top_k x page_tokens), none when s = 1.  The handle's own partials
+ * are untouched.
+ * Calls that overlap on one GPU -- on any handle -- race on the shared array.
+ */
+hs_status hs_attend_noalloc(hs_handle* h, int32_t layer, int32_t n_req, int32_t num_heads, const void* d_q,
+                            const int32_t* d_slots, float scale, void* d_out, float* d_lse, void* stream);
+
+/*
  * A step's attention split by residency, so that the attention of the selected tokens
  * already in the device buffer runs while the misses are still being copied in (paper
  * abstract: host-device IO is the only price of bounded residency; the note, section 3:
