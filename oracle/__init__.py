@@ -34,7 +34,8 @@ from functools import lru_cache
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SO = os.path.join(_HERE, "liboracle.so")
+# HS_ORACLE_LIB points at another build of hs_oracle.c (the sanitizer test's instrumented one)
+_SO = os.environ.get("HS_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _SRC = os.path.join(_HERE, "hs_oracle.c")
 
 OK, BAD_TOKEN, DUPLICATE, NO_ROOM, NOMEM, BAD_POLICY = 0, -1, -2, -3, -4, -5

@@ -71,8 +71,10 @@ def test_tiny_every_step(layout):
     say(f"worst abs error {worst:.3e}")
 
 
-@pytest.mark.parametrize("churn", [0.10])
+@pytest.mark.parametrize("churn", C.FP8_256_CHURNS)
 def test_fp8_256_full_size_sampled_steps(churn):
+    """Every request's attention at steps 0 (all misses), 5 and 11 (steady state) of the
+    256-request fp8 workload at each churn."""
     w = C.churn_point(churn)
     steps = 12
     say(f"attend fp8_256: 256 requests, k 2048, B 4096, churn {churn}, {steps} steps, attention at 0/5/11")

@@ -43,8 +43,12 @@ def _run(hs, w, x, qs, prefetch, split_attention=False):
 
 @pytest.mark.parametrize("full", [False, True])
 def test_prefetch_equals_serial_and_oracle(full):
+    """Serial and prefetch runs equal bitwise; tables, slots and misses of every layer equal the
+    oracle at every step; the attention of every request and layer equals the oracle's
+    attention over the history rows at step 4 and at the last step (11, steady state) of the
+    full workload (the reduced one: its last step)."""
     w = C.PREFETCH if full else C.PREFETCH.with_(n=6, ctx=8192, ratio=2)
-    T = 5 if full else 8
+    T = 12 if full else 8
     say(f"prefetch: {w.n} requests, {w.layers} layers, cap {w.cap}, fp8, {T} steps")
     x = trace_for(w, steps=T)
     hs = hsa.HiSparse(w.k, w.B, w.ratio, w.n, w.layers, w.layout, num_heads=16)
@@ -73,17 +77,20 @@ def test_prefetch_equals_serial_and_oracle(full):
             pt, rm, stamp = (u.cpu().numpy() for u in ser_tables[l][:3])
             assert (pt == orc.PT[:, 0]).all() and (rm == orc.RM[:, 0]).all()
             assert (stamp.astype(np.int64) == orc.ST[:, 0]).all()
-        # attention of the last step on sampled requests, against rows gathered from the history
-        qb = np.stack([skv.queries(w.seed, T - 1, w.n, l, 16) for l in range(w.layers)])
-        for l in range(w.layers):
-            for r in sorted({0, w.n // 2, w.n - 1}):
-                rows = skv.rows_at(w.seed, r, l, x[T - 1, r], w.layout)[None]
-                o_o, l_o = oracle.attend_rows(qb[l, r][None], np.arange(w.k, dtype=np.int32)[None], rows,
-                                              w.layout, SCALE)
-                og = ser[T - 1][2][l, r].float().cpu().numpy()
-                err = np.abs(og - o_o[0]).max()
-                assert err <= 2e-2, f"layer {l} request {r}: attention error {err}"
-                assert np.abs(ser[T - 1][3][l, r].cpu().numpy() - l_o[0]).max() <= 1e-3
+        # attention of every request and layer, against rows gathered from the history
+        idx = np.tile(np.arange(w.k, dtype=np.int32), (w.n, 1))
+        for t in ((4, T - 1) if full else (T - 1,)):
+            qb = np.stack([skv.queries(w.seed, t, w.n, l, 16) for l in range(w.layers)])
+            worst = 0.0
+            for l in range(w.layers):
+                rows = np.stack([skv.rows_at(w.seed, r, l, x[t, r], w.layout) for r in range(w.n)])
+                o_o, l_o = oracle.attend_rows(qb[l], idx, rows, w.layout, SCALE)
+                og = ser[t][2][l].float().cpu().numpy()
+                err = np.abs(og - o_o).max()
+                assert err <= 2e-2, f"step {t} layer {l}: attention error {err}"
+                assert np.abs(ser[t][3][l].cpu().numpy() - l_o).max() <= 1e-3, f"step {t} layer {l}: lse"
+                worst = max(worst, err)
+            say(f"step {t}: attention of {w.n} requests x {w.layers} layers, max abs error {worst:.3e}")
     finally:
         hs.close()
 

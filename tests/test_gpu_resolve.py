@@ -2,6 +2,8 @@
 output slots, miss counts and slot bytes against the CPU oracle, on the seeded workloads
 and on edge cases (padding, ragged sizes, B = k, k = 1, invalid input, no-IO mode,
 reset, graph capture)."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -16,17 +18,25 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")]
 
 
-def _run(w, steps=None, requests=None, check_every=1, oracle_rows=True, sample_rows=None, split=False):
+def _run(w, steps=None, requests=None, check_every=1, oracle_rows=True, sample_rows=None, split=False,
+         rows_every=None):
+    """Every step: output slots and miss counts bit-exact.  Every check_every steps (and the
+    last): page table, owners, stamps, step counters and the LRU order; slot bytes too, on
+    every occupied slot or on sample_rows per request, every rows_every steps (default: with
+    the tables)."""
     x = trace_for(w, steps=steps, requests=requests)
     n = x.shape[1]
     p = Pair(n, 1, w.k, w.B, w.ratio, w.layout, w.seed, oracle_rows=oracle_rows, split=split)
+    rows_every = rows_every or check_every
     misses = []
     try:
         for t in range(x.shape[0]):
-            check = (t % check_every == 0) or t == x.shape[0] - 1
+            last = t == x.shape[0] - 1
             _, m = p.step(0, x[t], check_state=False)
-            if check:
-                p.check_state(0, n, sample_rows=sample_rows)
+            if t % check_every == 0 or last:
+                p.check_state(0, n, rows=(t % rows_every == 0 or last), sample_rows=sample_rows)
+            if t % 50 == 0:
+                say(f"{w.name}: step {t} of {x.shape[0]} matches")
             misses.append(m)
     finally:
         p.close()
@@ -49,14 +59,25 @@ def test_batch64_full(mode):
 
 @pytest.mark.parametrize("B", C.SWEEP_BUFFERS)
 def test_sweep_buffers_full_size(B):
+    """All 100 steps of the 131072-token buffer sweep: slots and misses every step, tables
+    every 10 steps, slot bytes on 256 sampled slots per request (regenerated rows)."""
     w = C.sweep_point(B)
-    say(f"sweep: 32 requests, ctx 131072, k 2048, B {B}, cap {w.cap}")
-    m = _run(w, steps=40, check_every=13, oracle_rows=False, sample_rows=256)
-    assert (m[0] == 2048).all()
+    say(f"sweep: 32 requests, ctx 131072, k 2048, B {B}, cap {w.cap}, all {w.steps} steps")
+    m = _run(w, check_every=10, oracle_rows=False, sample_rows=256)
+    assert m.shape[0] == 100 and (m[0] == 2048).all()
 
 
-@pytest.mark.parametrize("churn", C.FP8_256_CHURNS)
-def test_fp8_256_resolve_full_size(churn):
+def test_fp8_256_resolve_all_steps_all_rows():
+    """The 256-request fp8 workload at 10 % churn over all 200 steps: slots and misses every
+    step, tables every 10 steps, and every occupied slot's bytes against the oracle's copy of
+    the device buffer every 50 steps and at the last."""
+    w = C.churn_point(0.10)
+    say(f"fp8_256 resolve: 256 requests, fp8 656 B, churn 0.1, all {w.steps} steps, all slot rows")
+    _run(w, check_every=10, rows_every=50)
+
+
+@pytest.mark.parametrize("churn", (0.02, 0.30))
+def test_fp8_256_resolve_other_churns(churn):
     w = C.churn_point(churn)
     say(f"fp8_256 resolve: 256 requests, fp8 656 B, churn {churn}, 25 steps")
     _run(w, steps=25, check_every=8, oracle_rows=False, sample_rows=128)
@@ -154,6 +175,35 @@ def test_fewer_requests_than_slots_and_layers_independent():
                 S = np.stack([rng.choice(512, 64, replace=False) for _ in range(nr)]).astype(np.int32)
                 p.step(layer, S, check_state=False)
                 p.check_state(layer, 6)
+    finally:
+        p.close()
+
+
+def test_injected_host_allocation_failure(monkeypatch):
+    """HS_FAULT_INJECT=host_alloc makes the pinned host allocation fail inside hs_create after
+    the library allocated its own device block: HS_ERR_OUT_OF_MEMORY, no handle, the device
+    block freed again (device memory back where it was after three attempts), and a handle
+    created afterwards resolves bit-exactly against the oracle."""
+    say("fault injection: pinned host allocation failure in hs_create")
+    cfg = hsa.make_config(2048, 4096, 8, 64, 1, hsa.LAYOUT_BF16)    # device_mem NULL: library-owned block
+    need = hsa.device_bytes(cfg)
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    monkeypatch.setenv("HS_FAULT_INJECT", "host_alloc")
+    h = ctypes.c_void_p()
+    for _ in range(3):
+        st = hsa.lib().hs_create(ctypes.byref(cfg), ctypes.byref(h))
+        assert st == hsa.HS_ERR_OUT_OF_MEMORY and not h.value
+        assert "injected" in hsa.lib().hs_last_error_message().decode()
+    free1 = torch.cuda.mem_get_info()[0]
+    assert abs(free0 - free1) < need // 2, f"device memory {free0 - free1} bytes lower after failed creations"
+    monkeypatch.delenv("HS_FAULT_INJECT")
+    rng = np.random.default_rng(55)
+    p = Pair(3, 1, 64, 128, 4, hsa.LAYOUT_BF16, seed=55)
+    try:
+        for t in range(6):
+            p.step(0, np.stack([rng.choice(512, 64, replace=False) for _ in range(3)]).astype(np.int32),
+                   check_state=True)
     finally:
         p.close()
 
