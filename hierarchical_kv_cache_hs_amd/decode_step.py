@@ -55,13 +55,18 @@ class DecodeSteps:
     """
 
     def __init__(self, hs: HiSparse, sels, qs, scale: float, prefetch: bool, attend: bool = True,
-                 split_attention: bool = False, capture: bool = True):
+                 split_attention: bool = False, capture: bool = True, split_last: bool = False):
         """With ``capture=False`` nothing is captured: :meth:`run_eager` enqueues the same
         launches, in the same stream order, one step at a time (used to time single kernels of
-        the schedule with HIP events, which a captured graph does not expose)."""
+        the schedule with HIP events, which a captured graph does not expose).  With
+        ``split_last`` (layer-wise prefetch only) just the last layer's attention is split by
+        residency: its resident part runs beside the last row copy, so that after the step's
+        last copy only the attention of that layer's misses remains."""
         assert len(sels) == len(qs) and len(sels) > 0
         assert not split_attention or (prefetch and attend)
+        assert not split_last or (prefetch and attend and not split_attention)
         self.hs, self.prefetch, self.attend, self.split_attention = hs, prefetch, attend, split_attention
+        self.split_last = split_last
         self.fetch_events = None   # run_eager(time_fetches=True): (start, end) per fetch launch
         n = sels[0].shape[0]
         L, k = hs.L, hs.top_k
@@ -87,10 +92,12 @@ class DecodeSteps:
 
     def run_eager(self, time_fetches: bool = False):
         """Enqueues every step without a graph (same kernels, streams and waits as the captured
-        schedule).  With ``time_fetches`` each step's row-copy launches are bracketed by timing
-        events on the stream they run on (one before the first copy, one after the last, so that
-        the layers' copies stay back to back); ``fetch_events`` then holds one (start, end) pair
-        per step."""
+        schedule).  With ``time_fetches`` (layer-wise prefetch with the copies on a stream of
+        their own) each step's row-copy launches are bracketed by timing events on that stream,
+        one before the first copy and one after the last, and the copies wait once for all the
+        step's table resolves (which run ahead of them anyway) instead of once per layer, so
+        they follow one another with no cross-stream wait in between; ``fetch_events`` then
+        holds one (start, end) pair per step."""
         dev = self.slots.device
         self.fetch_events = [] if time_fetches else None
         self.stream.wait_stream(torch.cuda.current_stream(dev))
@@ -128,9 +135,11 @@ class DecodeSteps:
             tables[l].record(side)
 
         def fetch(l):
-            if copy is not side:
-                copy.wait_event(tables[l])
             timing = self.fetch_events is not None
+            if copy is not side and not timing:
+                copy.wait_event(tables[l])
+            if copy is not side and timing and l == 0:
+                copy.wait_event(tables[hs.L - 1])      # every layer's tables (one side stream)
             if timing and l == 0:
                 self.fetch_events.append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
                 self.fetch_events[-1][0].record(copy)
@@ -141,6 +150,7 @@ class DecodeSteps:
             copied[l].record(copy)
 
         if copy is side:
+            assert self.fetch_events is None, "fetch timing needs the copies on their own stream"
             for l in range(hs.L):
                 resolve_tables(l)
                 fetch(l)
@@ -150,7 +160,7 @@ class DecodeSteps:
             for l in range(hs.L):
                 fetch(l)
         for l in range(hs.L):
-            if self.split_attention:
+            if self.split_attention or (self.split_last and l == hs.L - 1):
                 main.wait_event(tables[l])
                 hs.attend_resident(l, q[l], self.slots[l], scale, stream=main)
                 main.wait_event(copied[l])

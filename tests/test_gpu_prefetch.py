@@ -27,11 +27,12 @@ def _queries(w, t, L):
     return torch.from_numpy(q.view(np.int16)).cuda().view(torch.bfloat16)
 
 
-def _run(hs, w, x, qs, prefetch, split_attention=False):
+def _run(hs, w, x, qs, prefetch, split_attention=False, split_last=False):
     rec = []
     for t in range(x.shape[0]):
         sel = torch.from_numpy(x[t]).cuda()
-        steps = DecodeSteps(hs, [sel], [qs[t]], SCALE, prefetch=prefetch, split_attention=split_attention)
+        steps = DecodeSteps(hs, [sel], [qs[t]], SCALE, prefetch=prefetch, split_attention=split_attention,
+                            split_last=split_last)
         steps.replay()
         torch.cuda.synchronize()
         rec.append((steps.slots.clone(), steps.miss[0].clone(), steps.out.clone(), steps.lse.clone()))
@@ -95,14 +96,15 @@ def test_prefetch_equals_serial_and_oracle(full):
         hs.close()
 
 
-def test_prefetch_with_attention_split_by_residency():
-    """Layer-wise prefetch with each layer's attention split into the resident part (beside
-    the copies) and the fetched part: tables, slots and misses equal the serial run bitwise;
-    the attention, merged from two parts, matches the serial single-launch attention within the
-    bf16 tier and the oracle on sampled requests."""
+@pytest.mark.parametrize("which", ["every layer", "last layer"])
+def test_prefetch_with_attention_split_by_residency(which):
+    """Layer-wise prefetch with each layer's attention (or only the last layer's) split into
+    the resident part (beside the copies) and the fetched part: tables, slots and misses equal
+    the serial run bitwise; the attention, merged from two parts, matches the serial
+    single-launch attention within the bf16 tier and the oracle on sampled requests."""
     w = C.PREFETCH.with_(n=6, ctx=8192, ratio=2)
     T = 8
-    say(f"prefetch + split attention: {w.n} requests, {w.layers} layers, cap {w.cap}, fp8, {T} steps")
+    say(f"prefetch + split attention ({which}): {w.n} requests, {w.layers} layers, cap {w.cap}, fp8, {T} steps")
     x = trace_for(w, steps=T)
     hs = hsa.HiSparse(w.k, w.B, w.ratio, w.n, w.layers, w.layout, num_heads=16)
     try:
@@ -111,7 +113,8 @@ def test_prefetch_with_attention_split_by_residency():
         ser, ser_tables = _run(hs, w, x, qs, prefetch=False)
         hs.reset_requests(0, w.n)
         torch.cuda.synchronize()
-        spl, spl_tables = _run(hs, w, x, qs, prefetch=True, split_attention=True)
+        spl, spl_tables = _run(hs, w, x, qs, prefetch=True, split_attention=(which == "every layer"),
+                               split_last=(which == "last layer"))
         for t, (a, b) in enumerate(zip(ser, spl)):
             assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), f"step {t}: slots or misses differ"
             err = (a[2].float() - b[2].float()).abs().max().item()
