@@ -119,6 +119,14 @@ def _check(status: int):
         raise HSError(status, lib().hs_last_error_message().decode())
 
 
+def _require(ok: bool, msg: str = "tensor argument of the wrong dtype, shape, layout or size"):
+    """Argument check of the binding: the kernels index these tensors with the handle's sizes,
+    so a mismatch must stop the call before anything is enqueued (a plain raise, not an
+    assert, so it also holds under python -O)."""
+    if not ok:
+        raise ValueError(msg)
+
+
 def make_config(top_k, device_buffer_size, host_to_device_ratio, max_requests, num_layers=1, layout=LAYOUT_BF16,
                 num_heads=0, flags=0, eviction=0, eviction_seed=0, page_tokens=1) -> Config:
     return Config(top_k, device_buffer_size, host_to_device_ratio, max_requests, num_layers, layout, num_heads,
@@ -140,7 +148,7 @@ def host_bytes(cfg: Config) -> int:
 def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None):
     """Enqueue the library's dense streaming read of `src` (a measurement helper, not a step
     of the method); `sink` is a one-element int32 cuda tensor the kernel may overwrite."""
-    assert src.is_cuda and src.is_contiguous() and sink.is_cuda and sink.dtype == torch.int32
+    _require(src.is_cuda and src.is_contiguous() and sink.is_cuda and sink.dtype == torch.int32)
     _check(lib().hs_stream_read(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(),
                                 _stream_ptr(stream)))
 
@@ -222,13 +230,13 @@ class HiSparse:
                 miss: torch.Tensor | None = None, stream=None, split: bool = False):
         """hs_resolve; with split=True, hs_resolve_tables followed by hs_fetch_misses on the same stream."""
         n_req = sel.shape[0]
-        assert sel.dtype == torch.int32 and sel.is_contiguous() and sel.shape[1] == self.top_k
+        _require(sel.dtype == torch.int32 and sel.is_contiguous() and sel.shape[1] == self.top_k)
         if slots is None:
             slots = torch.empty_like(sel)
         if miss is None:
             miss = torch.empty(n_req, dtype=torch.int32, device=sel.device)
-        assert slots.shape == sel.shape and slots.dtype == torch.int32 and slots.is_contiguous()
-        assert miss.dtype == torch.int32 and miss.is_contiguous() and miss.numel() >= n_req
+        _require(slots.shape == sel.shape and slots.dtype == torch.int32 and slots.is_contiguous())
+        _require(miss.dtype == torch.int32 and miss.is_contiguous() and miss.numel() >= n_req)
         self._on_device(sel, slots, miss)
         if split:
             self.resolve_tables(layer, sel, slots, miss, stream)
@@ -239,9 +247,9 @@ class HiSparse:
         return slots, miss
 
     def resolve_tables(self, layer: int, sel: torch.Tensor, slots: torch.Tensor, miss: torch.Tensor, stream=None):
-        assert sel.dtype == torch.int32 and sel.is_contiguous() and sel.shape[1] == self.top_k
-        assert slots.shape == sel.shape and slots.dtype == torch.int32 and slots.is_contiguous()
-        assert miss.dtype == torch.int32 and miss.is_contiguous() and miss.numel() >= sel.shape[0]
+        _require(sel.dtype == torch.int32 and sel.is_contiguous() and sel.shape[1] == self.top_k)
+        _require(slots.shape == sel.shape and slots.dtype == torch.int32 and slots.is_contiguous())
+        _require(miss.dtype == torch.int32 and miss.is_contiguous() and miss.numel() >= sel.shape[0])
         self._on_device(sel, slots, miss)
         _check(lib().hs_resolve_tables(self._h, layer, sel.shape[0], sel.data_ptr(), slots.data_ptr(),
                                        miss.data_ptr(), _stream_ptr(stream)))
@@ -253,11 +261,11 @@ class HiSparse:
                stream=None):
         """hs_append: pos int32 [n_req] (-1 = none), rows uint8 [n_req][>= entry bytes] on the device."""
         n_req = pos.shape[0]
-        assert pos.dtype == torch.int32 and pos.is_contiguous()
-        assert rows.dtype == torch.uint8 and rows.dim() == 2 and rows.shape[0] == n_req and rows.stride(1) == 1
+        _require(pos.dtype == torch.int32 and pos.is_contiguous())
+        _require(rows.dtype == torch.uint8 and rows.dim() == 2 and rows.shape[0] == n_req and rows.stride(1) == 1)
         if slot_out is None:
             slot_out = torch.empty(n_req, dtype=torch.int32, device=pos.device)
-        assert slot_out.dtype == torch.int32 and slot_out.is_contiguous() and slot_out.numel() >= n_req
+        _require(slot_out.dtype == torch.int32 and slot_out.is_contiguous() and slot_out.numel() >= n_req)
         self._on_device(pos, rows, slot_out)
         _check(lib().hs_append(self._h, layer, n_req, pos.data_ptr(), rows.data_ptr(), rows.stride(0),
                                slot_out.data_ptr(), _stream_ptr(stream)))
@@ -266,11 +274,11 @@ class HiSparse:
     def topk(self, scores: torch.Tensor, lens: torch.Tensor, sel: torch.Tensor | None = None, stream=None):
         """hs_topk: scores float32 [n_req][stride] (stride % 4 == 0), lens int32 [n_req] -> sel [n_req][top_k]."""
         n_req = scores.shape[0]
-        assert scores.dtype == torch.float32 and scores.dim() == 2 and scores.stride(1) == 1
-        assert lens.dtype == torch.int32 and lens.is_contiguous() and lens.shape[0] == n_req
+        _require(scores.dtype == torch.float32 and scores.dim() == 2 and scores.stride(1) == 1)
+        _require(lens.dtype == torch.int32 and lens.is_contiguous() and lens.shape[0] == n_req)
         if sel is None:
             sel = torch.empty(n_req, self.top_k, dtype=torch.int32, device=scores.device)
-        assert sel.shape == (n_req, self.top_k) and sel.dtype == torch.int32 and sel.is_contiguous()
+        _require(sel.shape == (n_req, self.top_k) and sel.dtype == torch.int32 and sel.is_contiguous())
         self._on_device(scores, lens, sel)
         _check(lib().hs_topk(self._h, n_req, scores.data_ptr(), scores.stride(0), lens.data_ptr(), sel.data_ptr(),
                              _stream_ptr(stream)))
@@ -278,7 +286,7 @@ class HiSparse:
 
     def offload(self, layer: int, request: int, first: int, rows: torch.Tensor, stream=None):
         """hs_offload: rows uint8 [count][>= entry bytes] on the device -> history positions first.."""
-        assert rows.dtype == torch.uint8 and rows.dim() == 2 and rows.stride(1) == 1
+        _require(rows.dtype == torch.uint8 and rows.dim() == 2 and rows.stride(1) == 1)
         _check(lib().hs_offload(self._h, layer, request, first, rows.shape[0], rows.data_ptr(), rows.stride(0),
                                 _stream_ptr(stream)))
 
@@ -286,30 +294,30 @@ class HiSparse:
     def _on_device(self, *ts):
         for t in ts:
             if t is not None:
-                assert t.is_cuda and t.device == self.block.device, \
-                    f"tensor on {t.device}, handle on {self.block.device}"
+                _require(t.is_cuda and t.device == self.block.device,
+                         f"tensor on {t.device}, handle on {self.block.device}")
 
     def _attn_io(self, q: torch.Tensor, out, lse):
         """Checks q against the handle's head count and sizes out / lse (the kernels index all
         three with num_heads)."""
         n_req = q.shape[0]
-        assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.dim() == 3 and q.shape[2] == 576
+        _require(q.dtype == torch.bfloat16 and q.is_contiguous() and q.dim() == 3 and q.shape[2] == 576)
         # a handle without heads: the library itself refuses (HS_ERR_UNSUPPORTED)
         heads = self.heads if self.heads > 0 else q.shape[1]
-        assert q.shape[1] == heads, f"q has {q.shape[1]} heads, the handle {self.heads}"
+        _require(q.shape[1] == heads, f"q has {q.shape[1]} heads, the handle {self.heads}")
         if out is None:
             out = torch.empty(n_req, heads, 512, dtype=self.out_dtype, device=q.device)
-        assert out.dtype == self.out_dtype and out.is_contiguous() and out.shape == (n_req, heads, 512)
+        _require(out.dtype == self.out_dtype and out.is_contiguous() and out.shape == (n_req, heads, 512))
         if lse is None:
             lse = torch.empty(n_req, heads, dtype=torch.float32, device=q.device)
-        assert lse.dtype == torch.float32 and lse.is_contiguous() and lse.shape == (n_req, heads)
+        _require(lse.dtype == torch.float32 and lse.is_contiguous() and lse.shape == (n_req, heads))
         self._on_device(q, out, lse)
         return out, lse
 
     def attend(self, layer: int, q: torch.Tensor, slots: torch.Tensor, scale: float,
                out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream=None):
         n_req = q.shape[0]
-        assert slots.dtype == torch.int32 and slots.is_contiguous() and slots.shape == (n_req, self.top_k)
+        _require(slots.dtype == torch.int32 and slots.is_contiguous() and slots.shape == (n_req, self.top_k))
         out, lse = self._attn_io(q, out, lse)
         self._on_device(slots)
         _check(lib().hs_attend(self._h, layer, n_req, q.data_ptr(), slots.data_ptr(), float(scale), out.data_ptr(),
@@ -322,15 +330,15 @@ class HiSparse:
         partials in the library's static device array; out / lse are allocated here only when
         not given."""
         n_req, heads = q.shape[0], q.shape[1]
-        assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.dim() == 3 and q.shape[2] == 576
-        assert 1 <= heads <= 16
-        assert slots.dtype == torch.int32 and slots.is_contiguous() and slots.shape == (n_req, self.top_k)
+        _require(q.dtype == torch.bfloat16 and q.is_contiguous() and q.dim() == 3 and q.shape[2] == 576)
+        _require(1 <= heads <= 16)
+        _require(slots.dtype == torch.int32 and slots.is_contiguous() and slots.shape == (n_req, self.top_k))
         if out is None:
             out = torch.empty(n_req, heads, 512, dtype=self.out_dtype, device=q.device)
-        assert out.dtype == self.out_dtype and out.is_contiguous() and out.shape == (n_req, heads, 512)
+        _require(out.dtype == self.out_dtype and out.is_contiguous() and out.shape == (n_req, heads, 512))
         if lse is None:
             lse = torch.empty(n_req, heads, dtype=torch.float32, device=q.device)
-        assert lse.dtype == torch.float32 and lse.is_contiguous() and lse.shape == (n_req, heads)
+        _require(lse.dtype == torch.float32 and lse.is_contiguous() and lse.shape == (n_req, heads))
         self._on_device(q, slots, out, lse)
         _check(lib().hs_attend_noalloc(self._h, layer, n_req, heads, q.data_ptr(), slots.data_ptr(), float(scale),
                                        out.data_ptr(), lse.data_ptr(), _stream_ptr(stream)))
@@ -341,9 +349,9 @@ class HiSparse:
                      lse: torch.Tensor | None = None, stream=None):
         """hs_attend_pages: attend cut at lens[r] tokens (sel: the selection slots came from)."""
         n_req = q.shape[0]
-        assert slots.dtype == torch.int32 and slots.is_contiguous() and slots.shape == (n_req, self.top_k)
-        assert sel.dtype == torch.int32 and sel.is_contiguous() and sel.shape == (n_req, self.top_k)
-        assert lens.dtype == torch.int32 and lens.is_contiguous() and lens.dim() == 1 and lens.shape[0] >= n_req
+        _require(slots.dtype == torch.int32 and slots.is_contiguous() and slots.shape == (n_req, self.top_k))
+        _require(sel.dtype == torch.int32 and sel.is_contiguous() and sel.shape == (n_req, self.top_k))
+        _require(lens.dtype == torch.int32 and lens.is_contiguous() and lens.dim() == 1 and lens.shape[0] >= n_req)
         out, lse = self._attn_io(q, out, lse)
         self._on_device(slots, sel, lens)
         _check(lib().hs_attend_pages(self._h, layer, n_req, q.data_ptr(), slots.data_ptr(), sel.data_ptr(),
@@ -356,13 +364,13 @@ class HiSparse:
         """hs_attend_resident: after resolve_tables, attend the entries outside this step's victim
         slots into the handle's partials (may run beside fetch_misses of the same layer)."""
         n_req = q.shape[0]
-        assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.dim() == 3 and q.shape[2] == 576
-        assert self.heads == 0 or q.shape[1] == self.heads, f"q has {q.shape[1]} heads, the handle {self.heads}"
-        assert slots.dtype == torch.int32 and slots.is_contiguous() and slots.shape == (n_req, self.top_k)
-        assert (sel is None) == (lens is None)
+        _require(q.dtype == torch.bfloat16 and q.is_contiguous() and q.dim() == 3 and q.shape[2] == 576)
+        _require(self.heads == 0 or q.shape[1] == self.heads, f"q has {q.shape[1]} heads, the handle {self.heads}")
+        _require(slots.dtype == torch.int32 and slots.is_contiguous() and slots.shape == (n_req, self.top_k))
+        _require((sel is None) == (lens is None))
         if sel is not None:
-            assert sel.dtype == torch.int32 and sel.is_contiguous() and sel.shape == (n_req, self.top_k)
-            assert lens.dtype == torch.int32 and lens.is_contiguous() and lens.dim() == 1 and lens.shape[0] >= n_req
+            _require(sel.dtype == torch.int32 and sel.is_contiguous() and sel.shape == (n_req, self.top_k))
+            _require(lens.dtype == torch.int32 and lens.is_contiguous() and lens.dim() == 1 and lens.shape[0] >= n_req)
         self._on_device(q, slots, sel, lens)
         _check(lib().hs_attend_resident(self._h, layer, n_req, q.data_ptr(), slots.data_ptr(),
                                         None if sel is None else sel.data_ptr(),
@@ -374,7 +382,7 @@ class HiSparse:
         """hs_attend_fetched: after fetch_misses and attend_resident, attend the misses and merge."""
         n_req = q.shape[0]
         if lens is not None:
-            assert lens.dtype == torch.int32 and lens.is_contiguous() and lens.dim() == 1 and lens.shape[0] >= n_req
+            _require(lens.dtype == torch.int32 and lens.is_contiguous() and lens.dim() == 1 and lens.shape[0] >= n_req)
         out, lse = self._attn_io(q, out, lse)
         self._on_device(lens)
         _check(lib().hs_attend_fetched(self._h, layer, n_req, q.data_ptr(),
@@ -395,7 +403,7 @@ class HiSparse:
             return self.block[off: off + count * esz].view(dtype).view(*shape)
 
         n, B, cap = self.n, self.B, v.capacity
-        assert v.request_stride == (B + 1) * v.slot_stride
+        _require(v.request_stride == (B + 1) * v.slot_stride)
         rows = view(v.kv_buffer, n * v.request_stride, torch.uint8, (n, B + 1, v.slot_stride))
         return {
             "page_table": view(v.page_table, n * cap, torch.int32, (n, cap)),

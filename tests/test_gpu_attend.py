@@ -304,3 +304,36 @@ def test_attend_unsupported_without_heads():
                       torch.zeros(1, 8, dtype=torch.int32, device="cuda"), 0.1)
     finally:
         hs.close()
+
+
+def test_binding_refuses_mismatched_tensors():
+    """The binding checks every tensor against the handle's sizes before anything is enqueued:
+    a query with another head count, an undersized or wrongly typed lse, a CPU tensor or a
+    slot array of the wrong width raise ValueError, and the output buffers stay untouched."""
+    hs = hsa.HiSparse(8, 16, 2, 2, num_heads=16)
+    try:
+        dev = "cuda"
+        q = torch.zeros(2, 16, 576, dtype=torch.bfloat16, device=dev)
+        slots = torch.full((2, 8), -1, dtype=torch.int32, device=dev)
+        out = torch.full((2, 16, 512), 7.0, dtype=torch.bfloat16, device=dev)
+        lse = torch.full((2, 16), 7.0, dtype=torch.float32, device=dev)
+        bad = [
+            dict(q=torch.zeros(2, 8, 576, dtype=torch.bfloat16, device=dev)),     # 8 heads, handle 16
+            dict(lse=torch.zeros(2, 8, dtype=torch.float32, device=dev)),         # undersized lse
+            dict(lse=torch.zeros(2, 16, dtype=torch.float16, device=dev)),        # lse dtype
+            dict(out=torch.zeros(2, 16, 512, dtype=torch.bfloat16)),              # out on the CPU
+            dict(slots=torch.full((2, 4), -1, dtype=torch.int32, device=dev)),    # slots narrower than k
+        ]
+        for i, kw in enumerate(bad):
+            args = dict(q=q, slots=slots, out=out, lse=lse)
+            args.update(kw)
+            with pytest.raises(ValueError):
+                hs.attend(0, args["q"], args["slots"], SCALE, args["out"], args["lse"])
+        torch.cuda.synchronize()
+        assert (out.float() == 7.0).all() and (lse == 7.0).all(), "a refused call wrote its outputs"
+        # the same buffers with matching shapes are accepted (all padding: out 0, lse -inf)
+        hs.attend(0, q, slots, SCALE, out, lse)
+        torch.cuda.synchronize()
+        assert (out.float() == 0.0).all() and torch.isneginf(lse).all()
+    finally:
+        hs.close()
