@@ -19,12 +19,16 @@
 //   list     the next 12 and the last 8 key bits are resolved by histograms over the list,
 //            giving the k-th largest key exactly and how many keys equal to it are taken;
 //            candidates above it join the selection bitmap, those equal to it a tie bitmap;
-//   output   one block scan of (selected, tied) bit counts gives every thread its output
-//            offset -- ties before it that are taken = min(ties before it, ties needed) -- and
-//            the positions come out in order with no sort.
+//   output   one block scan of (selected, tied) bit counts over the bitmap words decides which
+//            ties are taken (the first ones in position order) and how many selected
+//            positions lie below each word; output i is then the (i - below)-th set bit of the
+//            last word whose count below is <= i, found by a binary search, so consecutive
+//            threads write consecutive outputs, with no sort.
 // If the candidate list would overflow (many equal scores), the last two digits are resolved
 // with re-reads of the row instead.  Reads are batched: eight 16-byte loads per thread are in
-// flight before any is used.
+// flight before any is used, and batches that lie wholly inside the row skip the per-key
+// bounds checks (the passes over the row are bound by VALU work per key and the histogram's
+// LDS atomics, not by the reads).
 
 #include "hs_internal.h"
 #include "hs_wave.h"
@@ -41,9 +45,8 @@ constexpr int NBIN = 4096;                // 12-bit digits
 constexpr int BPT = NBIN / TT;            // digits per thread in the search
 constexpr int MAXLEN = 1 << 18;           // positions per row
 constexpr int MAXW = MAXLEN / 32;         // bitmap words
-constexpr int CMAX = 8192;                // candidate list entries (the list also stages the output)
+constexpr int CMAX = 8192;                // candidate list entries
 static_assert(NBIN % TT == 0, "whole groups of digits per thread");
-static_assert(kMaxTopK <= 2 * CMAX, "the candidate list stages a row of output");
 
 constexpr size_t topk_lds_bytes() {
   return (NBIN + 2 * MAXW + 2 * CMAX) * sizeof(uint32_t);
@@ -51,10 +54,12 @@ constexpr size_t topk_lds_bytes() {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// key of a float given by its bits
+// key of a float given by its bits: negative floats are complemented, the others get the sign
+// bit set, so unsigned order is float order; -0 (complemented to 0x7FFFFFFF) moves up one to
+// +0's key 0x80000000
 __device__ __forceinline__ uint32_t order_key(uint32_t b) {
-  if (b == 0x80000000u) b = 0u;  // -0 equals +0
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  const uint32_t k = b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+  return k + (b == 0x80000000u ? 1u : 0u);
 }
 
 // Inclusive scan of v over the workgroup; *total gets the sum.  Every thread must call.
@@ -84,36 +89,45 @@ __device__ T block_scan_incl(T v, T* wtot, T* total) {
   return v + base;
 }
 
-// Calls batch(key, b0) for every batch of U tiles of the row, the loads of a batch all issued
+// Calls batch(key, b0) for every batch of UU tiles of the row, the loads of a batch all issued
 // first; this thread's key[j][e] is that of position b0 + j * TILE + 4 tid + e.  Positions
 // past the row get key 0, below every score's key (-inf maps to 0x007FFFFF).
-template <typename F>
+template <int UU, typename F>
 __device__ __forceinline__ void for_each_batch(const uint32_t* row, int n, F batch) {
   const int tid = threadIdx.x;
-  for (int b0 = 0; b0 < n; b0 += TILE * U) {
-    u32x4 key[U];
+  for (int b0 = 0; b0 < n; b0 += TILE * UU) {
+    u32x4 key[UU];
+    if (b0 + TILE * UU <= n) {  // the whole batch lies in the row: no per-key checks
 #pragma unroll
-    for (int j = 0; j < U; ++j) {  // in bounds: p < n <= stride, p and stride multiples of 4
-      const int p = b0 + j * TILE + 4 * tid;
-      key[j] = p < n ? *(const u32x4*)(row + p) : (u32x4){0u, 0u, 0u, 0u};
-    }
+      for (int j = 0; j < UU; ++j) key[j] = *(const u32x4*)(row + b0 + j * TILE + 4 * tid);
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const int p = b0 + j * TILE + 4 * tid;
+      for (int j = 0; j < UU; ++j)
 #pragma unroll
-      for (int e = 0; e < V; ++e) key[j][e] = (p + e < n) ? order_key(key[j][e]) : 0u;
+        for (int e = 0; e < V; ++e) key[j][e] = order_key(key[j][e]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < UU; ++j) {  // in bounds: p < n <= stride, p and stride multiples of 4
+        const int p = b0 + j * TILE + 4 * tid;
+        key[j] = p < n ? *(const u32x4*)(row + p) : (u32x4){0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int j = 0; j < UU; ++j) {
+        const int p = b0 + j * TILE + 4 * tid;
+#pragma unroll
+        for (int e = 0; e < V; ++e) key[j][e] = (p + e < n) ? order_key(key[j][e]) : 0u;
+      }
     }
     batch(key, b0);
   }
 }
 
 // for_each_batch, one key at a time: f(key, position)
-template <typename F>
+template <int UU, typename F>
 __device__ __forceinline__ void for_each_key(const uint32_t* row, int n, F f) {
   const int tid = threadIdx.x;
-  for_each_batch(row, n, [&](u32x4 (&key)[U], int b0) {
+  for_each_batch<UU>(row, n, [&](u32x4 (&key)[UU], int b0) {
 #pragma unroll
-    for (int j = 0; j < U; ++j)
+    for (int j = 0; j < UU; ++j)
 #pragma unroll
       for (int e = 0; e < V; ++e) f(key[j][e], b0 + j * TILE + 4 * tid + e);
   });
@@ -195,7 +209,7 @@ __global__ __launch_bounds__(TT) void topk_kernel(TopkArgs a) {
   if (tid == 0) s_ncand = 0;
   __syncthreads();
   // padding (key 0) lands in digit 0, which the search never reaches since len > k
-  for_each_key(row, n, [&](uint32_t u, int) { atomicAdd(&hist[u >> 20], 1u); });
+  for_each_key<U>(row, n, [&](uint32_t u, int) { atomicAdd(&hist[u >> 20], 1u); });
   __syncthreads();
   find_digit(hist, NBIN - 1, (uint32_t)k, wtot, &s_digit, &s_above);
   const uint32_t d1 = s_digit;
@@ -203,7 +217,7 @@ __global__ __launch_bounds__(TT) void topk_kernel(TopkArgs a) {
 
   // ---- pass B: above d1 -> selection bitmap; equal to d1 -> candidate list.  A thread masks
   // its candidates in a batch; one wave scan and one LDS atomic per wave place them.
-  for_each_batch(row, n, [&](u32x4 (&key)[U], int b0) {
+  for_each_batch<U>(row, n, [&](u32x4 (&key)[U], int b0) {
     uint32_t cmask = 0;
 #pragma unroll
     for (int j = 0; j < U; ++j) {
@@ -255,7 +269,7 @@ __global__ __launch_bounds__(TT) void topk_kernel(TopkArgs a) {
         if ((u >> (32 - fixed)) == prefix) atomicAdd(&hist[(u >> shift) & dmask], 1u);
       }
     } else {
-      for_each_key(row, n, [&](uint32_t u, int) {
+      for_each_key<U>(row, n, [&](uint32_t u, int) {
         if (u != 0u && (u >> (32 - fixed)) == prefix) atomicAdd(&hist[(u >> shift) & dmask], 1u);
       });
     }
@@ -276,17 +290,19 @@ __global__ __launch_bounds__(TT) void topk_kernel(TopkArgs a) {
       else if (u == thr) atomicOr(&tiemap[p >> 5], 1u << (p & 31));
     }
   } else {
-    for_each_key(row, n, [&](uint32_t u, int p) {
+    for_each_key<U>(row, n, [&](uint32_t u, int p) {
       if ((u >> 20) == d1 && u > thr) atomicOr(&selmap[p >> 5], 1u << (p & 31));
       else if (u == thr) atomicOr(&tiemap[p >> 5], 1u << (p & 31));
     });
   }
   __syncthreads();
 
-  // ---- output: each thread's consecutive bitmap words, in position order (the words are
-  // spread over all threads: ceil(words / threads) each), staged in LDS (the candidate list
-  // is no longer needed) and stored in whole rows
-  uint32_t* obuf = ckey;  // [k] <= 2 CMAX entries
+  // ---- output.  Each thread takes consecutive bitmap words (ceil(words / threads) each) and
+  // one block scan of their (selected, tied) bit counts gives it the ties before them, hence
+  // which of its ties are taken (the first `need` ties in position order); it writes each
+  // word's final mask over the selection bitmap and the number of selected positions below
+  // the word over the tie bitmap.  Then output i is found by thread i mod 1024: the last word
+  // whose count below is <= i (a binary search), and in it the (i - count)-th set bit.
   const int wpt = (nw + TT - 1) / TT;
   const int w0 = tid * wpt;
   const int w1 = min(nw, w0 + wpt);
@@ -300,6 +316,7 @@ __global__ __launch_bounds__(TT) void topk_kernel(TopkArgs a) {
   const uint64_t excl = block_scan_incl<uint64_t>(mine, wtot64, &tot) - mine;
   uint32_t tie_before = (uint32_t)excl;
   uint32_t o = (uint32_t)(excl >> 32) + min(tie_before, need);
+  uint32_t* below = tiemap;  // [nw] selected positions below each word
   for (int w = w0; w < w1; ++w) {
     uint32_t t = tiemap[w];
     // ties are taken in position order while fewer than `need` came before
@@ -315,23 +332,31 @@ __global__ __launch_bounds__(TT) void topk_kernel(TopkArgs a) {
       t = keep;
     }
     const uint32_t m = selmap[w] | t;
-    // every selected position of the word at once: offset = selected positions below it
-#pragma unroll
-    for (int b = 0; b < 32; ++b) {
-      const uint32_t idx = o + __popc(m & ((1u << b) - 1u));
-      if (((m >> b) & 1u) && idx < (uint32_t)k) obuf[idx] = (uint32_t)(w * 32 + b);
-    }
+    selmap[w] = m;
+    below[w] = o;
     o += __popc(m);
   }
   __syncthreads();
-  // the whole row of k positions leaves in 16-byte stores when it is aligned
-  const bool vec = (k & 3) == 0 && ((uintptr_t)out & 15u) == 0;
-  for (int i = 4 * tid; i < k; i += 4 * TT) {
-    if (vec) {
-      *(u32x4*)(out + i) = *(const u32x4*)(obuf + i);
-    } else {
-      for (int e = i; e < min(k, i + 4); ++e) out[e] = (int32_t)obuf[e];
+  for (int i = tid; i < k; i += TT) {
+    // the last word with below[w] <= i; below[0] = 0 <= i, and the word holds bit i - below[w]
+    int lo = 0, hi = nw - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (below[mid] <= (uint32_t)i) lo = mid;
+      else hi = mid - 1;
     }
+    uint32_t m = selmap[lo], j = (uint32_t)i - below[lo], pos = 0;
+    // the j-th set bit of m: halve the window five times
+#pragma unroll
+    for (int h = 16; h >= 1; h >>= 1) {
+      const uint32_t c = __popc(m & ((1u << h) - 1u));
+      if (j >= c) {
+        j -= c;
+        m >>= h;
+        pos += (uint32_t)h;
+      }
+    }
+    out[i] = (int32_t)(lo * 32 + (int)pos);
   }
 }
 

@@ -58,6 +58,35 @@ def test_topk_matches_oracle(k, stride, n, kind):
         hs.close()
 
 
+@pytest.mark.parametrize("plant", ["small", "large", "equal"])
+@pytest.mark.parametrize("stride,k", [(65536, 2048), (20000, 500), (8192, 8000)])
+def test_topk_rows_with_planted_values(plant, stride, k):
+    """Rows with a planted score at every position floor(i n / 4096), i < min(n, 4096): a
+    value far below the rest (the top-k avoids them), far above it (they fill the top of the
+    selection, or all of it), or one shared value (a digit full of ties); full and shortened
+    rows, k up to 8000 of 8192.  Bit-exact against the oracle."""
+    say(f"topk planted values: k {k}, stride {stride}, planted {plant}")
+    rng = np.random.default_rng(stride + k + len(plant))
+    n = 4
+    B = max(k, 8)
+    hs = hsa.HiSparse(k, B, (stride + B - 1) // B, n, 1, hsa.LAYOUT_BF16)
+    try:
+        s = rng.standard_normal((n, stride)).astype(np.float32)
+        lens = np.array([stride, stride - 7, max(k + 1, stride // 2), k + 1])
+        value = {"small": -3.0e38, "large": 3.0e38, "equal": 0.25}[plant]
+        for r in range(n):
+            m = int(lens[r])
+            S = min(m, 4096)
+            pos = (np.arange(S, dtype=np.int64) * m) // S
+            s[r, pos] = value
+        got = _run(hs, s, lens)
+        want = topk_oracle(s, lens, k)
+        assert (got == want).all(), "differs from the oracle"
+        assert hs.device_error() == 0
+    finally:
+        hs.close()
+
+
 def test_topk_length_out_of_range_sets_error():
     k, stride = 16, 64
     hs = hsa.HiSparse(k, 16, 2, 2, 1, hsa.LAYOUT_BF16)           # capacity 32 < stride
