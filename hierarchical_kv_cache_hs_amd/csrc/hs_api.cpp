@@ -226,7 +226,12 @@ void note_work(hs_handle* h, void* stream) {
   for (const hs_handle::Mark& m : h->marks)
     if (m.stream == s) ev = m.event;
   if (!ev) {
-    if (h->marks.size() >= kMaxStreams || hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
+    // no system-scope fence: these events only tell the host that the work has finished (the
+    // error word is written by device-scope atomics, and freeing memory needs no visibility),
+    // and a fenced record after every launch writes back the L2 and delays the stream's next
+    // kernel by several microseconds
+    if (h->marks.size() >= kMaxStreams ||
+        hipEventCreateWithFlags(&ev, hipEventDisableTiming | hipEventDisableSystemFence) != hipSuccess) {
       (void)hipGetLastError();
       h->untracked = true;
       return;
