@@ -174,3 +174,43 @@ def test_several_steps_in_one_graph(split_attention):
     finally:
         hs.close()
 
+
+
+@pytest.mark.parametrize("time_fetches", [False, True])
+def test_eager_schedule_equals_the_graph(time_fetches):
+    """The same steps enqueued without a graph (DecodeSteps(capture=False).run_eager, which the
+    bench uses to time the row copies): miss counts, slots, attention and tables equal the
+    serial graph bitwise; with timing, one (start, end) event pair per step on the copy
+    stream, each spanning a positive time."""
+    w = C.PREFETCH.with_(n=6, ctx=8192, ratio=2)
+    T = 4
+    say(f"prefetch eager, {T} steps, time_fetches {time_fetches}")
+    x = trace_for(w, steps=T)
+    hs = hsa.HiSparse(w.k, w.B, w.ratio, w.n, w.layers, w.layout, num_heads=16)
+    try:
+        fill_host_pool(hs, w.seed)
+        sels = [torch.from_numpy(x[t]).cuda() for t in range(T)]
+        qs = [_queries(w, t, w.layers) for t in range(T)]
+        ser = DecodeSteps(hs, sels, qs, SCALE, prefetch=False)
+        ser.replay()
+        torch.cuda.synchronize()
+        ser_tables = [tuple(hs.state(l)[k].clone() for k in ("page_table", "slot_owner", "slot_stamp", "step"))
+                      for l in range(w.layers)]
+        hs.reset_requests(0, w.n)
+        torch.cuda.synchronize()
+        eager = DecodeSteps(hs, sels, qs, SCALE, prefetch=True, capture=False)
+        assert eager.graph is None
+        eager.run_eager(time_fetches=time_fetches)
+        torch.cuda.synchronize()
+        assert torch.equal(ser.miss, eager.miss) and torch.equal(ser.slots, eager.slots)
+        assert torch.equal(ser.out, eager.out) and torch.equal(ser.lse, eager.lse)
+        for l in range(w.layers):
+            for u, k in zip(ser_tables[l], ("page_table", "slot_owner", "slot_stamp", "step")):
+                assert torch.equal(u, hs.state(l)[k]), f"layer {l}: {k} differs"
+        if time_fetches:
+            assert len(eager.fetch_events) == T
+            assert all(a.elapsed_time(b) > 0 for a, b in eager.fetch_events)
+        else:
+            assert eager.fetch_events is None
+    finally:
+        hs.close()
