@@ -343,3 +343,45 @@ def test_graph_capture_replays_match_eager():
     finally:
         eager.close()
         graphed.close()
+
+
+def test_empty_batches_are_accepted_and_change_nothing():
+    """Every enqueueing entry point with zero requests returns success, launches nothing and
+    leaves the tables, the device buffer and the error word as they were (between two steps of
+    a real trace, so the state is not empty)."""
+    w = C.TINY.with_(n=3)
+    x = trace_for(w, steps=4)
+    p = Pair(w.n, 1, w.k, w.B, w.ratio, w.layout, w.seed, heads=16)
+    try:
+        for t in range(2):
+            p.step(0, x[t], check_state=False)
+        hs = p.hs
+        torch.cuda.synchronize()
+        before = {k: v.clone() for k, v in hs.state(0).items() if isinstance(v, torch.Tensor)}
+        dev = "cuda"
+        sel0 = torch.empty(0, w.k, dtype=torch.int32, device=dev)
+        q0 = torch.empty(0, 16, 576, dtype=torch.bfloat16, device=dev)
+        lens0 = torch.empty(0, dtype=torch.int32, device=dev)
+        slots, miss = hs.resolve(0, sel0)
+        assert slots.shape == (0, w.k) and miss.shape == (0,)
+        hs.resolve(0, sel0, split=True)
+        hs.resolve_tables(0, sel0, torch.empty(0, w.k, dtype=torch.int32, device=dev),
+                          torch.empty(0, dtype=torch.int32, device=dev))
+        hs.fetch_misses(0, 0)
+        out, lse = hs.attend(0, q0, sel0, 0.1)
+        assert out.shape == (0, 16, 512) and lse.shape == (0, 16)
+        hs.attend_noalloc(0, q0, sel0, 0.1)
+        hs.attend_pages(0, q0, sel0, sel0, lens0, 0.1)
+        hs.append(0, torch.empty(0, dtype=torch.int32, device=dev),
+                  torch.empty(0, w.entry_bytes, dtype=torch.uint8, device=dev))
+        assert hs.topk(torch.empty(0, 64, dtype=torch.float32, device=dev), lens0).shape == (0, w.k)
+        torch.cuda.synchronize()
+        after = hs.state(0)
+        for k, v in before.items():
+            assert torch.equal(v, after[k]), f"{k} changed"
+        assert hs.device_error() == 0
+        # and the trace continues as if nothing had happened
+        for t in range(2, 4):
+            p.step(0, x[t], check_state=True)
+    finally:
+        p.close()
