@@ -1077,7 +1077,8 @@ def bench_prefetch(args, torch, hsa, w):
     table update, host-to-device fetch of the misses) and attends over its resolved slots.
     Schedules: serial (resolve and attend layer after layer), layer-wise prefetch (the tables of
     every layer on one side stream, the row copies on another, each attention waiting for its
-    layer's copy) and prefetch with each attention split by residency.  Each is captured as one
+    layer's copy), prefetch with each attention split by residency, and prefetch with the
+    attention of only the last 1 or 3 layers split.  Each is captured as one
     hipGraph of exactly --steps steps, replayed after --warmup untimed steps from an empty
     buffer; the line's value is the fastest schedule whose outputs match the serial run."""
     from hierarchical_kv_cache_hs_amd.decode_step import DecodeSteps
@@ -1111,7 +1112,7 @@ def bench_prefetch(args, torch, hsa, w):
         if W:
             DecodeSteps(hs, sels[:W], qsteps[:W], scale, prefetch=False, attend=attend).replay()
 
-    def timed(prefetch, attend, split_attention=False, split_last=False):
+    def timed(prefetch, attend, split_attention=False, split_last=0):
         warm(attend)
         steps = DecodeSteps(hs, sels[W:], qsteps[W:], scale, prefetch=prefetch, attend=attend,
                             split_attention=split_attention, split_last=split_last)
@@ -1126,25 +1127,34 @@ def bench_prefetch(args, torch, hsa, w):
 
     t_ser, s_ser = timed(False, True)
     t_pre, s_pre = timed(True, True)
-    t_spl, s_spl = timed(True, True, split_attention=True)
-    t_lst, s_lst = timed(True, True, split_last=True)
-    t_res, _ = timed(False, False)
     same = torch.equal(s_ser.out, s_pre.out) and torch.equal(s_ser.miss, s_pre.miss) and \
         torch.equal(s_ser.lse, s_pre.lse)
+    del s_pre
 
     # an attention merged from two parts equals the single launch up to fp32 summation order
     def close(s_x):
         return torch.equal(s_ser.miss, s_x.miss) and torch.equal(s_ser.slots, s_x.slots) and \
             (s_ser.out.float() - s_x.out.float()).abs().max().item() <= 2e-2
 
-    spl_close, lst_close = close(s_spl), close(s_lst)
+    t_spl, s_x = timed(True, True, split_attention=True)
+    spl_close = close(s_x)
+    # the attention of the last m layers split by residency: their resident parts run beside the
+    # last copies (on the compute units the copy kernel leaves free)
+    t_lst, lst_close = {}, {}
+    for m in (1, 3):
+        t_lst[m], s_x = timed(True, True, split_last=m)
+        lst_close[m] = close(s_x)
+    del s_x
+    t_res, _ = timed(False, False)
     log(f"serial {t_ser:.3f} ms, prefetch {t_pre:.3f} ms, prefetch + split attention {t_spl:.3f} ms, "
-        f"prefetch + last layer split {t_lst:.3f} ms, resolve only {t_res:.3f} ms per step")
+        + ", ".join(f"prefetch + last {m} split {t:.3f} ms" for m, t in t_lst.items())
+        + f", resolve only {t_res:.3f} ms per step")
     schedules = [(t_pre, "prefetch")]
     if spl_close:
         schedules.append((t_spl, "prefetch, attention split by residency"))
-    if lst_close:
-        schedules.append((t_lst, "prefetch, last layer's attention split by residency"))
+    for m, t in t_lst.items():
+        if lst_close[m]:
+            schedules.append((t, f"prefetch, attention of the last {m} layer{'s' if m > 1 else ''} split by residency"))
     t_best, best_name = min(schedules)
     misses = s_ser.miss.double()                                  # [K][L][n]
     miss_bytes_step = float(misses.sum()) * w.entry_bytes / K
@@ -1226,8 +1236,8 @@ def bench_prefetch(args, torch, hsa, w):
         "eager_ms_per_step": t_eager,
         "prefetch_equals_serial": bool(same),
         "prefetch_split_attention_within_bf16_tier_of_serial": bool(spl_close),
-        "prefetch_last_layer_split_ms_per_step": t_lst,
-        "prefetch_last_layer_split_within_bf16_tier_of_serial": bool(lst_close),
+        "prefetch_split_last_ms_per_step": {str(m): t for m, t in t_lst.items()},
+        "prefetch_split_last_within_bf16_tier_of_serial": {str(m): bool(c) for m, c in lst_close.items()},
         "overlap_saved_ms_per_step": t_ser - t_best,
         "attention_ms_per_step": t_att,
         "attention_hidden_fraction": (t_ser - t_best) / t_att if t_att > 0 else None,

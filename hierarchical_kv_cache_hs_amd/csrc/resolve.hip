@@ -506,15 +506,20 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
 // Copies the rows of the miss lists written by resolve_kernel<..., LIST>: grid (blocks per
 // request, request groups); a workgroup copies requests y, y + gridDim.y, ... in turn, its
 // threads covering consecutive 16-byte chunks of the request's rows (zero-copy loads from
-// pinned host memory, four in flight per thread; no LDS, at most 64 VGPRs).  128 workgroups
-// in all keep the link busy and leave half the compute units to an attention kernel running
-// beside the copy: an attention workgroup that shares a unit with the copy's long-latency
-// host reads proceeds at the link's pace.  Measured on 256 requests of 656-byte rows with the
-// attention of the resident tokens alongside (the whole step, in us): 64 workgroups 528-530,
-// 128 512-520, 192 520, 256 567 (blocks the attention's placement); LDS reserved to keep the
-// attention off the copy's units made no difference.
+// pinned host memory, four in flight per thread; at most 64 VGPRs).  128 workgroups in all
+// keep the link busy.  Each reserves kFetchLds bytes of LDS it never touches, so that no
+// attention workgroup (a ~126 KiB ring) fits on the same compute unit: an attention workgroup
+// that shares a unit with the copy's long-latency host reads proceeds at the link's pace,
+// while on the other 128 units it runs at its own.  Measured, 128 requests x 8 layers of
+// 656-byte rows, one graph-replayed step: 2.188 ms with no reservation, 2.155 ms with 96 KiB
+// (one copy workgroup per unit; 64 KiB, two per unit: 2.186), and 2.123-2.130 ms once the
+// attention of the last 2-4 layers is also split by residency (which without the reservation
+// is slower than not splitting).  64 workgroups of 512 threads: 2.165-2.19 ms; 64 of 256:
+// 2.21-2.29.  On 256 requests with the attention of the resident tokens alongside the whole
+// step is unchanged (518 against 520 us).
 constexpr int FT = 256;
-constexpr int kFetchGroups = 128;   // workgroups of a launch
+constexpr int kFetchGroups = 128;         // workgroups of a launch
+constexpr int kFetchLds = 96 * 1024;      // LDS reserved per workgroup (unused)
 
 __global__ __launch_bounds__(FT, 8) void fetch_kernel(const int32_t* __restrict__ ml_tok, const int32_t* __restrict__ ml_slot,
                                                       const int32_t* __restrict__ ml_cnt, const uint8_t* __restrict__ host,
@@ -617,6 +622,8 @@ hipError_t launch_width(const ResolveArgs& a, int mode, int n_req, size_t lds, h
 }  // namespace
 
 void prepare_resolve() {
+  (void)hipFuncSetAttribute((const void*)fetch_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kFetchLds);
+  (void)hipGetLastError();
   allow_large_lds<512, 4, 8>();
   allow_large_lds<512, 4, 32>();
   allow_large_lds<512, 16, 8>();
@@ -698,7 +705,7 @@ hipError_t launch_fetch(const Geometry& g, const LayerTables& t, const uint8_t* 
   const int groups = n_req < kFetchGroups ? n_req : kFetchGroups;
   int per_req = (kFetchGroups + n_req - 1) / n_req;
   if (per_req > 16) per_req = 16;
-  hipLaunchKernelGGL(fetch_kernel, dim3(per_req, groups), dim3(FT), 0, s, t.ml_tok, t.ml_slot, t.ml_cnt,
+  hipLaunchKernelGGL(fetch_kernel, dim3(per_req, groups), dim3(FT), kFetchLds, s, t.ml_tok, t.ml_slot, t.ml_cnt,
                      host_layer, t.buf, g.cap, g.host_stride, g.slot_stride, g.req_stride, g.k, g.B,
                      (int32_t)(g.unit_bytes / 16), n_req);
   return hipGetLastError();

@@ -9,7 +9,9 @@ resolves run on their own stream, ahead of the row copies, so the copies follow 
 With ``split_attention=True`` as well, each layer's attention is split by residency: the
 part over the resident tokens waits only for the layer's tables and runs beside the copies,
 the part over the fetched misses waits for the layer's copy, so after the last layer's copy
-only that part remains.
+only that part remains.  ``split_last=m`` splits only the last m layers' attention (the copy
+kernel keeps attention workgroups off its compute units, so a resident part beside a copy
+runs at its own pace on the other units).
 This is valid when the layers share one selection known at the start of the step
 (HiSparse paper abstract: exact layer-wise prefetching for models that share
 selections across layers); the results are the same as the serial order because
@@ -55,15 +57,17 @@ class DecodeSteps:
     """
 
     def __init__(self, hs: HiSparse, sels, qs, scale: float, prefetch: bool, attend: bool = True,
-                 split_attention: bool = False, capture: bool = True, split_last: bool = False):
+                 split_attention: bool = False, capture: bool = True, split_last: int = 0):
         """With ``capture=False`` nothing is captured: :meth:`run_eager` enqueues the same
         launches, in the same stream order, one step at a time (used to time single kernels of
         the schedule with HIP events, which a captured graph does not expose).  With
-        ``split_last`` (layer-wise prefetch only) just the last layer's attention is split by
-        residency: its resident part runs beside the last row copy, so that after the step's
-        last copy only the attention of that layer's misses remains."""
+        ``split_last=m`` (layer-wise prefetch only) the attention of the last m layers is split
+        by residency: their resident parts run beside the last row copies, so that after the
+        step's last copy only the attention of that layer's misses remains."""
         assert len(sels) == len(qs) and len(sels) > 0
         assert not split_attention or (prefetch and attend)
+        split_last = int(split_last)
+        assert 0 <= split_last <= hs.L
         assert not split_last or (prefetch and attend and not split_attention)
         self.hs, self.prefetch, self.attend, self.split_attention = hs, prefetch, attend, split_attention
         self.split_last = split_last
@@ -160,7 +164,7 @@ class DecodeSteps:
             for l in range(hs.L):
                 fetch(l)
         for l in range(hs.L):
-            if self.split_attention or (self.split_last and l == hs.L - 1):
+            if self.split_attention or l >= hs.L - self.split_last:
                 main.wait_event(tables[l])
                 hs.attend_resident(l, q[l], self.slots[l], scale, stream=main)
                 main.wait_event(copied[l])

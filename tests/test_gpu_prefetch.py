@@ -27,7 +27,7 @@ def _queries(w, t, L):
     return torch.from_numpy(q.view(np.int16)).cuda().view(torch.bfloat16)
 
 
-def _run(hs, w, x, qs, prefetch, split_attention=False, split_last=False):
+def _run(hs, w, x, qs, prefetch, split_attention=False, split_last=0):
     rec = []
     for t in range(x.shape[0]):
         sel = torch.from_numpy(x[t]).cuda()
@@ -96,9 +96,9 @@ def test_prefetch_equals_serial_and_oracle(full):
         hs.close()
 
 
-@pytest.mark.parametrize("which", ["every layer", "last layer"])
+@pytest.mark.parametrize("which", ["every layer", "last layer", "last 3 layers"])
 def test_prefetch_with_attention_split_by_residency(which):
-    """Layer-wise prefetch with each layer's attention (or only the last layer's) split into
+    """Layer-wise prefetch with each layer's attention (or only the last layers') split into
     the resident part (beside the copies) and the fetched part: tables, slots and misses equal
     the serial run bitwise; the attention, merged from two parts, matches the serial
     single-launch attention within the bf16 tier and the oracle on sampled requests."""
@@ -114,7 +114,7 @@ def test_prefetch_with_attention_split_by_residency(which):
         hs.reset_requests(0, w.n)
         torch.cuda.synchronize()
         spl, spl_tables = _run(hs, w, x, qs, prefetch=True, split_attention=(which == "every layer"),
-                               split_last=(which == "last layer"))
+                               split_last={"every layer": 0, "last layer": 1, "last 3 layers": 3}[which])
         for t, (a, b) in enumerate(zip(ser, spl)):
             assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), f"step {t}: slots or misses differ"
             err = (a[2].float() - b[2].float()).abs().max().item()
