@@ -41,9 +41,10 @@
 //       PCIe, row-major over the miss list so a wave reads ~1 KiB runs) into the victim
 //       slots.  hs_resolve does this inside the resolving workgroup (each request's copy
 //       starts as soon as its own tables are done).  hs_resolve_tables + hs_fetch_misses
-//       instead write the miss list and copy with a second, LDS-free kernel of 128 small
-//       workgroups: that kernel can share compute units with a running attention kernel,
-//       which a resolving workgroup holding its LDS for the whole PCIe-bound copy cannot.
+//       instead write the miss list and copy with a second kernel of 128 small workgroups,
+//       so that the copy can run beside other work (an attention kernel on the compute units
+//       it leaves free) instead of inside a resolving workgroup that holds its LDS for the
+//       whole PCIe-bound copy.
 // The new order equals the slots sorted by (stamp, slot): untouched slots keep their
 // relative order, and every touched slot now has the largest stamp, so among them the
 // slot index decides.  No sort is needed and a step costs O(k + B + capacity/32).

@@ -178,8 +178,10 @@ hs_status hs_resolve(hs_handle* h, int32_t layer, int32_t n_req, const int32_t* 
  * work (layer-wise prefetch runs the copies of later layers beside the attention of earlier
  * ones).  hs_resolve_tables does everything hs_resolve does except moving rows, and records
  * each request's miss list (token, slot) in the handle; hs_fetch_misses then copies those
- * rows with a kernel that uses no LDS and few registers, so it can share compute units with
- * a running attention kernel.  The pair must run in this order on the caller's streams,
+ * rows with a kernel of 128 small workgroups that keeps the link busy beside other work (each
+ * workgroup reserves 96 KiB of LDS it does not use, so that attention workgroups run on the
+ * other compute units rather than at the pace of the copy's host reads).  The pair must run
+ * in this order on the caller's streams,
  * with no other resolve of the same layer in between; together they equal hs_resolve.
  * hs_fetch_misses returns HS_ERR_INVALID_ARG (and enqueues nothing) unless the layer's last
  * resolve, append or reset call was an hs_resolve_tables of at least n_req requests: other
