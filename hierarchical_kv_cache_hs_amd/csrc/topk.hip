@@ -225,6 +225,7 @@ __global__ __launch_bounds__(TT) void topk_kernel(TopkArgs a) {
   __syncthreads();
   find_digit(hist, NBIN - 1, (uint32_t)k, wtot, &s_digit, &s_above);
   const uint32_t d1 = s_digit;
+  const uint32_t in_d1 = hist[d1];        // keys with top digit d1
   uint32_t need = (uint32_t)k - s_above;  // keys to take among those with top digit d1
 
   // ---- pass B: above d1 -> selection bitmap; equal to d1 -> candidate list.  A thread masks
@@ -266,10 +267,14 @@ __global__ __launch_bounds__(TT) void topk_kernel(TopkArgs a) {
   const uint32_t ncand = s_ncand;
   const bool overflow = ncand > (uint32_t)CMAX;
 
-  // ---- the next 12 bits, then the last 8: over the list, or over the row on overflow
+  // ---- the next 12 bits, then the last 8: over the list, or over the row on overflow.  When
+  // every key of the digit just chosen is taken (its count equals `need`), no tie is left to
+  // resolve and the remaining levels are skipped: the threshold drops to just below that
+  // digit's range and nothing is taken at it.
   uint32_t prefix = d1;
   int fixed = 12;
-  for (int level = 0; level < 2; ++level) {
+  bool all_taken = in_d1 == need;
+  for (int level = 0; level < 2 && !all_taken; ++level) {
     const int bits = level == 0 ? 12 : 8;
     const int shift = 32 - fixed - bits;
     const uint32_t dmask = (1u << bits) - 1u;
@@ -287,12 +292,20 @@ __global__ __launch_bounds__(TT) void topk_kernel(TopkArgs a) {
     }
     __syncthreads();
     find_digit(hist, (int)dmask, need, wtot, &s_digit, &s_above);
+    const uint32_t in_d = hist[s_digit];
     prefix = (prefix << bits) | s_digit;
     need -= s_above;
     fixed += bits;
+    all_taken = in_d == need;  // the same in every thread
     __syncthreads();
   }
-  const uint32_t thr = prefix;  // the k-th largest key; `need` of the keys equal to it are taken
+  // the k-th largest key, `need` of the keys equal to it taken; or, with all_taken, one below
+  // the lowest key of the chosen digit's range (keys > 0: the smallest, -inf's, is 0x007FFFFF)
+  uint32_t thr = prefix;
+  if (all_taken) {
+    thr = (prefix << (32 - fixed)) - 1u;
+    need = 0u;
+  }
 
   // ---- candidates above thr are taken; those equal to it are ties
   if (!overflow) {

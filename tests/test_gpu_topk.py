@@ -154,3 +154,38 @@ def test_topk_feeds_resolver_with_per_layer_selections(graph):
                 assert not np.array_equal(sel_d[0].cpu().numpy(), sel_d[1].cpu().numpy())
     finally:
         hs.close()
+
+
+@pytest.mark.parametrize("k,stride", [(2048, 65536), (64, 4096), (500, 20000)])
+def test_topk_whole_digit_taken(k, stride):
+    """Rows where the k largest keys fill whole digits of the radix select: exactly k positions
+    planted with one large value (the first digit holds exactly the k needed keys), and k
+    positions planted with distinct values that share their top 24 bits, with and without 50
+    lower keys in the same first digit (then the second digit holds exactly the k), over N(0,1)
+    scores.  Bit-exact against the oracle."""
+    say(f"topk whole digits: k {k}, stride {stride}")
+    rng = np.random.default_rng(k + stride)
+    n = 3
+    hs = hsa.HiSparse(k, max(k, 8), (stride + max(k, 8) - 1) // max(k, 8), n, 1, hsa.LAYOUT_BF16)
+    try:
+        s = rng.standard_normal((n, stride)).astype(np.float32)
+        lens = np.array([stride, stride - 5, stride // 2])
+        for r in range(n):
+            pos = rng.choice(int(lens[r]), size=k, replace=False)
+            if r == 0:
+                s[r, pos] = np.float32(1000.0)
+            else:
+                # distinct floats with equal top 24 key bits: 1000.0 plus small mantissa steps
+                base = np.float32(1000.0).view(np.uint32)
+                s[r, pos] = (base + np.arange(k, dtype=np.uint32) % 200).view(np.float32)
+            if r == 2:
+                # and 50 keys of 999.0 (the same top 12 key bits, lower next 12): the first digit
+                # then holds more than k keys and the second one exactly k
+                rest = np.setdiff1d(np.arange(int(lens[r])), pos)
+                s[r, rng.choice(rest, size=50, replace=False)] = np.float32(999.0)
+        got = _run(hs, s, lens)
+        want = topk_oracle(s, lens, k)
+        assert (got == want).all(), "differs from the oracle"
+        assert hs.device_error() == 0
+    finally:
+        hs.close()
