@@ -1101,6 +1101,25 @@ def bench_pages(args, torch, hsa, w):
     return line, trace
 
 
+def fill_history(torch, hs, w):
+    """Every history row of a handle from the seeded generator: whole rows into the host pool,
+    or with the resident-tail layout the first 640 bytes of each row there and the last 16
+    into the device tail plane."""
+    from synth import kv as skv
+    for l in range(hs.L):
+        tails = hs.tail_plane(l) if hs.tail_bytes else None
+        for r in range(hs.n):
+            ptr, cap, stride = hs.host_kv_ptr(l, r)
+            if tails is None:
+                skv.fill_rows(w.seed, r, l, 0, cap, w.layout, ptr, stride)
+            else:
+                stage = np.empty((cap, hs.tail_bytes), dtype=np.uint8)
+                skv.fill_rows_split(w.seed, r, l, 0, cap, w.layout, ptr, stride, stride, stage.ctypes.data,
+                                    hs.tail_bytes)
+                tails[r].copy_(torch.from_numpy(stage))
+    torch.cuda.synchronize()
+
+
 def bench_prefetch(args, torch, hsa, w):
     """Whole decode steps over 8 layers sharing one selection (128 requests, ctx 65536, fp8 rows,
     k 2048, B 4096): every layer resolves the step's selection (hit detection, LRU replacement,
@@ -1110,7 +1129,8 @@ def bench_prefetch(args, torch, hsa, w):
     layer's copy), prefetch with each attention split by residency, and prefetch with the
     attention of only the last 1 or 3 layers split.  Each is captured as one
     hipGraph of exactly --steps steps, replayed after --warmup untimed steps from an empty
-    buffer; the line's value is the fastest schedule whose outputs match the serial run."""
+    buffer; the line's value is the fastest schedule whose outputs match the serial run.  The
+    host pool keeps whole 656-byte rows."""
     from hierarchical_kv_cache_hs_amd.decode_step import DecodeSteps
     from synth import kv as skv
     from synth import trace as tr
@@ -1124,10 +1144,7 @@ def bench_prefetch(args, torch, hsa, w):
     d_trace = torch.from_numpy(trace).cuda()
     hs = hsa.HiSparse(w.k, w.B, w.ratio, w.n, w.layers, w.layout, 16, 0)
     t0 = time.perf_counter()
-    for l in range(w.layers):
-        for r in range(w.n):
-            ptr, cap, stride = hs.host_kv_ptr(l, r)
-            skv.fill_rows(w.seed, r, l, 0, cap, w.layout, ptr, stride)
+    fill_history(torch, hs, w)
     log(f"host pool {hsa.host_bytes(hs.cfg) / 2**30:.1f} GiB filled in {time.perf_counter() - t0:.1f}s")
     # every step and layer has its own queries
     t0 = time.perf_counter()
@@ -1187,7 +1204,10 @@ def bench_prefetch(args, torch, hsa, w):
             schedules.append((t, f"prefetch, attention of the last {m} layer{'s' if m > 1 else ''} split by residency"))
     t_best, best_name = min(schedules)
     misses = s_ser.miss.double()                                  # [K][L][n]
-    miss_bytes_step = float(misses.sum()) * w.entry_bytes / K
+    # bytes each miss moves over the host link: the whole row, or its host part (the rest comes
+    # from the device tail plane)
+    link_bytes = w.entry_bytes - hs.tail_bytes
+    miss_bytes_step = float(misses.sum()) * link_bytes / K
 
     # The row-copy kernel (fetch_kernel) timed on its own stream: the same steps again, enqueued
     # without a graph in the prefetch schedule (a captured graph exposes no per-kernel time on
@@ -1250,11 +1270,13 @@ def bench_prefetch(args, torch, hsa, w):
         "config": {"workload": w.description, "global_batch": w.n, "layers": w.layers, "seq_len": w.ctx,
                    "top_k": w.k, "device_buffer_size": w.B, "host_to_device_ratio": w.ratio,
                    "entry_bytes": w.entry_bytes, "kv_rows": "fp8 e4m3 latent + fp32 scales + bf16 rope",
+                   "host_rows": "whole 656-B rows in the host pool",
                    "graph": True, "steps_timed": f"{W}..{W + K - 1}", "queries": "distinct per step and layer",
                    "schedule": best_name},
         "selected_tokens_per_s": w.n * w.layers * w.k / (t_best / 1e3),
         "attended_tokens_per_s": w.n * w.layers * w.k / (t_best / 1e3),
         "misses_per_selection": float(misses.mean()),
+        "link_bytes_per_miss": link_bytes,
         "miss_GB_per_step": miss_bytes_step / 1e9,
         # whole-step miss rate: the step's miss bytes over its time
         "miss_fetch_GBps": step_GBps,

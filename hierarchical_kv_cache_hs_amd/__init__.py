@@ -32,6 +32,7 @@ LAYOUT_FP8 = 1       # HS_KV_FP8_MLA_656
 ENTRY_BYTES = {LAYOUT_BF16: 1152, LAYOUT_FP8: 656}
 FLAG_NO_IO = 0x1
 FLAG_ATTN_OUT_F32 = 0x2   # attention output in fp32 (P carried in fp32)
+FLAG_RESIDENT_TAIL = 0x4  # 656-byte rows: host keeps 640 bytes per row, the last 16 stay on the device
 EVICT_LRU, EVICT_FIFO, EVICT_RANDOM = 0, 1, 2   # hs_eviction
 DEVERR_TOKEN_RANGE = 0x1
 DEVERR_DUPLICATE = 0x2
@@ -60,7 +61,7 @@ class StateView(ctypes.Structure):
                 ("lru_order", ctypes.c_void_p), ("step", ctypes.c_void_p), ("kv_buffer", ctypes.c_void_p),
                 ("capacity", ctypes.c_int64), ("slot_stride", ctypes.c_int64), ("entry_bytes", ctypes.c_int64),
                 ("request_stride", ctypes.c_int64), ("page_tokens", ctypes.c_int64),
-                ("fresh_slots", ctypes.c_void_p)]
+                ("fresh_slots", ctypes.c_void_p), ("tail_plane", ctypes.c_void_p), ("tail_bytes", ctypes.c_int64)]
 
 
 class HSError(RuntimeError):
@@ -182,6 +183,7 @@ class HiSparse:
         self.layout, self.heads = layout, num_heads
         self.out_dtype = torch.float32 if flags & FLAG_ATTN_OUT_F32 else torch.bfloat16
         self.entry_bytes = ENTRY_BYTES[layout]
+        self.tail_bytes = 16 if flags & FLAG_RESIDENT_TAIL else 0   # row bytes kept in the device tail plane
         self.capacity = host_to_device_ratio * device_buffer_size     # page-table entries
         self.page_tokens = page_tokens
 
@@ -210,13 +212,19 @@ class HiSparse:
 
     # -- host pool -----------------------------------------------------------------------------
     def host_kv(self, layer: int, request: int) -> np.ndarray:
-        """[capacity * page_tokens][entry_bytes] uint8 view of the pinned host rows (one per token)."""
+        """[capacity * page_tokens][entry_bytes] uint8 view of the pinned host rows (one per token);
+        with FLAG_RESIDENT_TAIL [capacity][entry_bytes - 16], the rest being in :meth:`tail_plane`."""
         ptr = ctypes.c_void_p()
         cap = ctypes.c_int64()
         stride = ctypes.c_int64()
         _check(lib().hs_host_kv(self._h, layer, request, ctypes.byref(ptr), ctypes.byref(cap), ctypes.byref(stride)))
         buf = (ctypes.c_uint8 * (cap.value * stride.value)).from_address(ptr.value)
         return np.frombuffer(buf, dtype=np.uint8).reshape(cap.value, stride.value)[:, : self.entry_bytes]
+
+    def tail_plane(self, layer: int) -> torch.Tensor | None:
+        """FLAG_RESIDENT_TAIL: [max_requests][capacity][16] uint8 device view of the last 16 bytes
+        of every history row of the layer (None without the flag)."""
+        return self.state(layer)["tail_plane"]
 
     def host_kv_ptr(self, layer: int, request: int) -> tuple[int, int, int]:
         ptr = ctypes.c_void_p()
@@ -417,6 +425,8 @@ class HiSparse:
             "zero_row": rows[:, B],
             "entry_bytes": v.entry_bytes,
             "page_tokens": v.page_tokens,
+            "tail_plane": view(v.tail_plane, n * cap * v.tail_bytes, torch.uint8, (n, cap, v.tail_bytes))
+            if v.tail_plane else None,
         }
 
     def reset_requests(self, first: int, count: int, stream=None):

@@ -42,10 +42,20 @@ struct AppendArgs {
   uint32_t* fresh;        // [n][B/32] slots appended since the last resolve
   uint8_t* buf;
   uint8_t* host;          // the layer's host pool, device-mapped address
+  uint8_t* tail;          // the layer's tail plane (HS_FLAG_RESIDENT_TAIL), else null
   int32_t* err;
   int64_t cap, host_stride, slot_stride, req_stride;
   int32_t B, chunks, io, fifo;
+  int32_t body_chunks;    // chunks of a row kept in the host pool; the rest go to the tail plane
 };
+
+// Writes chunk c of token p's row into request r's history: the host pool, or for the chunks
+// past the host part of a row the device-resident tail plane.
+__device__ __forceinline__ void store_history(const AppendArgs& a, int r, int32_t p, int c, v4i v) {
+  const int64_t row = (int64_t)r * a.cap + p;
+  if (c < a.body_chunks) ((v4i*)(a.host + row * a.host_stride))[c] = v;
+  else ((v4i*)(a.tail + row * (int64_t)(a.chunks - a.body_chunks) * 16))[c - a.body_chunks] = v;
+}
 
 __global__ __launch_bounds__(AT) void append_kernel(AppendArgs a) {
   extern __shared__ int32_t ord_lds[];  // [B]
@@ -113,7 +123,7 @@ __global__ __launch_bounds__(AT) void append_kernel(AppendArgs a) {
     if (tid == 0 && a.slot_out) a.slot_out[r] = j;
     if (a.io && tid < a.chunks) {
       ((v4i*)(a.buf + (int64_t)r * a.req_stride + (int64_t)j * a.slot_stride))[tid] = rowv;
-      ((v4i*)(a.host + ((int64_t)r * a.cap + p) * a.host_stride))[tid] = rowv;
+      store_history(a, r, p, tid, rowv);
     }
     return;
   }
@@ -154,17 +164,20 @@ __global__ __launch_bounds__(AT) void append_kernel(AppendArgs a) {
   }
   if (a.io && tid < a.chunks) {
     ((v4i*)(a.buf + (int64_t)r * a.req_stride + (int64_t)j * a.slot_stride))[tid] = rowv;
-    ((v4i*)(a.host + ((int64_t)r * a.cap + p) * a.host_stride))[tid] = rowv;
+    store_history(a, r, p, tid, rowv);
   }
 }
 
-// Prefill offload of rows that are not contiguous (a padded row stride): a grid of small
-// workgroups copies 16-byte chunks from the device rows to the pinned history with
-// zero-copy stores, four chunks in flight per thread.
+// Prefill offload of rows that are not contiguous (a padded row stride) or that are split
+// between the pinned history and the tail plane: a grid of small workgroups copies 16-byte
+// chunks from the device rows, the first body_chunks of each row to the pinned history with
+// zero-copy stores (rows packed), the rest to the tail plane (packed), four chunks in flight
+// per thread.
 constexpr int OT = 256;
 
 __global__ __launch_bounds__(OT) void offload_kernel(const uint8_t* __restrict__ src, int64_t src_stride,
-                                                     uint8_t* __restrict__ dst, int64_t count, int32_t chunks) {
+                                                     uint8_t* __restrict__ dst, int64_t count, int32_t chunks,
+                                                     int32_t body_chunks, uint8_t* __restrict__ tail) {
   const int64_t total = count * chunks;
   const int64_t step = (int64_t)gridDim.x * OT;
   constexpr int U = 4;
@@ -181,7 +194,12 @@ __global__ __launch_bounds__(OT) void offload_kernel(const uint8_t* __restrict__
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t idx = base + u * step;
-      if (idx < total) ((v4i*)dst)[idx] = v[u];
+      if (idx < total) {
+        const int64_t row = idx / chunks;
+        const int c = (int)(idx - row * chunks);
+        if (c < body_chunks) ((v4i*)dst)[row * body_chunks + c] = v[u];
+        else ((v4i*)tail)[row * (chunks - body_chunks) + (c - body_chunks)] = v[u];
+      }
     }
   }
 }
@@ -232,12 +250,13 @@ hipError_t launch_append_pages(const Geometry& g, const LayerTables& t, uint8_t*
 }
 
 hipError_t launch_offload(const void* src, int64_t src_stride, uint8_t* dst_mapped, int64_t count, int64_t entry_bytes,
-                          hipStream_t s) {
+                          uint8_t* tail_dst, int64_t tail_bytes, hipStream_t s) {
   const int32_t chunks = (int32_t)(entry_bytes / 16);
+  const int32_t body_chunks = (int32_t)((entry_bytes - tail_bytes) / 16);
   const int64_t total = count * chunks;
   const int64_t blocks = (total + OT * 4 - 1) / (OT * 4);
   hipLaunchKernelGGL(offload_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(OT), 0, s,
-                     (const uint8_t*)src, src_stride, dst_mapped, count, chunks);
+                     (const uint8_t*)src, src_stride, dst_mapped, count, chunks, body_chunks, tail_dst);
   return hipGetLastError();
 }
 
@@ -263,6 +282,7 @@ hipError_t launch_append(const Geometry& g, const LayerTables& t, uint8_t* host_
   a.fresh = t.fresh;
   a.buf = t.buf;
   a.host = host_layer;
+  a.tail = t.tail;
   a.err = err;
   a.cap = g.cap;
   a.host_stride = g.host_stride;
@@ -270,6 +290,7 @@ hipError_t launch_append(const Geometry& g, const LayerTables& t, uint8_t* host_
   a.req_stride = g.req_stride;
   a.B = g.B;
   a.chunks = (int32_t)(g.entry_bytes / 16);
+  a.body_chunks = (int32_t)((g.entry_bytes - g.tail_bytes) / 16);
   a.io = (g.flags & HS_FLAG_NO_IO) ? 0 : 1;
   a.fifo = g.policy == HS_EVICT_FIFO ? 1 : 0;
   hipLaunchKernelGGL(append_kernel, dim3(n_req), dim3(AT), (size_t)g.B * sizeof(int32_t), s, a);

@@ -13,7 +13,9 @@
 //   ml_*  [L][n][k], [L][n]    per-request miss lists (token, slot) and counts for the fetch kernel
 //   buf   [L][n][B + 1][E]     KV rows of the slots, packed; row B stays zero (attention reads it
 //                              for padded selection entries)
-// Host pool (pinned, mapped): [L][n][cap][entry bytes].
+//   tail  [L][n][cap][16]      HS_FLAG_RESIDENT_TAIL: the last 16 bytes of every history row
+// Host pool (pinned, mapped): [L][n][cap][host stride]: whole rows, or with
+// HS_FLAG_RESIDENT_TAIL their first 640 bytes (five whole 128-byte lines per row).
 
 #include <cstdio>
 #include <cstdlib>
@@ -44,6 +46,7 @@ struct hs_handle {
   int32_t* ml_slot = nullptr;
   int32_t* ml_cnt = nullptr;
   uint8_t* buf = nullptr;
+  uint8_t* tail = nullptr;  // HS_FLAG_RESIDENT_TAIL: row tails [L][n][cap][tail_bytes]
   size_t part_floats = 0;  // per request
   // per layer: requests whose miss lists the last resolve-side call left in the handle (a
   // list-only resolve); 0 after any other resolve, append or reset.  The copy and the attention
@@ -100,7 +103,7 @@ bool add_ok(size_t a, size_t b, size_t* out) {
 }
 
 struct Layout {
-  size_t err, pt, rm, st, ord, step, fresh, part, ml_tok, ml_slot, ml_cnt, buf, total;
+  size_t err, pt, rm, st, ord, step, fresh, part, ml_tok, ml_slot, ml_cnt, buf, tail, total;
   size_t host_total;
   size_t part_floats;
 };
@@ -117,12 +120,17 @@ hs_status plan(const hs_config* cfg, hs::Geometry* g, Layout* lay) {
   if (cfg->layout != HS_KV_BF16_576 && cfg->layout != HS_KV_FP8_MLA_656)
     return fail(HS_ERR_INVALID_ARG, "unknown KV layout");
   if (cfg->num_heads < 0 || cfg->num_heads > 16) return fail(HS_ERR_INVALID_ARG, "num_heads must lie in [0, 16]");
-  if (cfg->flags & ~(HS_FLAG_NO_IO | HS_FLAG_ATTN_OUT_F32)) return fail(HS_ERR_INVALID_ARG, "unknown flag bits");
+  if (cfg->flags & ~(HS_FLAG_NO_IO | HS_FLAG_ATTN_OUT_F32 | HS_FLAG_RESIDENT_TAIL))
+    return fail(HS_ERR_INVALID_ARG, "unknown flag bits");
   if (cfg->eviction != HS_EVICT_LRU && cfg->eviction != HS_EVICT_FIFO && cfg->eviction != HS_EVICT_RANDOM)
     return fail(HS_ERR_INVALID_ARG, "unknown eviction policy");
   const int32_t P = cfg->page_tokens == 0 ? 1 : cfg->page_tokens;
   if (P < 1 || P > 256 || (P & (P - 1)))
     return fail(HS_ERR_INVALID_ARG, "page_tokens must be 0, 1 or a power of two <= 256");
+  const bool tail = (cfg->flags & HS_FLAG_RESIDENT_TAIL) != 0;
+  if (tail && (cfg->layout != HS_KV_FP8_MLA_656 || P != 1 || (cfg->flags & HS_FLAG_NO_IO)))
+    return fail(HS_ERR_INVALID_ARG,
+                "HS_FLAG_RESIDENT_TAIL needs token-granular 656-byte rows and a host pool (no HS_FLAG_NO_IO)");
   if (cfg->num_heads > 0 && (int64_t)cfg->top_k * P > 65536)
     return fail(HS_ERR_UNSUPPORTED, "attention over more than 65536 tokens (top_k * page_tokens)");
   if (cfg->top_k > hs::kMaxTopK) return fail(HS_ERR_UNSUPPORTED, "top_k above 8192");
@@ -144,7 +152,10 @@ hs_status plan(const hs_config* cfg, hs::Geometry* g, Layout* lay) {
   g->cap = cap;
   g->entry_bytes = cfg->layout == HS_KV_BF16_576 ? 1152 : 656;
   g->unit_bytes = (int64_t)P * g->entry_bytes;
-  g->host_stride = g->unit_bytes;
+  // a 656-byte row spans six 128-byte lines wherever it starts; its first 640 bytes at a
+  // 640-byte stride span five
+  g->tail_bytes = tail ? g->entry_bytes % 128 : 0;
+  g->host_stride = g->unit_bytes - g->tail_bytes;
   g->slot_stride = g->unit_bytes;  // packed: scattered 656-byte rows gather faster packed than padded to 768
   g->req_stride = ((int64_t)g->B + 1) * g->slot_stride;
   // the attention kernel addresses a request's rows with 32-bit offsets
@@ -171,6 +182,8 @@ hs_status plan(const hs_config* cfg, hs::Geometry* g, Layout* lay) {
   ok = ok && mul_ok(LN, (size_t)g->k, &t) && mul_ok(t, 4, &sz) && take(sz, &lay->ml_tok) && take(sz, &lay->ml_slot);
   ok = ok && take(LN * 4, &lay->ml_cnt);
   ok = ok && mul_ok(LN, (size_t)g->req_stride, &sz) && take(sz, &lay->buf);
+  lay->tail = 0;
+  if (tail) ok = ok && mul_ok(LN, (size_t)cap, &t) && mul_ok(t, (size_t)g->tail_bytes, &sz) && take(sz, &lay->tail);
   lay->total = off;
   // no rows ever move in no-IO mode, so no host pool is allocated
   lay->host_total = 0;
@@ -194,6 +207,7 @@ hs::LayerTables layer_tables(const hs_handle* h, int32_t layer) {
   t.ml_slot = h->ml_slot + base * (size_t)g.k;
   t.ml_cnt = h->ml_cnt + base;
   t.buf = h->buf + base * (size_t)g.req_stride;
+  t.tail = h->tail ? h->tail + base * (size_t)g.cap * (size_t)g.tail_bytes : nullptr;
   return t;
 }
 
@@ -345,6 +359,7 @@ hs_status hs_create(const hs_config* cfg, hs_handle** out) {
   h->ml_slot = (int32_t*)(b + lay.ml_slot);
   h->ml_cnt = (int32_t*)(b + lay.ml_cnt);
   h->buf = b + lay.buf;
+  h->tail = g.tail_bytes ? b + lay.tail : nullptr;
 
   hs::prepare_resolve();
   hs::prepare_attend();
@@ -554,7 +569,7 @@ hs_status hs_host_kv(hs_handle* h, int32_t layer, int32_t request, void** ptr, i
   const size_t units = ((size_t)layer * h->g.n + (size_t)request) * (size_t)h->g.cap;
   *ptr = h->host_pool + units * (size_t)h->g.host_stride;
   if (capacity) *capacity = h->g.cap * h->g.P;   // token rows
-  if (row_stride) *row_stride = h->g.entry_bytes;
+  if (row_stride) *row_stride = h->g.host_stride / h->g.P;
   return HS_OK;
 }
 
@@ -574,6 +589,8 @@ hs_status hs_device_state(hs_handle* h, int32_t layer, hs_state_view* v) {
   v->request_stride = h->g.req_stride;
   v->page_tokens = h->g.P;
   v->fresh_slots = t.fresh;
+  v->tail_plane = t.tail;
+  v->tail_bytes = h->g.tail_bytes;
   return HS_OK;
 }
 
@@ -613,18 +630,28 @@ hs_status hs_offload(hs_handle* h, int32_t layer, int32_t request, int64_t first
   if (!d_rows) return fail(HS_ERR_INVALID_ARG, "row pointer is NULL");
   if (row_stride < h->g.entry_bytes) return fail(HS_ERR_INVALID_ARG, "row_stride below the entry size");
   const size_t E = (size_t)h->g.entry_bytes;
-  const size_t off = (((size_t)layer * h->g.n + (size_t)request) * (size_t)cap_tokens + (size_t)first) * E;
+  const size_t T = (size_t)h->g.tail_bytes;  // bytes of each row kept in the device tail plane
+  const size_t HE = E - T;                    // bytes of each row in the host pool
+  const size_t row0 = ((size_t)layer * h->g.n + (size_t)request) * (size_t)cap_tokens + (size_t)first;
+  const size_t off = row0 * HE;
+  uint8_t* tail_dst = T ? h->tail + row0 * T : nullptr;
   // Contiguous rows go as one flat copy (the DMA engine's fast path, no compute units);
-  // 16-byte-aligned padded rows through a zero-copy store kernel (a 2-D copy of small rows
-  // runs at about a third of the link); anything else as a 2-D copy.
+  // 16-byte-aligned padded rows, and rows split between the host pool and the tail plane,
+  // through a zero-copy store kernel (a 2-D copy of small rows runs at about a third of the
+  // link); anything else as 2-D copies.
   hipError_t e;
-  if ((size_t)row_stride == E)
+  if ((size_t)row_stride == E && T == 0)
     e = hipMemcpyAsync(h->host_pool + off, d_rows, E * (size_t)count, hipMemcpyDeviceToHost, (hipStream_t)stream);
   else if (row_stride % 16 == 0 && ((uintptr_t)d_rows) % 16 == 0)
-    e = hs::launch_offload(d_rows, row_stride, h->host_pool_dev + off, count, h->g.entry_bytes, (hipStream_t)stream);
-  else
-    e = hipMemcpy2DAsync(h->host_pool + off, E, d_rows, (size_t)row_stride, E, (size_t)count, hipMemcpyDeviceToHost,
+    e = hs::launch_offload(d_rows, row_stride, h->host_pool_dev + off, count, h->g.entry_bytes, tail_dst,
+                           h->g.tail_bytes, (hipStream_t)stream);
+  else {
+    e = hipMemcpy2DAsync(h->host_pool + off, HE, d_rows, (size_t)row_stride, HE, (size_t)count, hipMemcpyDeviceToHost,
                          (hipStream_t)stream);
+    if (e == hipSuccess && T)
+      e = hipMemcpy2DAsync(tail_dst, T, (const uint8_t*)d_rows + HE, (size_t)row_stride, T, (size_t)count,
+                           hipMemcpyDeviceToDevice, (hipStream_t)stream);
+  }
   if (e != hipSuccess) return fail_hip(e, "offload copy");
   note_work(h, stream);
   return HS_OK;

@@ -26,6 +26,7 @@ struct LayerTables {
   uint8_t* buf;    // [n][req_stride]: B rows of slot_stride bytes, then a zero row (attention padding)
   float* part;     // attention split partials (see attend.hip)
   uint32_t* fresh; // [n][B/32] bits of slots appended since the last resolve (their stamp is its step)
+  uint8_t* tail;   // [n][cap][tail_bytes] device-resident row tails (HS_FLAG_RESIDENT_TAIL), else null
   int32_t* ml_tok;   // miss lists [n][k]
   int32_t* ml_slot;  // [n][k]
   int32_t* ml_cnt;   // [n]
@@ -38,7 +39,8 @@ struct Geometry {
   int64_t cap;
   int64_t entry_bytes;  // bytes of one token's row
   int64_t unit_bytes;   // bytes of one cached unit: P rows
-  int64_t host_stride;  // bytes between units in the host history (= unit_bytes)
+  int64_t host_stride;  // bytes between units in the host history (unit_bytes - tail_bytes)
+  int64_t tail_bytes;   // HS_FLAG_RESIDENT_TAIL: last bytes of each row kept on the device (16), else 0
   int64_t slot_stride;  // bytes between slots (= unit_bytes)
   int64_t req_stride;   // bytes per request in the slot buffer: B slot rows, then one row of zeros
   uint32_t flags;
@@ -78,10 +80,11 @@ hipError_t launch_append_pages(const Geometry& g, const LayerTables& t, uint8_t*
                                const int32_t* pos, const void* rows, int64_t row_stride, int32_t* slot_out,
                                int32_t* err, hipStream_t s);
 
-// Prefill offload of 16-byte-aligned rows with a padded stride into the pinned history
-// (dst_mapped: device-mapped address of the first destination row, rows packed).
+// Prefill offload of 16-byte-aligned rows into the pinned history (dst_mapped: device-mapped
+// address of the first destination row, rows of entry_bytes - tail_bytes packed); the last
+// tail_bytes of each row go to tail_dst (device, packed), when tail_bytes > 0.
 hipError_t launch_offload(const void* src, int64_t src_stride, uint8_t* dst_mapped, int64_t count, int64_t entry_bytes,
-                          hipStream_t s);
+                          uint8_t* tail_dst, int64_t tail_bytes, hipStream_t s);
 
 // Once per process, before the first top-k launch.
 void prepare_topk();

@@ -72,6 +72,7 @@ struct ResolveArgs {
   int32_t* step;
   uint32_t* fresh;  // [n][HB] slots appended since the last resolve
   const uint8_t* host;
+  const uint8_t* tail;  // device-resident row tails [n][cap][16 * (chunks - body_chunks)], or null
   uint8_t* buf;
   int32_t* err;
   int32_t* ml_tok;   // [n][k] missing tokens, ascending (mode LIST)
@@ -85,6 +86,7 @@ struct ResolveArgs {
   int32_t k;
   int32_t B;
   int32_t chunks;  // 16-byte chunks per row
+  int32_t body_chunks;  // chunks of a row read from the host pool (the rest: tail plane)
   int32_t policy;  // hs_eviction
   int32_t layer, nlayers;
   int32_t early_reads;  // FUSED: start the host reads in P2 (see launch_resolve)
@@ -119,6 +121,15 @@ __device__ uint32_t random_rank(uint64_t key, uint32_t n, uint32_t x) {
     x = (hi << h) | lo;
   } while (x >= n);
   return x;
+}
+
+// Chunk c (16 bytes) of row s of one request's history: the host part of a row from pinned
+// host memory (zero-copy, non-temporal), the chunks past it from the device-resident tail
+// plane.  Without a tail plane body_chunks covers the whole row.
+__device__ __forceinline__ v4i row_chunk(const uint8_t* host, int64_t host_stride, const uint8_t* tail,
+                                         int body_chunks, int chunks, int64_t s, int c) {
+  if (c < body_chunks) return __builtin_nontemporal_load((const v4i*)(host + s * host_stride) + c);
+  return ((const v4i*)(tail + s * (int64_t)(chunks - body_chunks) * 16))[c - body_chunks];
 }
 
 // A workgroup barrier that waits for this wave's LDS operations only.  From P2 on no thread
@@ -304,6 +315,8 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
   const int C = a.chunks;
   const int total = m * C;
   const uint8_t* host = a.host + (int64_t)r * cap * a.host_stride;
+  const uint8_t* tail = a.tail + (int64_t)r * cap * (int64_t)(C - a.body_chunks) * 16;
+  const int BC = a.body_chunks;
   int qv[KPT];
   v4i v0[U];
   if (early) {
@@ -325,7 +338,7 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
       if (idx < total) {
         const int q = idx / C;
         const int c = idx - q * C;
-        v0[u] = __builtin_nontemporal_load((const v4i*)(host + (int64_t)misstok[q] * a.host_stride) + c);
+        v0[u] = row_chunk(host, a.host_stride, tail, BC, C, (int64_t)misstok[q], c);
       }
     }
   }
@@ -489,7 +502,7 @@ __global__ __launch_bounds__(NT) void resolve_kernel(ResolveArgs a) {
         const int q = idx / C;
         const int c = idx - q * C;
         const int32_t s = (int32_t)misstok[q];
-        if (s >= 0) v[u] = __builtin_nontemporal_load((const v4i*)(host + (int64_t)s * a.host_stride) + c);
+        if (s >= 0) v[u] = row_chunk(host, a.host_stride, tail, BC, C, (int64_t)s, c);
       }
     }
 #pragma unroll
@@ -524,9 +537,10 @@ constexpr int kFetchLds = 96 * 1024;      // LDS reserved per workgroup (unused)
 
 __global__ __launch_bounds__(FT, 8) void fetch_kernel(const int32_t* __restrict__ ml_tok, const int32_t* __restrict__ ml_slot,
                                                       const int32_t* __restrict__ ml_cnt, const uint8_t* __restrict__ host,
-                                                      uint8_t* __restrict__ buf, int64_t cap, int64_t host_stride,
-                                                      int64_t slot_stride, int64_t req_stride, int32_t k, int32_t B,
-                                                      int32_t chunks, int32_t n_req) {
+                                                      const uint8_t* __restrict__ tail, uint8_t* __restrict__ buf,
+                                                      int64_t cap, int64_t host_stride, int64_t slot_stride,
+                                                      int64_t req_stride, int32_t k, int32_t B, int32_t chunks,
+                                                      int32_t body_chunks, int32_t n_req) {
   constexpr int U = 4;
   const int step = gridDim.x * FT;
   for (int r = blockIdx.y; r < n_req; r += gridDim.y) {
@@ -535,6 +549,7 @@ __global__ __launch_bounds__(FT, 8) void fetch_kernel(const int32_t* __restrict_
     const int32_t* tok = ml_tok + (int64_t)r * k;
     const int32_t* slot = ml_slot + (int64_t)r * k;
     const uint8_t* hrow = host + (int64_t)r * cap * host_stride;
+    const uint8_t* trow = tail + (int64_t)r * cap * (int64_t)(chunks - body_chunks) * 16;
     uint8_t* drow = buf + (int64_t)r * req_stride;
     for (int base = blockIdx.x * FT + threadIdx.x; base < total; base += step * U) {
       v4i v[U];
@@ -548,7 +563,7 @@ __global__ __launch_bounds__(FT, 8) void fetch_kernel(const int32_t* __restrict_
           const int c = idx - q * chunks;
           const int32_t s = tok[q], j = slot[q];
           if (s >= 0 && (int64_t)s < cap && j >= 0 && j < B) {
-            v[u] = __builtin_nontemporal_load((const v4i*)(hrow + (int64_t)s * host_stride) + c);
+            v[u] = row_chunk(hrow, host_stride, trow, body_chunks, chunks, (int64_t)s, c);
             dst[u] = j * chunks + c;
           }
         }
@@ -662,6 +677,7 @@ hipError_t launch_resolve(const Geometry& g, const LayerTables& t, int32_t layer
   a.step = t.step;
   a.fresh = t.fresh;
   a.host = host_layer;
+  a.tail = t.tail;
   a.buf = t.buf;
   a.err = err;
   a.cap = g.cap;
@@ -675,6 +691,7 @@ hipError_t launch_resolve(const Geometry& g, const LayerTables& t, int32_t layer
   a.k = g.k;
   a.B = g.B;
   a.chunks = (int32_t)(g.unit_bytes / 16);
+  a.body_chunks = (int32_t)(g.host_stride / 16);
   a.ml_tok = t.ml_tok;
   a.ml_slot = t.ml_slot;
   a.ml_cnt = t.ml_cnt;
@@ -707,8 +724,8 @@ hipError_t launch_fetch(const Geometry& g, const LayerTables& t, const uint8_t* 
   int per_req = (kFetchGroups + n_req - 1) / n_req;
   if (per_req > 16) per_req = 16;
   hipLaunchKernelGGL(fetch_kernel, dim3(per_req, groups), dim3(FT), kFetchLds, s, t.ml_tok, t.ml_slot, t.ml_cnt,
-                     host_layer, t.buf, g.cap, g.host_stride, g.slot_stride, g.req_stride, g.k, g.B,
-                     (int32_t)(g.unit_bytes / 16), n_req);
+                     host_layer, t.tail, t.buf, g.cap, g.host_stride, g.slot_stride, g.req_stride, g.k, g.B,
+                     (int32_t)(g.unit_bytes / 16), (int32_t)(g.host_stride / 16), n_req);
   return hipGetLastError();
 }
 

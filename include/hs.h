@@ -70,6 +70,23 @@ typedef enum hs_kv_layout {
 #define HS_FLAG_ATTN_OUT_F32 0x2u /* hs_attend / hs_attend_pages write fp32 output, with P
                                      carried in fp32 through the P V product (the 1e-5 tier)
                                      instead of rounded to bf16 */
+#define HS_FLAG_RESIDENT_TAIL 0x4u /* 656-byte token rows only (HS_KV_FP8_MLA_656, page_tokens
+                                      0 or 1, not with HS_FLAG_NO_IO).  The host pool keeps the
+                                      first 640 bytes of each row, at a 640-byte stride, so a row
+                                      read over the host link covers five whole 128-byte lines
+                                      instead of six; the last 16 bytes of every row (the last 8
+                                      rope values) stay in a device-resident tail plane
+                                      (hs_state_view.tail_plane, 16 bytes per token of history,
+                                      [max_requests][capacity] per layer, part of
+                                      hs_device_bytes).  Misses are assembled from both into the
+                                      slot, so slot rows, tables and attention are those of the
+                                      packed layout; hs_host_kv reports the 640-byte stride, and
+                                      hs_append / hs_offload write both parts.  Callers that
+                                      write history rows themselves write the tails into the
+                                      plane.  Cost: 16 bytes of HBM per token of history (2.4 %
+                                      of the rows).  A copy-kernel probe with these reads over
+                                      128 requests x 8 layers of history: each row copy 12 %
+                                      shorter (234 against 265 us). */
 
 /*
  * Eviction policies.  LRU is the method (paper abstract; note, section 2); the others exist
@@ -137,6 +154,9 @@ typedef struct hs_state_view {
   int64_t page_tokens;   /* tokens per slot (1 = token-granular)                        */
   uint32_t* fresh_slots; /* [max_requests][(B + 31) / 32] bits: slots appended since the  */
                          /* last resolve (their stamp is already the next step's)        */
+  uint8_t* tail_plane;   /* HS_FLAG_RESIDENT_TAIL: [max_requests][capacity][tail_bytes], the */
+                         /* last tail_bytes bytes of each history row; NULL otherwise     */
+  int64_t tail_bytes;    /* 16 with HS_FLAG_RESIDENT_TAIL, else 0                         */
 } hs_state_view;
 
 /* Bytes the device block must have for this configuration (0 and an error if invalid). */
@@ -241,7 +261,9 @@ hs_status hs_topk(hs_handle* h, int32_t n_req, const float* d_scores, int64_t sc
  * introduction: KV is actively offloaded to host memory).  Device tables are untouched: the
  * tokens arrive on the device as misses when a selection names them.  Stream-ordered: one
  * flat device-to-host copy when row_stride equals the entry size, a zero-copy store kernel
- * for 16-byte-aligned padded rows, a 2-D copy otherwise.  HS_ERR_INVALID_ARG for a range
+ * for 16-byte-aligned padded rows, a 2-D copy otherwise.  With HS_FLAG_RESIDENT_TAIL each
+ * row's last 16 bytes go to the tail plane instead (the store kernel for 16-byte-aligned
+ * rows, else two 2-D copies).  HS_ERR_INVALID_ARG for a range
  * outside [0, capacity * page_tokens) or row_stride < entry bytes.
  */
 hs_status hs_offload(hs_handle* h, int32_t layer, int32_t request, int64_t first, int64_t count,
@@ -347,7 +369,9 @@ hs_status hs_destroy(hs_handle* h);
 /*
  * Host rows of (layer, request): *ptr = first of `*capacity` token rows (the
  * page-table capacity times page_tokens), `*row_stride` bytes apart, in pinned
- * memory owned by the handle (valid until hs_destroy).
+ * memory owned by the handle (valid until hs_destroy).  With HS_FLAG_RESIDENT_TAIL a
+ * host row is the row's first 640 bytes (row_stride 640) and the rest is in the tail
+ * plane.
  * The caller writes a token's row before any selection names it, directly or
  * through hs_offload / hs_append; resolves read it for misses.
  * HS_ERR_UNSUPPORTED with HS_FLAG_NO_IO (no host pool).

@@ -56,6 +56,9 @@ def _lib():
         fn.restype = None
     lib.synth_fill_rows.argtypes = [ctypes.c_uint64, i64, i64, i64, i64, ctypes.c_int, p, p, p, i64, ctypes.c_int]
     lib.synth_rows_at.argtypes = [ctypes.c_uint64, i64, i64, p, i64, ctypes.c_int, p, p, p, i64, ctypes.c_int]
+    lib.synth_fill_rows_split.restype = None
+    lib.synth_fill_rows_split.argtypes = [ctypes.c_uint64, i64, i64, i64, i64, ctypes.c_int, p, p, p, i64, i64, p,
+                                          i64, ctypes.c_int]
     lib.synth_e4m3_encode.restype = ctypes.c_uint8
     lib.synth_e4m3_encode.argtypes = [ctypes.c_float]
     lib.synth_mix64.restype = ctypes.c_uint64
@@ -88,6 +91,18 @@ def fill_rows(seed: int, r: int, l: int, pos0: int, count: int, layout: int, dst
     nt = nthreads or min(16, os.cpu_count() or 1)
     _lib().synth_fill_rows(seed, r, l, pos0, count, layout, tb.ctypes.data, tf.ctypes.data,
                            ctypes.c_void_p(dst_ptr), stride, nt)
+
+
+def fill_rows_split(seed: int, r: int, l: int, pos0: int, count: int, layout: int, dst_ptr: int, stride: int,
+                    body: int, tail_ptr: int, tail_stride: int, nthreads: int | None = None) -> None:
+    """The rows of :func:`fill_rows`, split: the first ``body`` bytes of row i at
+    ``dst_ptr + i*stride``, the remaining bytes at ``tail_ptr + i*tail_stride``."""
+    if not 0 < body < ENTRY_BYTES[layout]:
+        raise ValueError("body must lie strictly inside a row")
+    tb, tf = normal_tables()
+    nt = nthreads or min(16, os.cpu_count() or 1)
+    _lib().synth_fill_rows_split(seed, r, l, pos0, count, layout, tb.ctypes.data, tf.ctypes.data,
+                                 ctypes.c_void_p(dst_ptr), stride, body, ctypes.c_void_p(tail_ptr), tail_stride, nt)
 
 
 def rows_at(seed: int, r: int, l: int, positions, layout: int, nthreads: int | None = None) -> np.ndarray:

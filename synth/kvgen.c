@@ -99,19 +99,31 @@ typedef struct {
   const float* tf;
   uint8_t* dst;
   int64_t stride;
+  int64_t body;      /* split rows: bytes of each row written at dst (0: whole rows) */
+  uint8_t* tail;     /* split rows: the rest of each row, at tail + i * tail_stride */
+  int64_t tail_stride;
 } job_t;
 
 static void* run_job(void* p) {
   job_t* j = (job_t*)p;
+  const int64_t E = j->layout == 0 ? 1152 : 656;
+  uint8_t row[1152];
   for (int64_t i = j->begin; i < j->end; ++i) {
     int64_t pos = j->pos ? j->pos[i] : j->pos0 + i;
-    make_row(j->seed, j->r, j->l, pos, j->layout, j->tb, j->tf, j->dst + i * j->stride);
+    if (!j->body) {
+      make_row(j->seed, j->r, j->l, pos, j->layout, j->tb, j->tf, j->dst + i * j->stride);
+      continue;
+    }
+    make_row(j->seed, j->r, j->l, pos, j->layout, j->tb, j->tf, row);
+    memcpy(j->dst + i * j->stride, row, (size_t)j->body);
+    memcpy(j->tail + i * j->tail_stride, row + j->body, (size_t)(E - j->body));
   }
   return NULL;
 }
 
-static void run(uint64_t seed, int64_t r, int64_t l, const int64_t* pos, int64_t pos0, int64_t count,
-                int layout, const uint16_t* tb, const float* tf, uint8_t* dst, int64_t stride, int nthreads) {
+static void run_split(uint64_t seed, int64_t r, int64_t l, const int64_t* pos, int64_t pos0, int64_t count,
+                      int layout, const uint16_t* tb, const float* tf, uint8_t* dst, int64_t stride,
+                      int64_t body, uint8_t* tail, int64_t tail_stride, int nthreads) {
   if (nthreads < 1) nthreads = 1;
   if (nthreads > 256) nthreads = 256;
   if (count < 4096) nthreads = 1;
@@ -119,11 +131,16 @@ static void run(uint64_t seed, int64_t r, int64_t l, const int64_t* pos, int64_t
   job_t jobs[256];
   for (int t = 0; t < nthreads; ++t) {
     jobs[t] = (job_t){seed, r, l, pos, pos0, count * t / nthreads, count * (t + 1) / nthreads,
-                      layout, tb, tf, dst, stride};
+                      layout, tb, tf, dst, stride, body, tail, tail_stride};
   }
   for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, run_job, &jobs[t]);
   run_job(&jobs[0]);
   for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
+}
+
+static void run(uint64_t seed, int64_t r, int64_t l, const int64_t* pos, int64_t pos0, int64_t count,
+                int layout, const uint16_t* tb, const float* tf, uint8_t* dst, int64_t stride, int nthreads) {
+  run_split(seed, r, l, pos, pos0, count, layout, tb, tf, dst, stride, 0, NULL, 0, nthreads);
 }
 
 /* Rows for positions pos0 .. pos0+count-1 of (request r, layer l), written at dst + i*stride. */
@@ -143,3 +160,12 @@ void synth_rows_at(uint64_t seed, int64_t r, int64_t l, const int64_t* pos, int6
 /* Exposed for the generator's own tests. */
 uint8_t synth_e4m3_encode(float v) { return e4m3_encode(v); }
 uint64_t synth_mix64(uint64_t z) { return mix64(z); }
+
+/* The same rows split in two: the first `body` bytes of row i at dst + i*stride, the rest at
+   tail + i*tail_stride (0 < body < entry bytes). */
+void synth_fill_rows_split(uint64_t seed, int64_t r, int64_t l, int64_t pos0, int64_t count, int layout,
+                           const uint16_t* tbl_bf16, const float* tbl_f32, uint8_t* dst, int64_t stride,
+                           int64_t body, uint8_t* tail, int64_t tail_stride, int nthreads) {
+  run_split(seed, r, l, NULL, pos0, count, layout, tbl_bf16, tbl_f32, dst, stride, body, tail, tail_stride,
+            nthreads);
+}

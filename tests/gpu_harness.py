@@ -21,10 +21,29 @@ def say(*a):
 
 
 def fill_host_pool(hs: hsa.HiSparse, seed: int, requests: int | None = None, layers: int | None = None):
+    """Writes every history row of the handle from the seeded generator; with the resident-tail
+    layout the host part of each row goes to the host pool and the rest to the tail plane."""
     for l in range(hs.L if layers is None else layers):
+        tails = hs.tail_plane(l) if hs.tail_bytes else None
         for r in range(hs.n if requests is None else requests):
             ptr, cap, stride = hs.host_kv_ptr(l, r)
-            skv.fill_rows(seed, r, l, 0, cap, hs.layout, ptr, stride)
+            if tails is None:
+                skv.fill_rows(seed, r, l, 0, cap, hs.layout, ptr, stride)
+            else:
+                stage = np.empty((cap, hs.tail_bytes), dtype=np.uint8)
+                skv.fill_rows_split(seed, r, l, 0, cap, hs.layout, ptr, stride, stride, stage.ctypes.data,
+                                    hs.tail_bytes)
+                tails[r].copy_(torch.from_numpy(stage))
+    torch.cuda.synchronize()
+
+
+def history(hs: hsa.HiSparse, layer: int, request: int) -> np.ndarray:
+    """[capacity][entry bytes] copy of a request's whole history rows: the host pool, joined
+    with the tail plane under the resident-tail layout."""
+    host = hs.host_kv(layer, request).copy()
+    if not hs.tail_bytes:
+        return host
+    return np.concatenate([host, hs.tail_plane(layer)[request].cpu().numpy()], axis=1)
 
 
 def oracle_host(seed: int, n: int, L: int, cap: int, layout: int) -> np.ndarray:

@@ -50,7 +50,9 @@ hipError_t launch_append_pages(const Geometry&, const LayerTables&, uint8_t*, in
                                int64_t, int32_t*, int32_t*, hipStream_t) {
   return hipErrorNotSupported;
 }
-hipError_t launch_offload(const void*, int64_t, uint8_t*, int64_t, int64_t, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_offload(const void*, int64_t, uint8_t*, int64_t, int64_t, uint8_t*, int64_t, hipStream_t) {
+  return hipErrorNotSupported;
+}
 hipError_t launch_topk(const Geometry&, int32_t, const float*, int64_t, const int32_t*, int32_t*, int32_t*,
                        hipStream_t) {
   return hipErrorNotSupported;

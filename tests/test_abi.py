@@ -59,6 +59,10 @@ def _cfg(**kw):
     (dict(top_k=2048, device_buffer_size=2048, page_tokens=64), hsa.HS_ERR_UNSUPPORTED),   # 131072 tokens
     (dict(device_buffer_size=16384, host_to_device_ratio=1, page_tokens=256), hsa.HS_ERR_UNSUPPORTED),  # > 4 GiB
     (dict(device_buffer_size=4096, host_to_device_ratio=4096, page_tokens=256), hsa.HS_ERR_INVALID_ARG),  # 2^32 tokens
+    # the resident tail needs token-granular 656-byte rows and a host pool
+    (dict(flags=hsa.FLAG_RESIDENT_TAIL, layout=hsa.LAYOUT_BF16), hsa.HS_ERR_INVALID_ARG),
+    (dict(flags=hsa.FLAG_RESIDENT_TAIL, layout=hsa.LAYOUT_FP8, page_tokens=16), hsa.HS_ERR_INVALID_ARG),
+    (dict(flags=hsa.FLAG_RESIDENT_TAIL | hsa.FLAG_NO_IO, layout=hsa.LAYOUT_FP8), hsa.HS_ERR_INVALID_ARG),
 ])
 def test_create_rejects_bad_config_before_hip(kw, status):
     cfg = _cfg(**kw)
@@ -103,6 +107,18 @@ def test_page_sizes():
                layout=hsa.LAYOUT_FP8, page_tokens=1)
     assert hsa.device_bytes(_cfg(top_k=128, device_buffer_size=256, host_to_device_ratio=8, max_requests=4,
                                  num_heads=0, layout=hsa.LAYOUT_FP8, page_tokens=0)) == hsa.device_bytes(tok)
+
+
+def test_resident_tail_sizes():
+    # 656-byte rows: the host pool keeps 640 bytes per token row, the device adds 16 bytes per
+    # token of history (the tail plane) to the packed layout's block
+    kw = dict(top_k=128, device_buffer_size=256, host_to_device_ratio=8, max_requests=4, num_heads=16,
+              layout=hsa.LAYOUT_FP8, num_layers=3)
+    packed, tail = _cfg(**kw), _cfg(flags=hsa.FLAG_RESIDENT_TAIL, **kw)
+    assert hsa.host_bytes(packed) == 3 * 4 * 2048 * 656
+    assert hsa.host_bytes(tail) == 3 * 4 * 2048 * 640
+    plane = 3 * 4 * 2048 * 16
+    assert plane <= hsa.device_bytes(tail) - hsa.device_bytes(packed) <= plane + 256
 
 
 def test_null_arguments():

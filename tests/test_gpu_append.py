@@ -13,7 +13,9 @@ import oracle
 from synth import configs as C
 from synth import kv as skv
 
-from gpu_harness import fill_host_pool, lru_order_ok, say, trace_for
+from gpu_harness import fill_host_pool, history, lru_order_ok, say, trace_for
+
+TAIL = hsa.FLAG_RESIDENT_TAIL
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")]
@@ -38,17 +40,17 @@ def _check_tables(hs, orc, nr, layer=0, rows=True):
         assert not bool(st["zero_row"].any()), "zero row written"
 
 
-@pytest.mark.parametrize("layout", [hsa.LAYOUT_BF16, hsa.LAYOUT_FP8])
-def test_append_interleaved_with_resolve_matches_oracle(layout):
+@pytest.mark.parametrize("layout,flags", [(hsa.LAYOUT_BF16, 0), (hsa.LAYOUT_FP8, 0), (hsa.LAYOUT_FP8, TAIL)])
+def test_append_interleaved_with_resolve_matches_oracle(layout, flags):
     n, B, k, ratio, seed = 3, 64, 24, 4, 77
     cap = ratio * B
-    say(f"append vs oracle: layout {layout}, n {n}, B {B}, k {k}, cap {cap}")
+    say(f"append vs oracle: layout {layout}, flags {flags}, n {n}, B {B}, k {k}, cap {cap}")
     rng = np.random.default_rng(5)
-    hs = hsa.HiSparse(k, B, ratio, n, 1, layout)
+    hs = hsa.HiSparse(k, B, ratio, n, 1, layout, flags=flags)
     try:
         fill_host_pool(hs, seed)
         E = skv.ENTRY_BYTES[layout]
-        host = np.stack([np.stack([hs.host_kv(0, r).copy()]) for r in range(n)])  # [n][1][cap][E]
+        host = np.stack([np.stack([history(hs, 0, r)]) for r in range(n)])  # [n][1][cap][E]
         orc = oracle.OracleCache(n, 1, B, cap, layout=layout, host=np.ascontiguousarray(host))
         nxt = np.array([10, 20, 30])
         for step in range(40):
@@ -73,7 +75,7 @@ def test_append_interleaved_with_resolve_matches_oracle(layout):
             assert (slots_d.cpu().numpy() == slots_o).all() and (miss_d.cpu().numpy() == miss_o).all()
             _check_tables(hs, orc, n)
         for r in range(n):
-            assert (hs.host_kv(0, r) == orc.host[r, 0]).all(), f"host history differs (request {r})"
+            assert (history(hs, 0, r) == orc.host[r, 0]).all(), f"host history differs (request {r})"
         assert hs.device_error() == 0
     finally:
         hs.close()
@@ -122,15 +124,16 @@ def test_append_out_of_range_sets_error_and_changes_nothing():
         hs.close()
 
 
-def test_append_and_resolve_in_a_graph_replay_like_eager():
+@pytest.mark.parametrize("flags", [0, TAIL])
+def test_append_and_resolve_in_a_graph_replay_like_eager(flags):
     n, B, k, ratio, seed = 4, 128, 48, 4, 9
     cap = ratio * B
-    say("append + resolve captured in a graph, replayed per step")
+    say(f"append + resolve captured in a graph, replayed per step, flags {flags}")
     rng = np.random.default_rng(11)
-    hs = hsa.HiSparse(k, B, ratio, n, 1, hsa.LAYOUT_FP8)
+    hs = hsa.HiSparse(k, B, ratio, n, 1, hsa.LAYOUT_FP8, flags=flags)
     try:
         fill_host_pool(hs, seed)
-        host = np.stack([np.stack([hs.host_kv(0, r).copy()]) for r in range(n)])
+        host = np.stack([np.stack([history(hs, 0, r)]) for r in range(n)])
         orc = oracle.OracleCache(n, 1, B, cap, layout=hsa.LAYOUT_FP8, host=np.ascontiguousarray(host))
         pos_d = torch.zeros(n, dtype=torch.int32, device="cuda")
         rows_d = torch.zeros(n, 656, dtype=torch.uint8, device="cuda")
@@ -171,21 +174,26 @@ def test_append_and_resolve_in_a_graph_replay_like_eager():
         hs.close()
 
 
-@pytest.mark.parametrize("pad", [0, 48, 5])  # flat copy, store kernel, 2-D copy
-def test_offload_writes_history_rows(pad):
+# without the tail plane: flat copy, store kernel, 2-D copy; with it: store kernel (0, 48),
+# two 2-D copies (5)
+@pytest.mark.parametrize("flags", [0, TAIL])
+@pytest.mark.parametrize("pad", [0, 48, 5])
+def test_offload_writes_history_rows(pad, flags):
     n, B, k, ratio = 2, 64, 16, 8
     cap = ratio * B
     E = 656
-    say(f"offload: row stride {E + pad}")
+    say(f"offload: row stride {E + pad}, flags {flags}")
     rng = np.random.default_rng(3 + pad)
-    hs = hsa.HiSparse(k, B, ratio, n, 1, hsa.LAYOUT_FP8)
+    hs = hsa.HiSparse(k, B, ratio, n, 1, hsa.LAYOUT_FP8, flags=flags)
     try:
-        before = hs.host_kv(0, 1).copy()
+        before = history(hs, 0, 1)
         first, count = 37, 300
         rows = rng.integers(0, 256, size=(count, E + pad), dtype=np.uint8)
         hs.offload(0, 1, first, torch.from_numpy(rows).cuda())
         torch.cuda.synchronize()
-        after = hs.host_kv(0, 1)
+        after = history(hs, 0, 1)
+        if flags:   # request 0's tails (zero, like the whole device block at creation) are untouched
+            assert not hs.tail_plane(0)[0].any()
         assert (after[first:first + count] == rows[:, :E]).all()
         assert (after[:first] == before[:first]).all() and (after[first + count:] == before[first + count:]).all()
         # the offloaded rows arrive as misses and land in their slots unchanged

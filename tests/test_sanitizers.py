@@ -80,7 +80,9 @@ def test_host_api_under_asan_and_ubsan(tmp_path):
                    layout=1, num_heads=16),
               dict(top_k=128, device_buffer_size=256, host_to_device_ratio=9, max_requests=4, layout=1, num_heads=16,
                    page_tokens=16),
-              dict(top_k=8192, device_buffer_size=16384, host_to_device_ratio=2, max_requests=2, flags=3)]
+              dict(top_k=8192, device_buffer_size=16384, host_to_device_ratio=2, max_requests=2, flags=3),
+              dict(top_k=2048, device_buffer_size=4096, host_to_device_ratio=16, max_requests=128, num_layers=8,
+                   layout=1, num_heads=16, flags=4)]
         bad = [dict(top_k=0, device_buffer_size=8, host_to_device_ratio=1, max_requests=1),
                dict(top_k=9, device_buffer_size=8, host_to_device_ratio=1, max_requests=1),
                dict(top_k=8, device_buffer_size=8, host_to_device_ratio=0, max_requests=1),
@@ -88,6 +90,7 @@ def test_host_api_under_asan_and_ubsan(tmp_path):
                dict(top_k=8, device_buffer_size=8, host_to_device_ratio=1, max_requests=1, num_heads=17),
                dict(top_k=8, device_buffer_size=8, host_to_device_ratio=1, max_requests=1, flags=0x80),
                dict(top_k=8, device_buffer_size=8, host_to_device_ratio=1, max_requests=1, page_tokens=3),
+               dict(top_k=8, device_buffer_size=8, host_to_device_ratio=1, max_requests=1, flags=4),
                dict(top_k=8, device_buffer_size=8, host_to_device_ratio=1 << 30, max_requests=1 << 30),
                dict(top_k=1 << 20, device_buffer_size=1 << 20, host_to_device_ratio=1, max_requests=1)]
         for kw in ok:
