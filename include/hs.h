@@ -217,7 +217,8 @@ hs_status hs_fetch_misses(hs_handle* h, int32_t layer, int32_t n_req, void* stre
  * actively offloaded to host memory; paper abstract: each request's full KV history lives in
  * host memory).  For each request r < n_req with d_pos[r] >= 0:
  *   - the row at d_rows + r * row_stride (entry_bytes bytes, device memory) is written to
- *     position d_pos[r] of the request's history in the host pool;
+ *     position d_pos[r] of the request's history in the host pool (with
+ *     HS_FLAG_RESIDENT_TAIL its last 16 bytes to the tail plane);
  *   - the token becomes resident before the next resolve: it keeps its slot if it has one,
  *     otherwise it takes the first slot in (stamp, slot) order -- empty slots first -- whose
  *     token leaves the page table; the slot's bytes become the row and its stamp the step
