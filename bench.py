@@ -505,6 +505,7 @@ def bench_attend(args, torch, hsa, w, legs=True):
     del flush
     hs_noio.close()
     res_ms = [region_ms / args.steps - att_graph_us / 1e3]
+    tail = bench_resident_tail_leg(args, torch, hsa, w, hs, d_trace, stream, timed)
     overlap = bench_overlap_leg(args, torch, hsa, w, hs, d_trace, qs, miss, stream, timed, scale, region_ms) \
         if legs else None
     append = bench_append_leg(args, torch, hsa, w, d_trace, miss, stream, timed) if legs else None
@@ -536,6 +537,7 @@ def bench_attend(args, torch, hsa, w, legs=True):
         "misses_per_selection": float(m.mean()),
         "append": append,
         "attend_while_fetching": overlap,
+        "resident_tail": tail,
         # resolution (table work, no row copies) + attention against HBM, over the sum of their
         # times: per selection 16k + 4B + 16m bytes of tables plus the attention bytes
         "hbm_resolve_plus_attend": {
@@ -571,6 +573,51 @@ def measure_d2h_peak(torch, nbytes=1 << 30, reps=5):
     ms = a.elapsed_time(b) / reps
     del src, dst
     return nbytes / ms / 1e6
+
+
+def bench_resident_tail_leg(args, torch, hsa, w, hs, d_trace, stream, timed):
+    """The fused resolve (tables and row copies in one kernel per request) alone, K steps in one
+    graph, on the packed handle and on a handle with the resident-tail layout (each row's first
+    640 bytes in the host pool, five 128-byte lines over the link instead of six; the last 16
+    bytes in device memory), back to back on the same GPU.  Both start from an empty buffer and
+    replay the same trace; misses, slots and the final slot bytes must be identical."""
+    K, W = args.steps, args.warmup
+    T = W + K
+
+    def resolve_only(h):
+        slots = torch.empty(T, w.n, w.k, dtype=torch.int32, device="cuda")
+        miss = torch.zeros(T, w.n, dtype=torch.int32, device="cuda")
+        h.reset_requests(0, w.n, stream=stream)
+        with torch.cuda.stream(stream):
+            for t in range(W):
+                h.resolve(0, d_trace[t], slots[t], miss[t], stream=stream)
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for t in range(W, T):
+                    h.resolve(0, d_trace[t], slots[t], miss[t], stream=stream)
+        us = timed(g) / K * 1e3
+        del g
+        return us, slots, miss
+
+    packed_us, p_slots, p_miss = resolve_only(hs)
+    ht = hsa.HiSparse(w.k, w.B, w.ratio, w.n, 1, w.layout, 16, hsa.FLAG_RESIDENT_TAIL)
+    fill_history(torch, ht, w)
+    tail_us, t_slots, t_miss = resolve_only(ht)
+    occ = hs.state(0)["slot_owner"] >= 0       # slots filled since the reset (others keep old bytes)
+    same = torch.equal(p_slots, t_slots) and torch.equal(p_miss, t_miss) and \
+        torch.equal(hs.state(0)["slot_owner"], ht.state(0)["slot_owner"]) and \
+        torch.equal(hs.state(0)["kv_buffer"][occ], ht.state(0)["kv_buffer"][occ])
+    ht.close()
+    misses = float(p_miss[W:].double().sum()) / K
+    log(f"fused resolve alone: packed rows {packed_us:.1f} us, resident tail {tail_us:.1f} us per step "
+        f"(identical results: {same})")
+    return {"packed_resolve_us_per_step": packed_us, "resolve_us_per_step": tail_us,
+            "speedup": packed_us / tail_us, "identical_to_packed": bool(same),
+            "packed_link_GBps": misses * w.entry_bytes / (packed_us * 1e-6) / 1e9,
+            "link_GBps": misses * (w.entry_bytes - 16) / (tail_us * 1e-6) / 1e9,
+            "link_bytes_per_miss": w.entry_bytes - 16, "tail_bytes_per_token_on_device": 16}
 
 
 def bench_overlap_leg(args, torch, hsa, w, hs, d_trace, qs, miss_serial, stream, timed, scale, serial_ms):
@@ -1321,7 +1368,8 @@ def bench_extras(args, torch, hsa):
     c1["unit"] = res["unit"]
     att = bench_attend(args, torch, hsa, C.FP8_256, legs=False)
     keep = ("value", "unit", "ms_per_step", "resolve_noio_us_per_step", "resolve_noio_cold_us_per_step",
-            "attention_f32_output_us", "misses_per_selection", "hbm_resolve_plus_attend", "roofline", "config")
+            "attention_f32_output_us", "misses_per_selection", "hbm_resolve_plus_attend", "resident_tail", "roofline",
+            "config")
     c2 = {k: att[k] for k in keep}
     return {"resolve_64_requests_bf16": c1, "resolve_attend_256_requests_fp8": c2}
 

@@ -1,7 +1,8 @@
 """Checkpoint and resume through the state views: the tables, the fresh-slot bits, the slot
-buffer and the host rows, exported from one handle between steps and copied into a fresh
-handle of the same configuration, continue the run exactly -- every later slot, miss count,
-attention output and table equals the uninterrupted run's, bit for bit."""
+buffer and the host rows (with the resident-tail layout also the tail plane), exported from one
+handle between steps and copied into a fresh handle of the same configuration, continue the run
+exactly -- every later slot, miss count, attention output and table equals the uninterrupted
+run's, bit for bit."""
 import math
 
 import numpy as np
@@ -22,8 +23,12 @@ KEYS = ("page_table", "slot_owner", "slot_stamp", "lru_order", "step", "fresh_sl
 SCALE = 1.0 / math.sqrt(576)
 
 
+def _keys(hs):
+    return KEYS + (("tail_plane",) if hs.tail_bytes else ())
+
+
 def _export(hs):
-    dev = [{key: hs.state(l)[key].clone() for key in KEYS} for l in range(hs.L)]
+    dev = [{key: hs.state(l)[key].clone() for key in _keys(hs)} for l in range(hs.L)]
     host = [[hs.host_kv(l, r).copy() for r in range(hs.n)] for l in range(hs.L)]
     return dev, host
 
@@ -32,7 +37,7 @@ def _import(hs, snap):
     dev, host = snap
     for l in range(hs.L):
         st = hs.state(l)
-        for key in KEYS:
+        for key in _keys(hs):
             st[key].copy_(dev[l][key])
         for r in range(hs.n):
             np.copyto(hs.host_kv(l, r), host[l][r])
@@ -42,20 +47,21 @@ def _import(hs, snap):
 def _same_state(a, b):
     for l in range(a.L):
         sa, sb = a.state(l), b.state(l)
-        for key in KEYS:
+        for key in _keys(a):
             assert torch.equal(sa[key], sb[key]), f"layer {l}: {key} differs"
         for r in range(a.n):
             assert np.array_equal(a.host_kv(l, r), b.host_kv(l, r)), f"layer {l} request {r}: host rows differ"
 
 
-@pytest.mark.parametrize("policy", [hsa.EVICT_LRU, hsa.EVICT_FIFO])
-def test_resume_with_appends_and_attention(policy):
+@pytest.mark.parametrize("policy,flags", [(hsa.EVICT_LRU, 0), (hsa.EVICT_FIFO, 0),
+                                          (hsa.EVICT_LRU, hsa.FLAG_RESIDENT_TAIL)])
+def test_resume_with_appends_and_attention(policy, flags):
     w = C.FP8_256.with_(n=6, k=256, B=512, ratio=8, steps=14, ctx=3000, window=32)
     L, s = 2, 6
-    say(f"resume: policy {policy}, n {w.n}, layers {L}, k {w.k}, B {w.B}, export at step {s}")
+    say(f"resume: policy {policy}, flags {flags}, n {w.n}, layers {L}, k {w.k}, B {w.B}, export at step {s}")
     x = tr.generate(w.trace_spec())
-    a = hsa.HiSparse(w.k, w.B, w.ratio, w.n, L, w.layout, 16, eviction=policy)
-    b = hsa.HiSparse(w.k, w.B, w.ratio, w.n, L, w.layout, 16, eviction=policy)
+    a = hsa.HiSparse(w.k, w.B, w.ratio, w.n, L, w.layout, 16, flags, eviction=policy)
+    b = hsa.HiSparse(w.k, w.B, w.ratio, w.n, L, w.layout, 16, flags, eviction=policy)
     try:
         fill_host_pool(a, w.seed)
         fill_host_pool(b, w.seed + 1)                      # different rows until the import
