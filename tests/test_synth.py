@@ -77,6 +77,23 @@ def test_c_rows_equal_numpy_restatement(layout):
     assert (big[[0, 1, 2, 77]] == a[:4]).all()
 
 
+@pytest.mark.parametrize("layout,body", [(skv.LAYOUT_FP8, 640), (skv.LAYOUT_BF16, 1024), (skv.LAYOUT_FP8, 16)])
+def test_split_rows_equal_whole_rows(layout, body):
+    """The split writer (host part of each row at one stride, the rest at another, as the
+    resident-tail layout stores them) writes exactly the whole rows' bytes, threaded or not."""
+    E = skv.ENTRY_BYTES[layout]
+    whole = np.empty((6000, E), np.uint8)
+    skv.fill_rows(77, 2, 1, 300, 6000, layout, whole.ctypes.data, E, nthreads=4)
+    head = np.full((6000, body + 32), 0xAB, np.uint8)          # a padded stride: the pad must stay
+    tail = np.empty((6000, E - body), np.uint8)
+    skv.fill_rows_split(77, 2, 1, 300, 6000, layout, head.ctypes.data, body + 32, body, tail.ctypes.data, E - body,
+                        nthreads=4)
+    assert (head[:, :body] == whole[:, :body]).all() and (head[:, body:] == 0xAB).all()
+    assert (tail == whole[:, body:]).all()
+    with pytest.raises(ValueError):
+        skv.fill_rows_split(77, 2, 1, 0, 1, layout, head.ctypes.data, E, E, tail.ctypes.data, 16)
+
+
 def test_normal_table_statistics():
     tb, tf = skv.normal_tables()
     assert abs(float(tf.mean())) < 1e-6 and abs(float(tf.std()) - 1.0) < 2e-3
