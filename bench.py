@@ -803,7 +803,9 @@ def bench_topk(args, torch, hsa):
     """On-GPU top-k from synthetic indexer scores feeding the resolver, one selection per layer
     (128 requests, 8 layers, 65536-token contexts, k 2048, B 4096, fp8 entries).  Scores follow
     the recipe of synth/scores.py -- per-(request, layer) importance, per-step noise 0.08,
-    +100 on the last 128 positions -- drawn on the device from a seeded generator."""
+    +100 on the last 128 positions -- drawn on the device from a seeded generator.  The steps
+    run the hinted top-k (hs_topk_hinted, one hint per layer carried from step to step, as in a
+    decode loop); the top-k launches are also timed alone, without and with hints."""
     import oracle
     from oracle.topk import topk as topk_oracle
     n, L, ctx, k, B, W = 128, 8, 65536, 2048, 4096, 128
@@ -822,12 +824,13 @@ def bench_topk(args, torch, hsa):
     sel = torch.empty(T, L, n, k, dtype=torch.int32, device="cuda")
     slots = torch.empty(L, n, k, dtype=torch.int32, device="cuda")
     miss = torch.zeros(T, L, n, dtype=torch.int32, device="cuda")
+    hints = torch.full((L, n), -1, dtype=torch.int32, device="cuda")   # no guess before the first step
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
 
     def step(t):
         for l in range(L):
-            hs.topk(scores[t, l], lens, sel[t, l], stream=stream)
+            hs.topk(scores[t, l], lens, sel[t, l], stream=stream, hint=hints[l])
             hs.resolve(l, sel[t, l], slots[l], miss[t, l], stream=stream)
 
     def timed(g):
@@ -851,12 +854,24 @@ def bench_topk(args, torch, hsa):
                 step(t)
     step_ms = timed(g) / K
     gt = torch.cuda.CUDAGraph()
+    sel_plain = torch.empty_like(sel)
     with torch.cuda.stream(stream):
         with torch.cuda.graph(gt, stream=stream):
             for t in range(warm, T):
                 for l in range(L):
-                    hs.topk(scores[t, l], lens, sel[t, l], stream=stream)
+                    hs.topk(scores[t, l], lens, sel_plain[t, l], stream=stream)
     topk_us = timed(gt) / (K * L) * 1e3
+    # the top-k alone with hints (each launch's guess is the previous step's result for that
+    # layer; the replay's first step takes the last step's): the same selections
+    gh = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(gh, stream=stream):
+            for t in range(warm, T):
+                for l in range(L):
+                    hs.topk(scores[t, l], lens, sel[t, l], stream=stream, hint=hints[l])
+    topk_hinted_us = timed(gh) / (K * L) * 1e3
+    hinted_same = bool(torch.equal(sel[warm:], sel_plain[warm:]))
+    del gt, gh, sel_plain
     # a sampled check against the oracle, and the oracle's own rate on the same rows
     rows = scores[T - 1, 3, :8].cpu().numpy()
     t0 = time.perf_counter()
@@ -864,7 +879,7 @@ def bench_topk(args, torch, hsa):
     cpu_s = time.perf_counter() - t0
     ok = bool((sel[T - 1, 3, :8].cpu().numpy() == want).all())
     bytes_launch = n * (ctx * 4 + k * 4 + 4)
-    achieved = bytes_launch / (topk_us * 1e-6) / 1e9
+    achieved = bytes_launch / (topk_hinted_us * 1e-6) / 1e9
     m = miss[warm:].double()
     s_prev, s_last = sel[T - 2].cpu().numpy(), sel[T - 1].cpu().numpy()
     churn = float(np.mean([k - np.intersect1d(s_prev[l, r], s_last[l, r]).size for l in range(L) for r in range(0, n, 16)]))
@@ -878,13 +893,17 @@ def bench_topk(args, torch, hsa):
                                "fp8 656 B, indexer scores: importance + 0.08 noise + recency 128",
                    "global_batch": n, "layers": L, "seq_len": ctx, "top_k": k},
         "topk_us_per_launch": topk_us,
+        "topk_hinted_us_per_launch": topk_hinted_us,
+        "topk_hinted_equals_plain": hinted_same,
+        "topk_plain_frac_of_hbm": bytes_launch / (topk_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
         "resolve_noio_plus_topk_us_per_layer": step_ms * 1e3 / L,
         "misses_per_selection": m.mean().item(),
         "history_churn_per_step": churn,
         "topk_verified_rows": ok,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": recorded_traffic("topk_c4", "topk.hip"),
-                     "kernel": "topk_kernel", "avg_kernel_us": topk_us, "algorithmic_bytes_per_launch": bytes_launch},
+                     "kernel": "topk_kernel (hinted)", "avg_kernel_us": topk_hinted_us,
+                     "algorithmic_bytes_per_launch": bytes_launch},
         "cpu_baseline": {"value": 8 * k / cpu_s, "unit": "selected positions/s", "cores": 1, "kind": "oracle",
                          "sample": f"oracle top-k (numpy stable sort) of 8 rows of {ctx} scores"},
     }

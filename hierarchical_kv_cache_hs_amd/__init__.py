@@ -45,7 +45,7 @@ SYMBOLS = ("hs_create", "hs_resolve", "hs_resolve_tables", "hs_fetch_misses", "h
            "hs_device_bytes", "hs_host_bytes", "hs_host_kv",
            "hs_device_state", "hs_reset_requests", "hs_get_device_error", "hs_status_string",
            "hs_last_error_message", "hs_stream_read", "hs_attend_resident", "hs_attend_fetched",
-           "hs_attend_noalloc")
+           "hs_attend_noalloc", "hs_topk_hinted")
 
 
 class Config(ctypes.Structure):
@@ -89,6 +89,7 @@ def lib():
         L.hs_fetch_misses.argtypes = [p, i32, i32, p]
         L.hs_append.argtypes = [p, i32, i32, p, p, ctypes.c_int64, p, p]
         L.hs_topk.argtypes = [p, i32, p, ctypes.c_int64, p, p, p]
+        L.hs_topk_hinted.argtypes = [p, i32, p, ctypes.c_int64, p, p, p, p]
         L.hs_offload.argtypes = [p, i32, i32, ctypes.c_int64, ctypes.c_int64, p, ctypes.c_int64, p]
         L.hs_attend.argtypes = [p, i32, i32, p, p, ctypes.c_float, p, p, p]
         L.hs_attend_pages.argtypes = [p, i32, i32, p, p, p, p, ctypes.c_float, p, p, p]
@@ -279,17 +280,25 @@ class HiSparse:
                                slot_out.data_ptr(), _stream_ptr(stream)))
         return slot_out
 
-    def topk(self, scores: torch.Tensor, lens: torch.Tensor, sel: torch.Tensor | None = None, stream=None):
-        """hs_topk: scores float32 [n_req][stride] (stride % 4 == 0), lens int32 [n_req] -> sel [n_req][top_k]."""
+    def topk(self, scores: torch.Tensor, lens: torch.Tensor, sel: torch.Tensor | None = None, stream=None,
+             hint: torch.Tensor | None = None):
+        """hs_topk: scores float32 [n_req][stride] (stride % 4 == 0), lens int32 [n_req] -> sel [n_req][top_k].
+        With ``hint`` (int32 [n_req], in/out, -1 = no guess; keep one per layer across steps),
+        hs_topk_hinted: the same selection, in one pass over a row whose guess is right."""
         n_req = scores.shape[0]
         _require(scores.dtype == torch.float32 and scores.dim() == 2 and scores.stride(1) == 1)
         _require(lens.dtype == torch.int32 and lens.is_contiguous() and lens.shape[0] == n_req)
         if sel is None:
             sel = torch.empty(n_req, self.top_k, dtype=torch.int32, device=scores.device)
         _require(sel.shape == (n_req, self.top_k) and sel.dtype == torch.int32 and sel.is_contiguous())
-        self._on_device(scores, lens, sel)
-        _check(lib().hs_topk(self._h, n_req, scores.data_ptr(), scores.stride(0), lens.data_ptr(), sel.data_ptr(),
-                             _stream_ptr(stream)))
+        self._on_device(scores, lens, sel, hint)
+        if hint is None:
+            _check(lib().hs_topk(self._h, n_req, scores.data_ptr(), scores.stride(0), lens.data_ptr(), sel.data_ptr(),
+                                 _stream_ptr(stream)))
+        else:
+            _require(hint.dtype == torch.int32 and hint.is_contiguous() and hint.shape == (n_req,))
+            _check(lib().hs_topk_hinted(self._h, n_req, scores.data_ptr(), scores.stride(0), lens.data_ptr(),
+                                        sel.data_ptr(), hint.data_ptr(), _stream_ptr(stream)))
         return sel
 
     def offload(self, layer: int, request: int, first: int, rows: torch.Tensor, stream=None):

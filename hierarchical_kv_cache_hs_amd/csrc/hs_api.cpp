@@ -657,18 +657,34 @@ hs_status hs_offload(hs_handle* h, int32_t layer, int32_t request, int64_t first
   return HS_OK;
 }
 
-hs_status hs_topk(hs_handle* h, int32_t n_req, const float* d_scores, int64_t score_stride, const int32_t* d_len,
-                  int32_t* d_sel, void* stream) {
+namespace {
+
+hs_status topk_impl(hs_handle* h, int32_t n_req, const float* d_scores, int64_t score_stride, const int32_t* d_len,
+                    int32_t* d_sel, int32_t* d_hint, void* stream) {
   if (!h) return fail(HS_ERR_INVALID_ARG, "handle is NULL");
   if (n_req < 0 || n_req > h->g.n) return fail(HS_ERR_INVALID_ARG, "n_req out of range");
   if (n_req == 0) return HS_OK;
   if (!d_scores || !d_len || !d_sel) return fail(HS_ERR_INVALID_ARG, "score, length or output pointer is NULL");
   if (score_stride < 4 || score_stride % 4 || ((uintptr_t)d_scores) % 16)
     return fail(HS_ERR_INVALID_ARG, "scores must be 16-byte aligned with a row stride that is a multiple of 4");
-  hipError_t e = hs::launch_topk(h->g, n_req, d_scores, score_stride, d_len, d_sel, h->err, (hipStream_t)stream);
+  hipError_t e =
+      hs::launch_topk(h->g, n_req, d_scores, score_stride, d_len, d_sel, d_hint, h->err, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "top-k launch");
   note_work(h, stream);
   return HS_OK;
+}
+
+}  // namespace
+
+hs_status hs_topk(hs_handle* h, int32_t n_req, const float* d_scores, int64_t score_stride, const int32_t* d_len,
+                  int32_t* d_sel, void* stream) {
+  return topk_impl(h, n_req, d_scores, score_stride, d_len, d_sel, nullptr, stream);
+}
+
+hs_status hs_topk_hinted(hs_handle* h, int32_t n_req, const float* d_scores, int64_t score_stride,
+                         const int32_t* d_len, int32_t* d_sel, int32_t* d_hint, void* stream) {
+  if (h && n_req > 0 && !d_hint) return fail(HS_ERR_INVALID_ARG, "hint pointer is NULL (use hs_topk)");
+  return topk_impl(h, n_req, d_scores, score_stride, d_len, d_sel, d_hint, stream);
 }
 
 hs_status hs_reset_requests(hs_handle* h, int32_t first, int32_t count, void* stream) {

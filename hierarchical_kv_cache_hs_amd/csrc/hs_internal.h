@@ -91,8 +91,10 @@ void prepare_topk();
 
 // Top-k selection from indexer scores: for each request, the top_k positions of largest
 // score in [0, len[r]) (ties to the smaller position), ascending; -1 padding when len < k.
+// hint (or null): per request, in a guess and out the exact top 12-bit digit of the k-th
+// largest key (-1: none); the selection does not depend on it.
 hipError_t launch_topk(const Geometry& g, int32_t n_req, const float* scores, int64_t stride, const int32_t* len,
-                       int32_t* sel, int32_t* err, hipStream_t s);
+                       int32_t* sel, int32_t* hint, int32_t* err, hipStream_t s);
 
 // Once per process, before the first attention launch.
 void prepare_attend();

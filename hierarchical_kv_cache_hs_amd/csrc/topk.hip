@@ -169,6 +169,7 @@ struct TopkArgs {
   const int32_t* len;  // [n]
   int32_t* sel;        // [n][k]
   int32_t* err;
+  int32_t* hint;       // [n] in/out: top digit of the k-th largest key (guess in, exact out), or null
   int64_t cap;
   int32_t k;
 };
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(TT) void topk_kernel(TopkArgs a) {
   uint32_t* cpos = ckey + CMAX;          //        and positions
   __shared__ uint32_t wtot[TW];
   __shared__ uint64_t wtot64[TW];
-  __shared__ uint32_t s_digit, s_above, s_ncand;
+  __shared__ uint32_t s_digit, s_above, s_ncand, s_nabove;
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -190,11 +191,15 @@ __global__ __launch_bounds__(TT) void topk_kernel(TopkArgs a) {
   int32_t* out = a.sel + (int64_t)r * k;
   const int64_t len = a.len[r];
   if (len < 0 || len > a.cap || len > a.stride || len > MAXLEN) {
-    if (tid == 0) atomicOr(a.err, (int32_t)HS_DEVERR_TOKEN_RANGE);
+    if (tid == 0) {
+      atomicOr(a.err, (int32_t)HS_DEVERR_TOKEN_RANGE);
+      if (a.hint) a.hint[r] = -1;
+    }
     for (int i = tid; i < k; i += TT) out[i] = -1;
     return;
   }
   if (len <= k) {  // every position, then padding
+    if (tid == 0 && a.hint) a.hint[r] = -1;
     for (int i = tid; i < k; i += TT) out[i] = (i < len) ? i : -1;
     return;
   }
@@ -202,80 +207,125 @@ __global__ __launch_bounds__(TT) void topk_kernel(TopkArgs a) {
   const int nw = (n + 31) >> 5;
   const uint32_t* row = (const uint32_t*)(a.scores + (int64_t)r * a.stride);
 
-  // ---- pass A: top digit
-  // Two interleaved copies of the histogram, chosen by lane parity, in the candidate list (not
-  // yet in use): lanes of a wave that hit one digit split over two adjacent words in different
-  // banks, which halves the same-address serialisation of the LDS atomics (the scores crowd
-  // into a few dozen digits); pass A 7.8 -> 7.2 us at 128 x 65536 (four copies: 7.6)
-  uint32_t* hist2 = ckey;  // [2 NBIN] <= CMAX
-  for (int i = tid; i < 2 * NBIN; i += TT) hist2[i] = 0u;
+  // ---- pass B, for the top digits dlo .. dhi: keys above dhi -> selection bitmap (and counted
+  // in s_nabove), keys inside -> candidate list.  A thread masks its candidates in a batch; one
+  // wave scan and one LDS atomic per wave place them.
+  auto classify = [&](uint32_t dlo, uint32_t dhi) {
+    uint32_t nabove = 0;
+    for_each_batch<U>(row, n, [&](u32x4 (&key)[U], int b0) {
+      uint32_t cmask = 0;
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        // a thread's four positions of a tile share one bitmap word: one atomic per tile
+        const int p = b0 + j * TILE + 4 * tid;
+        uint32_t nib = 0;
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const uint32_t u = key[j][e];
+          const uint32_t dg = u >> 20;
+          nib |= (dg > dhi ? 1u : 0u) << e;
+          cmask |= (dg >= dlo && dg <= dhi && u != 0u ? 1u : 0u) << (j * V + e);
+        }
+        if (nib) {
+          atomicOr(&selmap[p >> 5], nib << (p & 31));
+          nabove += __popc(nib);
+        }
+      }
+      const uint32_t c = __popc(cmask);
+      const uint32_t incl = wave_scan_incl(c);
+      uint32_t base = 0;
+      if (lane == 63 && incl) base = atomicAdd(&s_ncand, incl);
+      uint32_t idx = __shfl(base, 63) + incl - c;
+      // candidates are rare: walk the set bits and take each score again (an L2 hit) rather
+      // than branching over every slot of the batch
+      while (cmask) {
+        const int sb = __ffs(cmask) - 1;
+        cmask &= cmask - 1u;
+        const int p = b0 + (sb / V) * TILE + 4 * tid + (sb % V);
+        if (idx < (uint32_t)CMAX) {
+          ckey[idx] = order_key(row[p]);
+          cpos[idx] = (uint32_t)p;
+        }
+        ++idx;
+      }
+    });
+    const uint32_t total = wave_scan_incl(nabove);
+    if (lane == 63 && total) atomicAdd(&s_nabove, total);
+  };
+
   for (int i = tid; i < nw; i += TT) {
     selmap[i] = 0u;
     tiemap[i] = 0u;
   }
-  if (tid == 0) s_ncand = 0;
-  __syncthreads();
-  {
-    // padding (key 0) lands in digit 0, which the search never reaches since len > k
-    const uint32_t c = (uint32_t)(tid & 1);
-    for_each_key<U>(row, n, [&](uint32_t u, int) { atomicAdd(&hist2[((u >> 20) << 1) | c], 1u); });
+  if (tid == 0) {
+    s_ncand = 0;
+    s_nabove = 0;
   }
+  const int32_t h_in = a.hint ? a.hint[r] : -1;
+  bool hinted = h_in >= 0 && h_in < NBIN;  // the same in every thread
   __syncthreads();
-  for (int i = tid; i < NBIN; i += TT) hist[i] = hist2[2 * i] + hist2[2 * i + 1];
-  __syncthreads();
-  find_digit(hist, NBIN - 1, (uint32_t)k, wtot, &s_digit, &s_above);
-  const uint32_t d1 = s_digit;
-  const uint32_t in_d1 = hist[d1];        // keys with top digit d1
-  uint32_t need = (uint32_t)k - s_above;  // keys to take among those with top digit d1
-
-  // ---- pass B: above d1 -> selection bitmap; equal to d1 -> candidate list.  A thread masks
-  // its candidates in a batch; one wave scan and one LDS atomic per wave place them.
-  for_each_batch<U>(row, n, [&](u32x4 (&key)[U], int b0) {
-    uint32_t cmask = 0;
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
-      // a thread's four positions of a tile share one bitmap word: one atomic per tile
-      const int p = b0 + j * TILE + 4 * tid;
-      uint32_t nib = 0;
-#pragma unroll
-      for (int e = 0; e < V; ++e) {
-        const uint32_t u = key[j][e];
-        nib |= ((u >> 20) > d1 ? 1u : 0u) << e;
-        cmask |= ((u >> 20) == d1 && u != 0u ? 1u : 0u) << (j * V + e);
+  uint32_t d1 = 0, need = 0, prefix = 0;
+  int fixed = 0;
+  bool all_taken = false;
+  if (hinted) {
+    // ---- with a guess of the top digit (as from the previous decode step, whose scores moved
+    // little): one pass collects the keys of the digit and its two neighbours; when the k-th
+    // largest key is among them the histogram pass is not needed, and the levels below
+    // resolve all 32 bits over the list
+    const uint32_t dlo = h_in > 0 ? (uint32_t)h_in - 1u : 0u;
+    const uint32_t dhi = h_in < NBIN - 1 ? (uint32_t)h_in + 1u : (uint32_t)(NBIN - 1);
+    classify(dlo, dhi);
+    __syncthreads();
+    const uint32_t above = s_nabove, nc = s_ncand;
+    hinted = nc <= (uint32_t)CMAX && above < (uint32_t)k && (uint32_t)k <= above + nc;
+    need = (uint32_t)k - above;
+    __syncthreads();  // every thread has read the counts
+    if (!hinted) {    // the guess missed: start over on the exact path
+      for (int i = tid; i < nw; i += TT) selmap[i] = 0u;
+      if (tid == 0) {
+        s_ncand = 0;
+        s_nabove = 0;
       }
-      if (nib) atomicOr(&selmap[p >> 5], nib << (p & 31));
     }
-    const uint32_t c = __popc(cmask);
-    const uint32_t incl = wave_scan_incl(c);
-    uint32_t base = 0;
-    if (lane == 63 && incl) base = atomicAdd(&s_ncand, incl);
-    uint32_t idx = __shfl(base, 63) + incl - c;
-    // candidates are rare: walk the set bits and take each score again (an L2 hit) rather
-    // than branching over every slot of the batch
-    while (cmask) {
-      const int sb = __ffs(cmask) - 1;
-      cmask &= cmask - 1u;
-      const int p = b0 + (sb / V) * TILE + 4 * tid + (sb % V);
-      if (idx < (uint32_t)CMAX) {
-        ckey[idx] = order_key(row[p]);
-        cpos[idx] = (uint32_t)p;
-      }
-      ++idx;
+  }
+  if (!hinted) {
+    // ---- pass A: top digit
+    // Two interleaved copies of the histogram, chosen by lane parity, in the candidate list
+    // (not yet in use): lanes of a wave that hit one digit split over two adjacent words in
+    // different banks, which halves the same-address serialisation of the LDS atomics (the
+    // scores crowd into a few dozen digits); pass A 7.8 -> 7.2 us at 128 x 65536 (four copies: 7.6)
+    uint32_t* hist2 = ckey;  // [2 NBIN] <= CMAX
+    for (int i = tid; i < 2 * NBIN; i += TT) hist2[i] = 0u;
+    __syncthreads();
+    {
+      // padding (key 0) lands in digit 0, which the search never reaches since len > k
+      const uint32_t c = (uint32_t)(tid & 1);
+      for_each_key<U>(row, n, [&](uint32_t u, int) { atomicAdd(&hist2[((u >> 20) << 1) | c], 1u); });
     }
-  });
-  __syncthreads();
+    __syncthreads();
+    for (int i = tid; i < NBIN; i += TT) hist[i] = hist2[2 * i] + hist2[2 * i + 1];
+    __syncthreads();
+    find_digit(hist, NBIN - 1, (uint32_t)k, wtot, &s_digit, &s_above);
+    d1 = s_digit;
+    const uint32_t in_d1 = hist[d1];  // keys with top digit d1
+    need = (uint32_t)k - s_above;     // keys to take among those with top digit d1
+    classify(d1, d1);
+    __syncthreads();
+    prefix = d1;
+    fixed = 12;
+    all_taken = in_d1 == need;
+  }
   const uint32_t ncand = s_ncand;
-  const bool overflow = ncand > (uint32_t)CMAX;
+  const bool overflow = ncand > (uint32_t)CMAX;  // only on the exact path (a guess is refused)
 
-  // ---- the next 12 bits, then the last 8: over the list, or over the row on overflow.  When
-  // every key of the digit just chosen is taken (its count equals `need`), no tie is left to
-  // resolve and the remaining levels are skipped: the threshold drops to just below that
-  // digit's range and nothing is taken at it.
-  uint32_t prefix = d1;
-  int fixed = 12;
-  bool all_taken = in_d1 == need;
-  for (int level = 0; level < 2 && !all_taken; ++level) {
-    const int bits = level == 0 ? 12 : 8;
+  // ---- the remaining digits (after the guessed bracket all three: 12, 12 and 8 bits; after
+  // pass A the next 12 and the last 8), over the list, or over the row on overflow.  When every
+  // key of the digit just chosen is taken (its count equals `need`), no tie is left to resolve
+  // and the remaining levels are skipped: the threshold drops to just below that digit's range
+  // and nothing is taken at it.
+  const int nlev = hinted ? 3 : 2;
+  for (int level = 0; level < nlev && !all_taken; ++level) {
+    const int bits = level == nlev - 1 ? 8 : 12;
     const int shift = 32 - fixed - bits;
     const uint32_t dmask = (1u << bits) - 1u;
     for (int i = tid; i < NBIN; i += TT) hist[i] = 0u;
@@ -283,7 +333,7 @@ __global__ __launch_bounds__(TT) void topk_kernel(TopkArgs a) {
     if (!overflow) {
       for (uint32_t i = tid; i < ncand; i += TT) {
         const uint32_t u = ckey[i];
-        if ((u >> (32 - fixed)) == prefix) atomicAdd(&hist[(u >> shift) & dmask], 1u);
+        if (fixed == 0 || (u >> (32 - fixed)) == prefix) atomicAdd(&hist[(u >> shift) & dmask], 1u);
       }
     } else {
       for_each_key<U>(row, n, [&](uint32_t u, int) {
@@ -296,7 +346,8 @@ __global__ __launch_bounds__(TT) void topk_kernel(TopkArgs a) {
     prefix = (prefix << bits) | s_digit;
     need -= s_above;
     fixed += bits;
-    all_taken = in_d == need;  // the same in every thread
+    if (fixed == 12) d1 = prefix;  // after a guessed bracket: the top digit, found over the list
+    all_taken = in_d == need;      // the same in every thread
     __syncthreads();
   }
   // the k-th largest key, `need` of the keys equal to it taken; or, with all_taken, one below
@@ -383,6 +434,7 @@ __global__ __launch_bounds__(TT) void topk_kernel(TopkArgs a) {
     }
     out[i] = (int32_t)(lo * 32 + (int)pos);
   }
+  if (tid == 0 && a.hint) a.hint[r] = (int32_t)d1;  // exact: the next call's guess
 }
 
 }  // namespace
@@ -394,8 +446,9 @@ void prepare_topk() {
 }
 
 hipError_t launch_topk(const Geometry& g, int32_t n_req, const float* scores, int64_t stride, const int32_t* len,
-                       int32_t* sel, int32_t* err, hipStream_t s) {
+                       int32_t* sel, int32_t* hint, int32_t* err, hipStream_t s) {
   TopkArgs a;
+  a.hint = hint;
   a.scores = scores;
   a.stride = stride;
   a.len = len;

@@ -256,6 +256,23 @@ hs_status hs_topk(hs_handle* h, int32_t n_req, const float* d_scores, int64_t sc
                   int32_t* d_sel, void* stream);
 
 /*
+ * hs_topk for a decode loop: the same selection, computed with one pass over the score row
+ * instead of two when a guess of where the k-th largest score lies is right.  Consecutive
+ * steps of a request and layer have nearly the same scores (the note, section 2: the indexer
+ * scores every token at every step), so the previous call's result is such a guess.
+ *   d_hint  [n_req] int32 in/out: in, the value this call wrote for the same request and layer
+ *           at the previous step (or -1: no guess); out, the value for the next call (-1 when
+ *           len[r] <= top_k or the row is rejected).  It is the top 12 bits of the k-th largest
+ *           score's order key (scores mapped to 32-bit keys whose unsigned order is the float
+ *           order, -0 joined with +0); a guess g is used when that score's 12-bit digit lies
+ *           within g - 1 .. g + 1, and otherwise costs one extra pass over the row.
+ * d_sel is bit for bit that of hs_topk for any d_hint contents.  HS_ERR_INVALID_ARG for a
+ * NULL d_hint; other arguments as hs_topk.  Enqueue-only, graph-capturable.
+ */
+hs_status hs_topk_hinted(hs_handle* h, int32_t n_req, const float* d_scores, int64_t score_stride,
+                         const int32_t* d_len, int32_t* d_sel, int32_t* d_hint, void* stream);
+
+/*
  * Prefill offload: copies count rows (device memory, row_stride bytes apart) into positions
  * first .. first + count - 1 (token positions, also with pages) of request `request`'s
  * history in the host pool (the note's

@@ -54,7 +54,7 @@ hipError_t launch_offload(const void*, int64_t, uint8_t*, int64_t, int64_t, uint
   return hipErrorNotSupported;
 }
 hipError_t launch_topk(const Geometry&, int32_t, const float*, int64_t, const int32_t*, int32_t*, int32_t*,
-                       hipStream_t) {
+                       int32_t*, hipStream_t) {
   return hipErrorNotSupported;
 }
 hipError_t launch_stream_read(const void*, size_t, uint32_t*, hipStream_t) { return hipErrorNotSupported; }
