@@ -26,7 +26,13 @@
 //            last word whose count below is <= i, found by a binary search, so consecutive
 //            threads write consecutive outputs, with no sort.
 // If the candidate list would overflow (many equal scores), the last two digits are resolved
-// with re-reads of the row instead.  Reads are batched: eight 16-byte loads per thread are in
+// with re-reads of the row instead.
+// With a hint (hs_topk_hinted: per request a guess g of the top digit, as returned for the same
+// request and layer at the previous decode step), one pass sets the positions whose top digit
+// exceeds g + 1 in the selection bitmap, counts them, and lists the keys of digits g - 1 .. g + 1.
+// If the count shows the k-th largest key among them (and the list did not overflow), pass A is
+// skipped and the levels resolve all three digits (12, 12, 8 bits) over the list; otherwise the
+// bitmap is cleared and the two passes run as above.  The digit found is written back.  Reads are batched: eight 16-byte loads per thread are in
 // flight before any is used, and batches that lie wholly inside the row skip the per-key
 // bounds checks (the passes over the row are bound by VALU work per key and the histogram's
 // LDS atomics, not by the reads).
@@ -291,7 +297,7 @@ __global__ __launch_bounds__(TT) void topk_kernel(TopkArgs a) {
   if (!hinted) {
     // ---- pass A: top digit
     // Two interleaved copies of the histogram, chosen by lane parity, in the candidate list
-    // (not yet in use): lanes of a wave that hit one digit split over two adjacent words in
+    // (pass B rebuilds it): lanes of a wave that hit one digit split over two adjacent words in
     // different banks, which halves the same-address serialisation of the LDS atomics (the
     // scores crowd into a few dozen digits); pass A 7.8 -> 7.2 us at 128 x 65536 (four copies: 7.6)
     uint32_t* hist2 = ckey;  // [2 NBIN] <= CMAX
