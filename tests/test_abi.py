@@ -141,6 +141,7 @@ def test_new_entry_points_reject_bad_arguments_before_hip():
     assert L.hs_attend_resident(None, 0, 1, None, None, None, None, f, None) == hsa.HS_ERR_INVALID_ARG
     assert L.hs_attend_fetched(None, 0, 1, None, None, f, None, None, None) == hsa.HS_ERR_INVALID_ARG
     assert L.hs_attend_noalloc(None, 0, 1, 16, None, None, f, None, None, None) == hsa.HS_ERR_INVALID_ARG
+    assert L.hs_topk_hinted(None, 1, None, 4, None, None, None, None) == hsa.HS_ERR_INVALID_ARG
     sink = ctypes.c_uint32()
     assert L.hs_stream_read(None, 16, ctypes.byref(sink), None) == hsa.HS_ERR_INVALID_ARG
     buf = (ctypes.c_uint8 * 64)()

@@ -124,6 +124,7 @@ def test_host_api_under_asan_and_ubsan(tmp_path):
         assert L.hs_append(None, 0, 1, None, None, ctypes.c_int64(656), None, None) == 1
         assert L.hs_offload(None, 0, 0, ctypes.c_int64(0), ctypes.c_int64(1), None, ctypes.c_int64(656), None) == 1
         assert L.hs_topk(None, 1, None, ctypes.c_int64(4), None, None, None) == 1
+        assert L.hs_topk_hinted(None, 1, None, ctypes.c_int64(4), None, None, None, None) == 1
         assert L.hs_host_kv(None, 0, 0, None, None, None) == 1
         assert L.hs_device_state(None, 0, None) == 1
         assert L.hs_reset_requests(None, 0, 1, None) == 1
