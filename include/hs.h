@@ -84,9 +84,9 @@ typedef enum hs_kv_layout {
                                       hs_append / hs_offload write both parts.  Callers that
                                       write history rows themselves write the tails into the
                                       plane.  Cost: 16 bytes of HBM per token of history (2.4 %
-                                      of the rows).  A copy-kernel probe with these reads over
-                                      128 requests x 8 layers of history: each row copy 12 %
-                                      shorter (234 against 265 us). */
+                                      of the rows).  Measured on 256 requests of fp8 rows: the
+                                      fused resolve with its row copies 16 % shorter (387 against
+                                      461 us per step). */
 
 /*
  * Eviction policies.  LRU is the method (paper abstract; note, section 2); the others exist
