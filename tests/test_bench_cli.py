@@ -70,3 +70,25 @@ def test_profile_summary_averages_and_scales(tmp_path):
     assert f"(scaled FETCH + WRITE): {fetch_mb + write_mb:.2f} MB" in out
     assert "other_kernel" not in out
     assert np.isclose(fetch_mb + write_mb, 1.1776)
+
+
+def test_traffic_record_is_used_only_for_the_source_it_was_taken_on(tmp_path, monkeypatch):
+    sys.path.insert(0, ROOT)
+    import bench
+    src = tmp_path / "k.hip"
+    src.write_text("kernel v1\n")
+    rec = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "KERNEL_SRC", str(tmp_path))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(rec))
+    import json
+    rec.write_text(json.dumps({"k": {"bytes_per_launch": 123.0, "source_sha256": bench._sha256(str(src))}}))
+    assert bench.recorded_traffic("k", "k.hip") == 123.0
+    assert bench.recorded_traffic("missing", "k.hip") is None
+    src.write_text("kernel v2\n")                       # any edit voids the record
+    assert bench.recorded_traffic("k", "k.hip") is None
+    # every committed record matches its kernel source as it stands
+    committed = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+    csrc = os.path.join(ROOT, "hierarchical_kv_cache_hs_amd", "csrc")
+    shas = {bench._sha256(os.path.join(csrc, f)) for f in os.listdir(csrc) if f.endswith(".hip")}
+    for key, r in committed.items():
+        assert r["source_sha256"] in shas, f"{key}: traffic record of a kernel source that has changed"
