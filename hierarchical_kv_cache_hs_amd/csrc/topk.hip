@@ -31,8 +31,9 @@
 // request and layer at the previous decode step), one pass sets the positions whose top digit
 // exceeds g + 1 in the selection bitmap, counts them, and lists the keys of digits g - 1 .. g + 1.
 // If the count shows the k-th largest key among them (and the list did not overflow), pass A is
-// skipped and the levels resolve all three digits (12, 12, 8 bits) over the list; otherwise the
-// bitmap is cleared and the two passes run as above.  The digit found is written back.  Reads are batched: eight 16-byte loads per thread are in
+// skipped and two 11-bit levels over the listed keys' offsets from the bracket's lowest key
+// (less than 3 * 2^20) find the k-th largest; otherwise the bitmap is cleared and the two passes
+// run as above.  The digit found is written back.  Reads are batched: eight 16-byte loads per thread are in
 // flight before any is used, and batches that lie wholly inside the row skip the per-key
 // bounds checks (the passes over the row are bound by VALU work per key and the histogram's
 // LDS atomics, not by the reads).
@@ -276,8 +277,7 @@ __global__ __launch_bounds__(TT) void topk_kernel(TopkArgs a) {
   if (hinted) {
     // ---- with a guess of the top digit (as from the previous decode step, whose scores moved
     // little): one pass collects the keys of the digit and its two neighbours; when the k-th
-    // largest key is among them the histogram pass is not needed, and the levels below
-    // resolve all 32 bits over the list
+    // largest key is among them the histogram pass is not needed
     const uint32_t dlo = h_in > 0 ? (uint32_t)h_in - 1u : 0u;
     const uint32_t dhi = h_in < NBIN - 1 ? (uint32_t)h_in + 1u : (uint32_t)(NBIN - 1);
     classify(dlo, dhi);
@@ -324,44 +324,81 @@ __global__ __launch_bounds__(TT) void topk_kernel(TopkArgs a) {
   const uint32_t ncand = s_ncand;
   const bool overflow = ncand > (uint32_t)CMAX;  // only on the exact path (a guess is refused)
 
-  // ---- the remaining digits (after the guessed bracket all three: 12, 12 and 8 bits; after
-  // pass A the next 12 and the last 8), over the list, or over the row on overflow.  When every
-  // key of the digit just chosen is taken (its count equals `need`), no tie is left to resolve
-  // and the remaining levels are skipped: the threshold drops to just below that digit's range
-  // and nothing is taken at it.
-  const int nlev = hinted ? 3 : 2;
-  for (int level = 0; level < nlev && !all_taken; ++level) {
-    const int bits = level == nlev - 1 ? 8 : 12;
-    const int shift = 32 - fixed - bits;
-    const uint32_t dmask = (1u << bits) - 1u;
-    for (int i = tid; i < NBIN; i += TT) hist[i] = 0u;
+  uint32_t thr;
+  if (hinted) {
+    // ---- after the guessed bracket: the listed keys lie within three consecutive top digits,
+    // i.e. within 3 * 2^20 of the bracket's base, so two 11-bit levels over key - base find
+    // the k-th largest key (the top digit falls out of the first)
+    const uint32_t base = (uint32_t)(h_in > 0 ? h_in - 1 : 0) << 20;
+    const uint32_t end = (uint32_t)(h_in < NBIN - 1 ? h_in + 2 : NBIN) << 20;  // 0 for the last digit (2^32)
+    const int topA = (int)((end - base - 1u) >> 11);                          // <= 1535
+    for (int i = tid; i <= topA; i += TT) hist[i] = 0u;
     __syncthreads();
-    if (!overflow) {
-      for (uint32_t i = tid; i < ncand; i += TT) {
-        const uint32_t u = ckey[i];
-        if (fixed == 0 || (u >> (32 - fixed)) == prefix) atomicAdd(&hist[(u >> shift) & dmask], 1u);
-      }
-    } else {
-      for_each_key<U>(row, n, [&](uint32_t u, int) {
-        if (u != 0u && (u >> (32 - fixed)) == prefix) atomicAdd(&hist[(u >> shift) & dmask], 1u);
-      });
-    }
+    for (uint32_t i = tid; i < ncand; i += TT) atomicAdd(&hist[(ckey[i] - base) >> 11], 1u);
     __syncthreads();
-    find_digit(hist, (int)dmask, need, wtot, &s_digit, &s_above);
-    const uint32_t in_d = hist[s_digit];
-    prefix = (prefix << bits) | s_digit;
+    find_digit(hist, topA, need, wtot, &s_digit, &s_above);
+    const uint32_t dA = s_digit, in_a = hist[dA];
     need -= s_above;
-    fixed += bits;
-    if (fixed == 12) d1 = prefix;  // after a guessed bracket: the top digit, found over the list
-    all_taken = in_d == need;      // the same in every thread
+    d1 = (base + (dA << 11)) >> 20;
     __syncthreads();
-  }
-  // the k-th largest key, `need` of the keys equal to it taken; or, with all_taken, one below
-  // the lowest key of the chosen digit's range (keys > 0: the smallest, -inf's, is 0x007FFFFF)
-  uint32_t thr = prefix;
-  if (all_taken) {
-    thr = (prefix << (32 - fixed)) - 1u;
-    need = 0u;
+    if (in_a == need) {  // every key of the bin is taken
+      thr = base + (dA << 11) - 1u;
+      need = 0u;
+    } else {
+      for (int i = tid; i < 2048; i += TT) hist[i] = 0u;
+      __syncthreads();
+      for (uint32_t i = tid; i < ncand; i += TT) {
+        const uint32_t o = ckey[i] - base;
+        if ((o >> 11) == dA) atomicAdd(&hist[o & 0x7FFu], 1u);
+      }
+      __syncthreads();
+      find_digit(hist, 2047, need, wtot, &s_digit, &s_above);
+      const uint32_t in_b = hist[s_digit];
+      need -= s_above;
+      thr = base + (dA << 11) + s_digit;
+      if (in_b == need) {  // every key equal to it is taken: no tie left
+        thr -= 1u;
+        need = 0u;
+      }
+      __syncthreads();
+    }
+  } else {
+    // ---- the next 12 bits, then the last 8: over the list, or over the row on overflow.  When
+    // every key of the digit just chosen is taken (its count equals `need`), no tie is left to
+    // resolve and the remaining levels are skipped: the threshold drops to just below that
+    // digit's range and nothing is taken at it.
+    for (int level = 0; level < 2 && !all_taken; ++level) {
+      const int bits = level == 0 ? 12 : 8;
+      const int shift = 32 - fixed - bits;
+      const uint32_t dmask = (1u << bits) - 1u;
+      for (int i = tid; i < NBIN; i += TT) hist[i] = 0u;
+      __syncthreads();
+      if (!overflow) {
+        for (uint32_t i = tid; i < ncand; i += TT) {
+          const uint32_t u = ckey[i];
+          if ((u >> (32 - fixed)) == prefix) atomicAdd(&hist[(u >> shift) & dmask], 1u);
+        }
+      } else {
+        for_each_key<U>(row, n, [&](uint32_t u, int) {
+          if (u != 0u && (u >> (32 - fixed)) == prefix) atomicAdd(&hist[(u >> shift) & dmask], 1u);
+        });
+      }
+      __syncthreads();
+      find_digit(hist, (int)dmask, need, wtot, &s_digit, &s_above);
+      const uint32_t in_d = hist[s_digit];
+      prefix = (prefix << bits) | s_digit;
+      need -= s_above;
+      fixed += bits;
+      all_taken = in_d == need;  // the same in every thread
+      __syncthreads();
+    }
+    // the k-th largest key, `need` of the keys equal to it taken; or, with all_taken, one below
+    // the lowest key of the chosen digit's range (keys > 0: the smallest, -inf's, is 0x007FFFFF)
+    thr = prefix;
+    if (all_taken) {
+      thr = (prefix << (32 - fixed)) - 1u;
+      need = 0u;
+    }
   }
 
   // ---- candidates above thr are taken; those equal to it are ties
