@@ -166,3 +166,52 @@ def test_hinted_decode_loop_feeds_resolver(graph):
             assert (st["page_table"].cpu().numpy() == orc.PT[:, L - 1]).all()
     finally:
         hs.close()
+
+
+def _key_float(k: int) -> np.float32:
+    """The score whose order key is k (non-NaN keys 0x007FFFFF .. 0xFF800000)."""
+    bits = (k ^ 0x80000000) if (k & 0x80000000) else (~k & 0xFFFFFFFF)
+    return np.array([bits], dtype=np.uint32).view(np.float32)[0]
+
+
+@pytest.mark.parametrize("sign", [1, -1])
+def test_scores_on_digit_edges(sign):
+    """Rows whose scores sit on, one key below and one key above the top-digit edges around the
+    k-th largest score (the bracket's bounds and the plain pass's digit bounds are compared
+    against such floats), with a few hundred ties at the k-th largest: the k-th largest lies on
+    an edge, one key above it, or (rows 3 ..) one key below it.  Plain and hinted selections
+    and the returned digit equal the oracle's for hints at the true digit, one off and two off."""
+    n, k, B, stride = 6, 4000, 4096, 8192
+    say(f"topk digit edges: sign {sign}, k {k}, stride {stride}")
+    rng = np.random.default_rng(77 + sign)
+    hs = hsa.HiSparse(k, B, stride // B, n, 1, hsa.LAYOUT_BF16)
+    try:
+        mid = 0xBF8 if sign > 0 else 0x407                    # digit of +1.0 / of -1.125
+        s = np.empty((n, stride), dtype=np.float32)
+        for r in range(n):
+            keys = [(d << 20) + o for d in range(mid - 3, mid + 4) for o in (-1, 0, 1)]
+            if r >= 3:    # no key on or above the middle digit's lower edge: its top one below
+                keys = [kk for kk in keys if not (kk >> 20 == mid and kk & 0xFFFFF <= 1)]
+            edges = np.array([_key_float(kk) for kk in keys], dtype=np.float32)
+            pick = rng.integers(0, edges.size, size=stride)
+            s[r] = edges[pick]
+            spread = rng.random(stride) < 0.3
+            s[r, spread] = (edges[pick[spread]] * np.float32(1 + 0.01 * rng.standard_normal(spread.sum()))).astype(np.float32)
+        lens = np.full(n, stride)
+        lens[1] = stride - 5                                   # ragged tail
+        want = topk_oracle(s, lens, k)
+        hint_true = expected_hint(s, lens, want, k)
+        s_d = torch.from_numpy(s).cuda()
+        lens_d = torch.from_numpy(lens.astype(np.int32)).cuda()
+        sel = hs.topk(s_d, lens_d)
+        torch.cuda.synchronize()
+        assert (sel.cpu().numpy() == want).all(), "plain selection"
+        for delta in (0, -1, 1, -2, 2):
+            hint = torch.from_numpy((hint_true + delta).astype(np.int32)).cuda()
+            sel = hs.topk(s_d, lens_d, hint=hint)
+            torch.cuda.synchronize()
+            assert (sel.cpu().numpy() == want).all(), f"hint off by {delta}: selection"
+            assert (hint.cpu().numpy() == hint_true).all(), f"hint off by {delta}: digit written back"
+        assert hs.device_error() == 0
+    finally:
+        hs.close()
