@@ -235,3 +235,42 @@ def test_eager_schedule_equals_the_graph(time_fetches):
             assert eager.fetch_events is None
     finally:
         hs.close()
+
+
+@pytest.mark.parametrize("layers", [1, 3, 5])
+def test_prefetch_any_layer_count(layers):
+    """The prefetch schedule's copies wait for tables only at copies 0, 1, 2, 4 (the waits cover
+    the copies between them): with 1, 3 and 5 layers, four steps in one graph give the serial
+    run's miss counts, slots, attention and tables bitwise, and with the last layer's attention
+    split by residency within the bf16 tier."""
+    w = C.PREFETCH.with_(n=6, ctx=8192, ratio=2, layers=layers)
+    T = 4
+    say(f"prefetch, {layers} layers, {T} steps in one graph")
+    x = trace_for(w, steps=T)
+    hs = hsa.HiSparse(w.k, w.B, w.ratio, w.n, w.layers, w.layout, num_heads=16)
+    try:
+        fill_host_pool(hs, w.seed)
+        sels = [torch.from_numpy(x[t]).cuda() for t in range(T)]
+        qs = [_queries(w, t, w.layers) for t in range(T)]
+        ser = DecodeSteps(hs, sels, qs, SCALE, prefetch=False)
+        ser.replay()
+        torch.cuda.synchronize()
+        keys = ("page_table", "slot_owner", "slot_stamp", "step")
+        ser_tables = [tuple(hs.state(l)[k].clone() for k in keys) for l in range(w.layers)]
+        for split_last in (0, 1):
+            hs.reset_requests(0, w.n)
+            torch.cuda.synchronize()
+            pre = DecodeSteps(hs, sels, qs, SCALE, prefetch=True, split_last=split_last)
+            pre.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(ser.miss, pre.miss) and torch.equal(ser.slots, pre.slots)
+            if split_last:
+                assert (ser.out.float() - pre.out.float()).abs().max().item() <= 2e-2
+                assert (ser.lse - pre.lse).abs().max().item() <= 1e-3
+            else:
+                assert torch.equal(ser.out, pre.out) and torch.equal(ser.lse, pre.lse)
+            for l in range(w.layers):
+                for u, k in zip(ser_tables[l], keys):
+                    assert torch.equal(u, hs.state(l)[k]), f"split_last {split_last}, layer {l}: {k} differs"
+    finally:
+        hs.close()
